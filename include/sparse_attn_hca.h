@@ -1,0 +1,210 @@
+/*
+ * sparse_attn_hca.h -- C ABI of the HCA + MLA-DSA forward library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method is the hybrid sparse attention described for ERNIE-5.5-Flash-Base:
+ *
+ *   [P1] aitest123.com, "280B总参数、14B激活！百度开源文心5.5 Flash Base，拿下同尺寸SOTA",
+ *        section 二.1 "Latent-Gated Sparse Attention：37层省缓存，6层保精准检索".
+ *   [P2] qunfachuanzhen.com ERNIE-5.5-Flash-Base news page,
+ *        section "◆ 混合稀疏注意力,把 1M 上下文的成本压下来".
+ *   [P3] communeify.com, "百度 ERNIE 5.5 Flash Base 完整解析：280B 混合注意力 MoE 基座模型…",
+ *        section "六大核心架構創新深度解析", item 1
+ *        "潛在門控混合稀疏注意力（Hybrid MLA-DSA + HCA）與 VHA".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates device memory and keeps no pointer after a call
+ *    returns.  Buffers must stay alive until the enqueued work has finished.
+ *  - Every call only enqueues work on the given stream (NULL = the default
+ *    stream) and never synchronises.  Results are deterministic: the same
+ *    inputs give bit-identical outputs on every run.
+ *  - Inputs are read-only.  Outputs must not alias inputs.
+ *  - Tensors are dense and row-major in the shapes given below, with the last
+ *    (feature) dimension contiguous, unless strides are passed explicitly.
+ *    Every tensor base address must be 16-byte aligned.
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    non-OK status means nothing was enqueued; sa_last_error() then returns a
+ *    human-readable reason (thread-local, valid until the next call on the
+ *    same thread).
+ *  - Device-side CONTENTS (positions, indices) are not validated.  Values
+ *    outside their contract give unspecified results but never out-of-bounds
+ *    memory accesses: positions are clamped and indices outside [0, S) are
+ *    skipped.
+ */
+#ifndef SPARSE_ATTN_HCA_H
+#define SPARSE_ATTN_HCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's own hipStream_t (a typedef may be repeated). */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  SA_ERR_SHAPE = -2,       /* a size is non-positive or sizes are inconsistent  */
+  SA_ERR_UNSUPPORTED = -3, /* (dtype, head dim, ...) combination not compiled   */
+  SA_ERR_ALIGN = -4,       /* a pointer or stride breaks the 16-byte rule       */
+  SA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required        */
+  SA_ERR_HIP = -6          /* the HIP runtime rejected a launch                 */
+} sa_status;
+
+/* Detail for the last non-OK return on this thread ("" if none). */
+const char* sa_last_error(void);
+/* Library version string. */
+const char* sa_version(void);
+
+/* ------------------------------------------------------------------------
+ * hca_compress -- block-mean compression of K or V.
+ *
+ * [P1] §二.1, [P2] §混合稀疏注意力, [P3] §架構創新 1: every 128 consecutive
+ * tokens are pressed into one cache entry.  The pages do not name the
+ * operator; this library uses the arithmetic mean of the block's rows:
+ *
+ *   out[b,h,j,:] = (1/blk) * sum_{i<blk} x[b,h,j*blk+i,:],  j < floor(n_tokens/blk)
+ *
+ * Trailing tokens that do not fill a block produce no entry.
+ * x:   [B,H,n_tokens,d] with element strides (x_sb, x_sh, x_st), d contiguous.
+ * out: [B,H,n_tokens/blk,d] with element strides (o_sb, o_sh, o_sn).
+ * Arithmetic: fp32 sum, one division by blk, rounded (RNE) to the I/O dtype.
+ * Supported: SA_F32 with d in {64, 512}; SA_BF16 with d in {256, 512}.
+ * Strides must be multiples of 16 bytes / sizeof(element).
+ * ------------------------------------------------------------------------ */
+int hca_compress(const void* x, void* out, sa_dtype dtype,
+                 int64_t B, int64_t H, int64_t n_tokens, int64_t d, int64_t blk,
+                 int64_t x_sb, int64_t x_sh, int64_t x_st,
+                 int64_t o_sb, int64_t o_sh, int64_t o_sn,
+                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * hca_attention_fwd -- HCA attention, prefill or decode.
+ *
+ * [P1] §二.1: attention runs only over the compressed entries plus a window of
+ * the most recent uncompressed tokens.  [P3] §架構創新 1: each query attends to
+ * all compressed history entries and the short recent window; heads are 512
+ * wide.  Readings where the pages are silent:
+ *   - compressed entry j (tokens j*blk .. j*blk+blk-1) is visible to the query
+ *     at position t iff (j+1)*blk - 1 <= t - window, i.e. the first
+ *     max(0, floor((t-window+1)/blk)) entries (capped at the cache size);
+ *   - raw tokens t-window < s <= t (s >= 0) form the window;
+ *   - one softmax over both sets with logits scale*<q,k>; no sink/bias/gate.
+ *
+ * PREFILL (mode = HCA_PREFILL), T = seq_len:
+ *   q, k, v, o: [B,H,T,d];  k_c, v_c: [B,H,n_c,d] with n_c = n_c_cap (normally
+ *   T/blk, as written by hca_compress);  query row t sits at position t.
+ * DECODE (mode = HCA_DECODE), one query per sequence:
+ *   q, o: [B,H,d];  k_c, v_c: [B,H,n_c_cap,d];  k, v: the window ring
+ *   [B,H,window,d] where position s lives in slot s mod window;
+ *   pos: device int64[B], the query's position (its own K/V is already in
+ *   the ring).  pos values < 0 are treated as 0.
+ * lse: optional (NULL to skip) fp32 [B,H,T] (prefill) or [B,H] (decode):
+ *   natural-log normaliser of the scaled logits.
+ * scale <= 0 selects 1/sqrt(d).
+ * Arithmetic: bf16 inputs, fp32 accumulation and softmax, probabilities
+ * rounded to bf16 for the P*V product, output rounded (RNE) to the I/O dtype.
+ * Supported: SA_F32 with d = 64 (prefill); SA_BF16 with d = 512.
+ * Workspace: DECODE may need split-K partials; query
+ *   hca_attention_fwd_workspace_size() (0 for PREFILL).
+ * ------------------------------------------------------------------------ */
+typedef enum { HCA_PREFILL = 0, HCA_DECODE = 1 } hca_mode;
+
+typedef struct {
+  hca_mode mode;
+  sa_dtype dtype;
+  int64_t B, H, d;
+  int64_t blk;      /* compression block (128 in the model)               */
+  int64_t window;   /* uncompressed recent window (128)                   */
+  int64_t seq_len;  /* PREFILL: T.  DECODE: ignored                       */
+  int64_t n_c_cap;  /* number of entries in k_c / v_c                     */
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* k_c;
+  const void* v_c;
+  const int64_t* pos; /* DECODE only */
+  void* o;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+} hca_attention_args;
+
+size_t hca_attention_fwd_workspace_size(const hca_attention_args* args);
+int hca_attention_fwd(const hca_attention_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dsa_indexer_scores -- lightweight indexer of MLA-DSA.
+ *
+ * [P1] §二.1 and [P3] §架構創新 1: a lightweight indexer scores every history
+ * position for each query.  The pages give no formula; this library computes
+ *
+ *   scores[b,i,s] = sum_h w[b,i,h] * max(0, <q_idx[b,i,h,:], k_idx[b,s,:]>)
+ *
+ * for every s <= p_i, p_i = q_pos[b] + i (q_pos == NULL: p_i = i).  Entries
+ * with s > p_i are not written (their contents are unspecified).
+ * q_idx: [B,T,Hi,Di] bf16; k_idx: [B,S,Di] bf16 (one key per position, shared
+ * by the indexer heads); w: [B,T,Hi] fp32; scores: [B,T,S] fp32.
+ * Arithmetic: exact bf16 products accumulated in fp32, then fp32 ReLU,
+ * weighting and head sum.
+ * Supported: Di = 128, Hi = 4.
+ * ------------------------------------------------------------------------ */
+int dsa_indexer_scores(const void* q_idx, const void* k_idx, const float* w,
+                       const int64_t* q_pos, float* scores,
+                       int64_t B, int64_t T, int64_t S, int64_t Hi, int64_t Di,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dsa_topk -- exact top-k selection per query row.
+ *
+ * [P1] §二.1 / [P3] §架構創新 1: only the top-K scoring positions are kept.
+ * For row i of batch b the candidates are s <= p_i (p_i as above, capped at
+ * S-1).  The selected set is the first min(k, p_i+1) candidates in the order
+ * (score descending, position ascending): ties go to the lower position and
+ * -0.0 ranks equal to +0.0.  idx[b,i,:] lists the selected positions in
+ * ascending order, padded with -1.  NaN scores are unspecified.
+ * scores: [B,T,S] fp32; idx: [B,T,k] int32.
+ * Integer-exact: comparisons are on order-preserving 32-bit keys.
+ * Supported: 1 <= k <= 2048; S < 2^31.
+ * Workspace: dsa_topk_workspace_size() bytes (rows longer than the on-chip
+ * limit use a multi-workgroup path that needs histograms in global memory).
+ * ------------------------------------------------------------------------ */
+size_t dsa_topk_workspace_size(int64_t B, int64_t T, int64_t S, int64_t k);
+int dsa_topk(const float* scores, const int64_t* q_pos, int32_t* idx,
+             int64_t B, int64_t T, int64_t S, int64_t k,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dsa_sparse_attention_fwd -- exact attention over the selected positions.
+ *
+ * [P1] §二.1 / [P3] §架構創新 1: core attention runs only on the top-K
+ * positions, so its per-query cost is constant in the context length; MLA
+ * heads are 256 wide.  Multi-query layout: all Hq query heads share one K and
+ * one V row per position.
+ *
+ *   o[b,i,h,:] = sum_{s in idx[b,i]} softmax_s(scale*<q[b,i,h], k[b,s]>) * v[b,s,:]
+ *
+ * Entries of idx that are negative or >= S are skipped.  A row with no valid
+ * entry yields o = 0 and lse = -inf.
+ * q, o: [B,T,Hq,D] bf16; k, v: [B,S,D] bf16 (v == k is allowed);
+ * idx: [B,T,kk] int32; lse: optional fp32 [B,T,Hq].  scale <= 0 -> 1/sqrt(D).
+ * Supported: SA_BF16, D = 256, Hq = 64, kk >= 1.
+ * ------------------------------------------------------------------------ */
+int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v,
+                             const int32_t* idx, void* o, float* lse, sa_dtype dtype,
+                             int64_t B, int64_t T, int64_t S, int64_t Hq, int64_t D,
+                             int64_t kk, float scale, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_HCA_H */

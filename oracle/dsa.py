@@ -1,0 +1,105 @@
+"""MLA-DSA (indexer -> top-k -> sparse attention) oracle, float64.  TEST INFRASTRUCTURE ONLY.
+
+What the pages fix ([P1] §二.1, [P3] §架構創新 1):
+  * a lightweight indexer scores every history position for each query;
+  * only the top-k positions by that score are kept;
+  * exact (core) attention runs over those positions only, so its per-query
+    cost does not grow with the context;
+  * MLA heads are 256 wide.
+
+Readings taken where the pages are silent:
+  * indexer score(i, s) = sum_h w[i, h] * max(0, <q_I[i, h], k_I[s]>), one
+    indexer key per position shared by the indexer heads, one weight per
+    (query, head), no scale;
+  * candidates of query i at position p_i are the positions s <= p_i
+    (causal, self included);
+  * selection order is score descending, then position ascending (ties go to
+    the lower position); -0.0 ranks equal to +0.0; when p_i + 1 <= k every
+    candidate is kept;
+  * the index list is returned in ascending position order, padded with -1;
+  * attention is multi-query: all query heads share one K and one V row per
+    position; scale = 1/sqrt(D) unless given.
+"""
+
+import numpy as np
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None):
+    """Indexer scores for every (query, history position) pair.
+
+    q_idx: [B, T, Hi, Di]; k_idx: [B, S, Di]; w: [B, T, Hi];
+    q_pos: [B] position of query row 0 (row i sits at q_pos[b] + i);
+    None means row i sits at position i.
+    Returns [B, T, S] float64; entries with s > p_i (not candidates) are NaN.
+    """
+    q_idx, k_idx, w = map(_f64, (q_idx, k_idx, w))
+    B, T, Hi, Di = q_idx.shape
+    S = k_idx.shape[1]
+    out = np.full((B, T, S), np.nan)
+    for b in range(B):
+        base = 0 if q_pos is None else int(q_pos[b])
+        # dots[i, h, s] = <q_idx[b, i, h], k_idx[b, s]>
+        dots = (q_idx[b].reshape(T * Hi, Di) @ k_idx[b].T).reshape(T, Hi, S)
+        score = (w[b][:, :, None] * np.maximum(dots, 0.0)).sum(axis=1)
+        for i in range(T):
+            p = base + i
+            n = min(p + 1, S)
+            out[b, i, :n] = score[i, :n]
+    return out
+
+
+def dsa_topk(scores, k, q_pos=None):
+    """Top-k history positions per query row.
+
+    scores: [B, T, S]; row i of batch b has candidates s <= p_i with
+    p_i = q_pos[b] + i (or i).  Selection: the first min(k, p_i+1) candidates
+    in the order (score descending, position ascending).  Returned ascending,
+    padded with -1.  Output int64 [B, T, k].
+    """
+    scores = _f64(scores)
+    B, T, S = scores.shape
+    idx = np.full((B, T, k), -1, dtype=np.int64)
+    for b in range(B):
+        base = 0 if q_pos is None else int(q_pos[b])
+        for i in range(T):
+            n_cand = min(base + i + 1, S)
+            cand = scores[b, i, :n_cand] + 0.0  # -0.0 + 0.0 == +0.0
+            pos = np.arange(n_cand)
+            # lexsort: last key is primary -> score descending, then position ascending
+            order = np.lexsort((pos, -cand))
+            sel = np.sort(order[: min(k, n_cand)])
+            idx[b, i, : sel.size] = sel
+    return idx
+
+
+def dsa_sparse_attention(q, k, v, idx, scale=None):
+    """Exact multi-query attention over the selected positions only.
+
+    q: [B, T, Hq, D]; k, v: [B, S, D] (one KV head shared by all Hq query
+    heads); idx: [B, T, kk] with -1 entries skipped.
+    Returns (o [B, T, Hq, D], lse [B, T, Hq]) in float64.  A row with no
+    selected position returns o = 0 and lse = -inf.
+    """
+    q, k, v = map(_f64, (q, k, v))
+    B, T, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.zeros((B, T, Hq, D))
+    lse = np.full((B, T, Hq), -np.inf)
+    for b in range(B):
+        for i in range(T):
+            sel = idx[b, i]
+            sel = sel[sel >= 0]
+            if sel.size == 0:
+                continue
+            logits = scale * (q[b, i] @ k[b, sel].T)  # [Hq, n]
+            m = logits.max(axis=1, keepdims=True)
+            p = np.exp(logits - m)
+            l = p.sum(axis=1, keepdims=True)
+            o[b, i] = (p @ v[b, sel]) / l
+            lse[b, i] = (m + np.log(l))[:, 0]
+    return o, lse

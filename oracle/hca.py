@@ -1,0 +1,136 @@
+"""HCA (Heavily Compressed Attention) oracle, float64.  TEST INFRASTRUCTURE ONLY.
+
+What the pages fix ([P1] §二.1, [P2] §混合稀疏注意力, [P3] §架構創新 1):
+  * every 128 consecutive tokens become one cache entry (128x compression);
+  * a query attends over all compressed history entries plus a short window
+    of recent, uncompressed tokens;
+  * HCA heads are 512 wide.
+
+Readings taken where the pages are silent (each one is stated again in the
+function that uses it):
+  * the compression operator is the arithmetic mean of the block's K (and V)
+    rows; Q is not compressed;
+  * the window is the W most recent tokens, including the query's own token;
+  * a compressed entry j (tokens j*blk .. j*blk+blk-1) is visible to query t
+    iff the whole block lies at or before t-W, i.e. (j+1)*blk-1 <= t-W; the
+    window covers t-W < s <= t.  The two sets never overlap; the tokens of the
+    block that straddles t-W and lie outside the window are seen by neither;
+  * one softmax over the union of both key sets, logits scale*<q, key> with
+    scale = 1/sqrt(d) unless given; no sink, bias or gate.
+"""
+
+import numpy as np
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def hca_compress(x, blk):
+    """Mean of each complete block of ``blk`` consecutive tokens.
+
+    [P1] §二.1 / [P3] §架構創新 1: each run of 128 tokens is pressed into one
+    cache entry.  Reading: the entry is the arithmetic mean of the block's
+    rows.  Incomplete trailing tokens (fewer than ``blk``) form no entry.
+
+    x: [..., T, d]  ->  [..., T // blk, d]  (float64, no rounding of the mean)
+    """
+    x = _f64(x)
+    T, d = x.shape[-2], x.shape[-1]
+    n = T // blk
+    lead = x.shape[:-2]
+    blocks = x[..., : n * blk, :].reshape(*lead, n, blk, d)
+    return blocks.sum(axis=-2) / blk
+
+
+def hca_visible_blocks(t, blk, window):
+    """Number of compressed entries visible to the query at position t.
+
+    Entry j is visible iff (j+1)*blk - 1 <= t - window, so the count is
+    max(0, floor((t - window + 1) / blk)).
+    """
+    return max(0, (t - window + 1) // blk)
+
+
+def hca_window_range(t, window):
+    """Raw positions the query at position t sees uncompressed: (t-window, t], s >= 0."""
+    return max(0, t - window + 1), t + 1  # half-open [lo, hi)
+
+
+def hca_key_set(t, blk, window, n_entries=None):
+    """(visible compressed entry ids, visible raw positions) for query t."""
+    nc = hca_visible_blocks(t, blk, window)
+    if n_entries is not None:
+        nc = min(nc, n_entries)
+    lo, hi = hca_window_range(t, window)
+    return np.arange(nc), np.arange(lo, hi)
+
+
+def _attend(q, keys, vals, scale):
+    """One softmax over the given keys for a batch of heads.
+
+    q: [H, d]; keys, vals: [H, n, d].  Returns (o [H, d], lse [H]).
+    lse is the natural-log normaliser of the scaled logits.
+    """
+    logits = scale * np.einsum("hd,hnd->hn", q, keys)
+    m = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = np.einsum("hn,hnd->hd", p, vals) / l
+    lse = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def hca_attention_prefill(q, k, v, kc, vc, blk, window, scale=None, rows=None):
+    """HCA prefill attention for the query positions ``rows``.
+
+    [P1] §二.1: attention runs over the compressed entries plus a window of
+    the most recent uncompressed tokens.  [P3] §架構創新 1: the query attends
+    to all compressed history entries and the short recent window.
+
+    q, k, v: [B, H, T, d]; kc, vc: [B, H, Nc, d] (the compressed cache; for the
+    plain method Nc = T // blk and kc = hca_compress(k, blk)).
+    rows: iterable of query positions (default: all of 0..T-1).
+    Returns (o [B, H, len(rows), d], lse [B, H, len(rows)]) in float64.
+    """
+    q, k, v, kc, vc = map(_f64, (q, k, v, kc, vc))
+    B, H, T, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows = list(range(T)) if rows is None else [int(t) for t in rows]
+    o = np.zeros((B, H, len(rows), d))
+    lse = np.zeros((B, H, len(rows)))
+    for b in range(B):
+        for r, t in enumerate(rows):
+            cj, rs = hca_key_set(t, blk, window, n_entries=kc.shape[2])
+            keys = np.concatenate([kc[b][:, cj], k[b][:, rs]], axis=1)
+            vals = np.concatenate([vc[b][:, cj], v[b][:, rs]], axis=1)
+            o[b, :, r], lse[b, :, r] = _attend(q[b, :, t], keys, vals, scale)
+    return o, lse
+
+
+def hca_attention_decode(q, kc, vc, ring_k, ring_v, pos, blk, window, scale=None):
+    """HCA decode: one query per sequence at position pos[b].
+
+    Same key set as prefill row t = pos[b] ([P1] §二.1): compressed entries
+    j < min(visible(t), Nc) from the cache, and the window positions
+    t-window < s <= t read from a ring buffer of ``window`` slots where
+    position s lives in slot s mod window.
+
+    q: [B, H, d]; kc, vc: [B, H, Nc, d]; ring_k, ring_v: [B, H, window, d].
+    Returns (o [B, H, d], lse [B, H]).
+    """
+    q, kc, vc, ring_k, ring_v = map(_f64, (q, kc, vc, ring_k, ring_v))
+    B, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.zeros((B, H, d))
+    lse = np.zeros((B, H))
+    for b in range(B):
+        t = int(pos[b])
+        cj, rs = hca_key_set(t, blk, window, n_entries=kc.shape[2])
+        slots = rs % window
+        keys = np.concatenate([kc[b][:, cj], ring_k[b][:, slots]], axis=1)
+        vals = np.concatenate([vc[b][:, cj], ring_v[b][:, slots]], axis=1)
+        o[b], lse[b] = _attend(q[b], keys, vals, scale)
+    return o, lse

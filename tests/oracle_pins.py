@@ -1,0 +1,389 @@
+"""Pins for the float64 oracle: checks against facts other than the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+a closed form, a hand-derived golden value, a library routine (torch CPU
+scaled_dot_product_attention, NumPy matmul / sorted), an invariant of the
+definition, or brute force on tiny inputs.  tests/test_oracle_pins.py runs
+them against the oracle; tests/test_oracle_mutations.py plants plausible
+mistakes in the oracle and checks that at least one pin then fails.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _sdpa_causal(q, k, v):
+    """Dense causal attention from torch's CPU float64 library routine.  q,k,v: [B,H,T,d]."""
+    import torch
+    import torch.nn.functional as F
+
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)) for a in (q, k, v))
+    return F.scaled_dot_product_attention(tq, tk, tv, is_causal=True).numpy()
+
+
+def _close(a, b, tol=1e-12, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err} > {tol}"
+
+
+# ---------------------------------------------------------------------------
+# hca_compress
+# ---------------------------------------------------------------------------
+
+
+def pin_compress_constant_blocks():
+    """A block whose rows all equal one dyadic value compresses to it exactly."""
+    rng = _rng(1)
+    blk, n, d = 8, 5, 3
+    c = rng.integers(-1000, 1000, size=(2, n, d)) / 64.0
+    x = np.repeat(c, blk, axis=1)  # [2, n*blk, d]
+    out = oracle.hca_compress(x, blk)
+    assert out.shape == (2, n, d)
+    assert np.array_equal(out, c), "constant blocks must compress exactly"
+
+
+def pin_compress_ramp():
+    """x[t] = t compresses to the block midpoint j*blk + (blk-1)/2 (exact)."""
+    for blk in (1, 4, 128):
+        T = 5 * blk + (blk // 2)  # ragged tail that must be ignored
+        x = np.arange(T, dtype=np.float64)[:, None] * np.ones((1, 2))
+        out = oracle.hca_compress(x, blk)
+        assert out.shape == (T // blk, 2)
+        want = np.arange(T // blk) * blk + (blk - 1) / 2.0
+        assert np.array_equal(out[:, 0], want), f"ramp midpoint blk={blk}"
+
+
+def pin_compress_bruteforce():
+    rng = _rng(2)
+    B, H, T, d, blk = 2, 3, 13, 4, 3
+    x = rng.standard_normal((B, H, T, d))
+    out = oracle.hca_compress(x, blk)
+    assert out.shape == (B, H, T // blk, d)
+    for b in range(B):
+        for h in range(H):
+            for j in range(T // blk):
+                for e in range(d):
+                    s = 0.0
+                    for i in range(blk):
+                        s += float(x[b, h, j * blk + i, e])
+                    assert abs(out[b, h, j, e] - s / blk) < 1e-14
+
+
+def pin_compress_pages_ratio():
+    """The pages: one cache entry per 128 tokens, context up to 1,048,576 tokens."""
+    c = _load("pages_constants.json")
+    blk = c["tokens_per_compressed_entry"]["value"]
+    for n_tok in (c["pretraining_context_tokens"]["value"], c["max_context_tokens"]["value"]):
+        x = np.zeros((n_tok, 1), dtype=np.float32)
+        assert oracle.hca_compress(x, blk).shape[0] * blk == n_tok
+
+
+# ---------------------------------------------------------------------------
+# HCA attention
+# ---------------------------------------------------------------------------
+
+
+def _hca_inputs(seed, B, H, T, d, blk):
+    rng = _rng(seed)
+    q, k, v = (rng.standard_normal((B, H, T, d)) for _ in range(3))
+    return q, k, v, oracle.hca_compress(k, blk), oracle.hca_compress(v, blk)
+
+
+def pin_hca_blk1_is_dense_causal():
+    """blk = 1: visible entries and window tile 0..t exactly once -> dense causal."""
+    B, H, T, d = 1, 2, 23, 8
+    for window in (1, 3, 7, 40):
+        q, k, v, kc, vc = _hca_inputs(3, B, H, T, d, 1)
+        o, _ = oracle.hca_attention_prefill(q, k, v, kc, vc, 1, window)
+        _close(o, _sdpa_causal(q, k, v), 1e-12, f"blk=1 window={window}")
+
+
+def pin_hca_window_ge_T_is_dense_causal():
+    B, H, T, d = 2, 2, 19, 8
+    for blk in (2, 4, 16):
+        q, k, v, kc, vc = _hca_inputs(4, B, H, T, d, blk)
+        o, _ = oracle.hca_attention_prefill(q, k, v, kc, vc, blk, T)
+        _close(o, _sdpa_causal(q, k, v), 1e-12, f"window>=T blk={blk}")
+
+
+def pin_hca_rows_below_window_are_dense():
+    B, H, T, d, blk, window = 1, 2, 40, 8, 4, 9
+    q, k, v, kc, vc = _hca_inputs(5, B, H, T, d, blk)
+    rows = list(range(window))
+    o, _ = oracle.hca_attention_prefill(q, k, v, kc, vc, blk, window, rows=rows)
+    _close(o, _sdpa_causal(q, k, v)[:, :, :window], 1e-12, "rows t < window")
+
+
+def pin_hca_constant_v():
+    B, H, T, d, blk, window = 1, 2, 50, 4, 4, 6
+    q, k, _, kc, _ = _hca_inputs(6, B, H, T, d, blk)
+    v = np.full((B, H, T, d), 0.375)
+    vc = oracle.hca_compress(v, blk)
+    o, _ = oracle.hca_attention_prefill(q, k, v, kc, vc, blk, window)
+    _close(o, np.full_like(o, 0.375), 1e-14, "constant V")
+
+
+def _literal_weights(q, k, blk, window, t, scale):
+    """Brute force: enumerate every (block, token) and test the visibility rule literally.
+
+    Returns the attention weight each raw token receives (compressed entries
+    spread their weight evenly over their block's tokens)."""
+    T = k.shape[0]
+    keys = []  # (logit, list of (token, share))
+    for j in range(T // blk):
+        end = j * blk + blk - 1  # last token of block j
+        if end <= t - window:
+            mean = [sum(k[j * blk + i][e] for i in range(blk)) / blk for e in range(k.shape[1])]
+            keys.append((scale * sum(a * b for a, b in zip(q, mean)), [(j * blk + i, 1.0 / blk) for i in range(blk)]))
+    for s in range(T):
+        if t - window < s <= t:
+            keys.append((scale * sum(a * b for a, b in zip(q, k[s])), [(s, 1.0)]))
+    m = max(lg for lg, _ in keys)
+    z = sum(math.exp(lg - m) for lg, _ in keys)
+    wts = [0.0] * T
+    for lg, toks in keys:
+        p = math.exp(lg - m) / z
+        for s, share in toks:
+            wts[s] += p * share
+    return wts
+
+
+def pin_hca_identity_v_weights():
+    """V = identity exposes each query's weight on every raw token; compare with brute force."""
+    T, d, blk, window = 24, 24, 4, 6
+    rng = _rng(7)
+    q = rng.standard_normal((1, 1, T, d))
+    k = rng.standard_normal((1, 1, T, d))
+    v = np.eye(T)[None, None]
+    kc, vc = oracle.hca_compress(k, blk), oracle.hca_compress(v, blk)
+    o, _ = oracle.hca_attention_prefill(q, k, v, kc, vc, blk, window)
+    scale = 1.0 / math.sqrt(d)
+    for t in range(T):
+        w = o[0, 0, t]
+        assert abs(w.sum() - 1.0) < 1e-12, "weights sum to one"
+        assert np.all(w[t + 1:] == 0.0), "no weight on future tokens"
+        ref = _literal_weights(q[0, 0, t], k[0, 0], blk, window, t, scale)
+        _close(w, ref, 1e-12, f"identity-V weights t={t}")
+        # gap tokens: in the block straddling t-window, outside the window
+        lo = max(0, t - window + 1)
+        nvis = max(0, (t - window + 1) // blk)
+        for s in range(nvis * blk, lo):
+            assert w[s] == 0.0, f"gap token {s} of query {t} must get no weight"
+
+
+def pin_hca_uniform_golden():
+    """q = 0 makes attention uniform; hand-derived outputs in tests/golden/hca_uniform_q0.json."""
+    g = _load("hca_uniform_q0.json")
+    T, blk, window = g["T"], g["blk"], g["window"]
+    v = np.arange(T, dtype=np.float64).reshape(1, 1, T, 1)
+    k = _rng(8).standard_normal((1, 1, T, 1))
+    q = np.zeros((1, 1, T, 1))
+    o, lse = oracle.hca_attention_prefill(q, k, v, oracle.hca_compress(k, blk), oracle.hca_compress(v, blk), blk, window)
+    for row in g["rows"]:
+        t = row["t"]
+        want = float(Fraction(*row["o"]))
+        assert abs(o[0, 0, t, 0] - want) < 1e-12, f"t={t}: {o[0, 0, t, 0]} != {want}"
+        assert abs(lse[0, 0, t] - math.log(row["n_keys"])) < 1e-12, f"lse t={t}"
+        cj, rs = oracle.hca_key_set(t, blk, window)
+        assert list(cj) == row["visible_blocks"], f"visible blocks t={t}"
+        assert [int(rs[0]), int(rs[-1])] == row["window"], f"window t={t}"
+
+
+def pin_hca_decode_equals_prefill_row():
+    """Decode at position t with the ring holding positions t-window+1..t equals prefill row t."""
+    B, H, T, d, blk, window = 2, 3, 37, 8, 4, 6
+    q, k, v, kc, vc = _hca_inputs(9, B, H, T, d, blk)
+    rows = [0, 3, 5, 6, 11, 20, 36]
+    o_pre, lse_pre = oracle.hca_attention_prefill(q, k, v, kc, vc, blk, window, rows=rows)
+    for r, t in enumerate(rows):
+        ring_k = np.zeros((B, H, window, d))
+        ring_v = np.zeros((B, H, window, d))
+        for s in range(max(0, t - window + 1), t + 1):
+            ring_k[:, :, s % window] = k[:, :, s]
+            ring_v[:, :, s % window] = v[:, :, s]
+        o_dec, lse_dec = oracle.hca_attention_decode(q[:, :, t], kc, vc, ring_k, ring_v, [t] * B, blk, window)
+        _close(o_dec, o_pre[:, :, r], 1e-12, f"decode vs prefill t={t}")
+        _close(lse_dec, lse_pre[:, :, r], 1e-12, f"decode lse t={t}")
+
+
+def pin_hca_head_permutation():
+    B, H, T, d, blk, window = 1, 4, 30, 4, 4, 5
+    q, k, v, kc, vc = _hca_inputs(10, B, H, T, d, blk)
+    perm = [2, 0, 3, 1]
+    o, _ = oracle.hca_attention_prefill(q, k, v, kc, vc, blk, window)
+    op, _ = oracle.hca_attention_prefill(q[:, perm], k[:, perm], v[:, perm], kc[:, perm], vc[:, perm], blk, window)
+    _close(op, o[:, perm], 1e-14, "head permutation")
+
+
+# ---------------------------------------------------------------------------
+# DSA indexer
+# ---------------------------------------------------------------------------
+
+
+def pin_indexer_single_head_is_matmul():
+    """Hi = 1, w = 1, non-negative inputs: ReLU is inactive, scores = q @ k^T."""
+    rng = _rng(11)
+    T, S, Di = 9, 9, 5
+    qi = np.abs(rng.standard_normal((1, T, 1, Di)))
+    ki = np.abs(rng.standard_normal((1, S, Di)))
+    sc = oracle.dsa_indexer_scores(qi, ki, np.ones((1, T, 1)))
+    ref = qi[0, :, 0] @ ki[0].T
+    for i in range(T):
+        _close(sc[0, i, : i + 1], ref[i, : i + 1], 1e-12, f"matmul row {i}")
+        assert np.all(np.isnan(sc[0, i, i + 1:])), "non-candidates are NaN"
+
+
+def pin_indexer_integer_grid_exact():
+    """Inputs on a quarter grid with signs: exact rational brute force (pure Python Fractions)."""
+    rng = _rng(12)
+    B, T, S, Hi, Di = 2, 5, 8, 3, 4
+    qi = rng.integers(-3, 4, size=(B, T, Hi, Di)) / 4.0
+    ki = rng.integers(-3, 4, size=(B, S, Di)) / 4.0
+    w = rng.integers(0, 5, size=(B, T, Hi)) / 4.0
+    q_pos = [2, 0]
+    sc = oracle.dsa_indexer_scores(qi, ki, w, q_pos=q_pos)
+    for b in range(B):
+        for i in range(T):
+            p = q_pos[b] + i
+            for s in range(S):
+                if s > p:
+                    assert np.isnan(sc[b, i, s])
+                    continue
+                tot = Fraction(0)
+                for h in range(Hi):
+                    dot = sum(Fraction(qi[b, i, h, e]) * Fraction(ki[b, s, e]) for e in range(Di))
+                    tot += Fraction(w[b, i, h]) * max(dot, Fraction(0))
+                assert Fraction(sc[b, i, s]) == tot, f"b={b} i={i} s={s}"
+
+
+# ---------------------------------------------------------------------------
+# DSA top-k
+# ---------------------------------------------------------------------------
+
+
+def _brute_topk_row(row, n_cand, k):
+    cands = sorted(range(n_cand), key=lambda s: (-(row[s] + 0.0), s))
+    sel = sorted(cands[: min(k, n_cand)])
+    return sel + [-1] * (k - len(sel))
+
+
+def pin_topk_bruteforce():
+    rng = _rng(13)
+    B, T, S = 2, 12, 12
+    for k in (1, 3, 5, 12, 20):
+        sc = rng.integers(0, 4, size=(B, T, S)).astype(np.float64)  # heavy ties
+        idx = oracle.dsa_topk(sc, k)
+        for b in range(B):
+            for i in range(T):
+                assert list(idx[b, i]) == _brute_topk_row(sc[b, i], i + 1, k), f"k={k} b={b} i={i}"
+
+
+def pin_topk_short_rows_keep_all():
+    sc = _rng(14).standard_normal((1, 6, 6))
+    idx = oracle.dsa_topk(sc, 8)
+    for i in range(6):
+        assert list(idx[0, i]) == list(range(i + 1)) + [-1] * (8 - i - 1)
+
+
+def pin_topk_constant_scores_take_lowest():
+    sc = np.full((1, 1, 50), 0.25)
+    idx = oracle.dsa_topk(sc, 7, q_pos=[49])
+    assert list(idx[0, 0]) == list(range(7))
+
+
+def pin_topk_signed_zero_ties():
+    row = np.array([-0.0, 0.0, -0.0, 0.5, 0.0, -1.0])
+    idx = oracle.dsa_topk(row.reshape(1, 1, 6), 3, q_pos=[5])
+    assert list(idx[0, 0]) == [0, 1, 3], list(idx[0, 0])
+
+
+# ---------------------------------------------------------------------------
+# DSA sparse attention
+# ---------------------------------------------------------------------------
+
+
+def pin_sparse_all_positions_is_dense_mqa():
+    rng = _rng(15)
+    B, T, Hq, D = 1, 17, 4, 8
+    q = rng.standard_normal((B, T, Hq, D))
+    k = rng.standard_normal((B, T, D))
+    v = rng.standard_normal((B, T, D))
+    idx = np.full((B, T, T + 3), -1)
+    for i in range(T):
+        idx[0, i, : i + 1] = np.arange(i + 1)
+    o, _ = oracle.dsa_sparse_attention(q, k, v, idx)
+    qh = q.transpose(0, 2, 1, 3)
+    kh = np.repeat(k[:, None], Hq, axis=1)
+    vh = np.repeat(v[:, None], Hq, axis=1)
+    ref = _sdpa_causal(qh, kh, vh).transpose(0, 2, 1, 3)
+    _close(o, ref, 1e-12, "dense MQA")
+
+
+def pin_sparse_single_position():
+    rng = _rng(16)
+    B, T, S, Hq, D = 1, 3, 10, 2, 4
+    q = rng.standard_normal((B, T, Hq, D))
+    k = rng.standard_normal((B, S, D))
+    v = rng.standard_normal((B, S, D))
+    idx = np.array([[[7, -1, -1], [-1, 2, -1], [-1, -1, -1]]])
+    o, lse = oracle.dsa_sparse_attention(q, k, v, idx)
+    _close(o[0, 0], np.repeat(v[0, 7][None], Hq, 0), 1e-15, "single -> v[s]")
+    _close(o[0, 1], np.repeat(v[0, 2][None], Hq, 0), 1e-15, "single -> v[s]")
+    _close(lse[0, 0], q[0, 0] @ k[0, 7] / 2.0, 1e-14, "single lse = scaled logit")
+    assert np.all(o[0, 2] == 0) and np.all(np.isneginf(lse[0, 2])), "empty row"
+
+
+def pin_sparse_identity_support():
+    rng = _rng(17)
+    S, Hq = 12, 3
+    q = rng.standard_normal((1, 1, Hq, S))
+    k = rng.standard_normal((1, S, S))
+    v = np.eye(S)[None]
+    sel = [1, 4, 5, 9]
+    idx = np.array([[sel + [-1]]])
+    o, _ = oracle.dsa_sparse_attention(q, k, v, idx)
+    for h in range(Hq):
+        w = o[0, 0, h]
+        assert abs(w.sum() - 1) < 1e-12
+        assert set(np.nonzero(w)[0]) == set(sel)
+        logits = np.array([q[0, 0, h] @ k[0, s] for s in sel]) / math.sqrt(S)
+        p = np.exp(logits - logits.max())
+        _close(w[sel], p / p.sum(), 1e-12, "identity-V weights")
+
+
+def pin_dsa_end_to_end_k_ge_context_is_dense():
+    rng = _rng(18)
+    T, Hi, Di, Hq, D = 14, 2, 4, 3, 8
+    qi = rng.standard_normal((1, T, Hi, Di))
+    ki = rng.standard_normal((1, T, Di))
+    w = rng.random((1, T, Hi))
+    q = rng.standard_normal((1, T, Hq, D))
+    k = rng.standard_normal((1, T, D))
+    v = rng.standard_normal((1, T, D))
+    idx = oracle.dsa_topk(oracle.dsa_indexer_scores(qi, ki, w), T)
+    o, _ = oracle.dsa_sparse_attention(q, k, v, idx)
+    ref = _sdpa_causal(q.transpose(0, 2, 1, 3), np.repeat(k[:, None], Hq, 1), np.repeat(v[:, None], Hq, 1))
+    _close(o, ref.transpose(0, 2, 1, 3), 1e-12, "k >= context")
+
+
+ALL_PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_") and callable(fn)}

@@ -1,0 +1,139 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each one.
+
+Every mutation replaces one function of the oracle with a subtly wrong copy:
+an off-by-one in the visibility rule or the window, a dropped scale, a wrong
+mean divisor, a dropped ReLU, transposed head weights, the wrong tie-break,
+padding entries not skipped.  The pin suite must fail for every one.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.dsa as odsa
+import oracle.hca as ohca
+import oracle_pins
+
+
+def _run_all_pins():
+    failed = []
+    for name, fn in sorted(oracle_pins.ALL_PINS.items()):
+        try:
+            fn()
+        except Exception:  # a wrong result or a crash both count as caught
+            failed.append(name)
+    return failed
+
+
+def _mut_visible_off_by_one(t, blk, window):
+    return max(0, (t - window) // blk)
+
+
+def _mut_window_one_short(t, window):
+    return max(0, t - window + 2), t + 1
+
+
+def _mut_window_one_long(t, window):
+    return max(0, t - window), t + 1
+
+
+def _mut_attend_no_scale(q, keys, vals, scale):
+    return _orig_attend(q, keys, vals, 1.0)
+
+
+def _mut_compress_wrong_divisor(x, blk):
+    x = np.asarray(x, dtype=np.float64)
+    T, d = x.shape[-2], x.shape[-1]
+    n = T // blk
+    blocks = x[..., : n * blk, :].reshape(*x.shape[:-2], n, blk, d)
+    return blocks.sum(axis=-2) / (blk + 1)
+
+
+def _mut_compress_includes_tail(x, blk):
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[-2]
+    n = -(-T // blk)
+    out = [x[..., j * blk: (j + 1) * blk, :].mean(axis=-2) for j in range(n)]
+    return np.stack(out, axis=-2)
+
+
+_orig_attend = ohca._attend
+_orig_scores = odsa.dsa_indexer_scores
+_orig_topk = odsa.dsa_topk
+_orig_sparse = odsa.dsa_sparse_attention
+
+
+def _mut_scores_no_relu(q_idx, k_idx, w, q_pos=None):
+    q_idx, k_idx, w = (np.asarray(a, dtype=np.float64) for a in (q_idx, k_idx, w))
+    B, T, Hi, Di = q_idx.shape
+    S = k_idx.shape[1]
+    out = np.full((B, T, S), np.nan)
+    for b in range(B):
+        base = 0 if q_pos is None else int(q_pos[b])
+        dots = np.einsum("thd,sd->ths", q_idx[b], k_idx[b])
+        score = (w[b][:, :, None] * dots).sum(axis=1)
+        for i in range(T):
+            n = min(base + i + 1, S)
+            out[b, i, :n] = score[i, :n]
+    return out
+
+
+def _mut_scores_weights_reversed(q_idx, k_idx, w, q_pos=None):
+    w = np.asarray(w)[:, :, ::-1]
+    return _orig_scores(q_idx, k_idx, w, q_pos)
+
+
+def _mut_topk_ties_high(scores, k, q_pos=None):
+    scores = np.asarray(scores, dtype=np.float64)
+    B, T, S = scores.shape
+    idx = np.full((B, T, k), -1, dtype=np.int64)
+    for b in range(B):
+        base = 0 if q_pos is None else int(q_pos[b])
+        for i in range(T):
+            n = min(base + i + 1, S)
+            cand = scores[b, i, :n] + 0.0
+            order = np.lexsort((-np.arange(n), -cand))
+            sel = np.sort(order[: min(k, n)])
+            idx[b, i, : sel.size] = sel
+    return idx
+
+
+def _mut_topk_descending_output(scores, k, q_pos=None):
+    idx = _orig_topk(scores, k, q_pos)
+    out = idx.copy()
+    for b in range(idx.shape[0]):
+        for i in range(idx.shape[1]):
+            valid = idx[b, i][idx[b, i] >= 0]
+            out[b, i, : valid.size] = valid[::-1]
+    return out
+
+
+def _mut_sparse_keeps_padding(q, k, v, idx, scale=None):
+    idx = np.where(np.asarray(idx) < 0, 0, idx)
+    return _orig_sparse(q, k, v, idx, scale)
+
+
+MUTATIONS = {
+    "visible_off_by_one": (ohca, "hca_visible_blocks", _mut_visible_off_by_one),
+    "window_one_short": (ohca, "hca_window_range", _mut_window_one_short),
+    "window_one_long": (ohca, "hca_window_range", _mut_window_one_long),
+    "attend_no_scale": (ohca, "_attend", _mut_attend_no_scale),
+    "compress_wrong_divisor": (ohca, "hca_compress", _mut_compress_wrong_divisor),
+    "compress_includes_tail": (ohca, "hca_compress", _mut_compress_includes_tail),
+    "scores_no_relu": (odsa, "dsa_indexer_scores", _mut_scores_no_relu),
+    "scores_weights_reversed": (odsa, "dsa_indexer_scores", _mut_scores_weights_reversed),
+    "topk_ties_high": (odsa, "dsa_topk", _mut_topk_ties_high),
+    "topk_descending_output": (odsa, "dsa_topk", _mut_topk_descending_output),
+    "sparse_keeps_padding": (odsa, "dsa_sparse_attention", _mut_sparse_keeps_padding),
+}
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_pins_catch_mutation(mutation, monkeypatch):
+    mod, attr, fn = MUTATIONS[mutation]
+    monkeypatch.setattr(mod, attr, fn)
+    # the package namespace re-exports the public functions: patch it too
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    failed = _run_all_pins()
+    assert failed, f"no pin caught mutation {mutation}"
