@@ -72,12 +72,14 @@ const char* sa_version(void);
  *
  *   out[b,h,j,:] = (1/blk) * sum_{i<blk} x[b,h,j*blk+i,:],  j < floor(n_tokens/blk)
  *
- * Trailing tokens that do not fill a block produce no entry.
+ * Trailing tokens that do not fill a block produce no entry; with no complete
+ * block the call does nothing and x/out may be NULL.
  * x:   [B,H,n_tokens,d] with element strides (x_sb, x_sh, x_st), d contiguous.
  * out: [B,H,n_tokens/blk,d] with element strides (o_sb, o_sh, o_sn).
  * Arithmetic: fp32 sum, one division by blk, rounded (RNE) to the I/O dtype.
- * Supported: SA_F32 with d in {64, 512}; SA_BF16 with d in {256, 512}.
- * Strides must be multiples of 16 bytes / sizeof(element).
+ * Supported: SA_F32 and SA_BF16 with d*sizeof(element) = 16*2^n bytes, at
+ * most 4096 bytes (e.g. f32 d = 64, bf16 d = 256 or 512).  Strides must be
+ * multiples of 16 bytes.
  * ------------------------------------------------------------------------ */
 int hca_compress(const void* x, void* out, sa_dtype dtype,
                  int64_t B, int64_t H, int64_t n_tokens, int64_t d, int64_t blk,
@@ -196,7 +198,7 @@ int dsa_topk(const float* scores, const int64_t* q_pos, int32_t* idx,
  * entry yields o = 0 and lse = -inf.
  * q, o: [B,T,Hq,D] bf16; k, v: [B,S,D] bf16 (v == k is allowed);
  * idx: [B,T,kk] int32; lse: optional fp32 [B,T,Hq].  scale <= 0 -> 1/sqrt(D).
- * Supported: SA_BF16, D = 256, Hq = 64, kk >= 1.
+ * Supported: SA_BF16, D = 256, Hq = 64, 1 <= kk <= 2048.
  * ------------------------------------------------------------------------ */
 int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v,
                              const int32_t* idx, void* o, float* lse, sa_dtype dtype,

@@ -1,0 +1,37 @@
+"""HCA + MLA-DSA forward pass for AMD Instinct MI355X (gfx950).
+
+Python binding of the C ABI in include/sparse_attn_hca.h; every step of the
+path runs in the library's HIP kernels.
+"""
+
+from ._lib import (
+    HCA_DECODE,
+    HCA_PREFILL,
+    LIB_PATH,
+    SparseAttnError,
+    dsa_indexer_scores,
+    dsa_sparse_attention_fwd,
+    dsa_topk,
+    dsa_topk_workspace_size,
+    hca_attention_fwd,
+    hca_attention_workspace_size,
+    hca_compress,
+    lib,
+    version,
+)
+
+__all__ = [
+    "HCA_DECODE",
+    "HCA_PREFILL",
+    "LIB_PATH",
+    "SparseAttnError",
+    "dsa_indexer_scores",
+    "dsa_sparse_attention_fwd",
+    "dsa_topk",
+    "dsa_topk_workspace_size",
+    "hca_attention_fwd",
+    "hca_attention_workspace_size",
+    "hca_compress",
+    "lib",
+    "version",
+]

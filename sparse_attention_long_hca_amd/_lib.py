@@ -1,0 +1,267 @@
+"""ctypes binding of libsparse_attn_hca.so (argument marshalling only).
+
+Every function here validates nothing beyond what is needed to build the C
+call (tensor device/dtype/contiguity), allocates outputs with torch (device
+memory is the only thing torch provides), and calls the C entry point of the
+same name on the current torch stream.  All computation happens in the HIP
+kernels; if the library is missing the call fails loudly.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libsparse_attn_hca.so")
+
+SA_F32, SA_BF16 = 0, 1
+HCA_PREFILL, HCA_DECODE = 0, 1
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+
+
+class HcaAttentionArgs(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+        ("B", _c_i64),
+        ("H", _c_i64),
+        ("d", _c_i64),
+        ("blk", _c_i64),
+        ("window", _c_i64),
+        ("seq_len", _c_i64),
+        ("n_c_cap", _c_i64),
+        ("scale", ctypes.c_float),
+        ("q", _c_p),
+        ("k", _c_p),
+        ("v", _c_p),
+        ("k_c", _c_p),
+        ("v_c", _c_p),
+        ("pos", _c_p),
+        ("o", _c_p),
+        ("lse", _c_p),
+        ("workspace", _c_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+EXPORTS = {
+    "sa_last_error": (ctypes.c_char_p, []),
+    "sa_version": (ctypes.c_char_p, []),
+    "hca_compress": (ctypes.c_int, [_c_p, _c_p, ctypes.c_int] + [_c_i64] * 11 + [_c_p]),
+    "hca_attention_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HcaAttentionArgs)]),
+    "hca_attention_fwd": (ctypes.c_int, [ctypes.POINTER(HcaAttentionArgs), _c_p]),
+    "dsa_indexer_scores": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p] + [_c_i64] * 5 + [_c_p]),
+    "dsa_topk_workspace_size": (ctypes.c_size_t, [_c_i64] * 4),
+    "dsa_topk": (ctypes.c_int, [_c_p, _c_p, _c_p] + [_c_i64] * 4 + [_c_p, ctypes.c_size_t, _c_p]),
+    "dsa_sparse_attention_fwd": (
+        ctypes.c_int,
+        [_c_p] * 6 + [ctypes.c_int] + [_c_i64] * 6 + [ctypes.c_float, _c_p],
+    ),
+}
+
+
+def lib():
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m sparse_attention_long_hca_amd.build`"
+            )
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise SparseAttnError(fn, status, lib().sa_last_error().decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return SA_F32
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, name, dtype=None, dim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
+
+
+def version():
+    return lib().sa_version().decode()
+
+
+# ---------------------------------------------------------------------------
+def hca_compress(x, blk, out=None):
+    """Block mean of K or V: x [B,H,T,d] -> [B,H,T//blk,d] (same dtype)."""
+    _need(x, "x", dim=4)
+    B, H, T, d = x.shape
+    n = T // blk
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=x.dtype, device=x.device)
+    if out.dim() != 4 or out.shape[-1] != d or out.stride(-1) != 1:
+        raise ValueError("out must be [B,H,n,d] with a contiguous last dim")
+    st = _check(
+        "hca_compress",
+        lib().hca_compress(
+            _ptr(x), _ptr(out), _dtype_code(x), B, H, T, d, blk,
+            x.stride(0), x.stride(1), x.stride(2), out.stride(0), out.stride(1), out.stride(2),
+            _stream(),
+        ),
+    )
+    return out
+
+
+def _hca_args(mode, q, k, v, k_c, v_c, blk, window, seq_len, n_c_cap, scale, pos, o, lse, ws, ws_bytes):
+    a = HcaAttentionArgs()
+    a.mode = mode
+    a.dtype = _dtype_code(q)
+    a.B, a.H, a.d = q.shape[0], q.shape[1], q.shape[-1]
+    a.blk, a.window, a.seq_len, a.n_c_cap = blk, window, seq_len, n_c_cap
+    a.scale = 0.0 if scale is None else float(scale)
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.k_c = k_c.data_ptr() if k_c is not None else None
+    a.v_c = v_c.data_ptr() if v_c is not None else None
+    a.pos = pos.data_ptr() if pos is not None else None
+    a.o = o.data_ptr()
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.workspace = ws.data_ptr() if ws is not None else None
+    a.workspace_bytes = ws_bytes
+    return a
+
+
+def hca_attention_fwd(mode, q, k, v, k_c, v_c, blk, window, scale=None, pos=None, return_lse=False, workspace=None):
+    """HCA attention.
+
+    PREFILL: q,k,v [B,H,T,d]; k_c,v_c [B,H,Nc,d].  Returns o [B,H,T,d] (and lse [B,H,T]).
+    DECODE:  q [B,H,d]; k_c,v_c [B,H,Ncap,d]; k,v = window ring [B,H,window,d];
+             pos int64 [B] on the device.  Returns o [B,H,d] (and lse [B,H]).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("k_c", k_c), ("v_c", v_c)):
+        _need(t, name, dtype=q.dtype)
+    if mode == HCA_PREFILL:
+        B, H, T, d = q.shape
+        seq_len, n_c = T, k_c.shape[2]
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    elif mode == HCA_DECODE:
+        _need(pos, "pos", dtype=torch.int64, dim=1)
+        B, H, d = q.shape
+        seq_len, n_c = 0, k_c.shape[2]
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
+    else:
+        raise ValueError("mode must be HCA_PREFILL or HCA_DECODE")
+    o = torch.empty_like(q)
+    args = _hca_args(mode, q, k, v, k_c, v_c, blk, window, seq_len, n_c, scale, pos, o, lse, None, 0)
+    need = lib().hca_attention_fwd_workspace_size(ctypes.byref(args))
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("hca_attention_fwd", lib().hca_attention_fwd(ctypes.byref(args), _stream()))
+    return (o, lse) if return_lse else o
+
+
+def hca_attention_workspace_size(mode, q, k_c, blk, window):
+    a = HcaAttentionArgs()
+    a.mode, a.dtype = mode, _dtype_code(q)
+    a.B, a.H, a.d = q.shape[0], q.shape[1], q.shape[-1]
+    a.blk, a.window, a.n_c_cap = blk, window, k_c.shape[2]
+    return lib().hca_attention_fwd_workspace_size(ctypes.byref(a))
+
+
+def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None, out=None):
+    """q_idx [B,T,Hi,Di] bf16, k_idx [B,S,Di] bf16, w [B,T,Hi] f32 -> scores [B,T,S] f32."""
+    _need(q_idx, "q_idx", torch.bfloat16, 4)
+    _need(k_idx, "k_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 3)
+    B, T, Hi, Di = q_idx.shape
+    S = k_idx.shape[1]
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int64, 1)
+    if out is None:
+        out = torch.empty((B, T, S), dtype=torch.float32, device=q_idx.device)
+    _need(out, "out", torch.float32, 3)
+    _check(
+        "dsa_indexer_scores",
+        lib().dsa_indexer_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q_pos), _ptr(out), B, T, S, Hi, Di, _stream()),
+    )
+    return out
+
+
+def dsa_topk_workspace_size(B, T, S, k):
+    return lib().dsa_topk_workspace_size(B, T, S, k)
+
+
+def dsa_topk(scores, k, q_pos=None, out=None, workspace=None):
+    """scores [B,T,S] f32 -> idx [B,T,k] int32 (ascending positions, -1 padded)."""
+    _need(scores, "scores", torch.float32, 3)
+    B, T, S = scores.shape
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int64, 1)
+    if out is None:
+        out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
+    _need(out, "out", torch.int32, 3)
+    need = lib().dsa_topk_workspace_size(B, T, S, k)
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(
+        "dsa_topk",
+        lib().dsa_topk(_ptr(scores), _ptr(q_pos), _ptr(out), B, T, S, k, _ptr(workspace), wsb, _stream()),
+    )
+    return out
+
+
+def dsa_sparse_attention_fwd(q, k, v, idx, scale=None, return_lse=False):
+    """q [B,T,Hq,D], k,v [B,S,D] bf16, idx [B,T,kk] int32 -> o [B,T,Hq,D] (and lse [B,T,Hq])."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(idx, "idx", torch.int32, 3)
+    B, T, Hq, D = q.shape
+    S = k.shape[1]
+    kk = idx.shape[2]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(
+        "dsa_sparse_attention_fwd",
+        lib().dsa_sparse_attention_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o), _ptr(lse), SA_BF16, B, T, S, Hq, D, kk,
+            0.0 if scale is None else float(scale), _stream(),
+        ),
+    )
+    return (o, lse) if return_lse else o

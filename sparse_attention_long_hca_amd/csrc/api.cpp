@@ -1,0 +1,208 @@
+// C ABI of the HCA + MLA-DSA forward library: argument validation, workspace
+// sizing and dispatch to the gfx950 kernels.  Every check runs on the host
+// before anything is enqueued and touches no HIP state, so invalid calls are
+// rejected (with a status code and a message) even without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/sparse_attn_hca.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_size(sa_dtype dt) { return dt == SA_BF16 ? 2 : 4; }
+
+float resolve_scale_log2(float scale, int64_t d) {
+  const float s = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+  return s * 1.4426950408889634f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sa_last_error(void) { return g_err; }
+
+const char* sa_version(void) { return "sparse_attn_hca 0.1.0 (gfx950)"; }
+
+// ---------------------------------------------------------------------------
+int hca_compress(const void* x, void* out, sa_dtype dtype, int64_t B, int64_t H, int64_t n_tokens, int64_t d,
+                 int64_t blk, int64_t x_sb, int64_t x_sh, int64_t x_st, int64_t o_sb, int64_t o_sh, int64_t o_sn,
+                 hipStream_t stream) {
+  if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "hca_compress: unknown dtype %d", (int)dtype);
+  if (B <= 0 || H <= 0 || d <= 0 || blk <= 0 || n_tokens < 0)
+    return fail(SA_ERR_SHAPE, "hca_compress: B, H, d, blk must be > 0 and n_tokens >= 0");
+  if (n_tokens / blk == 0) return ok();  // no complete block: nothing to write (pointers may be NULL)
+  if (!x || !out) return fail(SA_ERR_NULL, "hca_compress: x and out must be non-NULL");
+  const int64_t es = (int64_t)elem_size(dtype);
+  const int64_t chunks = d * es / 16;
+  if ((d * es) % 16 != 0 || chunks > 256 || (chunks & (chunks - 1)) != 0)
+    return fail(SA_ERR_UNSUPPORTED, "hca_compress: d*sizeof(elem) must be 16 * 2^n bytes, at most 4096 (d=%lld)",
+                (long long)d);
+  if (blk > (1 << 20)) return fail(SA_ERR_SHAPE, "hca_compress: blk too large");
+  if (!aligned16(x) || !aligned16(out)) return fail(SA_ERR_ALIGN, "hca_compress: pointers must be 16-byte aligned");
+  const int64_t epc = 16 / es;
+  if (x_sb % epc || x_sh % epc || x_st % epc || o_sb % epc || o_sh % epc || o_sn % epc)
+    return fail(SA_ERR_ALIGN, "hca_compress: strides must be multiples of 16 bytes");
+  const int64_t n_out = n_tokens / blk;
+  if (B * H * n_out > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "hca_compress: too many output rows");
+  sa::HcaCompressParams p{x, out, B, H, n_out, d, blk, x_sb, x_sh, x_st, o_sb, o_sh, o_sn};
+  return hip_status(sa::launch_hca_compress(p, dtype == SA_BF16 ? 1 : 0, stream), "hca_compress launch");
+}
+
+// ---------------------------------------------------------------------------
+static int hca_check(const hca_attention_args* a) {
+  if (!a) return fail(SA_ERR_NULL, "hca_attention_fwd: args is NULL");
+  if (a->mode != HCA_PREFILL && a->mode != HCA_DECODE) return fail(SA_ERR_SHAPE, "hca_attention_fwd: unknown mode");
+  if (!a->q || !a->k || !a->v || !a->o) return fail(SA_ERR_NULL, "hca_attention_fwd: q, k, v, o must be non-NULL");
+  if (a->B <= 0 || a->H <= 0 || a->d <= 0 || a->blk <= 0 || a->window <= 0 || a->n_c_cap < 0)
+    return fail(SA_ERR_SHAPE, "hca_attention_fwd: B, H, d, blk, window must be > 0, n_c_cap >= 0");
+  if (a->n_c_cap > 0 && (!a->k_c || !a->v_c))
+    return fail(SA_ERR_NULL, "hca_attention_fwd: k_c, v_c must be non-NULL when n_c_cap > 0");
+  if (a->mode == HCA_PREFILL) {
+    if (a->seq_len <= 0) return fail(SA_ERR_SHAPE, "hca_attention_fwd: seq_len must be > 0 for PREFILL");
+    const bool sup = (a->dtype == SA_F32 && a->d == 64) || (a->dtype == SA_BF16 && a->d == 512);
+    if (!sup)
+      return fail(SA_ERR_UNSUPPORTED, "hca_attention_fwd PREFILL: supported (dtype, d) are (f32, 64) and (bf16, 512)");
+    if (a->n_c_cap > a->seq_len / a->blk)
+      return fail(SA_ERR_SHAPE, "hca_attention_fwd PREFILL: n_c_cap (%lld) exceeds seq_len/blk (%lld)",
+                  (long long)a->n_c_cap, (long long)(a->seq_len / a->blk));
+    if (a->seq_len >= ((int64_t)1 << 30) || a->blk >= ((int64_t)1 << 30) || a->window >= ((int64_t)1 << 30))
+      return fail(SA_ERR_SHAPE, "hca_attention_fwd PREFILL: seq_len, blk and window must be < 2^30");
+    const int64_t n_qt = (a->seq_len + 63) / 64;
+    if (a->B * a->H * n_qt > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "hca_attention_fwd: grid too large");
+  } else {
+    if (!a->pos) return fail(SA_ERR_NULL, "hca_attention_fwd DECODE: pos must be non-NULL");
+    if (!(a->dtype == SA_BF16 && a->d == 512))
+      return fail(SA_ERR_UNSUPPORTED, "hca_attention_fwd DECODE: supported (dtype, d) is (bf16, 512)");
+    if (a->n_c_cap < 1) return fail(SA_ERR_SHAPE, "hca_attention_fwd DECODE: n_c_cap must be >= 1");
+  }
+  const void* ptrs[] = {a->q, a->k, a->v, a->k_c, a->v_c, a->o, a->lse};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SA_ERR_ALIGN, "hca_attention_fwd: pointers must be 16-byte aligned");
+  return SA_OK;
+}
+
+static int64_t hca_dec_nsplit(const hca_attention_args* a) {
+  return sa::hca_decode_nsplit(a->B * a->H, a->n_c_cap + a->window);
+}
+
+size_t hca_attention_fwd_workspace_size(const hca_attention_args* a) {
+  if (!a || a->mode != HCA_DECODE || a->B <= 0 || a->H <= 0 || a->d <= 0) return 0;
+  return sa::hca_decode_workspace_bytes(a->B * a->H, hca_dec_nsplit(a), a->d);
+}
+
+int hca_attention_fwd(const hca_attention_args* a, hipStream_t stream) {
+  const int c = hca_check(a);
+  if (c != SA_OK) return c;
+  const float sl2 = resolve_scale_log2(a->scale, a->d);
+  if (a->mode == HCA_PREFILL) {
+    sa::HcaPrefillParams p{a->q, a->k, a->v, a->k_c, a->v_c, a->o, a->lse, a->B, a->H, a->seq_len,
+                           a->n_c_cap, a->blk, a->window, sl2, (a->seq_len + 63) / 64};
+    return hip_status(sa::launch_hca_prefill(p, a->dtype == SA_BF16 ? 1 : 0, (int)a->d, stream),
+                      "hca_attention_fwd prefill launch");
+  }
+  const int64_t BH = a->B * a->H;
+  const int64_t ns = hca_dec_nsplit(a);
+  const size_t need = sa::hca_decode_workspace_bytes(BH, ns, a->d);
+  if (need > 0) {
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "hca_attention_fwd DECODE: needs %zu workspace bytes, got %zu", need,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned16(a->workspace)) return fail(SA_ERR_ALIGN, "hca_attention_fwd: workspace must be 16-byte aligned");
+  }
+  if (BH * ns > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "hca_attention_fwd: grid too large");
+  const int64_t max_keys = a->n_c_cap + a->window;
+  float* part_o = reinterpret_cast<float*>(a->workspace);
+  float* part_lse = part_o ? part_o + BH * ns * a->d : nullptr;
+  sa::HcaDecodeParams p{a->q, a->k_c, a->v_c, a->k, a->v, a->pos, a->o, a->lse, part_o, part_lse,
+                        a->B, a->H, a->n_c_cap, a->blk, a->window, sl2, ns, (max_keys + ns - 1) / ns};
+  return hip_status(sa::launch_hca_decode(p, 1, (int)a->d, stream), "hca_attention_fwd decode launch");
+}
+
+// ---------------------------------------------------------------------------
+int dsa_indexer_scores(const void* q_idx, const void* k_idx, const float* w, const int64_t* q_pos, float* scores,
+                       int64_t B, int64_t T, int64_t S, int64_t Hi, int64_t Di, hipStream_t stream) {
+  if (!q_idx || !k_idx || !w || !scores) return fail(SA_ERR_NULL, "dsa_indexer_scores: q_idx, k_idx, w, scores must be non-NULL");
+  if (B <= 0 || T <= 0 || S <= 0 || Hi <= 0 || Di <= 0) return fail(SA_ERR_SHAPE, "dsa_indexer_scores: sizes must be > 0");
+  if (Hi != 4 || Di != 128) return fail(SA_ERR_UNSUPPORTED, "dsa_indexer_scores: supported Hi = 4, Di = 128");
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w) || !aligned16(scores))
+    return fail(SA_ERR_ALIGN, "dsa_indexer_scores: pointers must be 16-byte aligned");
+  const int64_t nblocks = B * ((T + 63) / 64) * ((S + 1023) / 1024);
+  if (nblocks > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "dsa_indexer_scores: grid too large");
+  sa::DsaIndexerParams p{q_idx, k_idx, w, q_pos, scores, B, T, S};
+  return hip_status(sa::launch_dsa_indexer(p, stream), "dsa_indexer_scores launch");
+}
+
+// ---------------------------------------------------------------------------
+size_t dsa_topk_workspace_size(int64_t B, int64_t T, int64_t S, int64_t k) {
+  if (B <= 0 || T <= 0 || S <= 0 || k <= 0) return 0;
+  return sa::dsa_topk_ws_bytes(B, T, S, k);
+}
+
+int dsa_topk(const float* scores, const int64_t* q_pos, int32_t* idx, int64_t B, int64_t T, int64_t S, int64_t k,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!scores || !idx) return fail(SA_ERR_NULL, "dsa_topk: scores and idx must be non-NULL");
+  if (B <= 0 || T <= 0 || S <= 0 || k <= 0) return fail(SA_ERR_SHAPE, "dsa_topk: sizes must be > 0");
+  if (k > 2048) return fail(SA_ERR_UNSUPPORTED, "dsa_topk: k must be <= 2048");
+  if (S >= (int64_t)1 << 31) return fail(SA_ERR_UNSUPPORTED, "dsa_topk: S must be < 2^31");
+  if (!aligned16(scores) || !aligned16(idx)) return fail(SA_ERR_ALIGN, "dsa_topk: pointers must be 16-byte aligned");
+  if (B * T > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "dsa_topk: too many rows");
+  const size_t need = sa::dsa_topk_ws_bytes(B, T, S, k);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "dsa_topk: needs %zu workspace bytes, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(SA_ERR_ALIGN, "dsa_topk: workspace must be 16-byte aligned");
+    const int64_t nchunk = (S + 16383) / 16384;
+    if (B * T * nchunk > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "dsa_topk: grid too large");
+  }
+  sa::DsaTopkParams p{scores, q_pos, idx, B, T, S, k, workspace};
+  return hip_status(sa::launch_dsa_topk(p, stream), "dsa_topk launch");
+}
+
+// ---------------------------------------------------------------------------
+int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v, const int32_t* idx, void* o, float* lse,
+                             sa_dtype dtype, int64_t B, int64_t T, int64_t S, int64_t Hq, int64_t D, int64_t kk,
+                             float scale, hipStream_t stream) {
+  if (!q || !k || !v || !idx || !o) return fail(SA_ERR_NULL, "dsa_sparse_attention_fwd: q, k, v, idx, o must be non-NULL");
+  if (B <= 0 || T <= 0 || S <= 0 || Hq <= 0 || D <= 0 || kk <= 0)
+    return fail(SA_ERR_SHAPE, "dsa_sparse_attention_fwd: sizes must be > 0");
+  if (dtype != SA_BF16 || D != 256 || Hq != 64)
+    return fail(SA_ERR_UNSUPPORTED, "dsa_sparse_attention_fwd: supported dtype bf16, D = 256, Hq = 64");
+  if (kk > 2048) return fail(SA_ERR_UNSUPPORTED, "dsa_sparse_attention_fwd: kk must be <= 2048");
+  const void* ptrs[] = {q, k, v, idx, o, lse};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SA_ERR_ALIGN, "dsa_sparse_attention_fwd: pointers must be 16-byte aligned");
+  if (B * T > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "dsa_sparse_attention_fwd: too many tokens");
+  sa::DsaSparseParams p{q, k, v, idx, o, lse, B, T, S, kk, resolve_scale_log2(scale, D)};
+  return hip_status(sa::launch_dsa_sparse(p, (int)D, (int)Hq, stream), "dsa_sparse_attention_fwd launch");
+}
+
+}  // extern "C"

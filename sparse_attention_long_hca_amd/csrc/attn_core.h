@@ -1,0 +1,305 @@
+// MFMA attention core for gfx950, shared by HCA prefill and DSA sparse
+// attention.  One workgroup = 4 waves; each wave owns 16 query rows (queries
+// for HCA, heads of one token for the multi-query DSA layout) and keeps its Q
+// operand and O accumulator in registers.  Keys arrive in tiles of 32 rows
+// that the whole workgroup stages into LDS; the per-tile key rows come from a
+// policy object (compressed entries + raw window for HCA, gathered positions
+// for DSA).
+//
+// Per tile and wave (transposed formulation, so no register shuffles are
+// needed between the two products):
+//   S^T[32 keys x 16 rows] = K_tile . Q^T          (A = K from LDS, B = Q regs)
+//   online softmax over the key axis (state per query row, fp32, exp2)
+//   O^T[D x 16 rows]     += V_tile^T . P^T        (A = V via transposing
+//                                                   LDS reads, B = P regs)
+// S^T's accumulator layout leaves lane l holding keys {4g..4g+3, 16+4g..16+4g+3}
+// (g = l/16) of query row l%16.  The contraction over keys is order-free, so
+// those eight values are used directly as the B operand of the P.V product
+// and the transposing V reads fetch the same eight keys.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace sa {
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnThreads = kAttnWaves * kWave;  // 256
+constexpr int kRowsPerWave = 16;
+constexpr int kBM = kAttnWaves * kRowsPerWave;  // query rows per workgroup
+constexpr int kBN = 32;                         // keys per tile
+
+template <typename T, int D>
+struct AttnGeom {
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int kEPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int kChunks = D / kEPC;          // 16-byte chunks per row
+  static constexpr int kRowBytes = D * (int)sizeof(T);
+  static constexpr int kTileBytes = kBN * kRowBytes;
+  static constexpr int kQRegs = kBf16 ? D / 32 : D / 4;
+  static constexpr int kONb = D / 16;
+  static constexpr int kStageBytes = 2 * kTileBytes;  // one pipeline stage: K tile + V tile
+  static_assert(kChunks >= 8, "the XOR swizzle needs at least 8 chunks per row");
+  // Row r, 16-byte chunk c -> byte offset in a tile.  XOR with r%8 spreads
+  // the 16 rows read by one MFMA operand fetch over all LDS banks.
+  __device__ static __forceinline__ uint32_t chunk_off(int r, int c) {
+    return (uint32_t)(r * kChunks + (c ^ (r & 7))) * 16u;
+  }
+};
+
+template <typename T, int D>
+struct AttnRegs {
+  using G = AttnGeom<T, D>;
+  using QReg = typename std::conditional<G::kBf16, i16x8_t, float>::type;
+  QReg q[G::kQRegs];
+  f32x4_t o[G::kONb];
+  float m;  // running max of scaled logits, log2 units
+  float l;  // running sum of exp2(logit - m)
+};
+
+// ---------------------------------------------------------------------------
+// Q operand: row pointer of this lane's query row (lane%16), or nullptr.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__device__ __forceinline__ void load_q(AttnRegs<T, D>& R, const T* qrow) {
+  using G = AttnGeom<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < G::kQRegs; ++ks) {
+    if constexpr (G::kBf16) {
+      if (qrow) {
+        uint4 u = *reinterpret_cast<const uint4*>(qrow + ks * 32 + g * 8);
+        R.q[ks] = __builtin_bit_cast(i16x8_t, u);
+      } else {
+        R.q[ks] = i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    } else {
+      R.q[ks] = qrow ? qrow[ks * 4 + g] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < G::kONb; ++nb) R.o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  R.m = -INFINITY;
+  R.l = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Global -> LDS staging of one K/V tile with gfx950's direct LDS loads
+// (global_load_lds_dwordx4: lane i of the wave writes 16 bytes at
+// lds_base + 16*i).  Wave w, step j fills the 64 physical chunks starting at
+// chunk (j*4 + w)*64; the lane picks the logical chunk that belongs at its
+// physical slot under the XOR swizzle, so reads stay contiguous within a row.
+// Every tile issues the same number of loads per wave (padding rows load the
+// fallback row, which is finite and masked), so a fixed vmcnt wait is exact.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct StageGeom {
+  using G = AttnGeom<T, D>;
+  static constexpr int kInstr = kBN * G::kChunks / kWave;  // wave loads per K (or V) tile
+  static constexpr int kPerWave = kInstr / kAttnWaves;
+  static_assert(kInstr % kAttnWaves == 0, "tile must split evenly over the waves");
+  static constexpr int kLoadsPerTile = 2 * kPerWave;  // K and V
+};
+
+__device__ __forceinline__ void global_load_lds_16(const void* g, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+// Tile source: uniform base pointers of the K and V rows; rowfn(r) gives the
+// row index of tile row r relative to them, or -1 for a padding row (which
+// loads row 0 of the same tensor: finite, and masked by the caller).
+template <typename T, int D, typename RowFn>
+__device__ __forceinline__ void stage_async(char* kbuf, char* vbuf, const T* kbase, const T* vbase,
+                                            RowFn&& rowfn) {
+  using G = AttnGeom<T, D>;
+  using SG = StageGeom<T, D>;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < SG::kPerWave; ++j) {
+    const int base = (j * kAttnWaves + wave) * kWave;  // first physical chunk of this load
+    const int P = base + lane;
+    const int r = P / G::kChunks, cp = P % G::kChunks;
+    const int c = cp ^ (r & 7);
+    int row = rowfn(r);
+    row = row < 0 ? 0 : row;
+    const uint32_t off = (uint32_t)row * (uint32_t)G::kRowBytes + (uint32_t)c * 16u;
+    global_load_lds_16(reinterpret_cast<const char*>(kbase) + off, kbuf + base * 16);
+    global_load_lds_16(reinterpret_cast<const char*>(vbase) + off, vbuf + base * 16);
+  }
+}
+
+// Wait until this wave's loads, except the newest `pending` tiles' worth, have
+// landed in LDS.
+template <int kPendingLoads>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(kPendingLoads >= 0 && kPendingLoads < 64, "vmcnt range");
+  if constexpr (kPendingLoads == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPendingLoads) : "memory");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One key tile for one wave.  visible(key_in_tile) is evaluated for this
+// lane's query row (lane%16) and the 8 keys the lane holds.
+// scale_log2 = softmax scale * log2(e).
+// ---------------------------------------------------------------------------
+template <typename T, int D, typename VisFn>
+__device__ __forceinline__ void attend_tile(AttnRegs<T, D>& R, const char* ks, const char* vs,
+                                            float scale_log2, VisFn&& visible) {
+  using G = AttnGeom<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, L = lane & 15;
+
+  // ---- S^T = K . Q^T -------------------------------------------------------
+  f32x4_t s[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  if constexpr (G::kBf16) {
+    // Row r = kb*16 + L, logical chunk g + 4*kstep.  With x = r%8 the swizzled
+    // chunk is (g ^ x%4) + 4*((kstep%2) ^ x/4) + 8*(kstep/2): two per-lane bases
+    // plus compile-time offsets.
+    const int x = L & 7;
+    const uint32_t rb = (uint32_t)L * G::kRowBytes + 16u * (uint32_t)(g ^ (x & 3));
+    const uint32_t kb0 = rb + 64u * (uint32_t)(x >> 2);
+    const uint32_t kb1 = rb + 64u * (uint32_t)(1 - (x >> 2));
+#pragma unroll
+    for (int kstep = 0; kstep < G::kQRegs; ++kstep) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t off = ((kstep & 1) ? kb1 : kb0) + 128u * (kstep >> 1) + kb * 16 * G::kRowBytes;
+        const uint4 a = lds_read_b128(ks, off);
+        s[kb] = mfma_bf16_16x16x32(__builtin_bit_cast(i16x8_t, a), R.q[kstep], s[kb]);
+      }
+      // Keep at most a few operand reads in flight (bounded register use).
+      if ((kstep & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int kstep = 0; kstep < G::kQRegs; ++kstep) {
+      const int e = kstep * 4 + g;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r = kb * 16 + L;
+        const float a = *reinterpret_cast<const float*>(ks + G::chunk_off(r, e >> 2) + (e & 3) * 4);
+        s[kb] = mfma_f32_16x16x4(a, R.q[kstep], s[kb]);
+      }
+    }
+  }
+
+  // ---- mask, online softmax ------------------------------------------------
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = kb * 16 + g * 4 + j;
+      const float x = visible(key) ? s[kb][j] * scale_log2 : -INFINITY;
+      s[kb][j] = x;
+      mx = fmaxf(mx, x);
+    }
+  }
+  mx = max_across_groups(mx);
+  // Lazy rescaling: the reference max only moves when the tile's max exceeds
+  // it by more than 2^kRescaleLog2.  Until then probabilities are computed
+  // against the stale max (values up to 2^kRescaleLog2, exact in fp32 and
+  // fine for bf16), and since l uses the same reference the result is
+  // unchanged.  This skips the O-accumulator rescale on almost every tile.
+  constexpr float kRescaleLog2 = 8.f;
+  if (__any(mx > R.m + kRescaleLog2)) {
+    const float m_new = fmaxf(R.m, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(R.m - m_new);
+    R.l *= alpha;
+    R.m = m_new;
+#pragma unroll
+    for (int nb = 0; nb < G::kONb; ++nb) {
+      R.o[nb] *= alpha;
+      if ((nb & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const float base = (R.m == -INFINITY) ? 0.f : R.m;
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p = fast_exp2(s[kb][j] - base);
+      s[kb][j] = p;
+      rs += p;
+    }
+  }
+  rs = sum_across_groups(rs);
+  R.l += rs;
+
+  // ---- O^T += V^T . P^T ----------------------------------------------------
+  if constexpr (G::kBf16) {
+    const uint32_t p01 = pack_bf16x2(s[0][0], s[0][1]), p23 = pack_bf16x2(s[0][2], s[0][3]);
+    const uint32_t p45 = pack_bf16x2(s[1][0], s[1][1]), p67 = pack_bf16x2(s[1][2], s[1][3]);
+    const i16x8_t pf = __builtin_bit_cast(i16x8_t, make_uint4(p01, p23, p45, p67));
+    // Transposing reads: group g's lane L points at row key1 = 4g + L/4 (and
+    // key1 + 16), dims nb*16 + 4*(L%4) .. +3.  With x = key1%8 the swizzled
+    // byte offset is 128*(nb/4) + 32*((nb%4) ^ x/2) + 16*(h ^ x%2) + 8*(L%2),
+    // h = (L%4)/2: four per-lane bases plus compile-time offsets.
+    const int key1 = 4 * g + (L >> 2);
+    const int x = key1 & 7;
+    const uint32_t vrow = (uint32_t)key1 * G::kRowBytes + 16u * (uint32_t)(((L & 3) >> 1) ^ (x & 1)) + 8u * (L & 1);
+    uint32_t vbase[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) vbase[n] = vrow + 32u * (uint32_t)(n ^ (x >> 1));
+#pragma unroll
+    for (int nb = 0; nb < G::kONb; ++nb) {
+      const uint32_t off = vbase[nb & 3] + 128u * (nb >> 2);
+      const i16x4_t lo = lds_read_tr16_b64(vs + off);
+      const i16x4_t hi = lds_read_tr16_b64(vs + off + 16 * G::kRowBytes);
+      const i16x8_t a = i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      R.o[nb] = mfma_bf16_16x16x32(a, pf, R.o[nb]);
+      if ((nb & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < G::kONb; ++nb) {
+      const int dim = nb * 16 + L;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = 16 * kb + 4 * g + j;
+          const float a = *reinterpret_cast<const float*>(vs + G::chunk_off(key, dim >> 2) + (dim & 3) * 4);
+          R.o[nb] = mfma_f32_16x16x4(a, s[kb][j], R.o[nb]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Normalise and write this wave's 16 output rows.  orow: row pointer for the
+// lane's query row (lane%16) or nullptr; lse_out: pointer for that row's lse
+// or nullptr.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__device__ __forceinline__ void finish_rows(const AttnRegs<T, D>& R, T* orow, float* lse_out) {
+  using G = AttnGeom<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const float inv = R.l > 0.f ? 1.f / R.l : 0.f;
+  if (orow) {
+#pragma unroll
+    for (int nb = 0; nb < G::kONb; ++nb) {
+      const int dim = nb * 16 + g * 4;
+      const f32x4_t v = R.o[nb] * inv;
+      if constexpr (G::kBf16) {
+        uint2 u = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        *reinterpret_cast<uint2*>(orow + dim) = u;
+      } else {
+        *reinterpret_cast<float4*>(orow + dim) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+  if (lse_out && g == 0) {
+    *lse_out = R.l > 0.f ? (R.m + __log2f(R.l)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace sa

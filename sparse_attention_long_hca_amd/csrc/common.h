@@ -1,0 +1,107 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion, MFMA
+// wrappers, LDS addressing, XCD-aware block numbering and wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // storage type of a bfloat16 value
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// bfloat16 <-> float
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round to nearest, ties to even (the usual bias-and-truncate construction);
+// NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA (operand layouts checked on gfx950):
+//  16x16x32 bf16: A lane l holds A[l%16][(l/16)*8 + 0..7], B lane l holds
+//    B[(l/16)*8 + 0..7][l%16], C lane l holds C[(l/16)*4 + 0..3][l%16].
+//  16x16x4 f32:   A lane l holds A[l%16][l/16], B lane l holds B[l/16][l%16],
+//    C as above.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(i16x8_t a, i16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f32_16x16x4(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// LDS access
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ uint4 lds_read_b128(const char* lds_base, uint32_t byte_off) {
+  return *reinterpret_cast<const uint4*>(lds_base + byte_off);
+}
+__device__ __forceinline__ void lds_write_b128(char* lds_base, uint32_t byte_off, uint4 v) {
+  *reinterpret_cast<uint4*>(lds_base + byte_off) = v;
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane L supplies the address of 4 consecutive 16-bit values M[L][0..3];
+// lane i receives {M[i/4 + 4c][i%4] : c = 0..3}.
+__device__ __forceinline__ i16x4_t lds_read_tr16_b64(const char* p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions over lanes that share lane%16 (xor 16 and xor 32).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float max_across_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float sum_across_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Workgroups are dispatched to the XCDs round-robin (block b runs on XCD
+// b % 8).  Renumber so that consecutive logical ids run on the same XCD and
+// share its L2: XCD x gets a contiguous range of logical ids.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t n) {
+  const uint32_t q = n / kNumXcd, r = n % kNumXcd;
+  const uint32_t x = b % kNumXcd, local = b / kNumXcd;
+  return x * q + (x < r ? x : r) + local;
+}
+
+// Wave index within the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+__device__ __forceinline__ int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+}  // namespace sa

@@ -1,0 +1,248 @@
+// HCA decode attention (gfx950): one query per sequence and head.
+//
+// Method: [P1] §二.1, [P3] §架構創新 1 -- the query at position t = pos[b]
+// attends to the compressed entries j < floor((t - window + 1) / blk)
+// (capped at the cache size) and to the window tokens t - window < s <= t,
+// which live in a ring of `window` slots (slot = s mod window).
+//
+// The step is bound by HBM: every visible K and V row is read once.  A
+// workgroup (4 waves) handles one (batch, head, key split).  Each wave walks
+// its keys 8 at a time, 8 lanes per key: lane (slot, part) reads 16-byte
+// chunks part, part+8, ... of its key's K and V rows, so one load instruction
+// covers 8 rows x 128 contiguous bytes.  Dot products are fp32; the
+// 8-lane reduction uses cross-lane shuffles; softmax is online per wave.
+// With more than one split per (batch, head) the partial (o, lse) go to the
+// workspace and a second kernel combines them in split order.
+#include "common.h"
+#include "kernels.h"
+
+namespace sa {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecWaves = kDecThreads / kWave;
+
+__device__ __forceinline__ int64_t hca_visible_dec(int64_t t, int64_t blk, int64_t window) {
+  const int64_t x = t - window + 1;
+  return x > 0 ? x / blk : 0;
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams p) {
+  constexpr int kChunks = D / 8;           // 16-byte chunks per bf16 row
+  constexpr int kPer = kChunks / 8;        // chunks per lane (8 lanes per key)
+  __shared__ float sh_o[kDecWaves][D];
+  __shared__ float sh_m[kDecWaves], sh_l[kDecWaves];
+
+  const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t split = lid % p.nsplit;
+  const int64_t bh = lid / p.nsplit;
+  const int64_t b = bh / p.H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slot = lane >> 3, part = lane & 7;
+
+  int64_t t = p.pos[b];
+  if (t < 0) t = 0;
+  const int64_t nc = imin64(p.Ncap, hca_visible_dec(t, p.blk, p.window));
+  const int64_t nw = imin64(p.window, t + 1);
+  const int64_t n_keys = nc + nw;
+  const int64_t u_begin = split * p.keys_per_split;
+  const int64_t u_end = imin64(n_keys, u_begin + p.keys_per_split);
+
+  const bf16_t* q = reinterpret_cast<const bf16_t*>(p.q) + bh * D;
+  const bf16_t* kc = reinterpret_cast<const bf16_t*>(p.kc) + bh * p.Ncap * D;
+  const bf16_t* vc = reinterpret_cast<const bf16_t*>(p.vc) + bh * p.Ncap * D;
+  const bf16_t* rk = reinterpret_cast<const bf16_t*>(p.rk) + bh * p.window * D;
+  const bf16_t* rv = reinterpret_cast<const bf16_t*>(p.rv) + bh * p.window * D;
+  const int64_t win_first = t - nw + 1;  // first window position
+
+  // Query chunks part, part+8, ... pre-scaled to log2 units.
+  float qf[kPer * 8];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const uint4 u = *reinterpret_cast<const uint4*>(q + (part + 8 * i) * 8);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[i * 8 + 2 * e] = bf16_to_f32(w[e] & 0xffffu) * p.scale_log2;
+      qf[i * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u) * p.scale_log2;
+    }
+  }
+
+  float acc[kPer * 8];
+#pragma unroll
+  for (int i = 0; i < kPer * 8; ++i) acc[i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  // Keys of this split handled by this wave: groups of 8 consecutive keys,
+  // interleaved over the 4 waves.
+  for (int64_t g0 = u_begin + (int64_t)wave * 8; g0 < u_end; g0 += kDecWaves * 8) {
+    const int64_t u = g0 + slot;
+    const bool valid = u < u_end;
+    const bf16_t* krow = nullptr;
+    const bf16_t* vrow = nullptr;
+    if (valid) {
+      if (u < nc) {
+        krow = kc + u * D;
+        vrow = vc + u * D;
+      } else {
+        const int64_t s = win_first + (u - nc);
+        const int64_t sl = s % p.window;
+        krow = rk + sl * D;
+        vrow = rv + sl * D;
+      }
+    }
+    uint4 kr[kPer], vr[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (valid) {
+        kr[i] = *reinterpret_cast<const uint4*>(krow + (part + 8 * i) * 8);
+        vr[i] = *reinterpret_cast<const uint4*>(vrow + (part + 8 * i) * 8);
+      } else {
+        kr[i] = make_uint4(0u, 0u, 0u, 0u);
+        vr[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot = fmaf(qf[i * 8 + 2 * e], bf16_to_f32(w[e] & 0xffffu), dot);
+        dot = fmaf(qf[i * 8 + 2 * e + 1], __uint_as_float(w[e] & 0xffff0000u), dot);
+      }
+    }
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    dot += __shfl_xor(dot, 4);
+    const float x = valid ? dot : -INFINITY;
+    float gm = fmaxf(x, __shfl_xor(x, 8));
+    gm = fmaxf(gm, __shfl_xor(gm, 16));
+    gm = fmaxf(gm, __shfl_xor(gm, 32));
+    const float m_new = fmaxf(m, gm);  // finite: group has >= 1 valid key
+    const float alpha = fast_exp2(m - m_new);
+    const float pr = fast_exp2(x - m_new);
+    float ps = pr;
+    ps += __shfl_xor(ps, 8);
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * alpha + ps;
+    m = m_new;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[i * 8 + 2 * e] = fmaf(pr, bf16_to_f32(w[e] & 0xffffu), acc[i * 8 + 2 * e] * alpha);
+        acc[i * 8 + 2 * e + 1] = fmaf(pr, __uint_as_float(w[e] & 0xffff0000u), acc[i * 8 + 2 * e + 1] * alpha);
+      }
+    }
+  }
+
+  // Sum the 8 key slots of the wave (lanes with equal part).
+#pragma unroll
+  for (int i = 0; i < kPer * 8; ++i) {
+    float a = acc[i];
+    a += __shfl_xor(a, 8);
+    a += __shfl_xor(a, 16);
+    a += __shfl_xor(a, 32);
+    acc[i] = a;
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sh_o[wave][(part + 8 * i) * 8 + e] = acc[i * 8 + e];
+  }
+  if (lane == 0) {
+    sh_m[wave] = m;
+    sh_l[wave] = l;
+  }
+  __syncthreads();
+
+  // Combine the 4 waves (fixed order).
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, sh_m[w]);
+  float scale_w[kDecWaves];
+  float Lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
+    scale_w[w] = (M == -INFINITY) ? 0.f : fast_exp2(sh_m[w] - M);
+    Lsum += scale_w[w] * sh_l[w];
+  }
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  const float lse2 = Lsum > 0.f ? M + __log2f(Lsum) : -INFINITY;
+  for (int dd = threadIdx.x * 2; dd < D; dd += kDecThreads * 2) {
+    float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      o0 += scale_w[w] * sh_o[w][dd];
+      o1 += scale_w[w] * sh_o[w][dd + 1];
+    }
+    o0 *= inv;
+    o1 *= inv;
+    if (p.nsplit == 1) {
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<bf16_t*>(p.o) + bh * D + dd) = pack_bf16x2(o0, o1);
+    } else {
+      *reinterpret_cast<float2*>(p.part_o + (bh * p.nsplit + split) * D + dd) = make_float2(o0, o1);
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (p.nsplit == 1) {
+      if (p.lse) p.lse[bh] = lse2 * kLn2;
+    } else {
+      p.part_lse[bh * p.nsplit + split] = lse2;
+    }
+  }
+}
+
+// Combine the splits of one (batch, head) in split order.
+template <int D>
+__global__ __launch_bounds__(256) void hca_decode_combine_kernel(HcaDecodeParams p) {
+  const int64_t bh = blockIdx.x;
+  const float* pl = p.part_lse + bh * p.nsplit;
+  float M = -INFINITY;
+  for (int64_t s = 0; s < p.nsplit; ++s) M = fmaxf(M, pl[s]);
+  float Lsum = 0.f;
+  for (int64_t s = 0; s < p.nsplit; ++s) Lsum += (M == -INFINITY) ? 0.f : fast_exp2(pl[s] - M);
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  for (int dd = threadIdx.x * 2; dd < D; dd += 512) {
+    float o0 = 0.f, o1 = 0.f;
+    for (int64_t s = 0; s < p.nsplit; ++s) {
+      const float w = (M == -INFINITY) ? 0.f : fast_exp2(pl[s] - M);
+      const float2 v = *reinterpret_cast<const float2*>(p.part_o + (bh * p.nsplit + s) * D + dd);
+      o0 = fmaf(w, v.x, o0);
+      o1 = fmaf(w, v.y, o1);
+    }
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<bf16_t*>(p.o) + bh * D + dd) = pack_bf16x2(o0 * inv, o1 * inv);
+  }
+  if (threadIdx.x == 0 && p.lse) p.lse[bh] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : -INFINITY;
+}
+
+int64_t hca_decode_nsplit(int64_t BH, int64_t max_keys) {
+  // Enough workgroups to fill 256 CUs several times over, but at least 256
+  // keys per split so the per-split fixed cost stays small.
+  int64_t ns = (2048 + BH - 1) / BH;
+  const int64_t cap = (max_keys + 255) / 256;
+  if (ns > cap) ns = cap;
+  if (ns < 1) ns = 1;
+  return ns;
+}
+
+size_t hca_decode_workspace_bytes(int64_t BH, int64_t nsplit, int64_t d) {
+  if (nsplit <= 1) return 0;
+  return (size_t)(BH * nsplit * d + BH * nsplit) * sizeof(float);
+}
+
+hipError_t launch_hca_decode(const HcaDecodeParams& p, int dtype, int d, hipStream_t stream) {
+  if (dtype != 1 || d != 512) return hipErrorInvalidValue;
+  const int64_t BH = p.B * p.H;
+  hipLaunchKernelGGL(hca_decode_kernel<512>, dim3((uint32_t)(BH * p.nsplit)), dim3(kDecThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  hipLaunchKernelGGL(hca_decode_combine_kernel<512>, dim3((uint32_t)BH), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace sa

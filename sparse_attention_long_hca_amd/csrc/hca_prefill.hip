@@ -1,0 +1,132 @@
+// HCA prefill attention (gfx950).
+//
+// Method: [P1] §二.1 and [P3] §架構創新 1 -- each query attends to the
+// compressed history entries plus a window of recent uncompressed tokens.
+// Visibility: compressed entry j is visible to query t iff
+// (j+1)*blk - 1 <= t - window; raw token s iff t - window < s <= t.
+//
+// Work split: one workgroup per (batch*head, 64-query tile).  The key stream
+// of a tile is first the compressed entries visible to its last query (in
+// tiles of 32), then the raw band [t0-window+1, t_last] (in tiles of 32).  A
+// wave skips the MFMA work of a tile that none of its 16 queries can see.
+// Workgroups of one head are kept on one XCD (shared L2 for the compressed
+// cache and the overlapping raw band) and the longest tiles start first.
+#include "attn_core.h"
+#include "kernels.h"
+
+namespace sa {
+
+// Number of compressed entries visible to the query at position t.
+__device__ __forceinline__ int hca_visible(int t, int blk, int window) {
+  const int x = t - window + 1;
+  return x > 0 ? x / blk : 0;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kAttnThreads) void hca_prefill_kernel(HcaPrefillParams p) {
+  using G = AttnGeom<T, D>;
+  // Two pipeline stages as separate LDS objects, so the compiler can tell the
+  // in-flight loads into one stage from the reads of the other.
+  __shared__ __attribute__((aligned(16))) char lds0[G::kStageBytes];
+  __shared__ __attribute__((aligned(16))) char lds1[G::kStageBytes];
+
+  // Positions fit in 32 bits (checked on the host); pointer offsets are 64-bit.
+  const int n_qtiles = (int)p.n_qtiles;
+  const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = (int)(lid / (uint32_t)n_qtiles);
+  const int qt = n_qtiles - 1 - (int)(lid % (uint32_t)n_qtiles);
+  const int Tn = (int)p.T, blk = (int)p.blk, W = (int)p.window, Nc = (int)p.Nc;
+  const int t0 = qt * kBM;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int L = lane & 15;
+
+  const int64_t head_off = (int64_t)bh * Tn * D;
+  const T* q = reinterpret_cast<const T*>(p.q) + head_off;
+  const T* k = reinterpret_cast<const T*>(p.k) + head_off;
+  const T* v = reinterpret_cast<const T*>(p.v) + head_off;
+  const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)bh * Nc * D;
+  const T* vc = reinterpret_cast<const T*>(p.vc) + (int64_t)bh * Nc * D;
+  T* o = reinterpret_cast<T*>(p.o) + head_off;
+
+  const int tw = t0 + wave * kRowsPerWave;  // first query of this wave
+  const int tq = tw + L;                    // this lane's query
+  const bool qvalid = tq < Tn;
+
+  AttnRegs<T, D> R;
+  load_q(R, qvalid ? q + (int64_t)tq * D : nullptr);
+
+  // Key stream of the workgroup.
+  const int t_last = min(t0 + kBM - 1, Tn - 1);
+  const int nc = min(Nc, hca_visible(t_last, blk, W));
+  const int n_ctiles = (nc + kBN - 1) / kBN;
+  const int s_lo = max(0, t0 - W + 1);
+  const int n_rtiles = (t_last - s_lo + kBN) / kBN;
+  const int n_tiles = n_ctiles + n_rtiles;
+
+  // This lane's visibility limits.
+  const int vis_c = qvalid ? min(Nc, hca_visible(tq, blk, W)) : 0;
+  const int win_lo = tq - W + 1;
+  // This wave's limits (for skipping whole tiles).
+  const bool wvalid = tw < Tn;
+  const int tw_last = min(tw + kRowsPerWave - 1, Tn - 1);
+  const int wave_nc = wvalid ? min(Nc, hca_visible(tw_last, blk, W)) : 0;
+  const int wave_lo = tw - W + 1;
+
+  // Tile t < n_ctiles: compressed entries [32t, 32t+32) of kc/vc; otherwise
+  // raw positions from s_lo onwards.  Rows past the segment end are padding.
+  auto issue = [&](int tile, char* buf) {
+    const bool ct = tile < n_ctiles;
+    const T* kbase = ct ? kc : k;
+    const T* vbase = ct ? vc : v;
+    const int first = ct ? tile * kBN : s_lo + (tile - n_ctiles) * kBN;
+    const int last = ct ? nc - 1 : t_last;
+    stage_async<T, D>(buf, buf + G::kTileBytes, kbase, vbase, [=](int r) -> int {
+      const int x = first + r;
+      return x <= last ? x : -1;
+    });
+  };
+  auto compute = [&](int tile, const char* buf) {
+    const bool ctile = tile < n_ctiles;
+    const int j0 = tile * kBN;
+    const int s0 = s_lo + (tile - n_ctiles) * kBN;
+    const bool need = ctile ? (j0 < wave_nc) : (wvalid && s0 <= tw_last && s0 + kBN - 1 >= wave_lo);
+    if (need)
+      attend_tile<T, D>(R, buf, buf + G::kTileBytes, p.scale_log2, [&](int key) {
+        if (ctile) return j0 + key < vis_c;
+        const int s = s0 + key;
+        return s >= win_lo && s <= tq;
+      });
+  };
+
+  // Two-stage pipeline, unrolled by two so each stage buffer has a fixed role.
+  if (n_tiles > 0) issue(0, lds0);
+  for (int tile = 0; tile < n_tiles; tile += 2) {
+    wait_loads<0>();
+    __syncthreads();
+    if (tile + 1 < n_tiles) issue(tile + 1, lds1);
+    compute(tile, lds0);
+    if (tile + 1 >= n_tiles) break;
+    wait_loads<0>();
+    __syncthreads();
+    if (tile + 2 < n_tiles) issue(tile + 2, lds0);
+    compute(tile + 1, lds1);
+  }
+  finish_rows<T, D>(R, qvalid ? o + (int64_t)tq * D : nullptr,
+                    (p.lse && qvalid) ? p.lse + (int64_t)bh * Tn + tq : nullptr);
+}
+
+template <typename T, int D>
+static hipError_t launch(const HcaPrefillParams& p, hipStream_t stream) {
+  const int64_t nblocks = p.B * p.H * p.n_qtiles;
+  hipLaunchKernelGGL((hca_prefill_kernel<T, D>), dim3((uint32_t)nblocks), dim3(kAttnThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_hca_prefill(const HcaPrefillParams& p, int dtype, int d, hipStream_t stream) {
+  if (dtype == 0 && d == 64) return launch<float, 64>(p, stream);
+  if (dtype == 1 && d == 512) return launch<bf16_t, 512>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa

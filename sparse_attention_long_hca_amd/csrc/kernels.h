@@ -1,0 +1,89 @@
+// Kernel parameter blocks and host launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+// ---- hca_compress ----------------------------------------------------------
+struct HcaCompressParams {
+  const void* x;
+  void* out;
+  int64_t B, H, n_out, d, blk;
+  int64_t x_sb, x_sh, x_st;
+  int64_t o_sb, o_sh, o_sn;
+};
+hipError_t launch_hca_compress(const HcaCompressParams& p, int dtype, hipStream_t stream);
+
+// ---- hca_attention_fwd, prefill ---------------------------------------------
+struct HcaPrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* kc;
+  const void* vc;
+  void* o;
+  float* lse;
+  int64_t B, H, T, Nc, blk, window;
+  float scale_log2;
+  int64_t n_qtiles;
+};
+hipError_t launch_hca_prefill(const HcaPrefillParams& p, int dtype, int d, hipStream_t stream);
+
+// ---- hca_attention_fwd, decode ----------------------------------------------
+struct HcaDecodeParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const void* rk;  // window ring [B,H,window,d]
+  const void* rv;
+  const int64_t* pos;
+  void* o;
+  float* lse;
+  float* part_o;    // [B*H*nsplit, d]  (nsplit > 1)
+  float* part_lse;  // [B*H*nsplit]     log2 units
+  int64_t B, H, Ncap, blk, window;
+  float scale_log2;
+  int64_t nsplit, keys_per_split;
+};
+int64_t hca_decode_nsplit(int64_t BH, int64_t max_keys);
+size_t hca_decode_workspace_bytes(int64_t BH, int64_t nsplit, int64_t d);
+hipError_t launch_hca_decode(const HcaDecodeParams& p, int dtype, int d, hipStream_t stream);
+
+// ---- dsa_indexer_scores -----------------------------------------------------
+struct DsaIndexerParams {
+  const void* q;   // [B,T,Hi,Di] bf16
+  const void* k;   // [B,S,Di] bf16
+  const float* w;  // [B,T,Hi]
+  const int64_t* q_pos;
+  float* scores;  // [B,T,S]
+  int64_t B, T, S;
+};
+hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream);
+
+// ---- dsa_topk ---------------------------------------------------------------
+struct DsaTopkParams {
+  const float* scores;
+  const int64_t* q_pos;
+  int32_t* idx;
+  int64_t B, T, S, k;
+  void* ws;
+};
+size_t dsa_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k);
+hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream);
+
+// ---- dsa_sparse_attention_fwd -----------------------------------------------
+struct DsaSparseParams {
+  const void* q;  // [B,T,Hq,D]
+  const void* k;  // [B,S,D]
+  const void* v;
+  const int32_t* idx;  // [B,T,kk]
+  void* o;
+  float* lse;
+  int64_t B, T, S, kk;
+  float scale_log2;
+};
+hipError_t launch_dsa_sparse(const DsaSparseParams& p, int d, int hq, hipStream_t stream);
+
+}  // namespace sa

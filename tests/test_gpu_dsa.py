@@ -1,0 +1,197 @@
+"""GPU parity: DSA indexer, top-k and sparse attention (HIP library through the C ABI) vs the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import BF16_ABS_TOL, DEV, f64, max_abs_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _indexer_inputs(B, T, S, workload, grid=False):
+    if grid:
+        qi = synth.np_int_grid((B, T, 4, 128), [v / 4 for v in range(-3, 4)], workload, 0)
+        ki = synth.np_int_grid((B, S, 128), [v / 4 for v in range(-3, 4)], workload, 1)
+        w = synth.np_int_grid((B, T, 4), [0, 0.25, 0.5, 0.75, 1.0], workload, 2)
+    else:
+        qi = synth.np_normal((B, T, 4, 128), 128 ** -0.5, "bf16", workload, 0)
+        ki = synth.np_normal((B, S, 128), 128 ** -0.5, "bf16", workload, 1)
+        w = synth.np_uniform((B, T, 4), workload, 2)
+    return qi, ki, w
+
+
+def _causal_mask(B, T, S, q_pos):
+    m = np.zeros((B, T, S), dtype=bool)
+    for b in range(B):
+        base = 0 if q_pos is None else q_pos[b]
+        for i in range(T):
+            m[b, i, : min(S, base + i + 1)] = True
+    return m
+
+
+# ---------------------------------------------------------------------------
+# indexer
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("B,T,S,q_pos", [(1, 300, 300, None), (2, 70, 333, [263, 100]), (1, 1, 5000, [4999]),
+                                         (1, 129, 1100, [900])])
+def test_indexer_random(B, T, S, q_pos):
+    sa = require_gpu()
+    qi, ki, w = _indexer_inputs(B, T, S, 30 + T)
+    qp = None if q_pos is None else torch.tensor(q_pos, dtype=torch.int64, device=DEV)
+    sc = sa.dsa_indexer_scores(synth.to_torch(qi, "bf16", DEV), synth.to_torch(ki, "bf16", DEV),
+                               synth.to_torch(w, "f32", DEV), q_pos=qp)
+    want = oracle.dsa_indexer_scores(qi, ki, w, q_pos=q_pos)
+    m = _causal_mask(B, T, S, q_pos)
+    got = f64(sc)
+    # fp32 accumulation of 128 exact bf16 products: |err| <= ~1e-6 on O(1) scores
+    assert np.max(np.abs(got[m] - want[m])) <= 2e-6
+
+
+def test_indexer_integer_grid_bit_exact():
+    sa = require_gpu()
+    B, T, S = 1, 200, 260
+    qi, ki, w = _indexer_inputs(B, T, S, 31, grid=True)
+    qp = torch.tensor([59], dtype=torch.int64, device=DEV)
+    sc = sa.dsa_indexer_scores(synth.to_torch(qi, "bf16", DEV), synth.to_torch(ki, "bf16", DEV),
+                               synth.to_torch(w, "f32", DEV), q_pos=qp)
+    want = oracle.dsa_indexer_scores(qi, ki, w, q_pos=[59])
+    m = _causal_mask(B, T, S, [59])
+    assert np.array_equal(f64(sc)[m], want[m])
+
+
+# ---------------------------------------------------------------------------
+# top-k: GPU top-k on the GPU's own scores vs the oracle top-k on the same scores -> bit-exact
+# ---------------------------------------------------------------------------
+
+
+def _topk_check(sa, scores_np, k, q_pos):
+    scores = torch.from_numpy(scores_np.astype(np.float32)).to(DEV)
+    qp = None if q_pos is None else torch.tensor(q_pos, dtype=torch.int64, device=DEV)
+    idx = sa.dsa_topk(scores, k, q_pos=qp)
+    want = oracle.dsa_topk(scores_np.astype(np.float32), k, q_pos=q_pos)
+    got = idx.cpu().numpy()
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"first mismatch at {bad[:3]}: got {got[tuple(bad[0][:2])][:8]} want {want[tuple(bad[0][:2])][:8]}"
+
+
+@pytest.mark.parametrize("T,S,k", [(300, 300, 64), (70, 2100, 2048), (40, 5000, 1)])
+def test_topk_random(T, S, k):
+    sa = require_gpu()
+    g = np.random.default_rng(40 + T)
+    sc = g.standard_normal((1, T, S)).astype(np.float32)
+    _topk_check(sa, sc, k, [S - T])
+
+
+def test_topk_heavy_ties_and_signed_zero():
+    sa = require_gpu()
+    g = np.random.default_rng(41)
+    sc = g.integers(-2, 3, size=(2, 50, 3000)).astype(np.float32) * 0.5
+    sc[sc == 0] = np.where(g.random(np.count_nonzero(sc == 0)) < 0.5, -0.0, 0.0)
+    _topk_check(sa, sc, 700, [2950, 1000])
+
+
+def test_topk_constant_rows_take_lowest():
+    sa = require_gpu()
+    sc = np.full((1, 3, 4000), 0.125, dtype=np.float32)
+    _topk_check(sa, sc, 2048, [3997])
+
+
+def test_topk_multi_workgroup_path():
+    """Rows longer than the on-chip limit (S > 32768) use the multi-workgroup path."""
+    sa = require_gpu()
+    g = np.random.default_rng(42)
+    S = 70000
+    sc = (g.integers(0, 5000, size=(2, 3, S)) / 64.0).astype(np.float32)  # many ties
+    _topk_check(sa, sc, 2048, [S - 3, 40000])
+
+
+def test_topk_on_indexer_scores():
+    """The real chain: GPU indexer scores -> GPU top-k vs oracle top-k on those scores."""
+    sa = require_gpu()
+    T, S, k = 400, 400, 128
+    qi, ki, w = _indexer_inputs(1, T, S, 43)
+    sc = sa.dsa_indexer_scores(synth.to_torch(qi, "bf16", DEV), synth.to_torch(ki, "bf16", DEV),
+                               synth.to_torch(w, "f32", DEV))
+    sc_np = sc.cpu().numpy()
+    idx = sa.dsa_topk(sc, k).cpu().numpy()
+    want = oracle.dsa_topk(np.where(_causal_mask(1, T, S, None), sc_np, np.nan), k)
+    assert np.array_equal(idx, want)
+
+
+# ---------------------------------------------------------------------------
+# sparse attention
+# ---------------------------------------------------------------------------
+
+
+def _random_idx(B, T, S, kk, g, q_pos=None):
+    idx = np.full((B, T, kk), -1, dtype=np.int64)
+    for b in range(B):
+        for i in range(T):
+            p = min(S - 1, (0 if q_pos is None else q_pos[b]) + i)
+            n = min(kk, p + 1)
+            sel = np.sort(g.choice(p + 1, size=n, replace=False))
+            idx[b, i, :n] = sel
+    return idx
+
+
+@pytest.mark.parametrize("B,T,S,kk", [(1, 40, 400, 128), (2, 9, 3000, 2048), (1, 64, 64, 100), (1, 5, 50, 33)])
+def test_sparse_attention_unit_variance(B, T, S, kk):
+    sa = require_gpu()
+    g = np.random.default_rng(50 + kk)
+    q = synth.np_normal((B, T, 64, 256), 1.0, "bf16", 51, 0)
+    k = synth.np_normal((B, S, 256), 1.0, "bf16", 51, 1)
+    v = synth.np_normal((B, S, 256), 1.0, "bf16", 51, 2)
+    idx = _random_idx(B, T, S, kk, g, q_pos=[S - T] * B)
+    o, lse = sa.dsa_sparse_attention_fwd(synth.to_torch(q, "bf16", DEV), synth.to_torch(k, "bf16", DEV),
+                                         synth.to_torch(v, "bf16", DEV),
+                                         torch.from_numpy(idx.astype(np.int32)).to(DEV), return_lse=True)
+    ow, lw = oracle.dsa_sparse_attention(q, k, v, idx)
+    assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL
+    assert max_abs_err(f64(lse), lw) <= 1e-2
+
+
+def test_sparse_attention_skips_out_of_range_and_empty_rows():
+    sa = require_gpu()
+    B, T, S, kk = 1, 4, 100, 40
+    q = synth.np_normal((B, T, 64, 256), 1.0, "bf16", 52, 0)
+    k = synth.np_normal((B, S, 256), 1.0, "bf16", 52, 1)
+    v = synth.np_normal((B, S, 256), 1.0, "bf16", 52, 2)
+    idx = np.full((B, T, kk), -1, dtype=np.int64)
+    idx[0, 0, :5] = [3, 150, 7, -9, 99]  # 150 and -9 are out of range
+    idx[0, 1, 10:12] = [42, 43]
+    idx[0, 3, :] = np.arange(kk)
+    o, lse = sa.dsa_sparse_attention_fwd(synth.to_torch(q, "bf16", DEV), synth.to_torch(k, "bf16", DEV),
+                                         synth.to_torch(v, "bf16", DEV),
+                                         torch.from_numpy(idx.astype(np.int32)).to(DEV), return_lse=True)
+    clean = np.where((idx >= 0) & (idx < S), idx, -1)
+    ow, lw = oracle.dsa_sparse_attention(q, k, v, clean)
+    assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL
+    assert np.all(f64(o)[0, 2] == 0) and np.all(np.isneginf(f64(lse)[0, 2]))
+    fin = np.isfinite(lw)
+    assert max_abs_err(f64(lse)[fin], lw[fin]) <= 1e-2
+
+
+def test_dsa_end_to_end_k_ge_context_is_dense():
+    """k >= context: the chain reduces to dense causal multi-query attention."""
+    sa = require_gpu()
+    T = 300
+    qi, ki, w = _indexer_inputs(1, T, T, 53)
+    q = synth.np_normal((1, T, 64, 256), 1.0, "bf16", 54, 0)
+    k = synth.np_normal((1, T, 256), 1.0, "bf16", 54, 1)
+    v = synth.np_normal((1, T, 256), 1.0, "bf16", 54, 2)
+    sc = sa.dsa_indexer_scores(synth.to_torch(qi, "bf16", DEV), synth.to_torch(ki, "bf16", DEV),
+                               synth.to_torch(w, "f32", DEV))
+    idx = sa.dsa_topk(sc, 512)
+    o = sa.dsa_sparse_attention_fwd(synth.to_torch(q, "bf16", DEV), synth.to_torch(k, "bf16", DEV),
+                                    synth.to_torch(v, "bf16", DEV), idx)
+    dense = np.full((1, T, 512), -1)
+    for i in range(T):
+        dense[0, i, : i + 1] = np.arange(i + 1)
+    assert np.array_equal(idx.cpu().numpy(), dense)
+    ow, _ = oracle.dsa_sparse_attention(q, k, v, dense)
+    assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL

@@ -1,0 +1,149 @@
+"""GPU parity: HCA compression and attention (HIP library through the C ABI) vs the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import BF16_ABS_TOL, DEV, F32_REL_TOL, f64, max_abs_err, rel_err_normwise, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(shape, dtype, sigma, workload):
+    arrs = [synth.np_normal(shape, sigma, dtype, workload, tid) for tid in range(3)]
+    return arrs, [synth.to_torch(a, dtype, DEV) for a in arrs]
+
+
+# ---------------------------------------------------------------------------
+# hca_compress
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype,d,T,blk", [("f32", 64, 1024, 128), ("f32", 64, 300, 128), ("bf16", 512, 700, 128),
+                                           ("bf16", 512, 37, 4), ("bf16", 256, 260, 128), ("f32", 64, 9, 1)])
+def test_compress(dtype, d, T, blk):
+    sa = require_gpu()
+    x = synth.np_normal((2, 3, T, d), 1.0, dtype, 101, 0)
+    out = sa.hca_compress(synth.to_torch(x, dtype, DEV), blk)
+    want = oracle.hca_compress(x, blk)
+    got = f64(out)
+    assert got.shape == want.shape
+    if dtype == "f32":
+        assert max_abs_err(got, want) <= 1e-6 * max(1.0, np.max(np.abs(want)))
+    else:  # fp32 sum, one RNE rounding to bf16: within one bf16 ulp
+        assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-30)
+
+
+def test_compress_strided_into_cache_slot():
+    """Compress a window ring [B,H,128,d] into slot j of a larger cache via strides."""
+    sa = require_gpu()
+    B, H, d, blk, ncap, slot = 2, 3, 512, 128, 8, 5
+    ring = synth.np_normal((B, H, blk, d), 1.0, "bf16", 102, 0)
+    cache = torch.zeros((B, H, ncap, d), dtype=torch.bfloat16, device=DEV)
+    sa.hca_compress(synth.to_torch(ring, "bf16", DEV), blk, out=cache[:, :, slot:slot + 1])
+    got = f64(cache)
+    want = oracle.hca_compress(ring, blk)[:, :, 0]
+    assert np.all(np.abs(got[:, :, slot] - want) <= 2.0 ** -8 * np.abs(want) + 1e-30)
+    others = [j for j in range(ncap) if j != slot]
+    assert np.all(got[:, :, others] == 0)
+
+
+# ---------------------------------------------------------------------------
+# HCA prefill
+# ---------------------------------------------------------------------------
+
+
+def _prefill_gpu(sa, tq, tk, tv, blk, window):
+    kc = sa.hca_compress(tk, blk)
+    vc = sa.hca_compress(tv, blk)
+    return sa.hca_attention_fwd(sa.HCA_PREFILL, tq, tk, tv, kc, vc, blk, window, return_lse=True)
+
+
+def test_prefill_tiny_f32_config():
+    """Tiny HCA forward, fp32: [1,4,1024,64], blk = window = 128; normwise rel <= 1e-5 on every row."""
+    sa = require_gpu()
+    (q, k, v), (tq, tk, tv) = _inputs((1, 4, 1024, 64), "f32", 1.0, 1)
+    o, lse = _prefill_gpu(sa, tq, tk, tv, 128, 128)
+    ow, lw = oracle.hca_attention_prefill(q, k, v, oracle.hca_compress(k, 128), oracle.hca_compress(v, 128), 128, 128)
+    assert rel_err_normwise(f64(o), ow) <= F32_REL_TOL
+    assert max_abs_err(f64(lse), lw) <= 1e-5 * max(1.0, np.max(np.abs(lw)))
+
+
+@pytest.mark.parametrize(
+    "T,blk,window,H",
+    [(700, 128, 128, 2), (257, 128, 128, 1), (64, 128, 128, 1), (200, 4, 6, 2), (130, 1, 5, 1), (150, 16, 200, 1),
+     (1, 128, 128, 1), (333, 32, 1, 1)],
+)
+def test_prefill_bf16_d512(T, blk, window, H):
+    """bf16 head dim 512 on unit-variance inputs: max-abs <= 2e-2 (covers several tiles, ragged tails,
+    blk = 1 (dense causal), window >= T (dense causal), window = 1)."""
+    sa = require_gpu()
+    (q, k, v), (tq, tk, tv) = _inputs((1, H, T, 512), "bf16", 1.0, 2 + T + blk)
+    o, lse = _prefill_gpu(sa, tq, tk, tv, blk, window)
+    ow, lw = oracle.hca_attention_prefill(q, k, v, oracle.hca_compress(k, blk), oracle.hca_compress(v, blk), blk, window)
+    assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL
+    assert max_abs_err(f64(lse), lw) <= 1e-2
+
+
+def test_prefill_same_cache_isolates_attention():
+    """Feed both sides the same bf16 compressed cache: attention error alone."""
+    sa = require_gpu()
+    T, blk, window = 600, 128, 128
+    (q, k, v), (tq, tk, tv) = _inputs((2, 2, T, 512), "bf16", 1.0, 7)
+    kc = sa.hca_compress(tk, blk)
+    vc = sa.hca_compress(tv, blk)
+    o = sa.hca_attention_fwd(sa.HCA_PREFILL, tq, tk, tv, kc, vc, blk, window)
+    ow, _ = oracle.hca_attention_prefill(q, k, v, f64(kc), f64(vc), blk, window)
+    assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL
+
+
+def test_prefill_deterministic():
+    sa = require_gpu()
+    (_, _, _), (tq, tk, tv) = _inputs((1, 2, 500, 512), "bf16", 1.0, 8)
+    a, la = _prefill_gpu(sa, tq, tk, tv, 128, 128)
+    b, lb = _prefill_gpu(sa, tq, tk, tv, 128, 128)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+# ---------------------------------------------------------------------------
+# HCA decode
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("B,H,ncap,positions", [(3, 2, 10, [0, 130, 1407]), (2, 3, 12, [5000, 127]),
+                                                 (1, 2, 2000, [256000]), (4, 1, 3, [255, 256, 383, 384])])
+def test_decode_bf16(B, H, ncap, positions):
+    sa = require_gpu()
+    blk, window, d = 128, 128, 512
+    q = synth.np_normal((B, H, d), 1.0, "bf16", 20, 0)
+    kc = synth.np_normal((B, H, ncap, d), 1.0, "bf16", 20, 1)
+    vc = synth.np_normal((B, H, ncap, d), 1.0, "bf16", 20, 2)
+    rk = synth.np_normal((B, H, window, d), 1.0, "bf16", 20, 3)
+    rv = synth.np_normal((B, H, window, d), 1.0, "bf16", 20, 4)
+    pos = torch.tensor(positions, dtype=torch.int64, device=DEV)
+    t = [synth.to_torch(a, "bf16", DEV) for a in (q, rk, rv, kc, vc)]
+    o, lse = sa.hca_attention_fwd(sa.HCA_DECODE, t[0], t[1], t[2], t[3], t[4], blk, window, pos=pos, return_lse=True)
+    ow, lw = oracle.hca_attention_decode(q, kc, vc, rk, rv, positions, blk, window)
+    assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL
+    assert max_abs_err(f64(lse), lw) <= 1e-2
+
+
+def test_decode_equals_prefill_row():
+    """Cross-mode: decode at position t (ring = last window tokens) equals prefill row t."""
+    sa = require_gpu()
+    T, blk, window, d = 900, 128, 128, 512
+    (q, k, v), (tq, tk, tv) = _inputs((1, 2, T, d), "bf16", 1.0, 21)
+    kc = sa.hca_compress(tk, blk)
+    vc = sa.hca_compress(tv, blk)
+    o_pre = sa.hca_attention_fwd(sa.HCA_PREFILL, tq, tk, tv, kc, vc, blk, window)
+    for t in (0, 200, 511, 767, 899):
+        ring_k = torch.zeros((1, 2, window, d), dtype=torch.bfloat16, device=DEV)
+        ring_v = torch.zeros_like(ring_k)
+        for s in range(max(0, t - window + 1), t + 1):
+            ring_k[:, :, s % window] = tk[:, :, s]
+            ring_v[:, :, s % window] = tv[:, :, s]
+        pos = torch.tensor([t], dtype=torch.int64, device=DEV)
+        o_dec = sa.hca_attention_fwd(sa.HCA_DECODE, tq[:, :, t].contiguous(), ring_k, ring_v, kc, vc, blk, window, pos=pos)
+        assert max_abs_err(f64(o_dec), f64(o_pre[:, :, t])) <= 1e-2, f"t={t}"
