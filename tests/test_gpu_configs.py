@@ -1,0 +1,164 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+
+The oracle cannot run these workloads whole, so each test checks sampled
+outputs that the oracle computes one by one (chosen rows / heads / sequences,
+including the first and last positions and the block and window edges).
+Inputs come from the seeded device generators in synth.py; the oracle gets
+the same bits by copying the needed slices to the host.
+
+Tolerances: fp32 workloads 1e-5 normwise relative; bf16 workloads 2e-2
+max-abs on unit-variance inputs, and 2e-2 * sigma_V on the workloads' own
+N(0,1)/sqrt(d) inputs.  Top-k is bit-exact on the GPU's own scores, and
+against the oracle's float64 scores with positions within 1e-6 of the k-th
+score excluded.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import BF16_ABS_TOL, DEV, f64, max_abs_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+BLK = WIN = 128
+
+
+def _hca_prefill_case(sa, sigma, seed):
+    T, H, d = 32768, 64, 512
+    q = synth.torch_normal((1, H, T, d), sigma, torch.bfloat16, seed, DEV)
+    k = synth.torch_normal((1, H, T, d), sigma, torch.bfloat16, seed + 1, DEV)
+    v = synth.torch_normal((1, H, T, d), sigma, torch.bfloat16, seed + 2, DEV)
+    kc = sa.hca_compress(k, BLK)
+    vc = sa.hca_compress(v, BLK)
+    o, lse = sa.hca_attention_fwd(sa.HCA_PREFILL, q, k, v, kc, vc, BLK, WIN, return_lse=True)
+    torch.cuda.synchronize()
+    rows = [0, 1, 126, 127, 128, 254, 255, 256, 383, 1000, 4097, 16384, 20000, 32639, 32640, 32767]
+    g = np.random.default_rng(seed)
+    rows += [int(x) for x in g.integers(0, T, size=8)]
+    worst = 0.0
+    for h in (0, 37, 63):
+        qh, kh, vh = f64(q[:, h:h + 1]), f64(k[:, h:h + 1]), f64(v[:, h:h + 1])
+        ow, lw = oracle.hca_attention_prefill(qh, kh, vh, oracle.hca_compress(kh, BLK), oracle.hca_compress(vh, BLK),
+                                              BLK, WIN, rows=rows)
+        got = f64(o[:, h:h + 1, rows])
+        worst = max(worst, max_abs_err(got, ow))
+        assert max_abs_err(f64(lse[:, h:h + 1, rows]), lw) <= 1e-2
+    del q, k, v, kc, vc, o, lse
+    torch.cuda.empty_cache()
+    return worst
+
+
+def test_hca_prefill_32768x64x512_unit_variance():
+    sa = require_gpu()
+    assert _hca_prefill_case(sa, 1.0, 1200) <= BF16_ABS_TOL
+
+
+def test_hca_prefill_32768x64x512_config_distribution():
+    sa = require_gpu()
+    sigma = 1.0 / math.sqrt(512)
+    assert _hca_prefill_case(sa, sigma, 1300) <= BF16_ABS_TOL * sigma
+
+
+@pytest.mark.parametrize("B,ncap,pos,sigma", [(64, 1024, 131071, 1.0), (64, 1024, 131071, 512 ** -0.5),
+                                              (4, 8192, 1048575, 1.0)])
+def test_hca_decode_full(B, ncap, pos, sigma):
+    sa = require_gpu()
+    H, d = 64, 512
+    q = synth.torch_normal((B, H, d), sigma, torch.bfloat16, 1400, DEV)
+    kc = synth.torch_normal((B, H, ncap, d), sigma, torch.bfloat16, 1401, DEV)
+    vc = synth.torch_normal((B, H, ncap, d), sigma, torch.bfloat16, 1402, DEV)
+    rk = synth.torch_normal((B, H, WIN, d), sigma, torch.bfloat16, 1403, DEV)
+    rv = synth.torch_normal((B, H, WIN, d), sigma, torch.bfloat16, 1404, DEV)
+    posd = torch.full((B,), pos, dtype=torch.int64, device=DEV)
+    o, lse = sa.hca_attention_fwd(sa.HCA_DECODE, q, rk, rv, kc, vc, BLK, WIN, pos=posd, return_lse=True)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (B - 1, 63), (B // 2, 17), (1, 40)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ow, lw = oracle.hca_attention_decode(f64(q[sl]), f64(kc[sl]), f64(vc[sl]), f64(rk[sl]), f64(rv[sl]), [pos],
+                                             BLK, WIN)
+        assert max_abs_err(f64(o[sl]), ow) <= BF16_ABS_TOL * sigma, (b, h)
+        assert max_abs_err(f64(lse[sl]), lw) <= 1e-2
+
+
+def _band_compare(got_idx, oracle_scores, k):
+    """Top-k vs the oracle's float64 scores: positions within 1e-6 of the k-th score are excluded."""
+    valid = np.isfinite(oracle_scores)
+    cand = np.nonzero(valid)[0]
+    want = oracle.dsa_topk(oracle_scores.reshape(1, 1, -1), k, q_pos=[cand.size - 1])[0, 0]
+    got = got_idx[got_idx >= 0]
+    want = want[want >= 0]
+    if cand.size <= k:
+        assert np.array_equal(got, want)
+        return 0
+    kth = np.sort(oracle_scores[cand])[::-1][k - 1]
+    band = set(np.nonzero(np.abs(oracle_scores - kth) <= 1e-6)[0].tolist())
+    g = set(got.tolist()) - band
+    w = set(want.tolist()) - band
+    assert g == w, (len(g ^ w), len(band))
+    return len(band)
+
+
+def _dsa_inputs(B, T, S, sigma, seed):
+    qi = synth.torch_normal((B, T, 4, 128), 128 ** -0.5, torch.bfloat16, seed, DEV)
+    ki = synth.torch_normal((B, S, 128), 128 ** -0.5, torch.bfloat16, seed + 1, DEV)
+    w = synth.torch_uniform((B, T, 4), seed + 2, DEV)
+    q = synth.torch_normal((B, T, 64, 256), sigma, torch.bfloat16, seed + 3, DEV)
+    k = synth.torch_normal((B, S, 256), sigma, torch.bfloat16, seed + 4, DEV)
+    v = synth.torch_normal((B, S, 256), sigma, torch.bfloat16, seed + 5, DEV)
+    return qi, ki, w, q, k, v
+
+
+@pytest.mark.parametrize("sigma", [1.0, 1.0 / 16])
+def test_dsa_prefill_32768_top2048(sigma):
+    sa = require_gpu()
+    T = S = 32768
+    kk = 2048
+    qi, ki, w, q, k, v = _dsa_inputs(1, T, S, sigma, 1500)
+    sc = sa.dsa_indexer_scores(qi, ki, w)
+    idx = sa.dsa_topk(sc, kk)
+    o, lse = sa.dsa_sparse_attention_fwd(q, k, v, idx, return_lse=True)
+    torch.cuda.synchronize()
+    rows = [0, 1, 2046, 2047, 2048, 2049, 4095, 10000, 32767]
+    rows += [int(x) for x in np.random.default_rng(1501).integers(2048, T, size=6)]
+    ki_h, q_h, k_h, v_h = f64(ki), None, f64(k), f64(v)
+    for i in rows:
+        sc_row = sc[0, i, : i + 1].cpu().numpy().astype(np.float64)
+        want_sc = oracle.dsa_indexer_scores(f64(qi[:, i:i + 1]), ki_h[:, : i + 1], f64(w[:, i:i + 1]), q_pos=[i])[0, 0]
+        assert np.max(np.abs(sc_row - want_sc)) <= 2e-6, i
+        got_idx = idx[0, i].cpu().numpy().astype(np.int64)
+        # bit-exact on the GPU's own scores
+        assert np.array_equal(got_idx, oracle.dsa_topk(sc_row.reshape(1, 1, -1), kk, q_pos=[i])[0, 0]), i
+        # band comparison against the oracle's float64 scores
+        _band_compare(got_idx, want_sc, kk)
+        # attention on the GPU's indices
+        ow, lw = oracle.dsa_sparse_attention(f64(q[:, i:i + 1]), k_h, v_h, got_idx.reshape(1, 1, -1))
+        assert max_abs_err(f64(o[:, i:i + 1]), ow) <= BF16_ABS_TOL * sigma, i
+        assert max_abs_err(f64(lse[:, i:i + 1]), lw) <= 1e-2, i
+
+
+def test_dsa_decode_1m():
+    sa = require_gpu()
+    B, S, kk = 4, 1 << 20, 2048
+    qi, ki, w, q, k, v = _dsa_inputs(B, 1, S, 1.0, 1600)
+    qpos = torch.full((B,), S - 1, dtype=torch.int64, device=DEV)
+    sc = sa.dsa_indexer_scores(qi, ki, w, q_pos=qpos)
+    idx = sa.dsa_topk(sc, kk, q_pos=qpos)
+    o = sa.dsa_sparse_attention_fwd(q, k, v, idx)
+    torch.cuda.synchronize()
+    for b in range(B):
+        sc_row = sc[b, 0].cpu().numpy().astype(np.float64)
+        want_sc = oracle.dsa_indexer_scores(f64(qi[b:b + 1]), f64(ki[b:b + 1]), f64(w[b:b + 1]), q_pos=[S - 1])[0, 0]
+        assert np.max(np.abs(sc_row - want_sc)) <= 2e-6, b
+        got_idx = idx[b, 0].cpu().numpy().astype(np.int64)
+        assert np.array_equal(got_idx, oracle.dsa_topk(sc_row.reshape(1, 1, -1), kk, q_pos=[S - 1])[0, 0]), b
+        _band_compare(got_idx, want_sc, kk)
+        # gather only the selected rows for the oracle (same math, positions renumbered 0..n-1)
+        sel = torch.from_numpy(got_idx[got_idx >= 0]).to(DEV)
+        local = np.arange(sel.numel()).reshape(1, 1, -1)
+        ow, _ = oracle.dsa_sparse_attention(f64(q[b:b + 1]), f64(k[b:b + 1, sel]), f64(v[b:b + 1, sel]), local)
+        assert max_abs_err(f64(o[b:b + 1]), ow) <= BF16_ABS_TOL, b
