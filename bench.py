@@ -39,7 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of parts: prefill,decode128k,decode1m (default all)")
+    ap.add_argument("--only", default="",
+                    help="comma list of parts: prefill,decode128k,decode1m (default all); "
+                         "'copy' runs a plain 1 GiB device copy used to calibrate counter byte totals")
     return ap.parse_args()
 
 
@@ -106,6 +108,14 @@ def main():
     parts = set(args.only.split(",")) if args.only else {"prefill", "decode128k", "decode1m"}
     result = {}
     kernels = {}
+    if "copy" in parts:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
+        return 0
 
     def progress(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -264,6 +274,8 @@ def main():
         sc5 = torch.empty((B5, 1, L5), dtype=torch.float32, device=dev)
         idx5 = torch.empty((B5, 1, TOPK), dtype=torch.int32, device=dev)
         wst5 = torch.empty(max(1, sa.dsa_topk_workspace_size(B5, 1, L5, TOPK)), dtype=torch.uint8, device=dev)
+        wss5 = torch.empty(max(1, sa.dsa_sparse_attention_fwd_workspace_size(B5, 1, HQ, D_DSA, TOPK)),
+                           dtype=torch.uint8, device=dev)
 
         def hca5():
             return sa.hca_attention_fwd(sa.HCA_DECODE, q5, rk5, rv5, kc5, vc5, BLK, WIN, pos=pos5, workspace=ws5)
@@ -271,7 +283,7 @@ def main():
         def dsa5():
             sa.dsa_indexer_scores(qi5, ki5, wi5, q_pos=qpos5, out=sc5)
             sa.dsa_topk(sc5, TOPK, q_pos=qpos5, out=idx5, workspace=wst5)
-            return sa.dsa_sparse_attention_fwd(qd5, kd5, vd5, idx5)
+            return sa.dsa_sparse_attention_fwd(qd5, kd5, vd5, idx5, workspace=wss5)
 
         for _ in range(args.warmup):
             hca5()
@@ -290,7 +302,7 @@ def main():
             "hca_hbm_frac": b_h / (t_h * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "dsa_hbm_frac": b_d / (t_d * 1e-6) / 1e9 / HBM_PEAK_GBS,
         }
-        del q5, kc5, vc5, rk5, rv5, ws5, qi5, ki5, wi5, qd5, kd5, vd5, sc5, idx5, wst5
+        del q5, kc5, vc5, rk5, rv5, ws5, qi5, ki5, wi5, qd5, kd5, vd5, sc5, idx5, wst5, wss5
         torch.cuda.empty_cache()
 
     # -------------------------------------------------------------------

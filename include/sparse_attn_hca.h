@@ -152,12 +152,12 @@ int hca_attention_fwd(const hca_attention_args* args, hipStream_t stream);
  *   scores[b,i,s] = sum_h w[b,i,h] * max(0, <q_idx[b,i,h,:], k_idx[b,s,:]>)
  *
  * for every s <= p_i, p_i = q_pos[b] + i (q_pos == NULL: p_i = i).  Entries
- * with s > p_i are not written (their contents are unspecified).
+ * with s > p_i are unspecified (they may or may not be written).
  * q_idx: [B,T,Hi,Di] bf16; k_idx: [B,S,Di] bf16 (one key per position, shared
  * by the indexer heads); w: [B,T,Hi] fp32; scores: [B,T,S] fp32.
  * Arithmetic: exact bf16 products accumulated in fp32, then fp32 ReLU,
  * weighting and head sum.
- * Supported: Di = 128, Hi = 4.
+ * Supported: Di = 128, Hi = 4, S <= 2^24.
  * ------------------------------------------------------------------------ */
 int dsa_indexer_scores(const void* q_idx, const void* k_idx, const float* w,
                        const int64_t* q_pos, float* scores,
@@ -198,12 +198,19 @@ int dsa_topk(const float* scores, const int64_t* q_pos, int32_t* idx,
  * entry yields o = 0 and lse = -inf.
  * q, o: [B,T,Hq,D] bf16; k, v: [B,S,D] bf16 (v == k is allowed);
  * idx: [B,T,kk] int32; lse: optional fp32 [B,T,Hq].  scale <= 0 -> 1/sqrt(D).
- * Supported: SA_BF16, D = 256, Hq = 64, 1 <= kk <= 2048.
+ * Arithmetic: bf16 inputs, fp32 accumulation and softmax, probabilities
+ * rounded to bf16 for the P*V product, output rounded (RNE) to bf16.
+ * Supported: SA_BF16, D = 256, Hq = 64, 1 <= kk <= 2048, S <= 2^23.
+ * Workspace: calls with few tokens (decode) split each token's index list
+ * over several workgroups and need dsa_sparse_attention_fwd_workspace_size()
+ * bytes of scratch for the partial results (0 for prefill-sized calls).
  * ------------------------------------------------------------------------ */
+size_t dsa_sparse_attention_fwd_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t D, int64_t kk);
 int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v,
                              const int32_t* idx, void* o, float* lse, sa_dtype dtype,
                              int64_t B, int64_t T, int64_t S, int64_t Hq, int64_t D,
-                             int64_t kk, float scale, hipStream_t stream);
+                             int64_t kk, float scale, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,7 @@ from ._lib import (
     SparseAttnError,
     dsa_indexer_scores,
     dsa_sparse_attention_fwd,
+    dsa_sparse_attention_fwd_workspace_size,
     dsa_topk,
     dsa_topk_workspace_size,
     hca_attention_fwd,
@@ -27,6 +28,7 @@ __all__ = [
     "SparseAttnError",
     "dsa_indexer_scores",
     "dsa_sparse_attention_fwd",
+    "dsa_sparse_attention_fwd_workspace_size",
     "dsa_topk",
     "dsa_topk_workspace_size",
     "hca_attention_fwd",

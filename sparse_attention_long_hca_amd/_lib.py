@@ -64,9 +64,10 @@ EXPORTS = {
     "dsa_indexer_scores": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p] + [_c_i64] * 5 + [_c_p]),
     "dsa_topk_workspace_size": (ctypes.c_size_t, [_c_i64] * 4),
     "dsa_topk": (ctypes.c_int, [_c_p, _c_p, _c_p] + [_c_i64] * 4 + [_c_p, ctypes.c_size_t, _c_p]),
+    "dsa_sparse_attention_fwd_workspace_size": (ctypes.c_size_t, [_c_i64] * 5),
     "dsa_sparse_attention_fwd": (
         ctypes.c_int,
-        [_c_p] * 6 + [ctypes.c_int] + [_c_i64] * 6 + [ctypes.c_float, _c_p],
+        [_c_p] * 6 + [ctypes.c_int] + [_c_i64] * 6 + [ctypes.c_float, _c_p, ctypes.c_size_t, _c_p],
     ),
 }
 
@@ -246,7 +247,11 @@ def dsa_topk(scores, k, q_pos=None, out=None, workspace=None):
     return out
 
 
-def dsa_sparse_attention_fwd(q, k, v, idx, scale=None, return_lse=False):
+def dsa_sparse_attention_fwd_workspace_size(B, T, Hq, D, kk):
+    return lib().dsa_sparse_attention_fwd_workspace_size(B, T, Hq, D, kk)
+
+
+def dsa_sparse_attention_fwd(q, k, v, idx, scale=None, return_lse=False, workspace=None):
     """q [B,T,Hq,D], k,v [B,S,D] bf16, idx [B,T,kk] int32 -> o [B,T,Hq,D] (and lse [B,T,Hq])."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 3)
@@ -257,11 +262,15 @@ def dsa_sparse_attention_fwd(q, k, v, idx, scale=None, return_lse=False):
     kk = idx.shape[2]
     o = torch.empty_like(q)
     lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    need = lib().dsa_sparse_attention_fwd_workspace_size(B, T, Hq, D, kk)
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(
         "dsa_sparse_attention_fwd",
         lib().dsa_sparse_attention_fwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o), _ptr(lse), SA_BF16, B, T, S, Hq, D, kk,
-            0.0 if scale is None else float(scale), _stream(),
+            0.0 if scale is None else float(scale), _ptr(workspace), wsb, _stream(),
         ),
     )
     return (o, lse) if return_lse else o

@@ -40,6 +40,10 @@ COMMON_FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Keep MFMA accumulators in ordinary VGPRs: the attention loops rescale
+    # and read them with VALU ops, and splitting them across the two register
+    # files makes the compiler copy every accumulator at each loop iteration.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]

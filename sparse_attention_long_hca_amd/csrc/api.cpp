@@ -9,7 +9,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/sparse_attn_hca.h"
+#include "sparse_attn_hca.h"
 #include "kernels.h"
 
 namespace {
@@ -152,6 +152,8 @@ int dsa_indexer_scores(const void* q_idx, const void* k_idx, const float* w, con
   if (!q_idx || !k_idx || !w || !scores) return fail(SA_ERR_NULL, "dsa_indexer_scores: q_idx, k_idx, w, scores must be non-NULL");
   if (B <= 0 || T <= 0 || S <= 0 || Hi <= 0 || Di <= 0) return fail(SA_ERR_SHAPE, "dsa_indexer_scores: sizes must be > 0");
   if (Hi != 4 || Di != 128) return fail(SA_ERR_UNSUPPORTED, "dsa_indexer_scores: supported Hi = 4, Di = 128");
+  if (S > ((int64_t)1 << 24) || T >= ((int64_t)1 << 31))
+    return fail(SA_ERR_UNSUPPORTED, "dsa_indexer_scores: S must be <= 2^24 and T < 2^31");
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w) || !aligned16(scores))
     return fail(SA_ERR_ALIGN, "dsa_indexer_scores: pointers must be 16-byte aligned");
   const int64_t nblocks = B * ((T + 63) / 64) * ((S + 1023) / 1024);
@@ -188,20 +190,39 @@ int dsa_topk(const float* scores, const int64_t* q_pos, int32_t* idx, int64_t B,
 }
 
 // ---------------------------------------------------------------------------
+size_t dsa_sparse_attention_fwd_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t D, int64_t kk) {
+  if (B <= 0 || T <= 0 || Hq <= 0 || D <= 0 || kk <= 0) return 0;
+  return sa::dsa_sparse_workspace_bytes(B * T, sa::dsa_sparse_nsplit(B * T, kk), Hq, D);
+}
+
 int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v, const int32_t* idx, void* o, float* lse,
                              sa_dtype dtype, int64_t B, int64_t T, int64_t S, int64_t Hq, int64_t D, int64_t kk,
-                             float scale, hipStream_t stream) {
+                             float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k || !v || !idx || !o) return fail(SA_ERR_NULL, "dsa_sparse_attention_fwd: q, k, v, idx, o must be non-NULL");
   if (B <= 0 || T <= 0 || S <= 0 || Hq <= 0 || D <= 0 || kk <= 0)
     return fail(SA_ERR_SHAPE, "dsa_sparse_attention_fwd: sizes must be > 0");
   if (dtype != SA_BF16 || D != 256 || Hq != 64)
     return fail(SA_ERR_UNSUPPORTED, "dsa_sparse_attention_fwd: supported dtype bf16, D = 256, Hq = 64");
   if (kk > 2048) return fail(SA_ERR_UNSUPPORTED, "dsa_sparse_attention_fwd: kk must be <= 2048");
+  if (S > ((int64_t)1 << 23)) return fail(SA_ERR_UNSUPPORTED, "dsa_sparse_attention_fwd: S must be <= 2^23");
   const void* ptrs[] = {q, k, v, idx, o, lse};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(SA_ERR_ALIGN, "dsa_sparse_attention_fwd: pointers must be 16-byte aligned");
-  if (B * T > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "dsa_sparse_attention_fwd: too many tokens");
-  sa::DsaSparseParams p{q, k, v, idx, o, lse, B, T, S, kk, resolve_scale_log2(scale, D)};
+  const int64_t BT = B * T;
+  const int64_t ns = sa::dsa_sparse_nsplit(BT, kk);
+  if (BT * ns > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "dsa_sparse_attention_fwd: too many tokens");
+  const size_t need = sa::dsa_sparse_workspace_bytes(BT, ns, Hq, D);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "dsa_sparse_attention_fwd: needs %zu workspace bytes, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(SA_ERR_ALIGN, "dsa_sparse_attention_fwd: workspace must be 16-byte aligned");
+  }
+  const int64_t tiles = (kk + 31) / 32;
+  float* part_o = reinterpret_cast<float*>(workspace);
+  float* part_lse = part_o ? part_o + BT * ns * Hq * D : nullptr;
+  sa::DsaSparseParams p{q, k, v, idx, o, lse, part_o, part_lse, B, T, S, kk, resolve_scale_log2(scale, D),
+                        ns, (tiles + ns - 1) / ns};
   return hip_status(sa::launch_dsa_sparse(p, (int)D, (int)Hq, stream), "dsa_sparse_attention_fwd launch");
 }
 

@@ -40,11 +40,10 @@ struct AttnGeom {
   static constexpr int kQRegs = kBf16 ? D / 32 : D / 4;
   static constexpr int kONb = D / 16;
   static constexpr int kStageBytes = 2 * kTileBytes;  // one pipeline stage: K tile + V tile
-  static_assert(kChunks >= 8, "the XOR swizzle needs at least 8 chunks per row");
-  // Row r, 16-byte chunk c -> byte offset in a tile.  XOR with r%8 spreads
-  // the 16 rows read by one MFMA operand fetch over all LDS banks.
+  static_assert(kChunks >= 16, "the LDS swizzle needs at least 16 chunks per row");
+  // Row r, 16-byte chunk c -> byte offset in a tile (see lds_swizzle).
   __device__ static __forceinline__ uint32_t chunk_off(int r, int c) {
-    return (uint32_t)(r * kChunks + (c ^ (r & 7))) * 16u;
+    return (uint32_t)(r * kChunks + (c ^ lds_swizzle(r))) * 16u;
   }
 };
 
@@ -111,8 +110,7 @@ __device__ __forceinline__ void global_load_lds_16(const void* g, char* lds_wave
 // row index of tile row r relative to them, or -1 for a padding row (which
 // loads row 0 of the same tensor: finite, and masked by the caller).
 template <typename T, int D, typename RowFn>
-__device__ __forceinline__ void stage_async(char* kbuf, char* vbuf, const T* kbase, const T* vbase,
-                                            RowFn&& rowfn) {
+__device__ __forceinline__ void stage_rows_async(char* buf, const T* base_ptr, RowFn&& rowfn) {
   using G = AttnGeom<T, D>;
   using SG = StageGeom<T, D>;
   const int wave = wave_id(), lane = threadIdx.x & 63;
@@ -121,35 +119,42 @@ __device__ __forceinline__ void stage_async(char* kbuf, char* vbuf, const T* kba
     const int base = (j * kAttnWaves + wave) * kWave;  // first physical chunk of this load
     const int P = base + lane;
     const int r = P / G::kChunks, cp = P % G::kChunks;
-    const int c = cp ^ (r & 7);
+    const int c = cp ^ lds_swizzle(r);
     int row = rowfn(r);
     row = row < 0 ? 0 : row;
     const uint32_t off = (uint32_t)row * (uint32_t)G::kRowBytes + (uint32_t)c * 16u;
-    global_load_lds_16(reinterpret_cast<const char*>(kbase) + off, kbuf + base * 16);
-    global_load_lds_16(reinterpret_cast<const char*>(vbase) + off, vbuf + base * 16);
+    global_load_lds_16(reinterpret_cast<const char*>(base_ptr) + off, buf + base * 16);
   }
 }
 
-// Wait until this wave's loads, except the newest `pending` tiles' worth, have
-// landed in LDS.
+template <typename T, int D, typename RowFn>
+__device__ __forceinline__ void stage_async(char* kbuf, char* vbuf, const T* kbase, const T* vbase,
+                                            RowFn&& rowfn) {
+  stage_rows_async<T, D>(kbuf, kbase, rowfn);
+  stage_rows_async<T, D>(vbuf, vbase, rowfn);
+}
+
+// Wait until this wave's direct LDS loads, except the newest kPendingLoads,
+// have landed.
 template <int kPendingLoads>
 __device__ __forceinline__ void wait_loads() {
-  static_assert(kPendingLoads >= 0 && kPendingLoads < 64, "vmcnt range");
-  if constexpr (kPendingLoads == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPendingLoads) : "memory");
-  }
+  wait_vmcnt<kPendingLoads>();
 }
 
 // ---------------------------------------------------------------------------
-// One key tile for one wave.  visible(key_in_tile) is evaluated for this
-// lane's query row (lane%16) and the 8 keys the lane holds.
-// scale_log2 = softmax scale * log2(e).
+// One key tile for one wave, in two stages so that callers can stream the V
+// tile while the first stage runs:
+//   attend_qk: S^T = K . Q^T, mask, online-softmax update -> probabilities
+//   attend_pv: O^T += V^T . P^T
+// visible(key_in_tile) is evaluated for this lane's query row (lane%16) and
+// the 8 keys the lane holds.  scale_log2 = softmax scale * log2(e).
 // ---------------------------------------------------------------------------
+struct PFrag {
+  f32x4_t s[2];  // probabilities of keys {4g..4g+3} (s[0]) and {16+4g..16+4g+3} (s[1])
+};
+
 template <typename T, int D, typename VisFn>
-__device__ __forceinline__ void attend_tile(AttnRegs<T, D>& R, const char* ks, const char* vs,
-                                            float scale_log2, VisFn&& visible) {
+__device__ __forceinline__ PFrag attend_qk(AttnRegs<T, D>& R, const char* ks, float scale_log2, VisFn&& visible) {
   using G = AttnGeom<T, D>;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, L = lane & 15;
@@ -157,24 +162,39 @@ __device__ __forceinline__ void attend_tile(AttnRegs<T, D>& R, const char* ks, c
   // ---- S^T = K . Q^T -------------------------------------------------------
   f32x4_t s[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
   if constexpr (G::kBf16) {
-    // Row r = kb*16 + L, logical chunk g + 4*kstep.  With x = r%8 the swizzled
-    // chunk is (g ^ x%4) + 4*((kstep%2) ^ x/4) + 8*(kstep/2): two per-lane bases
-    // plus compile-time offsets.
-    const int x = L & 7;
-    const uint32_t rb = (uint32_t)L * G::kRowBytes + 16u * (uint32_t)(g ^ (x & 3));
-    const uint32_t kb0 = rb + 64u * (uint32_t)(x >> 2);
-    const uint32_t kb1 = rb + 64u * (uint32_t)(1 - (x >> 2));
+    // Row r = kb*16 + L, logical chunk g + 4*kstep.  With s = lds_swizzle(L)
+    // the physical chunk is (g ^ s%4) + 4*((kstep%4) ^ s/4) + 16*(kstep/4):
+    // four per-lane bases plus compile-time offsets.
+    const int sw = lds_swizzle(L);
+    const uint32_t rb = (uint32_t)L * G::kRowBytes + 16u * (uint32_t)(g ^ (sw & 3));
+    uint32_t kbase[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) kbase[n] = rb + 64u * (uint32_t)(n ^ (sw >> 2));
+    // Four independent accumulator chains (key block x kstep parity) so that
+    // dependent MFMAs are never back to back; operand reads are software
+    // pipelined against the MFMAs (see the schedule groups below).
+    f32x4_t acc[2][2] = {{f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}},
+                         {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll
     for (int kstep = 0; kstep < G::kQRegs; ++kstep) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t off = ((kstep & 1) ? kb1 : kb0) + 128u * (kstep >> 1) + kb * 16 * G::kRowBytes;
+        const uint32_t off = kbase[kstep & 3] + 256u * (kstep >> 2) + kb * 16 * G::kRowBytes;
         const uint4 a = lds_read_b128(ks, off);
-        s[kb] = mfma_bf16_16x16x32(__builtin_bit_cast(i16x8_t, a), R.q[kstep], s[kb]);
+        acc[kb][kstep & 1] = mfma_bf16_16x16x32(__builtin_bit_cast(i16x8_t, a), R.q[kstep], acc[kb][kstep & 1]);
       }
-      // Keep at most a few operand reads in flight (bounded register use).
-      if ((kstep & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
+    // Schedule: 6 operand reads ahead, then alternate 2 MFMAs / 2 reads.
+    constexpr int kReads = 2 * G::kQRegs;
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < (kReads - 6) / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    s[0] = acc[0][0] + acc[0][1];
+    s[1] = acc[1][0] + acc[1][1];
   } else {
 #pragma unroll
     for (int kstep = 0; kstep < G::kQRegs; ++kstep) {
@@ -231,6 +251,15 @@ __device__ __forceinline__ void attend_tile(AttnRegs<T, D>& R, const char* ks, c
   }
   rs = sum_across_groups(rs);
   R.l += rs;
+  return PFrag{{s[0], s[1]}};
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void attend_pv(AttnRegs<T, D>& R, const char* vs, const PFrag& P) {
+  using G = AttnGeom<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, L = lane & 15;
+  const f32x4_t* s = P.s;
 
   // ---- O^T += V^T . P^T ----------------------------------------------------
   if constexpr (G::kBf16) {
@@ -238,24 +267,32 @@ __device__ __forceinline__ void attend_tile(AttnRegs<T, D>& R, const char* ks, c
     const uint32_t p45 = pack_bf16x2(s[1][0], s[1][1]), p67 = pack_bf16x2(s[1][2], s[1][3]);
     const i16x8_t pf = __builtin_bit_cast(i16x8_t, make_uint4(p01, p23, p45, p67));
     // Transposing reads: group g's lane L points at row key1 = 4g + L/4 (and
-    // key1 + 16), dims nb*16 + 4*(L%4) .. +3.  With x = key1%8 the swizzled
-    // byte offset is 128*(nb/4) + 32*((nb%4) ^ x/2) + 16*(h ^ x%2) + 8*(L%2),
-    // h = (L%4)/2: four per-lane bases plus compile-time offsets.
+    // key1 + 16), dims nb*16 + 4*(L%4) .. +3, i.e. logical chunk 2*nb + h with
+    // h = (L%4)/2, byte 8*(L%2) within it.  With s = lds_swizzle(key1) the
+    // physical byte offset is 256*(nb/8) + 32*((nb%8) ^ s/2) + 16*(h ^ s%2)
+    // + 8*(L%2): eight per-lane bases plus compile-time offsets.
     const int key1 = 4 * g + (L >> 2);
-    const int x = key1 & 7;
-    const uint32_t vrow = (uint32_t)key1 * G::kRowBytes + 16u * (uint32_t)(((L & 3) >> 1) ^ (x & 1)) + 8u * (L & 1);
-    uint32_t vbase[4];
+    const int sw = lds_swizzle(key1);
+    const uint32_t vrow = (uint32_t)key1 * G::kRowBytes + 16u * (uint32_t)(((L & 3) >> 1) ^ (sw & 1)) + 8u * (L & 1);
+    uint32_t vbase[8];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) vbase[n] = vrow + 32u * (uint32_t)(n ^ (x >> 1));
+    for (int n = 0; n < 8; ++n) vbase[n] = vrow + 32u * (uint32_t)(n ^ (sw >> 1));
 #pragma unroll
     for (int nb = 0; nb < G::kONb; ++nb) {
-      const uint32_t off = vbase[nb & 3] + 128u * (nb >> 2);
+      const uint32_t off = vbase[nb & 7] + 256u * (nb >> 3);
       const i16x4_t lo = lds_read_tr16_b64(vs + off);
       const i16x4_t hi = lds_read_tr16_b64(vs + off + 16 * G::kRowBytes);
       const i16x8_t a = i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       R.o[nb] = mfma_bf16_16x16x32(a, pf, R.o[nb]);
-      if ((nb & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
+    // Schedule: 8 transposing reads (4 blocks) ahead, then 1 MFMA / 2 reads.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+    for (int i = 0; i < G::kONb - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   } else {
 #pragma unroll
     for (int nb = 0; nb < G::kONb; ++nb) {
@@ -271,6 +308,14 @@ __device__ __forceinline__ void attend_tile(AttnRegs<T, D>& R, const char* ks, c
       }
     }
   }
+}
+
+// Both stages on one tile whose K and V are already in LDS.
+template <typename T, int D, typename VisFn>
+__device__ __forceinline__ void attend_tile(AttnRegs<T, D>& R, const char* ks, const char* vs, float scale_log2,
+                                            VisFn&& visible) {
+  const PFrag P = attend_qk<T, D>(R, ks, scale_log2, visible);
+  attend_pv<T, D>(R, vs, P);
 }
 
 // ---------------------------------------------------------------------------
@@ -300,6 +345,23 @@ __device__ __forceinline__ void finish_rows(const AttnRegs<T, D>& R, T* orow, fl
   if (lse_out && g == 0) {
     *lse_out = R.l > 0.f ? (R.m + __log2f(R.l)) * kLn2 : -INFINITY;
   }
+}
+
+// Split-K variant: write this wave's rows normalised in fp32 plus the
+// log2-domain normaliser (m + log2 l) of this split; a combine kernel merges
+// the splits.  Rows without any visible key get o = 0 and -inf.
+template <typename T, int D>
+__device__ __forceinline__ void finish_rows_partial(const AttnRegs<T, D>& R, float* orow, float* lse2_out) {
+  using G = AttnGeom<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const float inv = R.l > 0.f ? 1.f / R.l : 0.f;
+#pragma unroll
+  for (int nb = 0; nb < G::kONb; ++nb) {
+    const f32x4_t v = R.o[nb] * inv;
+    *reinterpret_cast<float4*>(orow + nb * 16 + g * 4) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  if (g == 0) *lse2_out = R.l > 0.f ? R.m + __log2f(R.l) : -INFINITY;
 }
 
 }  // namespace sa

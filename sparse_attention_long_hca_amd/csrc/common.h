@@ -98,6 +98,34 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t n) {
   return x * q + (x < r ? x : r) + local;
 }
 
+// LDS row swizzle for tiles stored as rows of >= 16 chunks of 16 bytes:
+// chunk c of row r lives at physical chunk c ^ lds_swizzle(r).  With 64 LDS
+// banks (256 bytes per cycle) this is conflict-free both for 16 lanes reading
+// the same chunk of 16 consecutive rows (an MFMA operand fetch) and for 8
+// consecutive rows read as 32-byte pieces (the transposing V reads).
+__device__ __forceinline__ int lds_swizzle(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+// ---------------------------------------------------------------------------
+// Wait counters and barriers for pipelines fed by direct global->LDS loads.
+// The builtin s_waitcnt is visible to the compiler's own wait insertion (an
+// asm one is not), so it does not add a full vmcnt(0) wait of its own before
+// LDS reads.  A plain __syncthreads() is a release fence and would wait for
+// every outstanding LDS load; lds_barrier() is the bare s_barrier with
+// compiler-only fences, for use after the caller's explicit waits.
+// s_waitcnt immediate (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Wave index within the workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 

@@ -9,111 +9,112 @@
 // With Hi = 4, one 16-row MFMA block is 4 queries x 4 heads and the 16x16x32
 // accumulator layout leaves each lane holding the 4 heads of one (query,
 // position) pair, so the ReLU, the weighting and the head sum happen in
-// registers.  A workgroup (4 waves x 16 queries) stages 64-position tiles of
-// k_idx into LDS once for all its waves and covers a chunk of 1024 positions;
-// chunks entirely after the workgroup's last query are skipped.
+// registers.  Each wave owns 16 queries (4 M-blocks, Q in registers); the
+// workgroup streams 64-position tiles of k_idx into a double-buffered LDS
+// ring with direct global->LDS loads and covers a chunk of 1024 positions.
+// Workgroups are ordered chunk-major, so the query tiles that read one k_idx
+// chunk run together and find it in L2.  Prefill shapes use 4 waves (64
+// queries) per workgroup; decode shapes (T <= 16) use 1 wave per workgroup so
+// that many workgroups stream the positions in parallel.
 #include "common.h"
 #include "kernels.h"
 
 namespace sa {
 
-constexpr int kIdxThreads = 256;
 constexpr int kIdxDi = 128;
 constexpr int kIdxHi = 4;
-constexpr int kIdxQPerWave = 16;                    // queries per wave (4 M-blocks)
-constexpr int kIdxQTile = 4 * kIdxQPerWave;         // queries per workgroup
-constexpr int kIdxKTile = 64;                       // positions per LDS tile
-constexpr int kIdxChunk = 16 * kIdxKTile;           // positions per workgroup
-constexpr int kIdxRowChunks = kIdxDi * 2 / 16;      // 16-byte chunks per k row (16)
-constexpr int kIdxCPT = kIdxKTile * kIdxRowChunks / kIdxThreads;  // 4
+constexpr int kIdxQPerWave = 16;                // queries per wave (4 M-blocks)
+constexpr int kIdxKTile = 64;                   // positions per LDS tile
+constexpr int kIdxTilesPerChunk = 16;
+constexpr int kIdxChunk = kIdxTilesPerChunk * kIdxKTile;  // positions per workgroup
+constexpr int kIdxRowBytes = kIdxDi * 2;                  // 256
+constexpr int kIdxRowChunks = kIdxRowBytes / 16;          // 16
+constexpr int kIdxTileBytes = kIdxKTile * kIdxRowBytes;   // 16 KB
 
 __device__ __forceinline__ uint32_t idx_off(int r, int c) {
-  return (uint32_t)(r * kIdxRowChunks + (c ^ (r & 7))) * 16u;
+  return (uint32_t)(r * kIdxRowChunks + (c ^ lds_swizzle(r))) * 16u;
 }
 
-__global__ __launch_bounds__(kIdxThreads) void dsa_indexer_kernel(DsaIndexerParams p, int64_t n_qtiles,
-                                                                  int64_t n_chunks) {
-  __shared__ __attribute__((aligned(16))) char lds[kIdxKTile * kIdxRowChunks * 16];
+// Direct global->LDS load of positions [s0, s0+64) (rows past `stop` load row 0).
+template <int kWaves>
+__device__ __forceinline__ void idx_stage(char* buf, const bf16_t* kI, int s0, int stop) {
+  constexpr int kLoads = kIdxTileBytes / 1024 / kWaves;  // wave loads of 1 KB
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int base = (j * kWaves + wave) * 64;  // physical chunk
+    const int P = base + lane;
+    const int r = P / kIdxRowChunks, cp = P % kIdxRowChunks;
+    const int c = cp ^ lds_swizzle(r);
+    const int s = s0 + r < stop ? s0 + r : 0;
+    const uint32_t off = (uint32_t)s * kIdxRowBytes + (uint32_t)c * 16u;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kI) + off, (lds_void_t*)(buf + base * 16), 16, 0,
+                                     0);
+  }
+}
 
+template <int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerParams p, int n_qtiles, int n_chunks) {
+  __shared__ __attribute__((aligned(16))) char lds0[kIdxTileBytes];
+  __shared__ __attribute__((aligned(16))) char lds1[kIdxTileBytes];
+  constexpr int kQTile = kWaves * kIdxQPerWave;
+
+  // Chunk-major order: consecutive workgroups (same XCD) share a k_idx chunk.
   const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t per_b = n_qtiles * n_chunks;
-  const int64_t b = lid / per_b;
-  const int64_t rem = lid % per_b;
-  const int64_t qt = n_qtiles - 1 - rem / n_chunks;  // longest rows first
-  const int64_t kc = rem % n_chunks;
+  const int per_b = n_qtiles * n_chunks;
+  const int b = (int)(lid / (uint32_t)per_b);
+  const int rem = (int)(lid % (uint32_t)per_b);
+  const int kc = rem / n_qtiles;
+  const int qt = n_qtiles - 1 - rem % n_qtiles;
 
-  const int64_t base = p.q_pos ? p.q_pos[b] : 0;
-  const int64_t i0 = qt * kIdxQTile;
-  const int64_t i_last = imin64(i0 + kIdxQTile - 1, p.T - 1);
-  const int64_t s_end = imin64(p.S, base + i_last + 1);  // exclusive, whole workgroup
-  const int64_t s_begin = kc * kIdxChunk;
+  const int T = (int)p.T, S = (int)p.S;
+  const int base = p.q_pos ? (int)p.q_pos[b] : 0;
+  const int i0 = qt * kQTile;
+  const int i_last = min(i0 + kQTile - 1, T - 1);
+  const int s_end = min(S, base + i_last + 1);  // exclusive, whole workgroup
+  const int s_begin = kc * kIdxChunk;
   if (s_begin >= s_end) return;
-  const int64_t s_stop = imin64(s_end, s_begin + kIdxChunk);
-  const int n_tiles = (int)((s_stop - s_begin + kIdxKTile - 1) / kIdxKTile);
+  const int s_stop = min(s_end, s_begin + kIdxChunk);
+  const int n_tiles = (s_stop - s_begin + kIdxKTile - 1) / kIdxKTile;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int L = lane & 15, g = lane >> 4;
-  const int64_t iw = i0 + wave * kIdxQPerWave;  // first query of the wave
-  const int n_mb = (int)imax64(0, imin64(4, (p.T - iw + 3) / 4));  // M-blocks with a valid query
+  const int iw = i0 + wave * kIdxQPerWave;                  // first query of the wave
+  const int n_mb = max(0, min(4, (T - iw + 3) / 4));          // M-blocks with a valid query
+  const int wave_plim = n_mb > 0 ? min(base + min(iw + kIdxQPerWave - 1, T - 1), S - 1) : -1;
 
-  const bf16_t* qI = reinterpret_cast<const bf16_t*>(p.q) + b * p.T * kIdxHi * kIdxDi;
-  const bf16_t* kI = reinterpret_cast<const bf16_t*>(p.k) + b * p.S * kIdxDi;
-  const float* wgt = p.w + b * p.T * kIdxHi;
-  float* out = p.scores + b * p.T * p.S;
+  const bf16_t* qI = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * T * kIdxHi * kIdxDi;
+  const bf16_t* kI = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * S * kIdxDi;
+  const float* wgt = p.w + (int64_t)b * T * kIdxHi;
+  float* out = p.scores + (int64_t)b * T * S;
 
   // A operand: row (query iw + mb*4 + L/4, head L%4), dims g*8 + 32*ks.
   i16x8_t qa[4][4];
   float wq[4][4];  // weights of this lane's accumulator query (iw + mb*4 + g), heads 0..3
-  int64_t plim[4];  // last position visible to that query (or -1)
+  int plim[4];     // last position visible to that query (-1 if none)
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const int64_t qa_i = iw + mb * 4 + (L >> 2);
-    const bool va = mb < n_mb && qa_i < p.T;
+    const int qa_i = iw + mb * 4 + (L >> 2);
+    const bool va = mb < n_mb && qa_i < T;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (va) {
-        const uint4 u = *reinterpret_cast<const uint4*>(qI + (qa_i * kIdxHi + (L & 3)) * kIdxDi + ks * 32 + g * 8);
+        const uint4 u = *reinterpret_cast<const uint4*>(qI + ((int64_t)qa_i * kIdxHi + (L & 3)) * kIdxDi + ks * 32 + g * 8);
         qa[mb][ks] = __builtin_bit_cast(i16x8_t, u);
       } else {
         qa[mb][ks] = i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
-    const int64_t qc_i = iw + mb * 4 + g;
-    const bool vc = mb < n_mb && qc_i < p.T;
+    const int qc_i = iw + mb * 4 + g;
+    const bool vc = mb < n_mb && qc_i < T;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) wq[mb][h] = vc ? wgt[qc_i * kIdxHi + h] : 0.f;
-    plim[mb] = vc ? imin64(base + qc_i, p.S - 1) : -1;
+    for (int h = 0; h < 4; ++h) wq[mb][h] = vc ? wgt[(int64_t)qc_i * kIdxHi + h] : 0.f;
+    plim[mb] = vc ? min(base + qc_i, S - 1) : -1;
   }
 
-  // Staging: thread handles chunks id = pass*256 + tid -> row id/16, chunk id%16.
-  uint4 st[kIdxCPT];
-  auto load_tile = [&](int tile) {
-    const int64_t s0 = s_begin + (int64_t)tile * kIdxKTile;
-#pragma unroll
-    for (int pp = 0; pp < kIdxCPT; ++pp) {
-      const int id = pp * kIdxThreads + threadIdx.x;
-      const int r = id / kIdxRowChunks, c = id % kIdxRowChunks;
-      const int64_t s = s0 + r;
-      st[pp] = (s < s_stop) ? *reinterpret_cast<const uint4*>(kI + s * kIdxDi + c * 8) : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-
-  load_tile(0);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    __syncthreads();
-#pragma unroll
-    for (int pp = 0; pp < kIdxCPT; ++pp) {
-      const int id = pp * kIdxThreads + threadIdx.x;
-      lds_write_b128(lds, idx_off(id / kIdxRowChunks, id % kIdxRowChunks), st[pp]);
-    }
-    __syncthreads();
-    if (tile + 1 < n_tiles) load_tile(tile + 1);
-    const int64_t s0 = s_begin + (int64_t)tile * kIdxKTile;
-    if (n_mb == 0) continue;
-    // Skip the tile if it lies entirely after the wave's last query.
-    const int64_t wave_plim = imin64(base + imin64(iw + kIdxQPerWave - 1, p.T - 1), p.S - 1);
-    if (s0 > wave_plim) continue;
-
+  auto compute = [&](int tile, const char* buf) {
+    const int s0 = s_begin + tile * kIdxKTile;
+    if (s0 > wave_plim) return;  // tile entirely after the wave's last query
     f32x4_t acc[4][4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -123,37 +124,57 @@ __global__ __launch_bounds__(kIdxThreads) void dsa_indexer_kernel(DsaIndexerPara
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const uint4 bu = lds_read_b128(lds, idx_off(nb * 16 + L, g + 4 * ks));
+        const uint4 bu = lds_read_b128(buf, idx_off(nb * 16 + L, g + 4 * ks));
         const i16x8_t bb = __builtin_bit_cast(i16x8_t, bu);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < 4; ++mb)
           if (mb < n_mb) acc[mb][nb] = mfma_bf16_16x16x32(qa[mb][ks], bb, acc[mb][nb]);
-        }
       }
     }
-    // Epilogue: lane holds heads 0..3 of (query iw + mb*4 + g, position s0 + nb*16 + L).
+    // Lane holds heads 0..3 of (query iw + mb*4 + g, position s0 + nb*16 + L).
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       if (mb >= n_mb) continue;
-      const int64_t qi = iw + mb * 4 + g;
+      float* orow = out + (int64_t)(iw + mb * 4 + g) * S;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const int64_t s = s0 + nb * 16 + L;
+        const int s = s0 + nb * 16 + L;
         float sc = 0.f;
 #pragma unroll
         for (int h = 0; h < 4; ++h) sc = fmaf(wq[mb][h], fmaxf(acc[mb][nb][h], 0.f), sc);
-        if (s <= plim[mb]) out[qi * p.S + s] = sc;
+        if (s <= plim[mb]) orow[s] = sc;
       }
     }
+  };
+
+  // Two-stage pipeline, unrolled by two so each buffer has a fixed role.
+  idx_stage<kWaves>(lds0, kI, s_begin, s_stop);
+  for (int tile = 0; tile < n_tiles; tile += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tile + 1 < n_tiles) idx_stage<kWaves>(lds1, kI, s_begin + (tile + 1) * kIdxKTile, s_stop);
+    compute(tile, lds0);
+    if (tile + 1 >= n_tiles) break;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tile + 2 < n_tiles) idx_stage<kWaves>(lds0, kI, s_begin + (tile + 2) * kIdxKTile, s_stop);
+    compute(tile + 1, lds1);
   }
 }
 
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
-  const int64_t n_qtiles = (p.T + kIdxQTile - 1) / kIdxQTile;
   const int64_t n_chunks = (p.S + kIdxChunk - 1) / kIdxChunk;
-  const int64_t nblocks = p.B * n_qtiles * n_chunks;
-  hipLaunchKernelGGL(dsa_indexer_kernel, dim3((uint32_t)nblocks), dim3(kIdxThreads), 0, stream, p, n_qtiles,
-                     n_chunks);
+  if (p.T <= kIdxQPerWave) {
+    const int64_t n_qtiles = 1;
+    const int64_t nblocks = p.B * n_qtiles * n_chunks;
+    hipLaunchKernelGGL(dsa_indexer_kernel<1>, dim3((uint32_t)nblocks), dim3(64), 0, stream, p, (int)n_qtiles,
+                       (int)n_chunks);
+  } else {
+    const int64_t n_qtiles = (p.T + 4 * kIdxQPerWave - 1) / (4 * kIdxQPerWave);
+    const int64_t nblocks = p.B * n_qtiles * n_chunks;
+    hipLaunchKernelGGL(dsa_indexer_kernel<4>, dim3((uint32_t)nblocks), dim3(256), 0, stream, p, (int)n_qtiles,
+                       (int)n_chunks);
+  }
   return hipGetLastError();
 }
 

@@ -14,8 +14,8 @@
 // key > K, or key == K and fewer than `need` copies of K precede it; its
 // output slot is #(key > K before s) + min(#(key == K before s), need).
 //
-// Rows up to kLdsRow positions: one 1024-thread workgroup per row keeps the
-// whole row of keys in LDS.  Longer rows: a multi-workgroup pipeline with
+// Rows up to 32768 positions: one workgroup per row keeps the whole row of
+// keys in registers.  Longer rows: a multi-workgroup pipeline with
 // histograms and per-chunk counts in the workspace.  All counts are integers,
 // so both paths give bit-identical, run-to-run stable results.
 #include "common.h"
@@ -24,8 +24,6 @@
 namespace sa {
 
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kLdsRow = 32768;
 constexpr int kBins = 2048;
 // Digit layout of the 32-bit key: bits 31..21, 20..10, 9..0.
 __device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
@@ -101,96 +99,134 @@ __device__ void select_bin(const uint32_t* hist, int nbins, uint32_t need, uint3
 }
 
 // ---------------------------------------------------------------------------
-// Rows that fit in LDS: one workgroup per row.
+// Rows up to kRegRow positions: one 512-thread workgroup per row holds the
+// whole row of keys in registers.  Thread t owns positions 4*(t + 512*j) + e
+// (j < 16, e < 4), read with 16-byte loads that are all in flight at once.
+// The ordered compaction scans packed (greater, equal) counts per 4-element
+// group: lane prefix inside the wave, then a table of per-(group, wave)
+// totals in LDS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kTopkThreads) void dsa_topk_lds_kernel(DsaTopkParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-  uint32_t* keys = smem;                 // [kLdsRow]
-  uint32_t* hist = smem + kLdsRow;       // [kBins]
-  uint32_t* scratch = hist + kBins;      // [32]
-  uint32_t* state = scratch + 32;        // [4]: bin, above
+constexpr int kRegThreads = 512;
+constexpr int kRegWaves = kRegThreads / kWave;
+constexpr int kRegVec = 16;                            // 4-element groups per thread
+constexpr int kRegRow = kRegThreads * kRegVec * 4;     // 32768
+
+__global__ __launch_bounds__(kRegThreads) void dsa_topk_reg_kernel(DsaTopkParams p) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t scratch[32];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t wtot[kRegVec][kRegWaves];  // packed counts per (group j, wave)
 
   const int64_t row = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t b = row / p.T, i = row % p.T;
-  const int64_t n = row_len(p, b, i);
+  const int n = (int)row_len(p, b, i);
   const int k = (int)p.k;
   int32_t* out = p.idx + row * p.k;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   if (n <= k) {
-    for (int j = tid; j < k; j += kTopkThreads) out[j] = j < n ? j : -1;
+    for (int j = tid; j < k; j += kRegThreads) out[j] = j < n ? j : -1;
     return;
   }
   const float* sc = p.scores + row * p.S;
 
-  for (int j = tid; j < kBins; j += kTopkThreads) hist[j] = 0;
-  __syncthreads();
-  for (int64_t s = tid; s < n; s += kTopkThreads) {
-    const uint32_t key = score_key(sc[s]);
-    keys[s] = key;
-    atomicAdd(&hist[key >> digit_shift(0)], 1u);
+  // Keys (0 marks a position past the row end; only an all-ones NaN also maps
+  // to 0).  Every load is unconditional (clamped into the row) so that all
+  // of them are in flight together; positions >= n are masked afterwards.
+  uint32_t key[kRegVec][4];
+  if ((p.S & 3) == 0) {  // 16-byte aligned rows
+    float4 f[kRegVec];
+#pragma unroll
+    for (int j = 0; j < kRegVec; ++j) {
+      const int pos0 = min(4 * (tid + kRegThreads * j), (int)p.S - 4);
+      f[j] = *reinterpret_cast<const float4*>(sc + pos0);
+    }
+#pragma unroll
+    for (int j = 0; j < kRegVec; ++j) {
+      const int pos0 = 4 * (tid + kRegThreads * j);
+      key[j][0] = pos0 + 0 < n ? score_key(f[j].x) : 0u;
+      key[j][1] = pos0 + 1 < n ? score_key(f[j].y) : 0u;
+      key[j][2] = pos0 + 2 < n ? score_key(f[j].z) : 0u;
+      key[j][3] = pos0 + 3 < n ? score_key(f[j].w) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRegVec; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = 4 * (tid + kRegThreads * j) + e;
+        const float f = sc[min(pos, (int)p.S - 1)];
+        key[j][e] = pos < n ? score_key(f) : 0u;
+      }
   }
-  __syncthreads();
 
-  uint32_t prefix = 0;  // selected high bits so far (key >> shift of the last pass)
-  uint32_t need = (uint32_t)k;
+  uint32_t prefix = 0, need = (uint32_t)k;
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
-    if (pass > 0) {
-      for (int j = tid; j < kBins; j += kTopkThreads) hist[j] = 0;
-      __syncthreads();
-      const int sh_prev = digit_shift(pass - 1);
-      for (int64_t s = tid; s < n; s += kTopkThreads) {
-        const uint32_t key = keys[s];
-        if ((key >> sh_prev) == prefix) atomicAdd(&hist[(key >> digit_shift(pass)) & digit_mask(pass)], 1u);
+    for (int j = tid; j < kBins; j += kRegThreads) hist[j] = 0;
+    __syncthreads();
+    const int sh = digit_shift(pass);
+    const uint32_t dm = digit_mask(pass);
+    const int sh_prev = pass > 0 ? digit_shift(pass - 1) : 0;
+#pragma unroll
+    for (int j = 0; j < kRegVec; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kv = key[j][e];
+        const bool match = kv != 0u && (pass == 0 || (kv >> sh_prev) == prefix);
+        if (match) atomicAdd(&hist[(kv >> sh) & dm], 1u);
       }
-      __syncthreads();
-    }
-    select_bin(hist, (int)digit_mask(pass) + 1, need, scratch, &state[0], &state[1]);
-    const uint32_t bin = state[0], above = state[1];
-    prefix = (prefix << (pass == 0 ? 0 : (digit_shift(pass - 1) - digit_shift(pass)))) | bin;
-    need -= above;
+    __syncthreads();
+    select_bin(hist, (int)dm + 1, need, scratch, &res[0], &res[1]);
+    prefix = (prefix << (pass == 0 ? 0 : (sh_prev - sh))) | res[0];
+    need -= res[1];
     __syncthreads();
   }
-  const uint32_t K = prefix;  // the k-th largest key
+  const uint32_t K = prefix;  // the k-th largest key; need = copies of K to take
 
-  // Ordered compaction: wave w owns positions [w*seg, min(n, (w+1)*seg)).
-  const int lane = tid & 63, wave = tid >> 6;
-  const int64_t seg = (((n + kTopkWaves - 1) / kTopkWaves) + 63) / 64 * 64;
-  const int64_t s_beg = wave * seg, s_fin = imin64(n, s_beg + seg);
-  uint32_t cnt_gt = 0, cnt_eq = 0;
-  for (int64_t s0 = s_beg; s0 < s_fin; s0 += 64) {
-    const int64_t s = s0 + lane;
-    const uint32_t key = s < s_fin ? keys[s] : 0u;
-    cnt_gt += __popcll(__ballot(s < s_fin && key > K));
-    cnt_eq += __popcll(__ballot(s < s_fin && key == K));
-  }
-  uint32_t* wgt = scratch;       // [16]
-  uint32_t* weq = scratch + 16;  // [16]
-  if (lane == 0) {
-    wgt[wave] = cnt_gt;
-    weq[wave] = cnt_eq;
+  // Packed counts: low 16 bits = keys > K, high 16 bits = keys == K.
+  uint32_t incl[kRegVec];
+#pragma unroll
+  for (int j = 0; j < kRegVec; ++j) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c += (key[j][e] > K ? 1u : 0u) + (key[j][e] == K ? 0x10000u : 0u);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(c, off);
+      if (lane >= off) c += y;
+    }
+    incl[j] = c;
+    if (lane == 63) wtot[j][wave] = c;
   }
   __syncthreads();
-  uint32_t gt_before = 0, eq_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    gt_before += wgt[w];
-    eq_before += weq[w];
+  // Exclusive prefix of the (group, wave) totals in position order (group-major).
+  if (tid == 0) {
+    uint32_t run = 0;
+    for (int j = 0; j < kRegVec; ++j)
+      for (int w = 0; w < kRegWaves; ++w) {
+        const uint32_t t = wtot[j][w];
+        wtot[j][w] = run;
+        run += t;
+      }
   }
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t s0 = s_beg; s0 < s_fin; s0 += 64) {
-    const int64_t s = s0 + lane;
-    const bool in = s < s_fin;
-    const uint32_t key = in ? keys[s] : 0u;
-    const uint64_t mgt = __ballot(in && key > K);
-    const uint64_t meq = __ballot(in && key == K);
-    const uint32_t g_b = gt_before + __popcll(mgt & below);
-    const uint32_t e_b = eq_before + __popcll(meq & below);
-    const bool take = in && (key > K || (key == K && e_b < need));
-    const uint32_t slot = g_b + (e_b < need ? e_b : need);
-    if (take && slot < (uint32_t)k) out[slot] = (int32_t)s;
-    gt_before += __popcll(mgt);
-    eq_before += __popcll(meq);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kRegVec; ++j) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c += (key[j][e] > K ? 1u : 0u) + (key[j][e] == K ? 0x10000u : 0u);
+    uint32_t before = wtot[j][wave] + incl[j] - c;
+    const int pos0 = 4 * (tid + kRegThreads * j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t kv = key[j][e];
+      const uint32_t g_b = before & 0xffffu, e_b = before >> 16;
+      const bool take = kv > K || (kv == K && e_b < need);
+      const uint32_t slot = g_b + (e_b < need ? e_b : need);
+      if (take && slot < (uint32_t)k) out[slot] = pos0 + e;
+      before += (kv > K ? 1u : 0u) + (kv == K ? 0x10000u : 0u);
+    }
   }
 }
 
@@ -382,7 +418,7 @@ __global__ __launch_bounds__(kMwThreads) void topk_mw_write(DsaTopkParams p) {
 
 size_t dsa_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k) {
   (void)k;
-  if (S <= kLdsRow) return 0;
+  if (S <= kRegRow) return 0;
   const int64_t rows = B * T;
   const int64_t nchunk = (S + kMwChunk - 1) / kMwChunk;
   return (size_t)(rows * kBins + rows * 4 + rows * nchunk * 2) * sizeof(uint32_t);
@@ -390,9 +426,8 @@ size_t dsa_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k) {
 
 hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream) {
   const int64_t rows = p.B * p.T;
-  if (p.S <= kLdsRow) {
-    const size_t lds = (size_t)(kLdsRow + kBins + 32 + 4) * sizeof(uint32_t);
-    hipLaunchKernelGGL(dsa_topk_lds_kernel, dim3((uint32_t)rows), dim3(kTopkThreads), lds, stream, p);
+  if (p.S <= kRegRow) {
+    hipLaunchKernelGGL(dsa_topk_reg_kernel, dim3((uint32_t)rows), dim3(kRegThreads), 0, stream, p);
     return hipGetLastError();
   }
   const int64_t nchunk = (p.S + kMwChunk - 1) / kMwChunk;

@@ -9,6 +9,7 @@
 // of a tile is first the compressed entries visible to its last query (in
 // tiles of 32), then the raw band [t0-window+1, t_last] (in tiles of 32).  A
 // wave skips the MFMA work of a tile that none of its 16 queries can see.
+// K and V tiles are staged with direct global->LDS loads.
 // Workgroups of one head are kept on one XCD (shared L2 for the compressed
 // cache and the overlapping raw band) and the longest tiles start first.
 #include "attn_core.h"
@@ -25,10 +26,8 @@ __device__ __forceinline__ int hca_visible(int t, int blk, int window) {
 template <typename T, int D>
 __global__ __launch_bounds__(kAttnThreads) void hca_prefill_kernel(HcaPrefillParams p) {
   using G = AttnGeom<T, D>;
-  // Two pipeline stages as separate LDS objects, so the compiler can tell the
-  // in-flight loads into one stage from the reads of the other.
-  __shared__ __attribute__((aligned(16))) char lds0[G::kStageBytes];
-  __shared__ __attribute__((aligned(16))) char lds1[G::kStageBytes];
+  __shared__ __attribute__((aligned(16))) char kbuf[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char vbuf[G::kTileBytes];
 
   // Positions fit in 32 bits (checked on the host); pointer offsets are 64-bit.
   const int n_qtiles = (int)p.n_qtiles;
@@ -75,42 +74,47 @@ __global__ __launch_bounds__(kAttnThreads) void hca_prefill_kernel(HcaPrefillPar
 
   // Tile t < n_ctiles: compressed entries [32t, 32t+32) of kc/vc; otherwise
   // raw positions from s_lo onwards.  Rows past the segment end are padding.
-  auto issue = [&](int tile, char* buf) {
+  auto rows_of = [&](int tile) {
     const bool ct = tile < n_ctiles;
-    const T* kbase = ct ? kc : k;
-    const T* vbase = ct ? vc : v;
     const int first = ct ? tile * kBN : s_lo + (tile - n_ctiles) * kBN;
     const int last = ct ? nc - 1 : t_last;
-    stage_async<T, D>(buf, buf + G::kTileBytes, kbase, vbase, [=](int r) -> int {
+    return [=](int r) -> int {
       const int x = first + r;
       return x <= last ? x : -1;
-    });
+    };
   };
-  auto compute = [&](int tile, const char* buf) {
+  auto issue_k = [&](int tile) { stage_rows_async<T, D>(kbuf, tile < n_ctiles ? kc : k, rows_of(tile)); };
+  auto issue_v = [&](int tile) { stage_rows_async<T, D>(vbuf, tile < n_ctiles ? vc : v, rows_of(tile)); };
+
+  // One stage of K and V per workgroup (64 KB for d = 512), so two
+  // workgroups share a CU: while one waits for its next tile the other runs
+  // its MFMA work.  No tile load is in flight while LDS is read, so the
+  // compiler adds no waits of its own.  Visibility inside a tile is a
+  // per-lane key range [lo, hi]: compressed tile: key < vis_c - j0; raw tile:
+  // win_lo <= s0 + key <= tq.
+  wait_vmcnt<0>();  // Q is in registers before any tile load is in flight
+  if (n_tiles > 0) {
+    issue_k(0);
+    issue_v(0);
+  }
+  for (int tile = 0; tile < n_tiles; ++tile) {
     const bool ctile = tile < n_ctiles;
     const int j0 = tile * kBN;
     const int s0 = s_lo + (tile - n_ctiles) * kBN;
     const bool need = ctile ? (j0 < wave_nc) : (wvalid && s0 <= tw_last && s0 + kBN - 1 >= wave_lo);
-    if (need)
-      attend_tile<T, D>(R, buf, buf + G::kTileBytes, p.scale_log2, [&](int key) {
-        if (ctile) return j0 + key < vis_c;
-        const int s = s0 + key;
-        return s >= win_lo && s <= tq;
-      });
-  };
+    const int lo = ctile ? 0 : win_lo - s0;
+    const int hi = ctile ? vis_c - j0 - 1 : tq - s0;
 
-  // Two-stage pipeline, unrolled by two so each stage buffer has a fixed role.
-  if (n_tiles > 0) issue(0, lds0);
-  for (int tile = 0; tile < n_tiles; tile += 2) {
-    wait_loads<0>();
-    __syncthreads();
-    if (tile + 1 < n_tiles) issue(tile + 1, lds1);
-    compute(tile, lds0);
-    if (tile + 1 >= n_tiles) break;
-    wait_loads<0>();
-    __syncthreads();
-    if (tile + 2 < n_tiles) issue(tile + 2, lds0);
-    compute(tile + 1, lds1);
+    wait_loads<0>();  // this wave's part of tile t has landed
+    lds_barrier();    // ... and every other wave's part
+    if (need)
+      attend_tile<T, D>(R, kbuf, vbuf, p.scale_log2, [=](int key) { return key >= lo && key <= hi; });
+    wait_lgkmcnt0();
+    lds_barrier();  // every wave is done reading the tile
+    if (tile + 1 < n_tiles) {
+      issue_k(tile + 1);
+      issue_v(tile + 1);
+    }
   }
   finish_rows<T, D>(R, qvalid ? o + (int64_t)tq * D : nullptr,
                     (p.lse && qvalid) ? p.lse + (int64_t)bh * Tn + tq : nullptr);

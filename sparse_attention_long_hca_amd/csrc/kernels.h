@@ -81,9 +81,14 @@ struct DsaSparseParams {
   const int32_t* idx;  // [B,T,kk]
   void* o;
   float* lse;
+  float* part_o;    // [B*T*nsplit, Hq, D] fp32 (nsplit > 1)
+  float* part_lse;  // [B*T*nsplit, Hq]    log2 units
   int64_t B, T, S, kk;
   float scale_log2;
+  int64_t nsplit, tiles_per_split;
 };
+int64_t dsa_sparse_nsplit(int64_t BT, int64_t kk);
+size_t dsa_sparse_workspace_bytes(int64_t BT, int64_t nsplit, int64_t hq, int64_t d);
 hipError_t launch_dsa_sparse(const DsaSparseParams& p, int d, int hq, hipStream_t stream);
 
 }  // namespace sa

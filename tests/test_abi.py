@@ -126,8 +126,9 @@ def test_topk_validation(sa):
 
 def test_sparse_attention_validation(sa):
     L = sa.lib()
-    # q, k, v, idx, o, lse, dtype, B, T, S, Hq, D, kk, scale, stream (never called valid on the CPU)
-    args = [4096] * 5 + [None, 1, 1, 4, 16, 64, 256, 32, 0.0, None]
+    # q, k, v, idx, o, lse, dtype, B, T, S, Hq, D, kk, scale, workspace, workspace_bytes, stream
+    # (never called with valid arguments on the CPU)
+    args = [4096] * 5 + [None, 1, 1, 4, 16, 64, 256, 32, 0.0, None, 0, None]
     bad = list(args)
     bad[0] = None
     assert L.dsa_sparse_attention_fwd(*bad) == SA_ERR_NULL
@@ -140,3 +141,9 @@ def test_sparse_attention_validation(sa):
     bad = list(args)
     bad[7] = 0  # T
     assert L.dsa_sparse_attention_fwd(*bad) == SA_ERR_SHAPE
+    # decode-sized calls (few tokens) need a workspace for the split partials
+    assert L.dsa_sparse_attention_fwd_workspace_size(4, 1, 64, 256, 2048) > 0
+    assert L.dsa_sparse_attention_fwd_workspace_size(1, 32768, 64, 256, 2048) == 0
+    dec = list(args)
+    dec[12] = 2048  # kk: a 4-token call with 2048 indices is split and needs a workspace
+    assert L.dsa_sparse_attention_fwd(*dec) == SA_ERR_WORKSPACE

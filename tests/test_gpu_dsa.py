@@ -139,8 +139,10 @@ def _random_idx(B, T, S, kk, g, q_pos=None):
     return idx
 
 
-@pytest.mark.parametrize("B,T,S,kk", [(1, 40, 400, 128), (2, 9, 3000, 2048), (1, 64, 64, 100), (1, 5, 50, 33)])
+@pytest.mark.parametrize("B,T,S,kk", [(1, 40, 400, 128), (2, 9, 3000, 2048), (1, 64, 64, 100), (1, 5, 50, 33),
+                                      (1, 600, 700, 64), (2, 300, 2500, 300)])
 def test_sparse_attention_unit_variance(B, T, S, kk):
+    """Covers the split index-list path (few tokens) and the one-workgroup-per-token path (>= 512 tokens)."""
     sa = require_gpu()
     g = np.random.default_rng(50 + kk)
     q = synth.np_normal((B, T, 64, 256), 1.0, "bf16", 51, 0)
