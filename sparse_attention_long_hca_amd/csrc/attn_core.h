@@ -30,7 +30,9 @@ constexpr int kRowsPerWave = 16;
 constexpr int kBM = kAttnWaves * kRowsPerWave;  // query rows per workgroup
 constexpr int kBN = 32;                         // keys per tile
 
-template <typename T, int D>
+// kSwz selects the LDS row swizzle: 0 = lds_swizzle (16-row core),
+// 1 = lds_swizzle32 (32-row core).
+template <typename T, int D, int kSwz = 0>
 struct AttnGeom {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int kEPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
@@ -41,9 +43,10 @@ struct AttnGeom {
   static constexpr int kONb = D / 16;
   static constexpr int kStageBytes = 2 * kTileBytes;  // one pipeline stage: K tile + V tile
   static_assert(kChunks >= 16, "the LDS swizzle needs at least 16 chunks per row");
-  // Row r, 16-byte chunk c -> byte offset in a tile (see lds_swizzle).
+  __device__ static __forceinline__ int swz(int r) { return kSwz == 0 ? lds_swizzle(r) : lds_swizzle32(r); }
+  // Row r, 16-byte chunk c -> byte offset in a tile.
   __device__ static __forceinline__ uint32_t chunk_off(int r, int c) {
-    return (uint32_t)(r * kChunks + (c ^ lds_swizzle(r))) * 16u;
+    return (uint32_t)(r * kChunks + (c ^ swz(r))) * 16u;
   }
 };
 
@@ -93,37 +96,60 @@ __device__ __forceinline__ void load_q(AttnRegs<T, D>& R, const T* qrow) {
 // Every tile issues the same number of loads per wave (padding rows load the
 // fallback row, which is finite and masked), so a fixed vmcnt wait is exact.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int kWaves = kAttnWaves>
 struct StageGeom {
   using G = AttnGeom<T, D>;
   static constexpr int kInstr = kBN * G::kChunks / kWave;  // wave loads per K (or V) tile
-  static constexpr int kPerWave = kInstr / kAttnWaves;
-  static_assert(kInstr % kAttnWaves == 0, "tile must split evenly over the waves");
+  static constexpr int kPerWave = kInstr / kWaves;
+  static_assert(kInstr % kWaves == 0, "tile must split evenly over the waves");
   static constexpr int kLoadsPerTile = 2 * kPerWave;  // K and V
 };
 
-__device__ __forceinline__ void global_load_lds_16(const void* g, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+// Direct global -> LDS loads go through a buffer descriptor (MUBUF with the
+// LDS bit) rather than the FLAT-encoded global form: the compiler then counts
+// them on vmcnt alone, and LDS reads issued while they are in flight keep
+// exact lgkmcnt waits.  The descriptor covers [base, base + 4 GiB); callers
+// pass byte offsets below 2^32 (bounds are checked before the offsets are
+// formed).
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc_t;
+__device__ __forceinline__ buffer_rsrc_t make_buffer_rsrc(const void* base) {
+  // Word 3 of a gfx9 raw buffer descriptor: 32-bit data format, no swizzle.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0xffffffff, 0x00020000);
+}
+// Lane i's 16 bytes at byte offset voff land at lds_wave_base + 16*i.
+__device__ __forceinline__ void buffer_load_lds_16(buffer_rsrc_t rsrc, uint32_t voff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 16, voff, 0, 0, 0);
 }
 
 // Tile source: uniform base pointers of the K and V rows; rowfn(r) gives the
 // row index of tile row r relative to them, or -1 for a padding row (which
 // loads row 0 of the same tensor: finite, and masked by the caller).
-template <typename T, int D, typename RowFn>
+template <typename T, int D, int kWaves = kAttnWaves, int kSwz = 0, typename RowFn>
 __device__ __forceinline__ void stage_rows_async(char* buf, const T* base_ptr, RowFn&& rowfn) {
-  using G = AttnGeom<T, D>;
-  using SG = StageGeom<T, D>;
+  using G = AttnGeom<T, D, kSwz>;
+  using SG = StageGeom<T, D, kWaves>;
   const int wave = wave_id(), lane = threadIdx.x & 63;
+  // All row lookups first: rowfn may read LDS, and such a read cannot be
+  // moved past a direct-to-LDS load, so interleaving them would serialise
+  // every load behind an LDS round trip.
+  int row[SG::kPerWave];
+#pragma unroll
+  for (int j = 0; j < SG::kPerWave; ++j) row[j] = rowfn((int)(((unsigned)(j * kWaves + wave) * kWave + lane) / G::kChunks));
+  // Keep the lookups together, ahead of every use.
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t off[SG::kPerWave];
 #pragma unroll
   for (int j = 0; j < SG::kPerWave; ++j) {
-    const int base = (j * kAttnWaves + wave) * kWave;  // first physical chunk of this load
-    const int P = base + lane;
-    const int r = P / G::kChunks, cp = P % G::kChunks;
-    const int c = cp ^ lds_swizzle(r);
-    int row = rowfn(r);
-    row = row < 0 ? 0 : row;
-    const uint32_t off = (uint32_t)row * (uint32_t)G::kRowBytes + (uint32_t)c * 16u;
-    global_load_lds_16(reinterpret_cast<const char*>(base_ptr) + off, buf + base * 16);
+    const unsigned P = (unsigned)(j * kWaves + wave) * kWave + lane;
+    const int r = (int)(P / G::kChunks), cp = (int)(P % G::kChunks);
+    const int c = cp ^ G::swz(r);
+    off[j] = (uint32_t)(row[j] < 0 ? 0 : row[j]) * (uint32_t)G::kRowBytes + (uint32_t)c * 16u;
+  }
+  const buffer_rsrc_t rsrc = make_buffer_rsrc(base_ptr);
+#pragma unroll
+  for (int j = 0; j < SG::kPerWave; ++j) {
+    const int base = (j * kWaves + wave) * kWave;  // first physical chunk of this load
+    buffer_load_lds_16(rsrc, off[j], buf + base * 16);
   }
 }
 

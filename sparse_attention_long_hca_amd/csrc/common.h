@@ -11,6 +11,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t bf16_t;  // storage type of a bfloat16 value
 
 constexpr int kWave = 64;
@@ -32,19 +33,29 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even,
+// with gfx950's v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
 // ---------------------------------------------------------------------------
 // MFMA (operand layouts checked on gfx950):
 //  16x16x32 bf16: A lane l holds A[l%16][(l/16)*8 + 0..7], B lane l holds
 //    B[(l/16)*8 + 0..7][l%16], C lane l holds C[(l/16)*4 + 0..3][l%16].
+//  32x32x16 bf16: A lane l holds A[l%32][(l/32)*8 + 0..7], B lane l holds
+//    B[(l/32)*8 + 0..7][l%32], C value j holds C[8*(j/4) + (l/32)*4 + j%4][l%32].
 //  16x16x4 f32:   A lane l holds A[l%16][l/16], B lane l holds B[l/16][l%16],
 //    C as above.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(i16x8_t a, i16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma_bf16_32x32x16(i16x8_t a, i16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4_t mfma_f32_16x16x4(float a, float b, f32x4_t c) {
@@ -72,18 +83,31 @@ __device__ __forceinline__ i16x4_t lds_read_tr16_b64(const char* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave reductions over lanes that share lane%16 (xor 16 and xor 32).
+// Cross-lane pairs without LDS: v_permlane16_swap / v_permlane32_swap with
+// both operands equal leave, in every lane, the values of the lane pair
+// (l, l^16) or (l, l^32), always in the same order, so the reductions below
+// give bit-identical results in both lanes of a pair.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float max_across_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float sum_across_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wave reductions over lanes that share lane%16 (xor 16 and xor 32).
+__device__ __forceinline__ float max_across_groups(float x) { return max_xor32(max_xor16(x)); }
+__device__ __forceinline__ float sum_across_groups(float x) { return sum_xor32(sum_xor16(x)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -104,6 +128,10 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t n) {
 // the same chunk of 16 consecutive rows (an MFMA operand fetch) and for 8
 // consecutive rows read as 32-byte pieces (the transposing V reads).
 __device__ __forceinline__ int lds_swizzle(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// Variant for the 32-row core, whose transposing reads take 64 bytes from
+// each of 4 consecutive rows per LDS cycle: distinct over any 16 consecutive
+// rows, and distinct in bits 2..3 over 4 aligned rows.
+__device__ __forceinline__ int lds_swizzle32(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // ---------------------------------------------------------------------------
 // Wait counters and barriers for pipelines fed by direct global->LDS loads.

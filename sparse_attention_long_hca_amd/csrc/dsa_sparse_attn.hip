@@ -5,26 +5,32 @@
 // depend on the context length; MLA heads are 256 wide.  Multi-query layout:
 // the query heads of a token share one K row and one V row per position.
 //
-// One workgroup per query token: its 64 heads are the 64 rows of the MFMA
-// tile (4 waves x 16 heads), so every gathered K/V row is read once and used
+// One workgroup per query token: its 64 heads are the rows of two 32x32 MFMA
+// tiles (2 waves x 32 heads), so every gathered K/V row is read once and used
 // by all heads.  The index list is walked in tiles of 32 positions; each
 // 512-byte row is gathered with 16-byte loads by 32 consecutive lanes (one
 // contiguous row per half-wave).  Indices outside [0, S) are skipped; a tile
 // without any valid index is skipped entirely.
-#include "attn_core.h"
+#include "attn_core32.h"
 #include "kernels.h"
 
 namespace sa {
 
 constexpr int kDsaMaxK = 2048;  // longest index list per query
 
+constexpr int kDsaWaves = 2;                   // 2 waves x 32 heads = 64 heads
+constexpr int kDsaThreads = kDsaWaves * kWave;  // 128
+
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void dsa_sparse_kernel(DsaSparseParams p) {
+__global__ __launch_bounds__(kDsaThreads) void dsa_sparse_kernel(DsaSparseParams p) {
   using T = bf16_t;
-  using G = AttnGeom<T, D>;
-  // One stage of K and V (32 KB for d = 256); several workgroups share a CU
-  // and cover each other's load latency (see hca_prefill.hip).
-  __shared__ __attribute__((aligned(16))) char lds0[G::kStageBytes];
+  using G = AttnGeom<T, D, 1>;
+  // One K tile and one V tile (16 KB each for d = 256) in separate arrays,
+  // plus the index list: four workgroups share a CU.  The next K tile is
+  // loaded while this tile's softmax and PV run, the next V tile while the
+  // next QK runs.
+  __shared__ __attribute__((aligned(16))) char kl[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char vl[G::kTileBytes];
   __shared__ int32_t sidx[kDsaMaxK];
 
   const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -33,58 +39,63 @@ __global__ __launch_bounds__(kAttnThreads) void dsa_sparse_kernel(DsaSparseParam
   const int64_t b = tok / p.T;
   const int wave = wave_id();
   const int lane = threadIdx.x & 63;
-  const int L = lane & 15;
-  constexpr int kHq = kBM;  // 64 heads
+  constexpr int kHq = 64;
 
   const T* q = reinterpret_cast<const T*>(p.q) + tok * kHq * D;
   const T* kb = reinterpret_cast<const T*>(p.k) + b * p.S * D;
   const T* vb = reinterpret_cast<const T*>(p.v) + b * p.S * D;
   const int32_t* idx = p.idx + tok * p.kk;
   T* o = reinterpret_cast<T*>(p.o) + tok * kHq * D;
-  const int h = wave * kRowsPerWave + L;
+  const int h = wave * 32 + (lane & 31);
   const int kk = (int)p.kk;
   const int64_t S = p.S;
 
-  // Index list -> LDS, out-of-range entries replaced by -1.
-  for (int n = threadIdx.x; n < kk; n += kAttnThreads) {
-    const int32_t s = idx[n];
+  // Index list -> LDS, out-of-range entries and the tail of the last tile
+  // replaced by -1.
+  const int kk_pad = (kk + kBN - 1) / kBN * kBN;
+  for (int n = threadIdx.x; n < kk_pad; n += kDsaThreads) {
+    const int32_t s = n < kk ? idx[n] : -1;
     sidx[n] = (s >= 0 && s < S) ? s : -1;
   }
-  AttnRegs<T, D> R;
-  load_q(R, q + h * D);
+  Attn32Regs<D> R;
+  load_q32<D>(R, q + h * D);
+  const Tile32Addr ad = tile32_addr<D>();
   __syncthreads();  // the index list is in LDS
 
   // This workgroup's share of the index list: tiles [t_first, t_first + n_tiles).
   const int t_first = split * (int)p.tiles_per_split;
   const int n_tiles = max(0, min((kk + kBN - 1) / kBN - t_first, (int)p.tiles_per_split));
-  auto issue = [&](int t, char* buf) {
-    const int tile = t_first + t;
-    stage_async<T, D>(buf, buf + G::kTileBytes, kb, vb, [=](int r) -> int {
-      const int n = tile * kBN + r;
-      return n < kk ? sidx[n] : -1;
-    });
+  auto rows_of = [&](int t) {
+    const int32_t* trow = sidx + (t_first + t) * kBN;
+    return [=](int r) -> int { return trow[r]; };
   };
-  auto compute = [&](int t, const char* buf) {
-    const int n = (t_first + t) * kBN + (lane & 31);
-    const uint32_t mask = (uint32_t)(__ballot(n < kk && sidx[n] >= 0) & 0xffffffffull);
-    if (mask) attend_tile<T, D>(R, buf, buf + G::kTileBytes, p.scale_log2, [&](int key) { return (mask >> key) & 1u; });
-  };
+  auto issue_k = [&](int t) { stage_rows_async<T, D, kDsaWaves, 1>(kl, kb, rows_of(t)); };
+  auto issue_v = [&](int t) { stage_rows_async<T, D, kDsaWaves, 1>(vl, vb, rows_of(t)); };
 
   wait_vmcnt<0>();  // Q is in registers before any tile load is in flight
-  if (n_tiles > 0) issue(0, lds0);
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  if (n_tiles > 0) {
+    issue_k(0);
+    issue_v(0);
+  }
+  for (int t = 0; t < n_tiles; ++t) {
     wait_loads<0>();
-    lds_barrier();
-    compute(tile, lds0);
+    lds_barrier();  // K and V of tile t are in LDS for both waves
+    const uint32_t mask = (uint32_t)(__ballot(sidx[(t_first + t) * kBN + (lane & 31)] >= 0) & 0xffffffffull);
+    f32x16_t s;
+    if (mask) s = attend_qk32<D>(R, kl, ad);
     wait_lgkmcnt0();
-    lds_barrier();
-    if (tile + 1 < n_tiles) issue(tile + 1, lds0);
+    lds_barrier();  // both waves are done with the K tile
+    if (t + 1 < n_tiles) issue_k(t + 1);
+    if (mask) attend_pv32<D>(R, s, vl, p.scale_log2, mask, ad);
+    wait_lgkmcnt0();
+    lds_barrier();  // both waves are done with the V tile
+    if (t + 1 < n_tiles) issue_v(t + 1);
   }
   if (p.nsplit == 1) {
-    finish_rows<T, D>(R, o + h * D, p.lse ? p.lse + tok * kHq + h : nullptr);
+    finish_rows32<D>(R, o + h * D, p.lse ? p.lse + tok * kHq + h : nullptr);
   } else {
     const int64_t ps = tok * p.nsplit + split;
-    finish_rows_partial<T, D>(R, p.part_o + (ps * kHq + h) * D, p.part_lse + ps * kHq + h);
+    finish_rows32_partial<D>(R, p.part_o + (ps * kHq + h) * D, p.part_lse + ps * kHq + h);
   }
 }
 
@@ -92,7 +103,7 @@ __global__ __launch_bounds__(kAttnThreads) void dsa_sparse_kernel(DsaSparseParam
 // exp2(lse_s - max).  One workgroup per (token, head), one thread per dim.
 template <int D>
 __global__ __launch_bounds__(D) void dsa_sparse_combine_kernel(DsaSparseParams p) {
-  constexpr int kHq = kBM;
+  constexpr int kHq = 64;
   const int64_t th = blockIdx.x;  // tok * kHq + h
   const int64_t tok = th / kHq;
   const int h = (int)(th % kHq);
@@ -128,12 +139,12 @@ size_t dsa_sparse_workspace_bytes(int64_t BT, int64_t nsplit, int64_t hq, int64_
 }
 
 hipError_t launch_dsa_sparse(const DsaSparseParams& p, int d, int hq, hipStream_t stream) {
-  if (d != 256 || hq != kBM) return hipErrorInvalidValue;
+  if (d != 256 || hq != 64) return hipErrorInvalidValue;
   const int64_t nblocks = p.B * p.T * p.nsplit;
-  hipLaunchKernelGGL(dsa_sparse_kernel<256>, dim3((uint32_t)nblocks), dim3(kAttnThreads), 0, stream, p);
+  hipLaunchKernelGGL(dsa_sparse_kernel<256>, dim3((uint32_t)nblocks), dim3(kDsaThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  hipLaunchKernelGGL(dsa_sparse_combine_kernel<256>, dim3((uint32_t)(p.B * p.T * kBM)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(dsa_sparse_combine_kernel<256>, dim3((uint32_t)(p.B * p.T * 64)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
