@@ -18,6 +18,8 @@
 // keys in registers.  Longer rows: a multi-workgroup pipeline with
 // histograms and per-chunk counts in the workspace.  All counts are integers,
 // so both paths give bit-identical, run-to-run stable results.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -69,6 +71,38 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t x, uint32_t* s
   return x + before;
 }
 
+// Two targets at once: for each t in {t1, t2} with 1 <= t <= total, the bin
+// where the count from the top reaches t (outputs as in select_bin; a target
+// above the total leaves its outputs untouched).  Ends with a barrier.
+__device__ void select_bins2(const uint32_t* hist, int nbins, uint32_t t1, uint32_t t2, uint32_t* scratch,
+                             uint32_t* out /* bin1, above1, bin2, above2 */) {
+  const int per = (nbins + blockDim.x - 1) / blockDim.x;
+  const int hi = nbins - (int)threadIdx.x * per;
+  uint32_t local = 0;
+  for (int j = 1; j <= per; ++j) {
+    const int bin = hi - j;
+    if (bin >= 0) local += hist[bin];
+  }
+  uint32_t tot;
+  const uint32_t incl = block_inclusive_scan(local, scratch, tot);
+  uint32_t above = incl - local;
+  for (int j = 1; j <= per; ++j) {
+    const int bin = hi - j;
+    if (bin < 0) break;
+    const uint32_t c = hist[bin];
+    if (above < t1 && above + c >= t1) {
+      out[0] = (uint32_t)bin;
+      out[1] = above;
+    }
+    if (above < t2 && above + c >= t2) {
+      out[2] = (uint32_t)bin;
+      out[3] = above;
+    }
+    above += c;
+  }
+  __syncthreads();
+}
+
 // Given hist[0..nbins) and need >= 1 (<= total count), find the bin where the
 // count from the top reaches need.  Result: *sel_bin, *sel_above (count in
 // bins strictly above).  Uses all threads; nbins <= 2 * blockDim.x.
@@ -102,20 +136,69 @@ __device__ void select_bin(const uint32_t* hist, int nbins, uint32_t need, uint3
 // Rows up to kRegRow positions: one 512-thread workgroup per row holds the
 // whole row of keys in registers.  Thread t owns positions 4*(t + 512*j) + e
 // (j < 16, e < 4), read with 16-byte loads that are all in flight at once.
-// The ordered compaction scans packed (greater, equal) counts per 4-element
-// group: lane prefix inside the wave, then a table of per-(group, wave)
-// totals in LDS.
+// The work is bound by vector ALU instructions per key, so every sweep over
+// the 64 keys of a thread is kept short:
+//
+//  1. Find the k-th largest key K* exactly.  Candidates are the keys in an
+//     interval [lo, hi] of key values, first the row's extremes.  A round
+//     histograms the candidates by (key - lo) >> shift, with shift chosen so
+//     that the bins are 2^shift keys wide and (hi - lo) lands in bins
+//     1024..2047; the bin where the count from the top reaches the number of
+//     keys still needed gives the next, exact interval (at least 1024 times
+//     narrower; one-key bins end it).  Once at most kCandLds candidates are
+//     left they move to LDS with their positions and further rounds run over
+//     those; at most kCandCap are finally ranked pairwise by one wave.
+//  2. With K* and need_eq (copies of K* to take, lowest positions first),
+//     an ordered compaction emits position s iff key > K*, or key == K* and
+//     fewer than need_eq copies precede s.  Packed (greater, equal) counts
+//     are scanned inside each wave with DPP, then across (group, wave).
 // ---------------------------------------------------------------------------
 constexpr int kRegThreads = 512;
 constexpr int kRegWaves = kRegThreads / kWave;
 constexpr int kRegVec = 16;                            // 4-element groups per thread
 constexpr int kRegRow = kRegThreads * kRegVec * 4;     // 32768
+constexpr int kCandLds = 2048;                         // candidates moved to LDS
+constexpr int kCandPer = kCandLds / kRegThreads;       // 4 per thread
+constexpr int kCandCap = kWave;                        // ranked pairwise by one wave
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, off));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
+  return x;
+}
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the
+// row broadcasts 15 and 31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+// Bin width exponent for an interval of (range + 1) keys: bins of 2^shift
+// keys with range >> shift in [1024, 2047] (or shift 0 for small ranges).
+__device__ __forceinline__ uint32_t bin_shift(uint32_t range) {
+  const int bits = 32 - __clz((int)range);  // 1..32 for range >= 1
+  return bits > 11 ? (uint32_t)(bits - 11) : 0u;
+}
 
 __global__ __launch_bounds__(kRegThreads) void dsa_topk_reg_kernel(DsaTopkParams p) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kBins];  // also the staging buffer of the output row
   __shared__ uint32_t scratch[32];
-  __shared__ uint32_t res[2];
-  __shared__ uint32_t wtot[kRegVec][kRegWaves];  // packed counts per (group j, wave)
+  __shared__ uint32_t res[8];
+  __shared__ uint32_t wtot[kRegVec * kRegWaves];
+  __shared__ uint32_t red[3][kRegWaves];
+  __shared__ uint32_t ckey[kCandLds];
+  __shared__ uint32_t cpos[kCandLds];
+  __shared__ int32_t sink[kWave];
 
   const int64_t row = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t b = row / p.T, i = row % p.T;
@@ -131,14 +214,16 @@ __global__ __launch_bounds__(kRegThreads) void dsa_topk_reg_kernel(DsaTopkParams
   const float* sc = p.scores + row * p.S;
 
   // Keys (0 marks a position past the row end; only an all-ones NaN also maps
-  // to 0).  Every load is unconditional (clamped into the row) so that all
-  // of them are in flight together; positions >= n are masked afterwards.
+  // to 0 and is never selected).  Every load is unconditional so that all of
+  // them are in flight together; loads past the row end are clamped onto its
+  // last 16 bytes (a cache hit) and masked afterwards.
   uint32_t key[kRegVec][4];
   if ((p.S & 3) == 0) {  // 16-byte aligned rows
+    const int last4 = (n - 1) & ~3;
     float4 f[kRegVec];
 #pragma unroll
     for (int j = 0; j < kRegVec; ++j) {
-      const int pos0 = min(4 * (tid + kRegThreads * j), (int)p.S - 4);
+      const int pos0 = min(4 * (tid + kRegThreads * j), last4);
       f[j] = *reinterpret_cast<const float4*>(sc + pos0);
     }
 #pragma unroll
@@ -155,79 +240,349 @@ __global__ __launch_bounds__(kRegThreads) void dsa_topk_reg_kernel(DsaTopkParams
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int pos = 4 * (tid + kRegThreads * j) + e;
-        const float f = sc[min(pos, (int)p.S - 1)];
+        const float f = sc[min(pos, n - 1)];
         key[j][e] = pos < n ? score_key(f) : 0u;
       }
   }
-
-  uint32_t prefix = 0, need = (uint32_t)k;
+  // A re-read of the key registers that the compiler cannot see through, so
+  // that a sweep recomputes its per-key predicates instead of keeping 64 of
+  // them alive (in scalar registers) from an earlier sweep.  Only used where
+  // every control path has merged: a refresh inside a branch would make the
+  // compiler keep both versions of the keys.
+  auto refresh_keys = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    for (int j = tid; j < kBins; j += kRegThreads) hist[j] = 0;
+    for (int j = 0; j < kRegVec; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(key[j][e]));
+  };
+  // Workgroup-wide (min, max, sum) of per-thread values; uniform results.
+  auto reduce3 = [&](uint32_t a, uint32_t z, uint32_t c, uint32_t& mn, uint32_t& mx, uint32_t& sum) __attribute__((always_inline)) {
+    a = wave_min_u32(a);
+    z = wave_max_u32(z);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) c += (uint32_t)__shfl_xor((int)c, off);
+    if (lane == 0) {
+      red[0][wave] = a;
+      red[1][wave] = z;
+      red[2][wave] = c;
+    }
     __syncthreads();
-    const int sh = digit_shift(pass);
-    const uint32_t dm = digit_mask(pass);
-    const int sh_prev = pass > 0 ? digit_shift(pass - 1) : 0;
+    mn = 0xffffffffu;
+    mx = 0u;
+    sum = 0u;
+#pragma unroll
+    for (int w = 0; w < kRegWaves; ++w) {
+      mn = min(mn, red[0][w]);
+      mx = max(mx, red[1][w]);
+      sum += red[2][w];
+    }
+    mn = uniform_u32(mn);
+    mx = uniform_u32(mx);
+    sum = uniform_u32(sum);
+    __syncthreads();  // red may be reused
+  };
+  // One refinement round over nk keys per thread: histogram of the keys in
+  // [lo, hi], select the bin where the count from the top reaches need, and
+  // narrow [lo, hi], need and cand to it.
+  auto round = [&](auto nk_tag, auto&& keys_of, uint32_t& lo, uint32_t& hi, uint32_t& need, uint32_t& cand) __attribute__((always_inline)) {
+    constexpr int nk = decltype(nk_tag)::value;
+    const uint32_t range = hi - lo, sh = bin_shift(range);
+    for (int j = tid; j < kBins; j += kRegThreads) hist[j] = 0;
+    if (tid == 0) {
+      res[0] = 0;
+      res[1] = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < nk; ++m) {
+      const uint32_t d = keys_of(m) - lo;  // wraps for keys below lo
+      if (d <= range) atomicAdd(&hist[d >> sh], 1u);
+    }
+    __syncthreads();
+    select_bin(hist, kBins, need, scratch, &res[0], &res[1]);
+    const uint32_t bsel = uniform_u32(res[0]);
+    need -= uniform_u32(res[1]);
+    cand = uniform_u32(hist[bsel]);
+    // Keys of bin bsel: lo + [bsel << sh, (bsel << sh) | (2^sh - 1)], clipped
+    // to the old range (no overflow: the upper offset never passes range's
+    // top bits).
+    hi = lo + min(range, (bsel << sh) | ((1u << sh) - 1u));
+    lo = lo + (bsel << sh);
+    __syncthreads();  // hist and res may be rewritten
+  };
+
+  // Candidates (keys in [lo, hi]) to LDS with their positions, thread t's at
+  // slots base_t, base_t + 1, ... (base_t from a scan of per-thread counts).
+  auto gather = [&](uint32_t glo, uint32_t ghi, uint32_t base) __attribute__((always_inline)) {
+    // Opaque copies of the bounds: the membership tests are recomputed here
+    // rather than kept (64 masks) from the counting sweep before the scan.
+    glo = uniform_u32(glo);
+    ghi = uniform_u32(ghi);
+    asm volatile("" : "+s"(glo), "+s"(ghi));
+    uint32_t pb = 4u * (uint32_t)tid;
+    asm volatile("" : "+v"(pb));
+    uint32_t r = base;
 #pragma unroll
     for (int j = 0; j < kRegVec; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t kv = key[j][e];
-        const bool match = kv != 0u && (pass == 0 || (kv >> sh_prev) == prefix);
-        if (match) atomicAdd(&hist[(kv >> sh) & dm], 1u);
+        const bool in = kv - glo <= ghi - glo;
+        if (in) {
+          ckey[r] = kv;
+          cpos[r] = pb + (uint32_t)(4 * kRegThreads * j + e);
+        }
+        r += in ? 1u : 0u;
       }
-    __syncthreads();
-    select_bin(hist, (int)dm + 1, need, scratch, &res[0], &res[1]);
-    prefix = (prefix << (pass == 0 ? 0 : (sh_prev - sh))) | res[0];
-    need -= res[1];
-    __syncthreads();
-  }
-  const uint32_t K = prefix;  // the k-th largest key; need = copies of K to take
+  };
 
-  // Packed counts: low 16 bits = keys > K, high 16 bits = keys == K.
-  uint32_t incl[kRegVec];
+  // ---- 1. the k-th largest key K* and the copies of it to take -------------
+  uint32_t lo, hi, nsel;
+  {
+    uint32_t a = 0xffffffffu, z = 0u, c = 0u;
 #pragma unroll
-  for (int j = 0; j < kRegVec; ++j) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c += (key[j][e] > K ? 1u : 0u) + (key[j][e] == K ? 0x10000u : 0u);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(c, off);
-      if (lane >= off) c += y;
-    }
-    incl[j] = c;
-    if (lane == 63) wtot[j][wave] = c;
-  }
-  __syncthreads();
-  // Exclusive prefix of the (group, wave) totals in position order (group-major).
-  if (tid == 0) {
-    uint32_t run = 0;
     for (int j = 0; j < kRegVec; ++j)
-      for (int w = 0; w < kRegWaves; ++w) {
-        const uint32_t t = wtot[j][w];
-        wtot[j][w] = run;
-        run += t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kv = key[j][e];
+        a = min(a, kv - 1u);  // an absent key (0) wraps to the top
+        z = max(z, kv);
+        c += kv != 0u ? 1u : 0u;
       }
+    reduce3(a, z, c, lo, hi, nsel);
+    lo += 1u;
   }
-  __syncthreads();
+  uint32_t need = (uint32_t)k;  // keys still to take from [lo, hi]
+  uint32_t Kt = 1u, need_eq = 0u, eq_total = 0u;  // defaults: take every selectable key
+  if (nsel > need) {
+    uint32_t cand = nsel;
+    bool in_lds = false;  // the cand candidates are in ckey/cpos[0, cand)
+    if (cand > (uint32_t)kCandLds && lo < hi) {
+      // Sampled bracket: histogram the keys at every 4th position, take the
+      // bins where the sample count from the top passes need/4 minus and
+      // plus a margin of about four standard deviations, then count the row
+      // exactly against the bracket [L, H].  If the k-th key lies inside and
+      // at most kCandLds keys do, those keys go straight to LDS and no
+      // full-row refinement round is needed.
+      const uint32_t range = hi - lo, sh = bin_shift(range);
+      for (int j = tid; j < kBins; j += kRegThreads) hist[j] = 0;
+      if (tid == 0) {
+        res[0] = 0;
+        res[1] = 0;
+        res[2] = 0;
+        res[3] = 0;
+      }
+      __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kRegVec; ++j) {
-    uint32_t c = 0;
+      for (int j = 0; j < kRegVec; ++j) {
+        const uint32_t d = key[j][0] - lo;
+        if (d <= range) atomicAdd(&hist[d >> sh], 1u);
+      }
+      __syncthreads();
+      const float ns = (float)((n + 3) >> 2);  // sampled positions
+      const float mu = (float)need * ns / (float)nsel;
+      const float margin = 4.f * sqrtf(mu) + 8.f;
+      const uint32_t t_hi = mu - margin >= 1.f ? (uint32_t)(mu - margin) : 0u;  // 0: no upper cut
+      const uint32_t t_lo = (uint32_t)fminf(mu + margin, ns);
+      select_bins2(hist, kBins, t_hi > 0u ? t_hi : 1u, max(t_lo, 1u), scratch, res);
+      const uint32_t b_hi = uniform_u32(res[0]), b_lo = uniform_u32(res[2]);
+      const uint32_t L = lo + (b_lo << sh);
+      // Top key of bin b_hi; (b << sh) | (2^sh - 1) cannot pass range's top bits.
+      const uint32_t H = t_hi > 0u ? lo + min(range, (b_hi << sh) | ((1u << sh) - 1u)) : hi;
+      // Exact counts: keys above H, keys in [L, H] (packed, each <= 32768),
+      // scanned so that every thread also gets its gather slot.
+      uint32_t g = 0, w = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) c += (key[j][e] > K ? 1u : 0u) + (key[j][e] == K ? 0x10000u : 0u);
-    uint32_t before = wtot[j][wave] + incl[j] - c;
-    const int pos0 = 4 * (tid + kRegThreads * j);
+      for (int j = 0; j < kRegVec; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t kv = key[j][e];
-      const uint32_t g_b = before & 0xffffu, e_b = before >> 16;
-      const bool take = kv > K || (kv == K && e_b < need);
-      const uint32_t slot = g_b + (e_b < need ? e_b : need);
-      if (take && slot < (uint32_t)k) out[slot] = pos0 + e;
-      before += (kv > K ? 1u : 0u) + (kv == K ? 0x10000u : 0u);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t kv = key[j][e];
+          g += kv > H ? 1u : 0u;
+          w += kv - L <= H - L ? 1u : 0u;
+        }
+      const uint32_t mine = g | (w << 16);
+      uint32_t tot;
+      const uint32_t incl = block_inclusive_scan(mine, scratch, tot);
+      const uint32_t c_above = uniform_u32(tot & 0xffffu), c_in = uniform_u32(tot >> 16);
+      if (c_above < need && need <= c_above + c_in && c_in <= (uint32_t)kCandLds) {
+        need -= c_above;
+        cand = c_in;
+        lo = L;
+        hi = H;
+        if (lo < hi) {
+          gather(L, H, (incl - mine) >> 16);
+          in_lds = true;
+        }
+      }
+    }
+    if (!in_lds) {
+      while (cand > (uint32_t)kCandLds && lo < hi)
+        round(std::integral_constant<int, kRegVec * 4>{}, [&](int m) { return key[m >> 2][m & 3]; }, lo, hi, need,
+              cand);
+      if (lo < hi) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < kRegVec; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w += key[j][e] - lo <= hi - lo ? 1u : 0u;
+        uint32_t tot;
+        const uint32_t incl = block_inclusive_scan(w, scratch, tot);
+        gather(lo, hi, incl - w);
+        in_lds = true;
+      }
+    }
+    __syncthreads();  // candidates are in LDS
+    if (lo < hi && cand > (uint32_t)kCandCap) {
+      // Further rounds over the LDS candidates (kCandPer per thread).
+      uint32_t ck[kCandPer], cp[kCandPer];
+#pragma unroll
+      for (int m = 0; m < kCandPer; ++m) {
+        const uint32_t c = (uint32_t)(tid + kRegThreads * m);
+        ck[m] = c < cand ? ckey[c] : 0u;
+        cp[m] = c < cand ? cpos[c] : 0u;
+      }
+      while (cand > (uint32_t)kCandCap && lo < hi)
+        round(std::integral_constant<int, kCandPer>{}, [&](int m) { return ck[m]; }, lo, hi, need, cand);
+      if (lo < hi) {
+        // At most kCandCap candidates left: gather them into the front of
+        // the LDS arrays for the ranking wave.
+        if (tid == 0) res[2] = 0;
+        __syncthreads();  // every thread has its candidates out of LDS
+#pragma unroll
+        for (int m = 0; m < kCandPer; ++m)
+          if ((ck[m] != 0u) & (ck[m] - lo <= hi - lo)) {
+            const uint32_t slot = atomicAdd(&res[2], 1u);
+            ckey[slot] = ck[m];
+            cpos[slot] = cp[m];
+          }
+        __syncthreads();
+      }
+    }
+    if (lo == hi) {
+      Kt = lo;  // every candidate is a copy of K*
+      need_eq = need;
+      eq_total = cand;
+    } else {
+      // Rank the <= kCandCap candidates (score descending, then position
+      // ascending); the one of rank need-1 is the k-th overall.
+      if (wave == 0) {
+        const bool act = (uint32_t)lane < cand;
+        const uint32_t kc = act ? ckey[lane] : 0u, pc = act ? cpos[lane] : 0u;
+        uint32_t rank = 0, gtc = 0, eqc = 0;
+        for (uint32_t o = 0; o < cand; ++o) {
+          const uint32_t ko = (uint32_t)__builtin_amdgcn_readlane((int)kc, (int)o);
+          const uint32_t po = (uint32_t)__builtin_amdgcn_readlane((int)pc, (int)o);
+          const uint32_t gt = (uint32_t)(ko > kc), eq = (uint32_t)(ko == kc);
+          gtc += gt;
+          eqc += eq;
+          rank += gt | (eq & (uint32_t)(po < pc));
+        }
+        if (act && rank == need - 1) {
+          res[3] = kc;
+          res[4] = need - gtc;
+          res[5] = eqc;  // copies of K* among the candidates (all of them)
+        }
+      }
+      __syncthreads();
+      Kt = uniform_u32(res[3]);
+      need_eq = uniform_u32(res[4]);
+      eq_total = uniform_u32(res[5]);
     }
   }
+
+  // ---- 2. ordered compaction -----------------------------------------------
+  // Usually every copy of K* is taken: the rule is key >= K* and two groups'
+  // counts share one scan (16-bit fields; a wave holds at most 256 per
+  // group).  Otherwise each group scans packed counts: keys > K* in the low
+  // 16 bits, copies of K* in the high 16 bits (each at most 32768).
+  const bool split_ties = need_eq < eq_total;
+  const uint32_t kt_lo = split_ties ? Kt + 1u : Kt;  // taken outright: key >= kt_lo
+  refresh_keys();
+  auto count4 = [&](int j) __attribute__((always_inline)) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c += key[j][e] >= kt_lo ? 1u : 0u;
+    return c;
+  };
+  auto count4_split = [&](int j) __attribute__((always_inline)) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c += (key[j][e] >= kt_lo ? 1u : 0u) + (key[j][e] == Kt ? 0x10000u : 0u);
+    return c;
+  };
+  if (!split_ties) {
+#pragma unroll
+    for (int jj = 0; jj < kRegVec; jj += 2) {
+      const uint32_t incl = wave_incl_scan(count4(jj) | (count4(jj + 1) << 16));
+      if (lane == 63) {
+        wtot[jj * kRegWaves + wave] = incl & 0xffffu;
+        wtot[(jj + 1) * kRegWaves + wave] = incl >> 16;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRegVec; ++j) {
+      const uint32_t incl = wave_incl_scan(count4_split(j));
+      if (lane == 63) wtot[j * kRegWaves + wave] = incl;
+    }
+  }
+  __syncthreads();
+  static_assert(kRegVec * kRegWaves == 2 * kWave, "one wave scans the (group, wave) totals");
+  if (wave == 0) {
+    const uint32_t a = wtot[2 * lane], z = wtot[2 * lane + 1];
+    const uint32_t x = wave_incl_scan(a + z);
+    const uint32_t ex = x - a - z;
+    wtot[2 * lane] = ex;
+    wtot[2 * lane + 1] = ex + a;
+  }
+  __syncthreads();
+  // Selected positions are staged in LDS (reusing the histogram), then
+  // written out with coalesced stores.  Every key stores: unselected ones
+  // into a per-lane sink, so the loop has no branches.
+  int32_t* sel = reinterpret_cast<int32_t*>(hist);
+  int32_t* my_sink = sink + lane;
+  refresh_keys();
+  uint32_t pb = 4u * (uint32_t)tid;
+  asm volatile("" : "+v"(pb));
+  if (!split_ties) {
+#pragma unroll
+    for (int jj = 0; jj < kRegVec; jj += 2) {
+      const uint32_t c = count4(jj) | (count4(jj + 1) << 16);
+      const uint32_t ex = wave_incl_scan(c) - c;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = jj + h;
+        uint32_t r = wtot[j * kRegWaves + wave] + (h ? ex >> 16 : ex & 0xffffu);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool t = key[j][e] >= kt_lo;
+          *(t ? sel + r : my_sink) = (int32_t)(pb + (uint32_t)(4 * kRegThreads * j + e));
+          r += t ? 1u : 0u;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRegVec; ++j) {
+      const uint32_t c = count4_split(j);
+      uint32_t r = wtot[j * kRegWaves + wave] + wave_incl_scan(c) - c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kv = key[j][e];
+        const uint32_t gb = r & 0xffffu, eb = r >> 16;
+        const bool g = kv >= kt_lo, q = kv == Kt;
+        const bool t = g || (q && eb < need_eq);
+        const uint32_t slot = gb + min(eb, need_eq);
+        *(t ? sel + slot : my_sink) = (int32_t)(pb + (uint32_t)(4 * kRegThreads * j + e));
+        r += g ? 1u : (q ? 0x10000u : 0u);
+      }
+    }
+  }
+  __syncthreads();
+  // Slots past the selected count (only rows with fewer than k selectable
+  // keys) are padded with -1.
+  const uint32_t taken = nsel > (uint32_t)k ? (uint32_t)k : nsel;
+  for (uint32_t j = tid; j < (uint32_t)k; j += kRegThreads) out[j] = j < taken ? sel[j] : -1;
 }
 
 // ---------------------------------------------------------------------------
