@@ -11,6 +11,8 @@
 // 512-byte row is gathered with 16-byte loads by 32 consecutive lanes (one
 // contiguous row per half-wave).  Indices outside [0, S) are skipped; a tile
 // without any valid index is skipped entirely.
+#include <type_traits>
+
 #include "attn_core32.h"
 #include "kernels.h"
 
@@ -22,7 +24,7 @@ constexpr int kDsaWaves = 2;                   // 2 waves x 32 heads = 64 heads
 constexpr int kDsaThreads = kDsaWaves * kWave;  // 128
 
 template <int D>
-__global__ __launch_bounds__(kDsaThreads) void dsa_sparse_kernel(DsaSparseParams p) {
+__global__ __launch_bounds__(kDsaThreads) __attribute__((amdgpu_waves_per_eu(2))) void dsa_sparse_kernel(DsaSparseParams p) {
   using T = bf16_t;
   using G = AttnGeom<T, D, 1>;
   // One K tile and one V tile (16 KB each for d = 256) in separate arrays,
@@ -72,24 +74,42 @@ __global__ __launch_bounds__(kDsaThreads) void dsa_sparse_kernel(DsaSparseParams
   auto issue_k = [&](int t) { stage_rows_async<T, D, kDsaWaves, 1>(kl, kb, rows_of(t)); };
   auto issue_v = [&](int t) { stage_rows_async<T, D, kDsaWaves, 1>(vl, vb, rows_of(t)); };
 
-  wait_vmcnt<0>();  // Q is in registers before any tile load is in flight
-  if (n_tiles > 0) {
-    issue_k(0);
-    issue_v(0);
-  }
-  for (int t = 0; t < n_tiles; ++t) {
-    wait_loads<0>();
-    lds_barrier();  // K and V of tile t are in LDS for both waves
+  // The last tile is peeled off (more = false) so that every load issue in
+  // the loop is unconditional: the compiler's wait tracking then keeps the K
+  // and V buffers apart instead of waiting for every load before an LDS
+  // read.  Each wait covers only the buffer about to be read (a thread's
+  // loads complete in issue order, kLoads per buffer).
+  constexpr int kLoads = StageGeom<T, D, kDsaWaves>::kPerWave;
+  auto step = [&](int t, auto more_tag) __attribute__((always_inline)) {
+    constexpr bool more = decltype(more_tag)::value;
+    wait_loads<kLoads>();  // K of tile t has landed (its V may be in flight)
+    lds_barrier();         // ... for both waves
     const uint32_t mask = (uint32_t)(__ballot(sidx[(t_first + t) * kBN + (lane & 31)] >= 0) & 0xffffffffull);
     f32x16_t s;
     if (mask) s = attend_qk32<D>(R, kl, ad);
     wait_lgkmcnt0();
     lds_barrier();  // both waves are done with the K tile
-    if (t + 1 < n_tiles) issue_k(t + 1);
+    if constexpr (more) {
+      issue_k(t + 1);
+      wait_loads<kLoads>();  // V of tile t has landed (the next K may be in flight)
+    } else {
+      wait_loads<0>();
+    }
+    lds_barrier();
     if (mask) attend_pv32<D>(R, s, vl, p.scale_log2, mask, ad);
-    wait_lgkmcnt0();
-    lds_barrier();  // both waves are done with the V tile
-    if (t + 1 < n_tiles) issue_v(t + 1);
+    if constexpr (more) {
+      wait_lgkmcnt0();
+      lds_barrier();  // both waves are done with the V tile
+      issue_v(t + 1);
+    }
+  };
+
+  wait_vmcnt<0>();  // Q is in registers before any tile load is in flight
+  if (n_tiles > 0) {
+    issue_k(0);
+    issue_v(0);
+    for (int t = 0; t + 1 < n_tiles; ++t) step(t, std::true_type{});
+    step(n_tiles - 1, std::false_type{});
   }
   if (p.nsplit == 1) {
     finish_rows32<D>(R, o + h * D, p.lse ? p.lse + tok * kHq + h : nullptr);

@@ -190,7 +190,7 @@ __device__ __forceinline__ uint32_t bin_shift(uint32_t range) {
   return bits > 11 ? (uint32_t)(bits - 11) : 0u;
 }
 
-__global__ __launch_bounds__(kRegThreads) void dsa_topk_reg_kernel(DsaTopkParams p) {
+__global__ __launch_bounds__(kRegThreads) __attribute__((amdgpu_waves_per_eu(4))) void dsa_topk_reg_kernel(DsaTopkParams p) {
   __shared__ uint32_t hist[kBins];  // also the staging buffer of the output row
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t res[8];

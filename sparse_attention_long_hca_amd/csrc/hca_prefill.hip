@@ -12,6 +12,8 @@
 // K and V tiles are staged with direct global->LDS loads.
 // Workgroups of one head are kept on one XCD (shared L2 for the compressed
 // cache and the overlapping raw band) and the longest tiles start first.
+#include <type_traits>
+
 #include "attn_core.h"
 #include "kernels.h"
 
@@ -24,7 +26,7 @@ __device__ __forceinline__ int hca_visible(int t, int blk, int window) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kAttnThreads) void hca_prefill_kernel(HcaPrefillParams p) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void hca_prefill_kernel(HcaPrefillParams p) {
   using G = AttnGeom<T, D>;
   __shared__ __attribute__((aligned(16))) char kbuf[G::kTileBytes];
   __shared__ __attribute__((aligned(16))) char vbuf[G::kTileBytes];
@@ -33,9 +35,8 @@ __global__ __launch_bounds__(kAttnThreads) void hca_prefill_kernel(HcaPrefillPar
   const int n_qtiles = (int)p.n_qtiles;
   const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = (int)(lid / (uint32_t)n_qtiles);
-  const int qt = n_qtiles - 1 - (int)(lid % (uint32_t)n_qtiles);
+  const int qt = n_qtiles - 1 - (int)(lid % (uint32_t)n_qtiles);  // longest tiles first
   const int Tn = (int)p.T, blk = (int)p.blk, W = (int)p.window, Nc = (int)p.Nc;
-  const int t0 = qt * kBM;
   const int wave = wave_id();
   const int lane = threadIdx.x & 63;
   const int L = lane & 15;
@@ -48,76 +49,97 @@ __global__ __launch_bounds__(kAttnThreads) void hca_prefill_kernel(HcaPrefillPar
   const T* vc = reinterpret_cast<const T*>(p.vc) + (int64_t)bh * Nc * D;
   T* o = reinterpret_cast<T*>(p.o) + head_off;
 
-  const int tw = t0 + wave * kRowsPerWave;  // first query of this wave
-  const int tq = tw + L;                    // this lane's query
-  const bool qvalid = tq < Tn;
+  {
+    const int t0 = qt * kBM;
+    const int tw = t0 + wave * kRowsPerWave;  // first query of this wave
+    const int tq = tw + L;                    // this lane's query
+    const bool qvalid = tq < Tn;
 
-  AttnRegs<T, D> R;
-  load_q(R, qvalid ? q + (int64_t)tq * D : nullptr);
+    AttnRegs<T, D> R;
+    load_q(R, qvalid ? q + (int64_t)tq * D : nullptr);
 
-  // Key stream of the workgroup.
-  const int t_last = min(t0 + kBM - 1, Tn - 1);
-  const int nc = min(Nc, hca_visible(t_last, blk, W));
-  const int n_ctiles = (nc + kBN - 1) / kBN;
-  const int s_lo = max(0, t0 - W + 1);
-  const int n_rtiles = (t_last - s_lo + kBN) / kBN;
-  const int n_tiles = n_ctiles + n_rtiles;
+    // Key stream of the tile.
+    const int t_last = min(t0 + kBM - 1, Tn - 1);
+    const int nc = min(Nc, hca_visible(t_last, blk, W));
+    const int n_ctiles = (nc + kBN - 1) / kBN;
+    const int s_lo = max(0, t0 - W + 1);
+    const int n_rtiles = (t_last - s_lo + kBN) / kBN;
+    const int n_tiles = n_ctiles + n_rtiles;
 
-  // This lane's visibility limits.
-  const int vis_c = qvalid ? min(Nc, hca_visible(tq, blk, W)) : 0;
-  const int win_lo = tq - W + 1;
-  // This wave's limits (for skipping whole tiles).
-  const bool wvalid = tw < Tn;
-  const int tw_last = min(tw + kRowsPerWave - 1, Tn - 1);
-  const int wave_nc = wvalid ? min(Nc, hca_visible(tw_last, blk, W)) : 0;
-  const int wave_lo = tw - W + 1;
+    // This lane's visibility limits.
+    const int vis_c = qvalid ? min(Nc, hca_visible(tq, blk, W)) : 0;
+    const int win_lo = tq - W + 1;
+    // This wave's limits (for skipping whole tiles).
+    const bool wvalid = tw < Tn;
+    const int tw_last = min(tw + kRowsPerWave - 1, Tn - 1);
+    const int wave_nc = wvalid ? min(Nc, hca_visible(tw_last, blk, W)) : 0;
+    const int wave_lo = tw - W + 1;
 
-  // Tile t < n_ctiles: compressed entries [32t, 32t+32) of kc/vc; otherwise
-  // raw positions from s_lo onwards.  Rows past the segment end are padding.
-  auto rows_of = [&](int tile) {
-    const bool ct = tile < n_ctiles;
-    const int first = ct ? tile * kBN : s_lo + (tile - n_ctiles) * kBN;
-    const int last = ct ? nc - 1 : t_last;
-    return [=](int r) -> int {
-      const int x = first + r;
-      return x <= last ? x : -1;
+    // Tile t < n_ctiles: compressed entries [32t, 32t+32) of kc/vc; otherwise
+    // raw positions from s_lo onwards.  Rows past the segment end are padding.
+    auto rows_of = [&](int tile) {
+      const bool ct = tile < n_ctiles;
+      const int first = ct ? tile * kBN : s_lo + (tile - n_ctiles) * kBN;
+      const int last = ct ? nc - 1 : t_last;
+      return [=](int r) -> int {
+        const int x = first + r;
+        return x <= last ? x : -1;
+      };
     };
-  };
-  auto issue_k = [&](int tile) { stage_rows_async<T, D>(kbuf, tile < n_ctiles ? kc : k, rows_of(tile)); };
-  auto issue_v = [&](int tile) { stage_rows_async<T, D>(vbuf, tile < n_ctiles ? vc : v, rows_of(tile)); };
+    auto issue_k = [&](int tile) { stage_rows_async<T, D>(kbuf, tile < n_ctiles ? kc : k, rows_of(tile)); };
+    auto issue_v = [&](int tile) { stage_rows_async<T, D>(vbuf, tile < n_ctiles ? vc : v, rows_of(tile)); };
 
-  // One stage of K and V per workgroup (64 KB for d = 512), so two
-  // workgroups share a CU: while one waits for its next tile the other runs
-  // its MFMA work.  No tile load is in flight while LDS is read, so the
-  // compiler adds no waits of its own.  Visibility inside a tile is a
-  // per-lane key range [lo, hi]: compressed tile: key < vis_c - j0; raw tile:
-  // win_lo <= s0 + key <= tq.
-  wait_vmcnt<0>();  // Q is in registers before any tile load is in flight
-  if (n_tiles > 0) {
-    issue_k(0);
-    issue_v(0);
-  }
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const bool ctile = tile < n_ctiles;
-    const int j0 = tile * kBN;
-    const int s0 = s_lo + (tile - n_ctiles) * kBN;
-    const bool need = ctile ? (j0 < wave_nc) : (wvalid && s0 <= tw_last && s0 + kBN - 1 >= wave_lo);
-    const int lo = ctile ? 0 : win_lo - s0;
-    const int hi = ctile ? vis_c - j0 - 1 : tq - s0;
+    // One K tile and one V tile per workgroup (32 KB each for d = 512), so
+    // two workgroups share a CU.  The next K tile streams in while this
+    // tile's softmax and PV run, the next V tile while the next QK runs; each
+    // wait covers only the buffer about to be read (loads of one thread
+    // complete in issue order, kLoads per buffer).  Visibility inside a tile
+    // is a per-lane key range [lo, hi]: compressed tile: key < vis_c - j0;
+    // raw tile: win_lo <= s0 + key <= tq.
+    constexpr int kLoads = StageGeom<T, D>::kPerWave;
+    // The last tile is peeled off (more = false) so that every load issue in
+    // the loop is unconditional: the compiler's wait tracking then keeps the
+    // K and V buffers apart instead of waiting for every load before an LDS
+    // read.
+    auto step = [&](int tile, auto more_tag) __attribute__((always_inline)) {
+      constexpr bool more = decltype(more_tag)::value;
+      const bool ctile = tile < n_ctiles;
+      const int j0 = tile * kBN;
+      const int s0 = s_lo + (tile - n_ctiles) * kBN;
+      const bool need = ctile ? (j0 < wave_nc) : (wvalid && s0 <= tw_last && s0 + kBN - 1 >= wave_lo);
+      const int lo = ctile ? 0 : win_lo - s0;
+      const int hi = ctile ? vis_c - j0 - 1 : tq - s0;
 
-    wait_loads<0>();  // this wave's part of tile t has landed
-    lds_barrier();    // ... and every other wave's part
-    if (need)
-      attend_tile<T, D>(R, kbuf, vbuf, p.scale_log2, [=](int key) { return key >= lo && key <= hi; });
-    wait_lgkmcnt0();
-    lds_barrier();  // every wave is done reading the tile
-    if (tile + 1 < n_tiles) {
-      issue_k(tile + 1);
-      issue_v(tile + 1);
+      wait_loads<kLoads>();  // K of this tile has landed (its V may be in flight)
+      lds_barrier();         // ... for every wave
+      PFrag P;
+      if (need) P = attend_qk<T, D>(R, kbuf, p.scale_log2, [=](int key) { return key >= lo && key <= hi; });
+      wait_lgkmcnt0();
+      lds_barrier();  // every wave is done reading the K tile
+      if constexpr (more) {
+        issue_k(tile + 1);
+        wait_loads<kLoads>();  // V of this tile has landed (the next K may be in flight)
+      } else {
+        wait_loads<0>();
+      }
+      lds_barrier();
+      if (need) attend_pv<T, D>(R, vbuf, P);
+      if constexpr (more) {
+        wait_lgkmcnt0();
+        lds_barrier();  // every wave is done reading the V tile
+        issue_v(tile + 1);
+      }
+    };
+    wait_vmcnt<0>();  // Q is in registers before any tile load is in flight
+    if (n_tiles > 0) {
+      issue_k(0);
+      issue_v(0);
+      for (int tile = 0; tile + 1 < n_tiles; ++tile) step(tile, std::true_type{});
+      step(n_tiles - 1, std::false_type{});
     }
+    finish_rows<T, D>(R, qvalid ? o + (int64_t)tq * D : nullptr,
+                      (p.lse && qvalid) ? p.lse + (int64_t)bh * Tn + tq : nullptr);
   }
-  finish_rows<T, D>(R, qvalid ? o + (int64_t)tq * D : nullptr,
-                    (p.lse && qvalid) ? p.lse + (int64_t)bh * Tn + tq : nullptr);
 }
 
 template <typename T, int D>
