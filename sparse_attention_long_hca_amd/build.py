@@ -56,10 +56,18 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
+# Per-source flags.  The indexer's scores are finite for finite inputs; without
+# NaN semantics its ReLU (max(x, 0)) is one instruction instead of a quieting
+# max followed by the max.
+SOURCE_FLAGS = {
+    "dsa_indexer.hip": ["-fno-honor-nans"],
+}
+
+
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc()] + lang + COMMON_FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + lang + COMMON_FLAGS + SOURCE_FLAGS.get(src, []) + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; that note is harmless.
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)

@@ -105,21 +105,6 @@ struct StageGeom {
   static constexpr int kLoadsPerTile = 2 * kPerWave;  // K and V
 };
 
-// Direct global -> LDS loads go through a buffer descriptor (MUBUF with the
-// LDS bit) rather than the FLAT-encoded global form: the compiler then counts
-// them on vmcnt alone, and LDS reads issued while they are in flight keep
-// exact lgkmcnt waits.  The descriptor covers [base, base + 4 GiB); callers
-// pass byte offsets below 2^32 (bounds are checked before the offsets are
-// formed).
-typedef __amdgpu_buffer_rsrc_t buffer_rsrc_t;
-__device__ __forceinline__ buffer_rsrc_t make_buffer_rsrc(const void* base) {
-  // Word 3 of a gfx9 raw buffer descriptor: 32-bit data format, no swizzle.
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0xffffffff, 0x00020000);
-}
-// Lane i's 16 bytes at byte offset voff land at lds_wave_base + 16*i.
-__device__ __forceinline__ void buffer_load_lds_16(buffer_rsrc_t rsrc, uint32_t voff, char* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 16, voff, 0, 0, 0);
-}
 
 // Tile source: uniform base pointers of the K and V rows; rowfn(r) gives the
 // row index of tile row r relative to them, or -1 for a padding row (which

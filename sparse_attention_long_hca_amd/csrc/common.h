@@ -83,6 +83,23 @@ __device__ __forceinline__ i16x4_t lds_read_tr16_b64(const char* p) {
 }
 
 // ---------------------------------------------------------------------------
+// Direct global -> LDS loads go through a buffer descriptor (MUBUF with the
+// LDS bit) rather than the FLAT-encoded global form: the compiler then counts
+// them on vmcnt alone, and LDS reads issued while they are in flight keep
+// exact lgkmcnt waits.  The descriptor covers [base, base + 4 GiB); callers
+// pass byte offsets below 2^32 (bounds are checked before the offsets are
+// formed).
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc_t;
+__device__ __forceinline__ buffer_rsrc_t make_buffer_rsrc(const void* base) {
+  // Word 3 of a gfx9 raw buffer descriptor: 32-bit data format, no swizzle.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0xffffffff, 0x00020000);
+}
+// Lane i's 16 bytes at byte offset voff land at lds_wave_base + 16*i.
+__device__ __forceinline__ void buffer_load_lds_16(buffer_rsrc_t rsrc, uint32_t voff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane pairs without LDS: v_permlane16_swap / v_permlane32_swap with
 // both operands equal leave, in every lane, the values of the lane pair
 // (l, l^16) or (l, l^32), always in the same order, so the reductions below

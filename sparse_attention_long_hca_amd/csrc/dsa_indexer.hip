@@ -16,6 +16,8 @@
 // chunk run together and find it in L2.  Prefill shapes use 4 waves (64
 // queries) per workgroup; decode shapes (T <= 16) use 1 wave per workgroup so
 // that many workgroups stream the positions in parallel.
+// The build compiles this file without NaN semantics (scores of finite inputs
+// are finite), which makes the ReLU a single max instruction.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,7 +39,7 @@ __device__ __forceinline__ uint32_t idx_off(int r, int c) {
 
 // Direct global->LDS load of positions [s0, s0+64) (rows past `stop` load row 0).
 template <int kWaves>
-__device__ __forceinline__ void idx_stage(char* buf, const bf16_t* kI, int s0, int stop) {
+__device__ __forceinline__ void idx_stage(char* buf, buffer_rsrc_t rsrc, int s0, int stop) {
   constexpr int kLoads = kIdxTileBytes / 1024 / kWaves;  // wave loads of 1 KB
   const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
@@ -48,8 +50,7 @@ __device__ __forceinline__ void idx_stage(char* buf, const bf16_t* kI, int s0, i
     const int c = cp ^ lds_swizzle(r);
     const int s = s0 + r < stop ? s0 + r : 0;
     const uint32_t off = (uint32_t)s * kIdxRowBytes + (uint32_t)c * 16u;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kI) + off, (lds_void_t*)(buf + base * 16), 16, 0,
-                                     0);
+    buffer_load_lds_16(rsrc, off, buf + base * 16);
   }
 }
 
@@ -112,54 +113,93 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
     plim[mb] = vc ? min(base + qc_i, S - 1) : -1;
   }
 
-  auto compute = [&](int tile, const char* buf) {
-    const int s0 = s_begin + tile * kIdxKTile;
-    if (s0 > wave_plim) return;  // tile entirely after the wave's last query
-    f32x4_t acc[4][4];
+  // Scores of the previous tile, held in registers and stored after the next
+  // wait: on this GPU a wait for loads also waits for every earlier store
+  // of the wave, so stores issued just before a wait would stall it.
+  float held[4][4];
+  int held_s0 = -1;  // first position of the held tile (-1: nothing held)
+  // Every position of a tile is visible to every query of the wave when the
+  // tile ends at or before the first query's limit (all 16 queries valid).
+  const int wave_full_lim = n_mb == 4 ? min(base + iw, S - 1) : -1;
+  auto store_held = [&]() __attribute__((always_inline)) {
+    if (held_s0 < 0) return;
+    if (held_s0 + kIdxKTile - 1 <= wave_full_lim) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb) {
+        float* orow = out + (int64_t)(iw + mb * 4 + g) * S + held_s0 + L;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const uint4 bu = lds_read_b128(buf, idx_off(nb * 16 + L, g + 4 * ks));
-        const i16x8_t bb = __builtin_bit_cast(i16x8_t, bu);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          if (mb < n_mb) acc[mb][nb] = mfma_bf16_16x16x32(qa[mb][ks], bb, acc[mb][nb]);
+        for (int nb = 0; nb < 4; ++nb) orow[nb * 16] = held[mb][nb];
       }
-    }
-    // Lane holds heads 0..3 of (query iw + mb*4 + g, position s0 + nb*16 + L).
+    } else {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (mb >= n_mb) continue;
-      float* orow = out + (int64_t)(iw + mb * 4 + g) * S;
+      for (int mb = 0; mb < 4; ++mb) {
+        // Rows past the sequence end have plim = -1: nothing is stored.
+        float* orow = out + (int64_t)(iw + mb * 4 + g) * S;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int s = s0 + nb * 16 + L;
-        float sc = 0.f;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) sc = fmaf(wq[mb][h], fmaxf(acc[mb][nb][h], 0.f), sc);
-        if (s <= plim[mb]) orow[s] = sc;
+        for (int nb = 0; nb < 4; ++nb) {
+          const int s = held_s0 + nb * 16 + L;
+          if (s <= plim[mb]) orow[s] = held[mb][nb];
+        }
       }
     }
   };
+  auto compute = [&](int tile, const char* buf) __attribute__((always_inline)) {
+    const int s0 = s_begin + tile * kIdxKTile;
+    if (s0 > wave_plim) {  // tile entirely after the wave's last query
+      held_s0 = -1;
+      return;
+    }
+    // All four M-blocks always run (rows past the sequence end have zero Q
+    // and are never stored), so the MFMA stream has no branches.  B operand
+    // reads are issued one step ahead of the four MFMAs that use them.
+    f32x4_t acc[4][4];
+    auto bread = [&](int i) __attribute__((always_inline)) {
+      return __builtin_bit_cast(i16x8_t, lds_read_b128(buf, idx_off((i & 3) * 16 + L, g + 4 * (i >> 2))));
+    };
+    i16x8_t bq[2];
+    bq[0] = bread(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // i = 4*ks + nb
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < 16) bq[(i + 1) & 1] = bread(i + 1);
+      const int ks = i >> 2, nb = i & 3;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        acc[mb][nb] = mfma_bf16_16x16x32(qa[mb][ks], bq[i & 1], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[mb][nb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Lane holds heads 0..3 of (query iw + mb*4 + g, position s0 + nb*16 + L).
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        float sc = 0.f;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) sc = fmaf(wq[mb][h], fmaxf(acc[mb][nb][h], 0.f), sc);
+        held[mb][nb] = sc;
+      }
+    held_s0 = s0;
+  };
 
   // Two-stage pipeline, unrolled by two so each buffer has a fixed role.
-  idx_stage<kWaves>(lds0, kI, s_begin, s_stop);
+  const buffer_rsrc_t rsrc = make_buffer_rsrc(kI);
+  idx_stage<kWaves>(lds0, rsrc, s_begin, s_stop);
   for (int tile = 0; tile < n_tiles; tile += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tile + 1 < n_tiles) idx_stage<kWaves>(lds1, kI, s_begin + (tile + 1) * kIdxKTile, s_stop);
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (tile + 1 < n_tiles) idx_stage<kWaves>(lds1, rsrc, s_begin + (tile + 1) * kIdxKTile, s_stop);
+    store_held();
     compute(tile, lds0);
     if (tile + 1 >= n_tiles) break;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tile + 2 < n_tiles) idx_stage<kWaves>(lds0, kI, s_begin + (tile + 2) * kIdxKTile, s_stop);
+    wait_lgkmcnt0();
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (tile + 2 < n_tiles) idx_stage<kWaves>(lds0, rsrc, s_begin + (tile + 2) * kIdxKTile, s_stop);
+    store_held();
     compute(tile + 1, lds1);
+    wait_lgkmcnt0();
   }
+  store_held();
 }
 
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
