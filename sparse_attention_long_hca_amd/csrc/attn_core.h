@@ -164,8 +164,11 @@ struct PFrag {
   f32x4_t s[2];  // probabilities of keys {4g..4g+3} (s[0]) and {16+4g..16+4g+3} (s[1])
 };
 
-template <typename T, int D, typename VisFn>
-__device__ __forceinline__ PFrag attend_qk(AttnRegs<T, D>& R, const char* ks, float scale_log2, VisFn&& visible) {
+// Raw scores of one key tile: S^T = K . Q^T (no mask, no softmax).
+// kValuSlots > 0 interleaves that many independent VALU instructions per MFMA
+// pair into the MFMA stream (for callers that overlap other work with it).
+template <typename T, int D, int kValuSlots = 0>
+__device__ __forceinline__ PFrag qk_raw(const AttnRegs<T, D>& R, const char* ks) {
   using G = AttnGeom<T, D>;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, L = lane & 15;
@@ -176,11 +179,12 @@ __device__ __forceinline__ PFrag attend_qk(AttnRegs<T, D>& R, const char* ks, fl
     // Row r = kb*16 + L, logical chunk g + 4*kstep.  With s = lds_swizzle(L)
     // the physical chunk is (g ^ s%4) + 4*((kstep%4) ^ s/4) + 16*(kstep/4):
     // four per-lane bases plus compile-time offsets.
+    // Bits 6..7 of rb are zero, so kbase ^ 64*(kstep%4) gives the swizzled
+    // chunk with one base register; the opaque copy keeps the compiler from
+    // hoisting the four variants out of the caller's key loop.
     const int sw = lds_swizzle(L);
-    const uint32_t rb = (uint32_t)L * G::kRowBytes + 16u * (uint32_t)(g ^ (sw & 3));
-    uint32_t kbase[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) kbase[n] = rb + 64u * (uint32_t)(n ^ (sw >> 2));
+    uint32_t kb0 = (uint32_t)L * G::kRowBytes + 16u * (uint32_t)(g ^ (sw & 3)) + 64u * (uint32_t)(sw >> 2);
+    asm volatile("" : "+v"(kb0));
     // Four independent accumulator chains (key block x kstep parity) so that
     // dependent MFMAs are never back to back; operand reads are software
     // pipelined against the MFMAs (see the schedule groups below).
@@ -190,18 +194,22 @@ __device__ __forceinline__ PFrag attend_qk(AttnRegs<T, D>& R, const char* ks, fl
     for (int kstep = 0; kstep < G::kQRegs; ++kstep) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t off = kbase[kstep & 3] + 256u * (kstep >> 2) + kb * 16 * G::kRowBytes;
+        const uint32_t off = (kb0 ^ (64u * (kstep & 3))) + 256u * (kstep >> 2) + kb * 16 * G::kRowBytes;
         const uint4 a = lds_read_b128(ks, off);
         acc[kb][kstep & 1] = mfma_bf16_16x16x32(__builtin_bit_cast(i16x8_t, a), R.q[kstep], acc[kb][kstep & 1]);
       }
     }
-    // Schedule: 6 operand reads ahead, then alternate 2 MFMAs / 2 reads.
+    // Schedule: 6 operand reads ahead, then alternate 2 MFMAs / 2 reads,
+    // with room for up to kValuSlots independent VALU instructions (the
+    // previous tile's softmax, when the caller overlaps it) after each MFMA
+    // pair.
     constexpr int kReads = 2 * G::kQRegs;
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
     for (int i = 0; i < (kReads - 6) / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if constexpr (kValuSlots > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValuSlots, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     s[0] = acc[0][0] + acc[0][1];
@@ -218,7 +226,18 @@ __device__ __forceinline__ PFrag attend_qk(AttnRegs<T, D>& R, const char* ks, fl
       }
     }
   }
+  return PFrag{{s[0], s[1]}};
+}
 
+// Mask and online-softmax update of one tile's raw scores, in place: on
+// return P holds the tile's probabilities (against R.m) and R.l, R.m and the
+// O accumulators are updated.
+template <typename T, int D, typename VisFn>
+__device__ __forceinline__ void softmax_update(AttnRegs<T, D>& R, PFrag& P, float scale_log2, VisFn&& visible) {
+  using G = AttnGeom<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  f32x4_t* s = P.s;
   // ---- mask, online softmax ------------------------------------------------
   float mx = -INFINITY;
 #pragma unroll
@@ -262,7 +281,13 @@ __device__ __forceinline__ PFrag attend_qk(AttnRegs<T, D>& R, const char* ks, fl
   }
   rs = sum_across_groups(rs);
   R.l += rs;
-  return PFrag{{s[0], s[1]}};
+}
+
+template <typename T, int D, typename VisFn>
+__device__ __forceinline__ PFrag attend_qk(AttnRegs<T, D>& R, const char* ks, float scale_log2, VisFn&& visible) {
+  PFrag P = qk_raw<T, D>(R, ks);
+  softmax_update<T, D>(R, P, scale_log2, visible);
+  return P;
 }
 
 template <typename T, int D>
@@ -282,15 +307,16 @@ __device__ __forceinline__ void attend_pv(AttnRegs<T, D>& R, const char* vs, con
     // h = (L%4)/2, byte 8*(L%2) within it.  With s = lds_swizzle(key1) the
     // physical byte offset is 256*(nb/8) + 32*((nb%8) ^ s/2) + 16*(h ^ s%2)
     // + 8*(L%2): eight per-lane bases plus compile-time offsets.
+    // Bits 5..7 of the row offset are zero: one base register, XOR-ed with
+    // 32*(nb%8) (opaque copy: recomputed here, not hoisted by the caller).
     const int key1 = 4 * g + (L >> 2);
     const int sw = lds_swizzle(key1);
-    const uint32_t vrow = (uint32_t)key1 * G::kRowBytes + 16u * (uint32_t)(((L & 3) >> 1) ^ (sw & 1)) + 8u * (L & 1);
-    uint32_t vbase[8];
-#pragma unroll
-    for (int n = 0; n < 8; ++n) vbase[n] = vrow + 32u * (uint32_t)(n ^ (sw >> 1));
+    uint32_t vb0 = (uint32_t)key1 * G::kRowBytes + 16u * (uint32_t)(((L & 3) >> 1) ^ (sw & 1)) + 8u * (L & 1) +
+                   32u * (uint32_t)(sw >> 1);
+    asm volatile("" : "+v"(vb0));
 #pragma unroll
     for (int nb = 0; nb < G::kONb; ++nb) {
-      const uint32_t off = vbase[nb & 7] + 256u * (nb >> 3);
+      const uint32_t off = (vb0 ^ (32u * (nb & 7))) + 256u * (nb >> 3);
       const i16x4_t lo = lds_read_tr16_b64(vs + off);
       const i16x4_t hi = lds_read_tr16_b64(vs + off + 16 * G::kRowBytes);
       const i16x8_t a = i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
