@@ -101,6 +101,54 @@ def test_topk_constant_rows_take_lowest():
     _topk_check(sa, sc, 2048, [3997])
 
 
+def test_topk_long_rows_few_distinct_values():
+    """32768-wide rows with four distinct scores: the k-th key has thousands of copies, so the
+    sampled bracket holds too many candidates and the full-row refinement rounds run."""
+    sa = require_gpu()
+    g = np.random.default_rng(44)
+    S = 32768
+    sc = (g.integers(0, 4, size=(1, 4, S)) * 0.25).astype(np.float32)
+    _topk_check(sa, sc, 2048, [S - 4])
+
+
+def test_topk_position_structured_scores():
+    """Scores that depend on the position modulo 4 mislead a sample of every 4th position
+    (the bracket check fails and the full-row path decides)."""
+    sa = require_gpu()
+    g = np.random.default_rng(45)
+    S = 32768
+    pos = np.arange(S)
+    sc = np.where(pos % 4 == 0, 10.0 + g.random(S), g.random(S)).astype(np.float32)[None, None, :]
+    sc = np.repeat(sc, 3, axis=1)
+    sc[0, 1] = np.where(pos % 4 == 2, -g.random(S), g.random(S) * 1e-3)  # mostly tiny values
+    _topk_check(sa, sc, 2048, [S - 3])
+
+
+def test_topk_relu_like_scores_many_zeros():
+    """ReLU-like scores with exact zeros at every 4th position (the positions the bracket samples,
+    so the full-row path decides); k = 2048 of 32768, and rows just longer than k."""
+    sa = require_gpu()
+    g = np.random.default_rng(46)
+    S = 32768
+    sc = np.maximum(g.standard_normal((1, 5, S)), 0).astype(np.float32)
+    sc[:, :, ::4] = 0.0
+    _topk_check(sa, sc, 2048, [S - 5])
+    _topk_check(sa, sc[:, :, :2050].copy(), 2048, [2045])
+
+
+def test_topk_tie_split_at_threshold():
+    """The k-th score has more copies than the selection can take: the lowest positions of
+    the tied score are taken (split ties)."""
+    sa = require_gpu()
+    g = np.random.default_rng(47)
+    S = 20000
+    sc = g.standard_normal((1, 2, S)).astype(np.float32) - 5.0
+    sc[0, :, g.choice(S, 1000, replace=False)] = 3.0        # 1000 clear winners
+    tie = g.choice(np.nonzero(sc[0, 0] < 0)[0], 3000, replace=False)
+    sc[0, :, tie] = 1.5                                       # 3000 copies straddle k = 2048
+    _topk_check(sa, sc, 2048, [S - 2])
+
+
 def test_topk_multi_workgroup_path():
     """Rows longer than the on-chip limit (S > 32768) use the multi-workgroup path."""
     sa = require_gpu()
