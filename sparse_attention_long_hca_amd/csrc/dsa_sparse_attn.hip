@@ -21,6 +21,7 @@ namespace sa {
 constexpr int kDsaMaxK = 2048;  // longest index list per query
 
 constexpr int kDsaWaves = 2;                   // 2 waves x 32 heads = 64 heads
+constexpr uint32_t kResidentPerXcd = 128;      // workgroups resident on one XCD (32 CUs x 4)
 constexpr int kDsaThreads = kDsaWaves * kWave;  // 128
 
 template <int D>
@@ -67,8 +68,22 @@ __global__ __launch_bounds__(kDsaThreads) __attribute__((amdgpu_waves_per_eu(2))
   // This workgroup's share of the index list: tiles [t_first, t_first + n_tiles).
   const int t_first = split * (int)p.tiles_per_split;
   const int n_tiles = max(0, min((kk + kBN - 1) / kBN - t_first, (int)p.tiles_per_split));
+  // Tile order.  Workgroups on one XCD start one after another, so without
+  // care the resident ones sit at every phase of their tile loops and gather
+  // from the whole key range at once.  Starting workgroup j of its XCD at
+  // tile j * n_tiles / kResidentPerXcd (and wrapping around) lines the
+  // resident workgroups up on about the same tile at the same time; since
+  // neighbouring tokens' sorted index lists cover the key range at the same
+  // rate, their gathers then share a narrow key window in L2.  (The softmax
+  // is order-independent up to rounding.)
+  int rot = 0;
+  if (p.nsplit == 1 && n_tiles > 0) rot = (int)((blockIdx.x / kNumXcd) * (uint32_t)n_tiles / kResidentPerXcd % (uint32_t)n_tiles);
+  auto tile_of = [=](int t) {
+    const int u = t + rot;
+    return u < n_tiles ? u : u - n_tiles;
+  };
   auto rows_of = [&](int t) {
-    const int32_t* trow = sidx + (t_first + t) * kBN;
+    const int32_t* trow = sidx + (t_first + tile_of(t)) * kBN;
     return [=](int r) -> int { return trow[r]; };
   };
   auto issue_k = [&](int t) { stage_rows_async<T, D, kDsaWaves, 1>(kl, kb, rows_of(t)); };
@@ -84,7 +99,7 @@ __global__ __launch_bounds__(kDsaThreads) __attribute__((amdgpu_waves_per_eu(2))
     constexpr bool more = decltype(more_tag)::value;
     wait_loads<kLoads>();  // K of tile t has landed (its V may be in flight)
     lds_barrier();         // ... for both waves
-    const uint32_t mask = (uint32_t)(__ballot(sidx[(t_first + t) * kBN + (lane & 31)] >= 0) & 0xffffffffull);
+    const uint32_t mask = (uint32_t)(__ballot(sidx[(t_first + tile_of(t)) * kBN + (lane & 31)] >= 0) & 0xffffffffull);
     f32x16_t s;
     if (mask) s = attend_qk32<D>(R, kl, ad);
     wait_lgkmcnt0();
