@@ -387,9 +387,9 @@ def cpu_baseline():
     cores = len(os.sched_getaffinity(0))
     torch.set_num_threads(cores)
     g = np.random.default_rng(7)
-    # HCA: 2 heads of the 32768 x 512 prefill.  Compression is a per-token cost
+    # HCA: 4 heads of the 32768 x 512 prefill.  Compression is a per-token cost
     # over all T tokens; attention is timed on query rows spread over T.
-    hs, rows = 2, list(np.linspace(0, T_PREFILL - 1, 4096).astype(int))
+    hs, rows = 4, list(np.linspace(0, T_PREFILL - 1, 8192).astype(int))
     sig = 1.0 / math.sqrt(D_HCA)
     q = synth.np_normal((1, hs, T_PREFILL, D_HCA), sig, "bf16", 901, 0)
     k = synth.np_normal((1, hs, T_PREFILL, D_HCA), sig, "bf16", 901, 1)
@@ -403,7 +403,7 @@ def cpu_baseline():
     hca_s_per_token = (t_comp / T_PREFILL + t_att / len(rows)) * (H / hs)
     # MLA-DSA: query rows at positions >= 2048 (indexer over the prefix, top-2048, 64-head attention).
     S = T_PREFILL
-    nq = 96
+    nq = 384
     qi = synth.np_normal((1, nq, HI, DI), DI ** -0.5, "bf16", 902, 0)
     ki = synth.np_normal((1, S, DI), DI ** -0.5, "bf16", 902, 1)
     w = synth.np_uniform((1, nq, HI), 902, 2)
