@@ -65,6 +65,16 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     const int s_lo = max(0, t0 - W + 1);
     const int n_rtiles = (t_last - s_lo + kBN) / kBN;
     const int n_tiles = n_ctiles + n_rtiles;
+    // Raw tiles are taken in a rotated order: at step `tile` this workgroup
+    // reads the band tile whose global index (s_lo / kBN + r) is congruent to
+    // `tile` modulo n_rtiles.  Co-resident tiles of one head overlap in most
+    // of their band, and the rotation makes them read the shared rows at the
+    // same step, while those rows are still in L2.
+    const int rot = n_rtiles > 0 ? ((n_ctiles - s_lo / kBN) % n_rtiles + n_rtiles) % n_rtiles : 0;
+    auto band = [&](int tile) {
+      const int r = tile - n_ctiles + rot;
+      return r >= n_rtiles ? r - n_rtiles : r;
+    };
 
     // This lane's visibility limits.
     const int vis_c = qvalid ? min(Nc, hca_visible(tq, blk, W)) : 0;
@@ -79,7 +89,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     // raw positions from s_lo onwards.  Rows past the segment end are padding.
     auto rows_of = [&](int tile) {
       const bool ct = tile < n_ctiles;
-      const int first = ct ? tile * kBN : s_lo + (tile - n_ctiles) * kBN;
+      const int first = ct ? tile * kBN : s_lo + band(tile) * kBN;
       const int last = ct ? nc - 1 : t_last;
       return [=](int r) -> int {
         const int x = first + r;
@@ -105,7 +115,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       constexpr bool more = decltype(more_tag)::value;
       const bool ctile = tile < n_ctiles;
       const int j0 = tile * kBN;
-      const int s0 = s_lo + (tile - n_ctiles) * kBN;
+      const int s0 = s_lo + band(tile) * kBN;
       const bool need = ctile ? (j0 < wave_nc) : (wvalid && s0 <= tw_last && s0 + kBN - 1 >= wave_lo);
       const int lo = ctile ? 0 : win_lo - s0;
       const int hi = ctile ? vis_c - j0 - 1 : tq - s0;
