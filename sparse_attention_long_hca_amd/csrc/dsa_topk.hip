@@ -18,6 +18,7 @@
 // keys in registers.  Longer rows: a multi-workgroup pipeline with
 // histograms and per-chunk counts in the workspace.  All counts are integers,
 // so both paths give bit-identical, run-to-run stable results.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -133,9 +134,12 @@ __device__ void select_bin(const uint32_t* hist, int nbins, uint32_t need, uint3
 }
 
 // ---------------------------------------------------------------------------
-// Rows up to kRegRow positions: one 512-thread workgroup per row holds the
-// whole row of keys in registers.  Thread t owns positions 4*(t + 512*j) + e
-// (j < 16, e < 4), read with 16-byte loads that are all in flight at once.
+// Rows up to kRegRow positions: one workgroup per row holds the whole row
+// of keys in registers.  Thread t of kThreads owns positions
+// 4*(t + kThreads*j) + e (j < 16, e < 4), read with 16-byte loads that are
+// all in flight at once.  The workgroup is sized to the row: 128, 256 or 512
+// threads for rows of up to 8192, 16384 or 32768 positions, so that short
+// (causal) rows take fewer lanes and more of them run on a CU at once.
 // The work is bound by vector ALU instructions per key, so every sweep over
 // the 64 keys of a thread is kept short:
 //
@@ -153,13 +157,10 @@ __device__ void select_bin(const uint32_t* hist, int nbins, uint32_t need, uint3
 //     fewer than need_eq copies precede s.  Packed (greater, equal) counts
 //     are scanned inside each wave with DPP, then across (group, wave).
 // ---------------------------------------------------------------------------
-constexpr int kRegThreads = 512;
-constexpr int kRegWaves = kRegThreads / kWave;
-constexpr int kRegVec = 16;                            // 4-element groups per thread
-constexpr int kRegRow = kRegThreads * kRegVec * 4;     // 32768
-constexpr int kCandLds = 2048;                         // candidates moved to LDS
-constexpr int kCandPer = kCandLds / kRegThreads;       // 4 per thread
-constexpr int kCandCap = kWave;                        // ranked pairwise by one wave
+constexpr int kRegVec = 16;                  // 4-element groups per thread
+constexpr int kRegRow = 512 * kRegVec * 4;   // 32768: longest row of the largest workgroup
+constexpr int kCandPer = 4;                  // LDS candidates per thread
+constexpr int kCandCap = kWave;              // ranked pairwise by one wave
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
 #pragma unroll
@@ -190,7 +191,13 @@ __device__ __forceinline__ uint32_t bin_shift(uint32_t range) {
   return bits > 11 ? (uint32_t)(bits - 11) : 0u;
 }
 
-__global__ __launch_bounds__(kRegThreads) __attribute__((amdgpu_waves_per_eu(4))) void dsa_topk_reg_kernel(DsaTopkParams p) {
+// Rows i0 .. i0 + ni - 1 of every batch entry, one workgroup each.
+template <int kThreads>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void dsa_topk_reg_kernel(
+    DsaTopkParams p, int64_t i0, int64_t ni) {
+  constexpr int kRegThreads = kThreads;
+  constexpr int kRegWaves = kRegThreads / kWave;
+  constexpr int kCandLds = kCandPer * kRegThreads;  // candidates moved to LDS
   __shared__ uint32_t hist[kBins];  // also the staging buffer of the output row
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t res[8];
@@ -200,8 +207,9 @@ __global__ __launch_bounds__(kRegThreads) __attribute__((amdgpu_waves_per_eu(4))
   __shared__ uint32_t cpos[kCandLds];
   __shared__ int32_t sink[kWave];
 
-  const int64_t row = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t b = row / p.T, i = row % p.T;
+  const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = lid / ni, i = i0 + lid % ni;
+  const int64_t row = b * p.T + i;
   const int n = (int)row_len(p, b, i);
   const int k = (int)p.k;
   int32_t* out = p.idx + row * p.k;
@@ -527,13 +535,14 @@ __global__ __launch_bounds__(kRegThreads) __attribute__((amdgpu_waves_per_eu(4))
     }
   }
   __syncthreads();
-  static_assert(kRegVec * kRegWaves == 2 * kWave, "one wave scans the (group, wave) totals");
+  constexpr int kTot = kRegVec * kRegWaves;  // (group, wave) totals, lane l holds 2l and 2l + 1
+  static_assert(kTot <= 2 * kWave, "one wave scans the (group, wave) totals");
   if (wave == 0) {
-    const uint32_t a = wtot[2 * lane], z = wtot[2 * lane + 1];
-    const uint32_t x = wave_incl_scan(a + z);
-    const uint32_t ex = x - a - z;
-    wtot[2 * lane] = ex;
-    wtot[2 * lane + 1] = ex + a;
+    const bool has_a = 2 * lane < kTot, has_z = 2 * lane + 1 < kTot;
+    const uint32_t a = has_a ? wtot[2 * lane] : 0u, z = has_z ? wtot[2 * lane + 1] : 0u;
+    const uint32_t ex = wave_incl_scan(a + z) - a - z;
+    if (has_a) wtot[2 * lane] = ex;
+    if (has_z) wtot[2 * lane + 1] = ex + a;
   }
   __syncthreads();
   // Selected positions are staged in LDS (reusing the histogram), then
@@ -782,7 +791,26 @@ size_t dsa_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k) {
 hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream) {
   const int64_t rows = p.B * p.T;
   if (p.S <= kRegRow) {
-    hipLaunchKernelGGL(dsa_topk_reg_kernel, dim3((uint32_t)rows), dim3(kRegThreads), 0, stream, p);
+    if (p.q_pos) {  // row lengths are on the device: one size fits all
+      hipLaunchKernelGGL(dsa_topk_reg_kernel<512>, dim3((uint32_t)rows), dim3(512), 0, stream, p, (int64_t)0, p.T);
+      return hipGetLastError();
+    }
+    // Causal rows from position 0: row i holds min(i + 1, S) positions, so
+    // the rows that fit a smaller workgroup (kThreads * 64 positions) form
+    // contiguous ranges, one launch each.
+    auto run = [&](auto threads_tag, int64_t& i0) {
+      constexpr int kThreads = decltype(threads_tag)::value;
+      const int64_t i1 = kThreads == 512 ? p.T : std::min<int64_t>(p.T, (int64_t)kThreads * kRegVec * 4);
+      if (i1 > i0) {
+        hipLaunchKernelGGL(dsa_topk_reg_kernel<kThreads>, dim3((uint32_t)(p.B * (i1 - i0))), dim3(kThreads), 0,
+                           stream, p, i0, i1 - i0);
+        i0 = i1;
+      }
+    };
+    int64_t i0 = 0;
+    run(std::integral_constant<int, 128>{}, i0);
+    run(std::integral_constant<int, 256>{}, i0);
+    run(std::integral_constant<int, 512>{}, i0);
     return hipGetLastError();
   }
   const int64_t nchunk = (p.S + kMwChunk - 1) / kMwChunk;

@@ -123,7 +123,7 @@ def test_dsa_prefill_32768_top2048(sigma):
     idx = sa.dsa_topk(sc, kk)
     o, lse = sa.dsa_sparse_attention_fwd(q, k, v, idx, return_lse=True)
     torch.cuda.synchronize()
-    rows = [0, 1, 2046, 2047, 2048, 2049, 4095, 10000, 32767]
+    rows = [0, 1, 2046, 2047, 2048, 2049, 4095, 8191, 8192, 10000, 16383, 16384, 32767]
     rows += [int(x) for x in np.random.default_rng(1501).integers(2048, T, size=6)]
     ki_h, q_h, k_h, v_h = f64(ki), None, f64(k), f64(v)
     for i in rows:

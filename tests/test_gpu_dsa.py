@@ -149,6 +149,24 @@ def test_topk_tie_split_at_threshold():
     _topk_check(sa, sc, 2048, [S - 2])
 
 
+def test_topk_causal_row_classes():
+    """Causal rows from position 0 are split by length over three workgroup sizes (rows up to
+    8192, 16384 and longer positions); rows on both sides of each cut, on normal scores and on
+    ReLU-like scores whose zeros straddle the k-th key."""
+    sa = require_gpu()
+    B, T, k = 2, 17000, 2048
+    sc = synth.torch_normal((B, T, T), 1.0, torch.float32, 48, DEV)
+    sc[1].clamp_(min=0.0)
+    idx = sa.dsa_topk(sc, k)
+    torch.cuda.synchronize()
+    rows = [0, 1, 2047, 2048, 2049, 3000, 8191, 8192, 8193, 12000, 16383, 16384, 16385, T - 1]
+    for b in range(B):
+        for i in rows:
+            row = sc[b, i, : i + 1].cpu().numpy()
+            want = oracle.dsa_topk(row.reshape(1, 1, -1), k, q_pos=[i])[0, 0]
+            assert np.array_equal(idx[b, i].cpu().numpy(), want), (b, i)
+
+
 def test_topk_multi_workgroup_path():
     """Rows longer than the on-chip limit (S > 32768) use the multi-workgroup path."""
     sa = require_gpu()
