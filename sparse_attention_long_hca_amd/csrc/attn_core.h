@@ -108,11 +108,14 @@ struct StageGeom {
 
 // Tile source: uniform base pointers of the K and V rows; rowfn(r) gives the
 // row index of tile row r relative to them, or -1 for a padding row (which
-// loads row 0 of the same tensor: finite, and masked by the caller).
-template <typename T, int D, int kWaves = kAttnWaves, int kSwz = 0, typename RowFn>
+// loads row 0 of the same tensor: finite, and masked by the caller).  The
+// tile holds D elements of each row; kSrcRowBytes is the row pitch in memory
+// when that differs from the tile's row (a tile of half rows), else 0.
+template <typename T, int D, int kWaves = kAttnWaves, int kSwz = 0, int kSrcRowBytes = 0, typename RowFn>
 __device__ __forceinline__ void stage_rows_async(char* buf, const T* base_ptr, RowFn&& rowfn) {
   using G = AttnGeom<T, D, kSwz>;
   using SG = StageGeom<T, D, kWaves>;
+  constexpr uint32_t kPitch = kSrcRowBytes > 0 ? (uint32_t)kSrcRowBytes : (uint32_t)G::kRowBytes;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   // All row lookups first: rowfn may read LDS, and such a read cannot be
   // moved past a direct-to-LDS load, so interleaving them would serialise
@@ -128,7 +131,7 @@ __device__ __forceinline__ void stage_rows_async(char* buf, const T* base_ptr, R
     const unsigned P = (unsigned)(j * kWaves + wave) * kWave + lane;
     const int r = (int)(P / G::kChunks), cp = (int)(P % G::kChunks);
     const int c = cp ^ G::swz(r);
-    off[j] = (uint32_t)(row[j] < 0 ? 0 : row[j]) * (uint32_t)G::kRowBytes + (uint32_t)c * 16u;
+    off[j] = (uint32_t)(row[j] < 0 ? 0 : row[j]) * kPitch + (uint32_t)c * 16u;
   }
   const buffer_rsrc_t rsrc = make_buffer_rsrc(base_ptr);
 #pragma unroll

@@ -110,26 +110,15 @@ __device__ __forceinline__ f32x16_t attend_qk32(const Attn32Regs<D>& R, const ch
   return s;
 }
 
-// Mask, online-softmax update and O^T += V^T . P^T for the tile whose raw
-// scores attend_qk32 returned.  Bit n of key_mask (wave-uniform) says whether
-// key n of the tile takes part.
+// Online-softmax update and O^T += V^T . P^T for one tile, given its logits
+// s (scaled, log2 units, -INFINITY for keys that take no part) and mx, this
+// lane's maximum of them.
 template <int D>
-__device__ __forceinline__ void attend_pv32(Attn32Regs<D>& R, f32x16_t s, const char* vs, float scale_log2,
-                                            uint32_t key_mask, Tile32Addr ad) {
-  const int q = (threadIdx.x & 63) >> 5;
+__device__ __forceinline__ void softmax_pv32(Attn32Regs<D>& R, f32x16_t s, float mx, const char* vs, Tile32Addr ad) {
   constexpr int kPairs = D / 32 * 2;  // (dims block, key half)
   constexpr int kAhead = 2;  // pairs of LDS reads in flight (register budget)
   asm volatile("" : "+v"(ad.v0), "+v"(ad.v1));
 
-  // Shift the mask by 4q once, then every test is against a compile-time bit.
-  const uint32_t kbits = key_mask >> (4 * q);
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float x = (kbits & (1u << (8 * (j >> 2) + (j & 3)))) ? s[j] * scale_log2 : -INFINITY;
-    s[j] = x;
-    mx = fmaxf(mx, x);
-  }
   mx = max_xor32(mx);
   // Lazy rescale as in the 16-row core: only when the running max grows by
   // more than 2^8.
@@ -180,6 +169,44 @@ __device__ __forceinline__ void attend_pv32(Attn32Regs<D>& R, f32x16_t s, const 
     if (i + kAhead < kPairs) va[i % kAhead] = vread(i + kAhead);
   }
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// Mask, online-softmax update and O^T += V^T . P^T for the tile whose raw
+// scores attend_qk32 returned.  Bit n of key_mask (wave-uniform) says whether
+// key n of the tile takes part.
+template <int D>
+__device__ __forceinline__ void attend_pv32(Attn32Regs<D>& R, f32x16_t s, const char* vs, float scale_log2,
+                                            uint32_t key_mask, Tile32Addr ad) {
+  const int q = (threadIdx.x & 63) >> 5;
+  // Shift the mask by 4q once, then every test is against a compile-time bit.
+  const uint32_t kbits = key_mask >> (4 * q);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float x = (kbits & (1u << (8 * (j >> 2) + (j & 3)))) ? s[j] * scale_log2 : -INFINITY;
+    s[j] = x;
+    mx = fmaxf(mx, x);
+  }
+  softmax_pv32<D>(R, s, mx, vs, ad);
+}
+
+// As attend_pv32, with a per-row key range instead: key n of the tile takes
+// part in row l%32 iff lo <= n <= hi (this lane's bounds).
+template <int D>
+__device__ __forceinline__ void attend_pv32_range(Attn32Regs<D>& R, f32x16_t s, const char* vs, float scale_log2,
+                                                  int lo, int hi, Tile32Addr ad) {
+  const int q = (threadIdx.x & 63) >> 5;
+  // Key of value j: 8*(j/4) + 4q + j%4; shift the bounds by 4q once.
+  const int lo_q = lo - 4 * q, hi_q = hi - 4 * q;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int kj = 8 * (j >> 2) + (j & 3);
+    const float x = (kj >= lo_q && kj <= hi_q) ? s[j] * scale_log2 : -INFINITY;
+    s[j] = x;
+    mx = fmaxf(mx, x);
+  }
+  softmax_pv32<D>(R, s, mx, vs, ad);
 }
 
 // Normalise and write row l%32 (bf16), and its lse; lane holds dims

@@ -14,7 +14,7 @@
 // cache and the overlapping raw band) and the longest tiles start first.
 #include <type_traits>
 
-#include "attn_core.h"
+#include "attn_core32.h"
 #include "kernels.h"
 
 namespace sa {
@@ -152,6 +152,165 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, d = 512: wave pairs on the 32-row core.  A workgroup of 4 waves takes
+// 64 queries; waves 2p and 2p+1 share queries [32p, 32p + 32) of the tile and
+// split the 512 dimensions: wave 2p + h holds Q and O for dims
+// [256h, 256h + 256).  Per key tile each wave computes S over its half of the
+// dims, the pair adds its two partial S through LDS (both waves then hold
+// the same full S and run the same softmax), and each wave accumulates
+// O^T += V^T . P^T for its half.  K and V tiles are stored as two half-row
+// tiles of 512-byte rows, so every LDS operand read serves 32 queries instead
+// of 16 and a wave reads half of each tile.
+// ---------------------------------------------------------------------------
+constexpr int kHalfD = 256;
+constexpr int kPairRows = 32;
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void hca_prefill32_kernel(HcaPrefillParams p) {
+  static_assert(D == 2 * kHalfD, "two halves of 256 dims");
+  using T = bf16_t;
+  using GH = AttnGeom<T, kHalfD, 1>;
+  constexpr int kHalfTile = GH::kTileBytes;  // 16 KB: 32 rows x 512 bytes
+  __shared__ __attribute__((aligned(16))) char kbuf[2 * kHalfTile];
+  __shared__ __attribute__((aligned(16))) char vbuf[2 * kHalfTile];
+  __shared__ __attribute__((aligned(16))) char xbuf[kAttnWaves * 16 * kWave * 4];  // partial S, 4 KB per wave
+
+  const int n_qtiles = (int)p.n_qtiles;
+  const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = (int)(lid / (uint32_t)n_qtiles);
+  const int qt = n_qtiles - 1 - (int)(lid % (uint32_t)n_qtiles);  // longest tiles first
+  const int Tn = (int)p.T, blk = (int)p.blk, W = (int)p.window, Nc = (int)p.Nc;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int pair = wave >> 1, half = wave & 1;
+
+  const int64_t head_off = (int64_t)bh * Tn * D;
+  const T* q = reinterpret_cast<const T*>(p.q) + head_off;
+  const T* k = reinterpret_cast<const T*>(p.k) + head_off;
+  const T* v = reinterpret_cast<const T*>(p.v) + head_off;
+  const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)bh * Nc * D;
+  const T* vc = reinterpret_cast<const T*>(p.vc) + (int64_t)bh * Nc * D;
+  T* o = reinterpret_cast<T*>(p.o) + head_off;
+
+  const int t0 = qt * kBM;
+  const int tp = t0 + pair * kPairRows;  // first query of this pair
+  const int tq = tp + (lane & 31);       // this lane's query (row l%32)
+  const bool qvalid = tq < Tn;
+
+  Attn32Regs<kHalfD> R;
+  // Rows past T load the last row (their results are never written).
+  load_q32<kHalfD>(R, q + (int64_t)min(tq, Tn - 1) * D + half * kHalfD);
+  const Tile32Addr ad = tile32_addr<kHalfD>();
+
+  // Key stream of the tile (as in the 16-row kernel).
+  const int t_last = min(t0 + kBM - 1, Tn - 1);
+  const int nc = min(Nc, hca_visible(t_last, blk, W));
+  const int n_ctiles = (nc + kBN - 1) / kBN;
+  const int s_lo = max(0, t0 - W + 1);
+  const int n_rtiles = (t_last - s_lo + kBN) / kBN;
+  const int n_tiles = n_ctiles + n_rtiles;
+  // Raw tiles in a rotated order: at step `tile` the band tile whose global
+  // index (s_lo / kBN + r) is congruent to `tile` modulo n_rtiles, so that
+  // co-resident tiles of one head read their shared rows at the same step.
+  const int rot = n_rtiles > 0 ? ((n_ctiles - s_lo / kBN) % n_rtiles + n_rtiles) % n_rtiles : 0;
+  auto band = [&](int tile) {
+    const int r = tile - n_ctiles + rot;
+    return r >= n_rtiles ? r - n_rtiles : r;
+  };
+
+  // This lane's visibility limits, and the pair's (for skipping tiles).
+  const int vis_c = qvalid ? min(Nc, hca_visible(tq, blk, W)) : 0;
+  const int win_lo = tq - W + 1;
+  const bool pvalid = tp < Tn;
+  const int tp_last = min(tp + kPairRows - 1, Tn - 1);
+  const int pair_nc = pvalid ? min(Nc, hca_visible(tp_last, blk, W)) : 0;
+  const int pair_lo = tp - W + 1;
+
+  auto rows_of = [&](int tile) {
+    const bool ct = tile < n_ctiles;
+    const int first = ct ? tile * kBN : s_lo + band(tile) * kBN;
+    const int last = ct ? nc - 1 : t_last;
+    return [=](int r) -> int {
+      const int x = first + r;
+      return x <= last ? x : -1;
+    };
+  };
+  // A K (or V) tile is two half-row tiles: dims [0, 256) at buf, [256, 512)
+  // at buf + kHalfTile.
+  auto issue = [&](char* buf, const T* src, int tile) __attribute__((always_inline)) {
+    const auto rf = rows_of(tile);
+    stage_rows_async<T, kHalfD, kAttnWaves, 1, D * 2>(buf, src, rf);
+    stage_rows_async<T, kHalfD, kAttnWaves, 1, D * 2>(buf + kHalfTile, src + kHalfD, rf);
+  };
+  auto issue_k = [&](int tile) { issue(kbuf, tile < n_ctiles ? kc : k, tile); };
+  auto issue_v = [&](int tile) { issue(vbuf, tile < n_ctiles ? vc : v, tile); };
+
+  // Partial-S exchange: value j of lane l at xbuf + wave*4096 + (j/4)*1024 + l*16.
+  float* xs_mine = reinterpret_cast<float*>(xbuf + wave * 4096 + lane * 16);
+  const float* xs_other = reinterpret_cast<const float*>(xbuf + (wave ^ 1) * 4096 + lane * 16);
+
+  constexpr int kLoads = 2 * StageGeom<T, kHalfD, kAttnWaves>::kPerWave;  // per K (or V) tile
+  const char* kh = kbuf + half * kHalfTile;
+  const char* vh = vbuf + half * kHalfTile;
+  // Same pipeline as the 16-row kernel (last tile peeled off); the partial
+  // S is written before the barrier that ends the K tile and read after it.
+  auto step = [&](int tile, auto more_tag) __attribute__((always_inline)) {
+    constexpr bool more = decltype(more_tag)::value;
+    const bool ctile = tile < n_ctiles;
+    const int j0 = tile * kBN;
+    const int s0 = s_lo + band(tile) * kBN;
+    const bool need = ctile ? (j0 < pair_nc) : (pvalid && s0 <= tp_last && s0 + kBN - 1 >= pair_lo);
+    const int lo = ctile ? 0 : win_lo - s0;
+    const int hi = ctile ? vis_c - j0 - 1 : tq - s0;
+
+    wait_loads<kLoads>();  // K of this tile has landed (its V may be in flight)
+    lds_barrier();         // ... for every wave
+    f32x16_t s;
+    if (need) {
+      s = attend_qk32<kHalfD>(R, kh, ad);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<f32x4_t*>(xs_mine + c * 256) = f32x4_t{s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3]};
+    }
+    wait_lgkmcnt0();
+    lds_barrier();  // every wave is done reading the K tile; partial S is visible
+    if constexpr (more) {
+      issue_k(tile + 1);
+      wait_loads<kLoads>();  // V of this tile has landed (the next K may be in flight)
+    } else {
+      wait_loads<0>();
+    }
+    if (need) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(xs_other + c * 256);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * c + e] += x[e];
+      }
+    }
+    lds_barrier();
+    if (need) attend_pv32_range<kHalfD>(R, s, vh, p.scale_log2, lo, hi, ad);
+    if constexpr (more) {
+      wait_lgkmcnt0();
+      lds_barrier();  // every wave is done reading the V tile (and the partner's S)
+      issue_v(tile + 1);
+    }
+  };
+  // Q is in registers before any tile load is in flight (otherwise the
+  // compiler waits for every load, tile 0's included, before the loop).
+  wait_vmcnt<0>();
+  if (n_tiles > 0) {
+    issue_k(0);
+    issue_v(0);
+    for (int tile = 0; tile + 1 < n_tiles; ++tile) step(tile, std::true_type{});
+    step(n_tiles - 1, std::false_type{});
+  }
+  if (qvalid)
+    finish_rows32<kHalfD>(R, o + (int64_t)tq * D + half * kHalfD,
+                          (p.lse && half == 0) ? p.lse + (int64_t)bh * Tn + tq : nullptr);
+}
+
 template <typename T, int D>
 static hipError_t launch(const HcaPrefillParams& p, hipStream_t stream) {
   const int64_t nblocks = p.B * p.H * p.n_qtiles;
@@ -161,7 +320,11 @@ static hipError_t launch(const HcaPrefillParams& p, hipStream_t stream) {
 
 hipError_t launch_hca_prefill(const HcaPrefillParams& p, int dtype, int d, hipStream_t stream) {
   if (dtype == 0 && d == 64) return launch<float, 64>(p, stream);
-  if (dtype == 1 && d == 512) return launch<bf16_t, 512>(p, stream);
+  if (dtype == 1 && d == 512) {
+    const int64_t nblocks = p.B * p.H * p.n_qtiles;
+    hipLaunchKernelGGL(hca_prefill32_kernel<512>, dim3((uint32_t)nblocks), dim3(kAttnThreads), 0, stream, p);
+    return hipGetLastError();
+  }
   return hipErrorInvalidValue;
 }
 
