@@ -165,16 +165,18 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
 // ---------------------------------------------------------------------------
 constexpr int kHalfD = 256;
 constexpr int kPairRows = 32;
+constexpr int kH32Waves = 4;  // 2 wave pairs: 64 queries per workgroup
 
-template <int D>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void hca_prefill32_kernel(HcaPrefillParams p) {
+template <int D, int kWaves>
+__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void hca_prefill32_kernel(HcaPrefillParams p) {
   static_assert(D == 2 * kHalfD, "two halves of 256 dims");
+  constexpr int kRows = kWaves / 2 * kPairRows;  // queries per workgroup
   using T = bf16_t;
   using GH = AttnGeom<T, kHalfD, 1>;
   constexpr int kHalfTile = GH::kTileBytes;  // 16 KB: 32 rows x 512 bytes
   __shared__ __attribute__((aligned(16))) char kbuf[2 * kHalfTile];
   __shared__ __attribute__((aligned(16))) char vbuf[2 * kHalfTile];
-  __shared__ __attribute__((aligned(16))) char xbuf[kAttnWaves * 16 * kWave * 4];  // partial S, 4 KB per wave
+  __shared__ __attribute__((aligned(16))) char xbuf[kWaves * 16 * kWave * 4];  // partial S, 4 KB per wave
 
   const int n_qtiles = (int)p.n_qtiles;
   const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const T* vc = reinterpret_cast<const T*>(p.vc) + (int64_t)bh * Nc * D;
   T* o = reinterpret_cast<T*>(p.o) + head_off;
 
-  const int t0 = qt * kBM;
+  const int t0 = qt * kRows;
   const int tp = t0 + pair * kPairRows;  // first query of this pair
   const int tq = tp + (lane & 31);       // this lane's query (row l%32)
   const bool qvalid = tq < Tn;
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const Tile32Addr ad = tile32_addr<kHalfD>();
 
   // Key stream of the tile (as in the 16-row kernel).
-  const int t_last = min(t0 + kBM - 1, Tn - 1);
+  const int t_last = min(t0 + kRows - 1, Tn - 1);
   const int nc = min(Nc, hca_visible(t_last, blk, W));
   const int n_ctiles = (nc + kBN - 1) / kBN;
   const int s_lo = max(0, t0 - W + 1);
@@ -240,8 +242,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   // at buf + kHalfTile.
   auto issue = [&](char* buf, const T* src, int tile) __attribute__((always_inline)) {
     const auto rf = rows_of(tile);
-    stage_rows_async<T, kHalfD, kAttnWaves, 1, D * 2>(buf, src, rf);
-    stage_rows_async<T, kHalfD, kAttnWaves, 1, D * 2>(buf + kHalfTile, src + kHalfD, rf);
+    stage_rows_async<T, kHalfD, kWaves, 1, D * 2>(buf, src, rf);
+    stage_rows_async<T, kHalfD, kWaves, 1, D * 2>(buf + kHalfTile, src + kHalfD, rf);
   };
   auto issue_k = [&](int tile) { issue(kbuf, tile < n_ctiles ? kc : k, tile); };
   auto issue_v = [&](int tile) { issue(vbuf, tile < n_ctiles ? vc : v, tile); };
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   float* xs_mine = reinterpret_cast<float*>(xbuf + wave * 4096 + lane * 16);
   const float* xs_other = reinterpret_cast<const float*>(xbuf + (wave ^ 1) * 4096 + lane * 16);
 
-  constexpr int kLoads = 2 * StageGeom<T, kHalfD, kAttnWaves>::kPerWave;  // per K (or V) tile
+  constexpr int kLoads = 2 * StageGeom<T, kHalfD, kWaves>::kPerWave;  // per K (or V) tile
   const char* kh = kbuf + half * kHalfTile;
   const char* vh = vbuf + half * kHalfTile;
   // Same pipeline as the 16-row kernel (last tile peeled off); the partial
@@ -321,8 +323,11 @@ static hipError_t launch(const HcaPrefillParams& p, hipStream_t stream) {
 hipError_t launch_hca_prefill(const HcaPrefillParams& p, int dtype, int d, hipStream_t stream) {
   if (dtype == 0 && d == 64) return launch<float, 64>(p, stream);
   if (dtype == 1 && d == 512) {
-    const int64_t nblocks = p.B * p.H * p.n_qtiles;
-    hipLaunchKernelGGL(hca_prefill32_kernel<512>, dim3((uint32_t)nblocks), dim3(kAttnThreads), 0, stream, p);
+    constexpr int kWaves = kH32Waves;
+    HcaPrefillParams p32 = p;
+    p32.n_qtiles = (p.T + kWaves / 2 * kPairRows - 1) / (kWaves / 2 * kPairRows);
+    const int64_t nblocks = p.B * p.H * p32.n_qtiles;
+    hipLaunchKernelGGL((hca_prefill32_kernel<512, kWaves>), dim3((uint32_t)nblocks), dim3(kWaves * kWave), 0, stream, p32);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;
