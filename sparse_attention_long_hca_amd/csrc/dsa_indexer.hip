@@ -61,11 +61,16 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   constexpr int kQTile = kWaves * kIdxQPerWave;
 
   // Chunk-major order: consecutive workgroups (same XCD) share a k_idx chunk.
+  // The chunks are taken in folded order 0, n-1, 1, n-2, ...: under the
+  // causal limit chunk c has work for the queries past 1024*c only, so a
+  // heavy chunk is followed by a light one and every XCD's contiguous range
+  // of workgroups gets about the same amount of work.
   const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_b = n_qtiles * n_chunks;
   const int b = (int)(lid / (uint32_t)per_b);
   const int rem = (int)(lid % (uint32_t)per_b);
-  const int kc = rem / n_qtiles;
+  const int kf = rem / n_qtiles;
+  const int kc = (kf & 1) ? n_chunks - 1 - (kf >> 1) : (kf >> 1);
   const int qt = n_qtiles - 1 - rem % n_qtiles;
 
   const int T = (int)p.T, S = (int)p.S;
