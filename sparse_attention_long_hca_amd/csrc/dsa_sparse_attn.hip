@@ -36,7 +36,10 @@ __global__ __launch_bounds__(kDsaThreads) __attribute__((amdgpu_waves_per_eu(2))
   __shared__ __attribute__((aligned(16))) char vl[G::kTileBytes];
   __shared__ int32_t sidx[kDsaMaxK];
 
-  const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
+  // Tokens are dealt round-robin over the XCDs (the hardware's own order):
+  // early tokens see fewer than k positions, and a contiguous range per XCD
+  // would leave the XCD holding them idle at the end.
+  const int64_t lid = blockIdx.x;
   const int64_t tok = lid / p.nsplit;  // b*T + i
   const int split = (int)(lid % p.nsplit);
   const int64_t b = tok / p.T;
