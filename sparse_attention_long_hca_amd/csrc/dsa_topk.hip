@@ -207,7 +207,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __shared__ uint32_t cpos[kCandLds];
   __shared__ int32_t sink[kWave];
 
-  const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
+  // Rows are dealt round-robin over the XCDs (the hardware's own order):
+  // causal rows grow with i, and a contiguous range per XCD would give the
+  // last XCD the longest loads.
+  const int64_t lid = blockIdx.x;
   const int64_t b = lid / ni, i = i0 + lid % ni;
   const int64_t row = b * p.T + i;
   const int n = (int)row_len(p, b, i);
