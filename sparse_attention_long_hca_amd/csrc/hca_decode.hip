@@ -7,12 +7,16 @@
 //
 // The step is bound by HBM: every visible K and V row is read once.  A
 // workgroup (4 waves) handles one (batch, head, key split).  Each wave walks
-// its keys 8 at a time, 8 lanes per key: lane (slot, part) reads 16-byte
-// chunks part, part+8, ... of its key's K and V rows, so one load instruction
-// covers 8 rows x 128 contiguous bytes.  Dot products are fp32; the
-// 8-lane reduction uses cross-lane shuffles; softmax is online per wave.
-// With more than one split per (batch, head) the partial (o, lse) go to the
-// workspace and a second kernel combines them in split order.
+// its keys 4 at a time, 16 lanes per key: lane (slot, part) reads 16-byte
+// chunks part, part+16, ... of its key's K and V rows, so one load
+// instruction covers 4 rows x 256 contiguous bytes.  The rows of the next
+// group of keys are loaded while the current group is used, so every wave
+// keeps two groups (16 KB) in flight.  Dot products use the bf16 dot2
+// instruction with fp32 accumulation; the 16-lane reduction uses cross-lane
+// shuffles; softmax is online per wave with the running max raised only when
+// it grows by more than 2^8.  With more than one split per (batch, head) the
+// partial (o, lse) go to the workspace and a second kernel combines them in
+// split order.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,10 +30,16 @@ __device__ __forceinline__ int64_t hca_visible_dec(int64_t t, int64_t blk, int64
   return x > 0 ? x / blk : 0;
 }
 
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 template <int D>
 __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams p) {
+  constexpr int kLanes = 16;               // lanes per key
+  constexpr int kSlots = kWave / kLanes;   // keys per wave step
   constexpr int kChunks = D / 8;           // 16-byte chunks per bf16 row
-  constexpr int kPer = kChunks / 8;        // chunks per lane (8 lanes per key)
+  constexpr int kPer = kChunks / kLanes;   // chunks per lane
   __shared__ float sh_o[kDecWaves][D];
   __shared__ float sh_m[kDecWaves], sh_l[kDecWaves];
 
@@ -38,7 +48,7 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
   const int64_t bh = lid / p.nsplit;
   const int64_t b = bh / p.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int slot = lane >> 3, part = lane & 7;
+  const int slot = lane / kLanes, part = lane % kLanes;
 
   int64_t t = p.pos[b];
   if (t < 0) t = 0;
@@ -55,104 +65,113 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
   const bf16_t* rv = reinterpret_cast<const bf16_t*>(p.rv) + bh * p.window * D;
   const int64_t win_first = t - nw + 1;  // first window position
 
-  // Query chunks part, part+8, ... pre-scaled to log2 units.
-  float qf[kPer * 8];
+  // Query chunks part, part+16, ... as bf16 pairs.
+  uint4 qc[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const uint4 u = *reinterpret_cast<const uint4*>(q + (part + 8 * i) * 8);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qf[i * 8 + 2 * e] = bf16_to_f32(w[e] & 0xffffu) * p.scale_log2;
-      qf[i * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u) * p.scale_log2;
-    }
-  }
+  for (int i = 0; i < kPer; ++i) qc[i] = *reinterpret_cast<const uint4*>(q + (part + kLanes * i) * 8);
 
   float acc[kPer * 8];
 #pragma unroll
   for (int i = 0; i < kPer * 8; ++i) acc[i] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  // Keys of this split handled by this wave: groups of 8 consecutive keys,
-  // interleaved over the 4 waves.
-  for (int64_t g0 = u_begin + (int64_t)wave * 8; g0 < u_end; g0 += kDecWaves * 8) {
+  // One group: keys g0 + slot (a group of kSlots consecutive keys).
+  struct Rows {
+    uint4 k[kPer], v[kPer];
+  };
+  auto load = [&](int64_t g0, Rows& r) __attribute__((always_inline)) {
     const int64_t u = g0 + slot;
-    const bool valid = u < u_end;
-    const bf16_t* krow = nullptr;
-    const bf16_t* vrow = nullptr;
-    if (valid) {
+    if (u < u_end) {
+      const bf16_t* krow;
+      const bf16_t* vrow;
       if (u < nc) {
         krow = kc + u * D;
         vrow = vc + u * D;
       } else {
-        const int64_t s = win_first + (u - nc);
-        const int64_t sl = s % p.window;
+        const int64_t sl = (win_first + (u - nc)) % p.window;
         krow = rk + sl * D;
         vrow = rv + sl * D;
       }
-    }
-    uint4 kr[kPer], vr[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (valid) {
-        kr[i] = *reinterpret_cast<const uint4*>(krow + (part + 8 * i) * 8);
-        vr[i] = *reinterpret_cast<const uint4*>(vrow + (part + 8 * i) * 8);
-      } else {
-        kr[i] = make_uint4(0u, 0u, 0u, 0u);
-        vr[i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < kPer; ++i) {
+        r.k[i] = *reinterpret_cast<const uint4*>(krow + (part + kLanes * i) * 8);
+        r.v[i] = *reinterpret_cast<const uint4*>(vrow + (part + kLanes * i) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        r.k[i] = make_uint4(0u, 0u, 0u, 0u);
+        r.v[i] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
+  };
+  constexpr float kRescaleLog2 = 8.f;
+  auto use = [&](int64_t g0, const Rows& r) __attribute__((always_inline)) {
+    const bool valid = g0 + slot < u_end;
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dot = fmaf(qf[i * 8 + 2 * e], bf16_to_f32(w[e] & 0xffffu), dot);
-        dot = fmaf(qf[i * 8 + 2 * e + 1], __uint_as_float(w[e] & 0xffff0000u), dot);
-      }
+      dot = dot2_bf16(qc[i].x, r.k[i].x, dot);
+      dot = dot2_bf16(qc[i].y, r.k[i].y, dot);
+      dot = dot2_bf16(qc[i].z, r.k[i].z, dot);
+      dot = dot2_bf16(qc[i].w, r.k[i].w, dot);
     }
-    dot += __shfl_xor(dot, 1);
-    dot += __shfl_xor(dot, 2);
-    dot += __shfl_xor(dot, 4);
-    const float x = valid ? dot : -INFINITY;
-    float gm = fmaxf(x, __shfl_xor(x, 8));
-    gm = fmaxf(gm, __shfl_xor(gm, 16));
-    gm = fmaxf(gm, __shfl_xor(gm, 32));
-    const float m_new = fmaxf(m, gm);  // finite: group has >= 1 valid key
-    const float alpha = fast_exp2(m - m_new);
-    const float pr = fast_exp2(x - m_new);
+#pragma unroll
+    for (int off = 1; off < kLanes; off <<= 1) dot += __shfl_xor(dot, off);
+    const float x = valid ? dot * p.scale_log2 : -INFINITY;
+    float gm = x;
+#pragma unroll
+    for (int off = kLanes; off < kWave; off <<= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+    // gm is finite: the group has at least one valid key.
+    if (gm > m + kRescaleLog2) {  // wave-uniform
+      const float alpha = fast_exp2(m - gm);
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < kPer * 8; ++i) acc[i] *= alpha;
+      m = gm;
+    }
+    const float pr = fast_exp2(x - m);
     float ps = pr;
-    ps += __shfl_xor(ps, 8);
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l = l * alpha + ps;
-    m = m_new;
+#pragma unroll
+    for (int off = kLanes; off < kWave; off <<= 1) ps += __shfl_xor(ps, off);
+    l += ps;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+      const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[i * 8 + 2 * e] = fmaf(pr, bf16_to_f32(w[e] & 0xffffu), acc[i * 8 + 2 * e] * alpha);
-        acc[i * 8 + 2 * e + 1] = fmaf(pr, __uint_as_float(w[e] & 0xffff0000u), acc[i * 8 + 2 * e + 1] * alpha);
+        acc[i * 8 + 2 * e] = fmaf(pr, bf16_to_f32(w[e] & 0xffffu), acc[i * 8 + 2 * e]);
+        acc[i * 8 + 2 * e + 1] = fmaf(pr, __uint_as_float(w[e] & 0xffff0000u), acc[i * 8 + 2 * e + 1]);
       }
     }
+  };
+
+  // Groups of this wave: g0 = u_begin + kSlots*wave + stride*n, two in flight.
+  constexpr int64_t kStride = kDecWaves * kSlots;
+  Rows ra, rb;
+  int64_t g = u_begin + (int64_t)wave * kSlots;
+  if (g < u_end) load(g, ra);
+  for (; g < u_end; g += 2 * kStride) {
+    load(g + kStride, rb);
+    use(g, ra);
+    if (g + kStride >= u_end) break;
+    load(g + 2 * kStride, ra);
+    use(g + kStride, rb);
   }
 
-  // Sum the 8 key slots of the wave (lanes with equal part).
+  // Sum the key slots of the wave (lanes with equal part).
 #pragma unroll
   for (int i = 0; i < kPer * 8; ++i) {
     float a = acc[i];
-    a += __shfl_xor(a, 8);
-    a += __shfl_xor(a, 16);
-    a += __shfl_xor(a, 32);
+#pragma unroll
+    for (int off = kLanes; off < kWave; off <<= 1) a += __shfl_xor(a, off);
     acc[i] = a;
   }
   if (slot == 0) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sh_o[wave][(part + 8 * i) * 8 + e] = acc[i * 8 + e];
+      for (int e = 0; e < 8; ++e) sh_o[wave][(part + kLanes * i) * 8 + e] = acc[i * 8 + e];
   }
   if (lane == 0) {
     sh_m[wave] = m;
