@@ -138,35 +138,61 @@ __global__ __launch_bounds__(kDsaThreads) __attribute__((amdgpu_waves_per_eu(2))
 }
 
 // Merge the splits of one (token, head) in split order: weights
-// exp2(lse_s - max).  One workgroup per (token, head), one thread per dim.
+// exp2(lse_s - max).  One workgroup per (token, head), one thread per dim;
+// the split weights are computed once into LDS, then every thread sums its
+// dim over the splits with independent loads.
 template <int D>
 __global__ __launch_bounds__(D) void dsa_sparse_combine_kernel(DsaSparseParams p) {
   constexpr int kHq = 64;
+  constexpr int kMaxSplit = kDsaMaxK / kBN;  // one tile per split at most
+  __shared__ float wgt[kMaxSplit];
+  __shared__ float stat[2];
   const int64_t th = blockIdx.x;  // tok * kHq + h
   const int64_t tok = th / kHq;
   const int h = (int)(th % kHq);
   const int ns = (int)p.nsplit;
   const float* pl = p.part_lse + tok * ns * kHq + h;  // stride kHq per split
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pl[s * kHq]);
+  if (threadIdx.x < kWave) {
+    // Wave 0: max and weights (fixed order of the splits in the sum below).
+    float M = -INFINITY;
+    for (int s = threadIdx.x; s < ns; s += kWave) M = fmaxf(M, pl[s * kHq]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    for (int s = threadIdx.x; s < ns; s += kWave) wgt[s] = (M == -INFINITY) ? 0.f : fast_exp2(pl[s * kHq] - M);
+    if (threadIdx.x == 0) stat[0] = M;
+  }
+  __syncthreads();
   float wsum = 0.f, acc = 0.f;
   const float* po = p.part_o + (tok * ns * kHq + h) * D + threadIdx.x;  // stride kHq*D per split
-  for (int s = 0; s < ns; ++s) {
-    const float w = (M == -INFINITY) ? 0.f : fast_exp2(pl[s * kHq] - M);
-    wsum += w;
-    acc = fmaf(w, po[(int64_t)s * kHq * D], acc);
+  constexpr int kU = 8;
+  int s = 0;
+  for (; s + kU <= ns; s += kU) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = po[(int64_t)(s + u) * kHq * D];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      wsum += wgt[s + u];
+      acc = fmaf(wgt[s + u], v[u], acc);
+    }
+  }
+  for (; s < ns; ++s) {
+    wsum += wgt[s];
+    acc = fmaf(wgt[s], po[(int64_t)s * kHq * D], acc);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   reinterpret_cast<bf16_t*>(p.o)[th * D + threadIdx.x] = (bf16_t)f32_to_bf16_rne(acc * inv);
-  if (p.lse && threadIdx.x == 0) p.lse[th] = wsum > 0.f ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
+  if (p.lse && threadIdx.x == 0) p.lse[th] = wsum > 0.f ? (stat[0] + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 // Decode-sized calls (few tokens) split each token's index list over several
-// workgroups so that the whole chip streams the gathered rows.
+// workgroups so that more CUs gather rows at once.  About 128 workgroups in
+// all: more splits cost more in partial results (64 KB per split and token)
+// than they gain in parallel gathers.
 int64_t dsa_sparse_nsplit(int64_t BT, int64_t kk) {
   const int64_t tiles = (kk + kBN - 1) / kBN;
   if (BT >= 512) return 1;
-  int64_t ns = (1024 + BT - 1) / BT;
+  int64_t ns = (128 + BT - 1) / BT;
   if (ns > tiles) ns = tiles;
   return ns < 1 ? 1 : ns;
 }
