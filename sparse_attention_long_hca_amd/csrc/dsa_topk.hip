@@ -26,13 +26,12 @@
 
 namespace sa {
 
-constexpr int kTopkThreads = 1024;
 constexpr int kBins = 2048;
 // Digit layout of the 32-bit key: bits 31..21, 20..10, 9..0.
 __device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __device__ __forceinline__ uint32_t digit_mask(int pass) { return pass == 2 ? 0x3ffu : 0x7ffu; }
 constexpr int kMwThreads = 256;
-constexpr int kMwChunk = 16384;  // positions per workgroup in the multi-workgroup path
+constexpr int kMwChunk = 4096;   // positions per workgroup in the multi-workgroup path
 
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -598,10 +597,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // ---------------------------------------------------------------------------
-// Long rows: multi-workgroup pipeline.
-// Workspace layout (uint32): hist[rows][kBins] | state[rows][4] | cnt[rows][nchunk][2]
+// Long rows: multi-workgroup pipeline over chunks of kMwChunk positions.
+// Three digit passes (11 + 11 + 10 bits): every chunk histograms the digit of
+// its keys that match the prefix chosen so far and adds its histogram to one
+// of the row's sub-histograms; one workgroup per row then picks the bin where
+// the count from the top reaches `need` and extends the prefix.  After the
+// third pass the prefix is the k-th key K; each chunk then counts its keys
+// > K and == K, and an ordered write places every kept position at its slot.
+// Workspace (uint32): hist[rows][kMwSub][kBins] | state[rows][4] | cnt[rows][nchunk][2]
 // state: 0 = prefix, 1 = need, 2 = above_total, 3 = unused
 // ---------------------------------------------------------------------------
+constexpr int kMwPer = kMwChunk / kMwThreads;  // positions per thread
+constexpr int kMwSub = 8;                       // sub-histograms per row
+
 struct MwLayout {
   uint32_t* hist;
   uint32_t* state;
@@ -613,16 +621,42 @@ __device__ __forceinline__ MwLayout mw_layout(const DsaTopkParams& p) {
   const int64_t rows = p.B * p.T;
   MwLayout m;
   m.hist = reinterpret_cast<uint32_t*>(p.ws);
-  m.state = m.hist + rows * kBins;
+  m.state = m.hist + rows * kMwSub * kBins;
   m.cnt = m.state + rows * 4;
   m.nchunk = (p.S + kMwChunk - 1) / kMwChunk;
   return m;
 }
 
+// Keys of this thread's positions of a chunk: wave w, lane l holds positions
+// s_beg + 1024*w + 64*i + l (i < kMwPer), so that a wave's positions are
+// contiguous and in order.  Every load is issued (positions past s_fin read
+// the chunk's first position); valid(i) says whether position i exists.
+struct MwKeys {
+  uint32_t key[kMwPer];
+};
+__device__ __forceinline__ MwKeys mw_load(const float* sc, int64_t s_beg, int64_t s_fin) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = s_beg + (int64_t)wave * (kWave * kMwPer) + lane;
+  float f[kMwPer];
+#pragma unroll
+  for (int i = 0; i < kMwPer; ++i) {
+    const int64_t s = base + kWave * i;
+    f[i] = sc[s < s_fin ? s : s_beg];
+  }
+  MwKeys k;
+#pragma unroll
+  for (int i = 0; i < kMwPer; ++i) k.key[i] = score_key(f[i]);
+  return k;
+}
+__device__ __forceinline__ bool mw_valid(int64_t s_beg, int64_t s_fin, int i) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return s_beg + (int64_t)wave * (kWave * kMwPer) + kWave * i + lane < s_fin;
+}
+
 __global__ __launch_bounds__(kMwThreads) void topk_mw_init(DsaTopkParams p) {
   const MwLayout m = mw_layout(p);
   const int64_t row = blockIdx.x;
-  for (int j = threadIdx.x; j < kBins; j += kMwThreads) m.hist[row * kBins + j] = 0;
+  for (int j = threadIdx.x; j < kMwSub * kBins; j += kMwThreads) m.hist[row * kMwSub * kBins + j] = 0;
   if (threadIdx.x == 0) {
     m.state[row * 4 + 0] = 0;
     m.state[row * 4 + 1] = (uint32_t)p.k;
@@ -640,26 +674,32 @@ __global__ __launch_bounds__(kMwThreads) void topk_mw_hist(DsaTopkParams p, int 
   if (n <= p.k) return;
   const int64_t s_beg = chunk * kMwChunk, s_fin = imin64(n, s_beg + kMwChunk);
   if (s_beg >= s_fin) return;
+  const MwKeys k = mw_load(p.scores + row * p.S, s_beg, s_fin);
   for (int j = threadIdx.x; j < kBins; j += kMwThreads) lh[j] = 0;
   __syncthreads();
   const uint32_t prefix = m.state[row * 4 + 0];
-  const float* sc = p.scores + row * p.S;
   const int sh = digit_shift(pass);
   const uint32_t dm = digit_mask(pass);
   const int sh_prev = pass > 0 ? digit_shift(pass - 1) : 32;
-  for (int64_t s = s_beg + threadIdx.x; s < s_fin; s += kMwThreads) {
-    const uint32_t key = score_key(sc[s]);
+#pragma unroll
+  for (int e = 0; e < kMwPer; ++e) {
+    const uint32_t key = k.key[e];
     const bool match = pass == 0 || (key >> sh_prev) == prefix;
-    if (match) atomicAdd(&lh[(key >> sh) & dm], 1u);
+    if (mw_valid(s_beg, s_fin, e) && match) atomicAdd(&lh[(key >> sh) & dm], 1u);
   }
   __syncthreads();
+  // Chunks add their histograms into sub-histogram chunk % kMwSub, which
+  // spreads the atomics on the few busy bins over kMwSub addresses.
+  uint32_t* gh = m.hist + (row * kMwSub + chunk % kMwSub) * kBins;
   for (int j = threadIdx.x; j <= (int)dm; j += kMwThreads) {
     const uint32_t c = lh[j];
-    if (c) atomicAdd(&m.hist[row * kBins + j], c);
+    if (c) atomicAdd(&gh[j], c);
   }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_mw_select(DsaTopkParams p, int pass) {
+// One workgroup per row: sum the sub-histograms (and clear them for the next
+// pass), pick the bin where the count from the top reaches `need`.
+__global__ __launch_bounds__(kMwThreads) void topk_mw_select(DsaTopkParams p, int pass) {
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t res[2];
@@ -669,9 +709,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_mw_select(DsaTopkParams p, 
   const int64_t n = row_len(p, b, i);
   if (n <= p.k) return;
   const int nb = (int)digit_mask(pass) + 1;
-  for (int j = threadIdx.x; j < kBins; j += kTopkThreads) {
-    h[j] = m.hist[row * kBins + j];
-    m.hist[row * kBins + j] = 0;  // ready for the next pass
+  for (int j = threadIdx.x; j < kBins; j += kMwThreads) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < kMwSub; ++u) {
+      uint32_t* gh = m.hist + (row * kMwSub + u) * kBins + j;
+      c += *gh;
+      *gh = 0;  // ready for the next pass
+    }
+    h[j] = j < nb ? c : 0u;
   }
   __syncthreads();
   const uint32_t need = m.state[row * 4 + 1];
@@ -685,6 +731,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_mw_select(DsaTopkParams p, 
   }
 }
 
+// Per chunk: keys > K and keys == K.
 __global__ __launch_bounds__(kMwThreads) void topk_mw_count(DsaTopkParams p) {
   __shared__ uint32_t part[2][kMwThreads / kWave];
   const MwLayout m = mw_layout(p);
@@ -693,13 +740,16 @@ __global__ __launch_bounds__(kMwThreads) void topk_mw_count(DsaTopkParams p) {
   const int64_t n = row_len(p, b, i);
   if (n <= p.k) return;
   const int64_t s_beg = chunk * kMwChunk, s_fin = imin64(n, s_beg + kMwChunk);
-  const uint32_t K = m.state[row * 4 + 0];
-  const float* sc = p.scores + row * p.S;
   uint32_t gt = 0, eq = 0;
-  for (int64_t s = s_beg + threadIdx.x; s < s_fin; s += kMwThreads) {
-    const uint32_t key = score_key(sc[s]);
-    gt += key > K;
-    eq += key == K;
+  if (s_beg < s_fin) {
+    const uint32_t K = m.state[row * 4 + 0];
+    const MwKeys k = mw_load(p.scores + row * p.S, s_beg, s_fin);
+#pragma unroll
+    for (int e = 0; e < kMwPer; ++e) {
+      const bool v = mw_valid(s_beg, s_fin, e);
+      gt += (v && k.key[e] > K) ? 1u : 0u;
+      eq += (v && k.key[e] == K) ? 1u : 0u;
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -723,8 +773,12 @@ __global__ __launch_bounds__(kMwThreads) void topk_mw_count(DsaTopkParams p) {
   }
 }
 
+// Ordered write: position s is kept iff key > K, or key == K and fewer than
+// `need` copies of K precede it; its slot is #(key > K before s) +
+// #(key == K before s).
 __global__ __launch_bounds__(kMwThreads) void topk_mw_write(DsaTopkParams p) {
   __shared__ uint32_t wcnt[2][kMwThreads / kWave];
+  __shared__ uint32_t before[2][kMwThreads / kWave];
   const MwLayout m = mw_layout(p);
   const int64_t row = blockIdx.x / m.nchunk, chunk = blockIdx.x % m.nchunk;
   const int64_t b = row / p.T, i = row % p.T;
@@ -739,45 +793,56 @@ __global__ __launch_bounds__(kMwThreads) void topk_mw_write(DsaTopkParams p) {
   if (s_beg >= s_fin) return;
   const uint32_t K = m.state[row * 4 + 0];
   const uint32_t need = m.state[row * 4 + 1];
-  uint32_t gt_before = 0, eq_before = 0;
-  for (int64_t c = 0; c < chunk; ++c) {
-    gt_before += m.cnt[(row * m.nchunk + c) * 2 + 0];
-    eq_before += m.cnt[(row * m.nchunk + c) * 2 + 1];
-  }
-  // Wave w of this chunk owns positions [s_beg + w*seg, ...).
+  const MwKeys k = mw_load(p.scores + row * p.S, s_beg, s_fin);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kW = kMwThreads / kWave;
-  const int64_t seg = kMwChunk / kW;
-  const int64_t w_beg = s_beg + wave * seg, w_fin = imin64(s_fin, w_beg + seg);
-  const float* sc = p.scores + row * p.S;
+  // Counts of the earlier chunks, summed by all threads.
+  uint32_t gb = 0, eb = 0;
+  for (int64_t c = threadIdx.x; c < chunk; c += kMwThreads) {
+    gb += m.cnt[(row * m.nchunk + c) * 2 + 0];
+    eb += m.cnt[(row * m.nchunk + c) * 2 + 1];
+  }
   uint32_t g = 0, e = 0;
-  for (int64_t s0 = w_beg; s0 < w_fin; s0 += 64) {
-    const int64_t s = s0 + lane;
-    const bool in = s < w_fin;
-    const uint32_t key = in ? score_key(sc[s]) : 0u;
-    g += __popcll(__ballot(in && key > K));
-    e += __popcll(__ballot(in && key == K));
+#pragma unroll
+  for (int j = 0; j < kMwPer; ++j) {
+    const bool v = mw_valid(s_beg, s_fin, j);
+    g += (v && k.key[j] > K) ? 1u : 0u;
+    e += (v && k.key[j] == K) ? 1u : 0u;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    gb += __shfl_xor(gb, off);
+    eb += __shfl_xor(eb, off);
+    g += __shfl_xor(g, off);
+    e += __shfl_xor(e, off);
   }
   if (lane == 0) {
+    before[0][wave] = gb;
+    before[1][wave] = eb;
     wcnt[0][wave] = g;
     wcnt[1][wave] = e;
   }
   __syncthreads();
-  for (int w = 0; w < wave; ++w) {
-    gt_before += wcnt[0][w];
-    eq_before += wcnt[1][w];
+  uint32_t gt_before = 0, eq_before = 0;
+  for (int w = 0; w < kMwThreads / kWave; ++w) {
+    gt_before += before[0][w];
+    eq_before += before[1][w];
+    if (w < wave) {
+      gt_before += wcnt[0][w];
+      eq_before += wcnt[1][w];
+    }
   }
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t s0 = w_beg; s0 < w_fin; s0 += 64) {
-    const int64_t s = s0 + lane;
-    const bool in = s < w_fin;
-    const uint32_t key = in ? score_key(sc[s]) : 0u;
-    const uint64_t mgt = __ballot(in && key > K);
-    const uint64_t meq = __ballot(in && key == K);
+  const int64_t base = s_beg + (int64_t)wave * (kWave * kMwPer) + lane;
+#pragma unroll
+  for (int j = 0; j < kMwPer; ++j) {
+    const bool v = mw_valid(s_beg, s_fin, j);
+    const uint32_t key = k.key[j];
+    const uint64_t mgt = __ballot(v && key > K);
+    const uint64_t meq = __ballot(v && key == K);
     const uint32_t g_b = gt_before + __popcll(mgt & below);
     const uint32_t e_b = eq_before + __popcll(meq & below);
     const uint32_t slot = g_b + (e_b < need ? e_b : need);
-    if (in && (key > K || (key == K && e_b < need)) && slot < (uint32_t)p.k) out[slot] = (int32_t)s;
+    if (v && (key > K || (key == K && e_b < need)) && slot < (uint32_t)p.k) out[slot] = (int32_t)(base + kWave * j);
     gt_before += __popcll(mgt);
     eq_before += __popcll(meq);
   }
@@ -788,7 +853,7 @@ size_t dsa_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k) {
   if (S <= kRegRow) return 0;
   const int64_t rows = B * T;
   const int64_t nchunk = (S + kMwChunk - 1) / kMwChunk;
-  return (size_t)(rows * kBins + rows * 4 + rows * nchunk * 2) * sizeof(uint32_t);
+  return (size_t)(rows * kMwSub * kBins + rows * 4 + rows * nchunk * 2) * sizeof(uint32_t);
 }
 
 hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream) {
@@ -820,7 +885,7 @@ hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(topk_mw_init, dim3((uint32_t)rows), dim3(kMwThreads), 0, stream, p);
   for (int pass = 0; pass < 3; ++pass) {
     hipLaunchKernelGGL(topk_mw_hist, dim3((uint32_t)(rows * nchunk)), dim3(kMwThreads), 0, stream, p, pass);
-    hipLaunchKernelGGL(topk_mw_select, dim3((uint32_t)rows), dim3(kTopkThreads), 0, stream, p, pass);
+    hipLaunchKernelGGL(topk_mw_select, dim3((uint32_t)rows), dim3(kMwThreads), 0, stream, p, pass);
   }
   hipLaunchKernelGGL(topk_mw_count, dim3((uint32_t)(rows * nchunk)), dim3(kMwThreads), 0, stream, p);
   hipLaunchKernelGGL(topk_mw_write, dim3((uint32_t)(rows * nchunk)), dim3(kMwThreads), 0, stream, p);

@@ -176,6 +176,17 @@ def test_topk_multi_workgroup_path():
     _topk_check(sa, sc, 2048, [S - 3, 40000])
 
 
+def test_topk_multi_workgroup_odd_width_and_short_rows():
+    """Long rows of odd width (positions not a multiple of 4 or of the chunk size) with ties
+    across chunk boundaries, plus rows no longer than k in the same call."""
+    sa = require_gpu()
+    g = np.random.default_rng(49)
+    S = 50001
+    sc = (g.integers(0, 3000, size=(2, 2, S)) / 32.0).astype(np.float32)
+    sc[0, 0, 4090:4100] = 200.0  # equal top scores on both sides of a chunk boundary
+    _topk_check(sa, sc, 2048, [S - 2, 1000])
+
+
 def test_topk_on_indexer_scores():
     """The real chain: GPU indexer scores -> GPU top-k vs oracle top-k on those scores."""
     sa = require_gpu()
