@@ -38,6 +38,7 @@ def _causal_mask(B, T, S, q_pos):
 
 
 @pytest.mark.parametrize("B,T,S,q_pos", [(1, 300, 300, None), (2, 70, 333, [263, 100]), (1, 1, 5000, [4999]),
+                                         (2, 1, 4500, [4499, 2047]), (1, 1, 70, None),
                                          (1, 129, 1100, [900])])
 def test_indexer_random(B, T, S, q_pos):
     sa = require_gpu()
