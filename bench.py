@@ -245,7 +245,25 @@ def main():
         kernels["hca_attention_decode_128k"] = {"ms": us * 1e-3, "alg_bytes": bytes3,
                                                 "hbm_GBs": result["decode_128k_b64"]["hbm_GBs"],
                                                 "hbm_frac": result["decode_128k_b64"]["hbm_frac"]}
-        del q3, kc3, vc3, rk3, rv3, ws3
+        # The same step over an FP8 (E4M3) copy of the cache: an extra figure
+        # beside the bf16 headline (one byte per element plus a 4-byte scale per row).
+        enc3 = {n: sa.hca_quantize_fp8(t) for n, t in (("rk", rk3), ("rv", rv3), ("kc", kc3), ("vc", vc3))}
+        ws3f = torch.empty(max(1, sa.hca_decode_fp8_workspace_size(q3, kc3, BLK, WIN)), dtype=torch.uint8, device=dev)
+
+        def dec3f():
+            return sa.hca_decode_fp8(q3, *enc3["rk"], *enc3["rv"], *enc3["kc"], *enc3["vc"], BLK, WIN, pos3,
+                                     workspace=ws3f)
+
+        for _ in range(args.warmup):
+            dec3f()
+        torch.cuda.synchronize()
+        t = timer.time(dec3f, max(20, args.steps * 5))
+        us_f = sorted(t)[len(t) // 2] * 1e3
+        bytes3f = B3 * H * keys3 * 2 * (D_HCA + 4) + 2 * B3 * H * D_HCA * 2
+        result["decode_128k_b64_fp8_cache"] = {"us_per_step": us_f, "alg_bytes": bytes3f,
+                                               "hbm_GBs": bytes3f / (us_f * 1e-6) / 1e9,
+                                               "hbm_frac": bytes3f / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        del q3, kc3, vc3, rk3, rv3, ws3, enc3, ws3f
         torch.cuda.empty_cache()
 
     # -------------------------------------------------------------------

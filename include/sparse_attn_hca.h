@@ -144,6 +144,65 @@ size_t hca_attention_fwd_workspace_size(const hca_attention_args* args);
 int hca_attention_fwd(const hca_attention_args* args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * FP8 decode cache (an extension: the pages fix no cache format).
+ *
+ * [P1] §二.1 / [P3] §架構創新 1: HCA decode reads every visible compressed
+ * entry and window token once, so its cost is the size of the cache.  Beside
+ * bf16 the library offers OCP E4M3 codes ("fn" variant: exponent bias 7,
+ * largest finite value 448, no infinities) with one fp32 scale per row.
+ *
+ * hca_quantize_fp8 -- encode bf16 rows.  For each row r of x [rows, d]:
+ *   amax = max_j |x[r,j]|;  inv = 448 / amax (fp32; 0 when amax == 0);
+ *   codes[r,j] = E4M3(x[r,j] * inv)   (fp32 product, round to nearest even);
+ *   scales[r] = amax / 448            (fp32)
+ * so that x[r,j] ~= scales[r] * value(codes[r,j]).  |x * inv| <= 448 holds,
+ * so no code saturates.  NaN or infinite inputs give unspecified codes.
+ * x: bf16 [rows, d]; codes: uint8 [rows, d]; scales: fp32 [rows].
+ * Supported: d a multiple of 16, at most 4096.  rows == 0 does nothing.
+ * ------------------------------------------------------------------------ */
+int hca_quantize_fp8(const void* x, void* codes, float* scales, int64_t rows, int64_t d, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * hca_decode_fp8 -- HCA decode (one query per sequence, as HCA_DECODE of
+ * hca_attention_fwd) over an FP8 cache: every K/V row is scale * E4M3 codes
+ * as written by hca_quantize_fp8.
+ *   q, o: bf16 [B,H,d];  k_c, v_c: codes [B,H,n_c_cap,d] with scales
+ *   k_c_scale, v_c_scale: fp32 [B,H,n_c_cap];  k, v: the window ring, codes
+ *   [B,H,window,d] (position s in slot s mod window) with scales k_scale,
+ *   v_scale: fp32 [B,H,window];  pos: device int64[B];  lse: optional fp32
+ *   [B,H] (natural log).  Visibility, scale and softmax as in HCA_DECODE.
+ * Arithmetic: codes widened exactly to fp32; fp32 dot products multiplied by
+ * the K row's scale, fp32 softmax, the V row's scale folded into the
+ * probability, fp32 accumulation, output rounded (RNE) to bf16.
+ * Supported: d = 512, n_c_cap >= 1.  Workspace as for hca_attention_fwd
+ * DECODE: hca_decode_fp8_workspace_size() bytes.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t B, H, d;
+  int64_t blk;      /* compression block (128)                            */
+  int64_t window;   /* window ring size (128)                             */
+  int64_t n_c_cap;  /* number of entries in k_c / v_c                     */
+  float scale;      /* <= 0 selects 1/sqrt(d)                             */
+  const void* q;
+  const void* k_c;
+  const float* k_c_scale;
+  const void* v_c;
+  const float* v_c_scale;
+  const void* k;
+  const float* k_scale;
+  const void* v;
+  const float* v_scale;
+  const int64_t* pos;
+  void* o;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+} hca_decode_fp8_args;
+
+size_t hca_decode_fp8_workspace_size(const hca_decode_fp8_args* args);
+int hca_decode_fp8(const hca_decode_fp8_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * dsa_indexer_scores -- lightweight indexer of MLA-DSA.
  *
  * [P1] §二.1 and [P3] §架構創新 1: a lightweight indexer scores every history

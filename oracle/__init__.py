@@ -43,6 +43,12 @@ from .dsa import (
     dsa_topk,
     dsa_sparse_attention,
 )
+from .fp8 import (
+    e4m3_value,
+    e4m3_encode,
+    quantize_fp8_rows,
+    dequantize_fp8_rows,
+)
 
 __all__ = [
     "hca_compress",
@@ -54,4 +60,8 @@ __all__ = [
     "dsa_indexer_scores",
     "dsa_topk",
     "dsa_sparse_attention",
+    "e4m3_value",
+    "e4m3_encode",
+    "quantize_fp8_rows",
+    "dequantize_fp8_rows",
 ]

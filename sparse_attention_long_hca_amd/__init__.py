@@ -17,6 +17,9 @@ from ._lib import (
     hca_attention_fwd,
     hca_attention_workspace_size,
     hca_compress,
+    hca_decode_fp8,
+    hca_decode_fp8_workspace_size,
+    hca_quantize_fp8,
     lib,
     version,
 )
@@ -34,6 +37,9 @@ __all__ = [
     "hca_attention_fwd",
     "hca_attention_workspace_size",
     "hca_compress",
+    "hca_decode_fp8",
+    "hca_decode_fp8_workspace_size",
+    "hca_quantize_fp8",
     "lib",
     "version",
 ]

@@ -47,6 +47,32 @@ class HcaAttentionArgs(ctypes.Structure):
     ]
 
 
+class HcaDecodeFp8Args(ctypes.Structure):
+    _fields_ = [
+        ("B", _c_i64),
+        ("H", _c_i64),
+        ("d", _c_i64),
+        ("blk", _c_i64),
+        ("window", _c_i64),
+        ("n_c_cap", _c_i64),
+        ("scale", ctypes.c_float),
+        ("q", _c_p),
+        ("k_c", _c_p),
+        ("k_c_scale", _c_p),
+        ("v_c", _c_p),
+        ("v_c_scale", _c_p),
+        ("k", _c_p),
+        ("k_scale", _c_p),
+        ("v", _c_p),
+        ("v_scale", _c_p),
+        ("pos", _c_p),
+        ("o", _c_p),
+        ("lse", _c_p),
+        ("workspace", _c_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class SparseAttnError(RuntimeError):
     def __init__(self, fn, status, msg):
         super().__init__(f"{fn} failed with status {status}: {msg}")
@@ -61,6 +87,9 @@ EXPORTS = {
     "hca_compress": (ctypes.c_int, [_c_p, _c_p, ctypes.c_int] + [_c_i64] * 11 + [_c_p]),
     "hca_attention_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HcaAttentionArgs)]),
     "hca_attention_fwd": (ctypes.c_int, [ctypes.POINTER(HcaAttentionArgs), _c_p]),
+    "hca_quantize_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p]),
+    "hca_decode_fp8_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HcaDecodeFp8Args)]),
+    "hca_decode_fp8": (ctypes.c_int, [ctypes.POINTER(HcaDecodeFp8Args), _c_p]),
     "dsa_indexer_scores": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p] + [_c_i64] * 5 + [_c_p]),
     "dsa_topk_workspace_size": (ctypes.c_size_t, [_c_i64] * 4),
     "dsa_topk": (ctypes.c_int, [_c_p, _c_p, _c_p] + [_c_i64] * 4 + [_c_p, ctypes.c_size_t, _c_p]),
@@ -202,6 +231,67 @@ def hca_attention_workspace_size(mode, q, k_c, blk, window):
     a.B, a.H, a.d = q.shape[0], q.shape[1], q.shape[-1]
     a.blk, a.window, a.n_c_cap = blk, window, k_c.shape[2]
     return lib().hca_attention_fwd_workspace_size(ctypes.byref(a))
+
+
+def hca_quantize_fp8(x, codes=None, scales=None):
+    """bf16 rows x [..., d] -> (E4M3 codes uint8 [..., d], fp32 scales [...]), one scale per row."""
+    _need(x, "x", torch.bfloat16)
+    d = x.shape[-1]
+    rows = x.numel() // d if d > 0 else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _need(codes, "codes", torch.uint8)
+    _need(scales, "scales", torch.float32)
+    _check("hca_quantize_fp8", lib().hca_quantize_fp8(_ptr(x), _ptr(codes), _ptr(scales), rows, d, _stream()))
+    return codes, scales
+
+
+def _fp8_args(q, k, k_scale, v, v_scale, k_c, k_c_scale, v_c, v_c_scale, blk, window, scale, pos, o, lse):
+    a = HcaDecodeFp8Args()
+    a.B, a.H, a.d = q.shape
+    a.blk, a.window, a.n_c_cap = blk, window, k_c.shape[2]
+    a.scale = 0.0 if scale is None else float(scale)
+    a.q = q.data_ptr()
+    a.k_c, a.k_c_scale, a.v_c, a.v_c_scale = k_c.data_ptr(), k_c_scale.data_ptr(), v_c.data_ptr(), v_c_scale.data_ptr()
+    a.k, a.k_scale, a.v, a.v_scale = k.data_ptr(), k_scale.data_ptr(), v.data_ptr(), v_scale.data_ptr()
+    a.pos = pos.data_ptr()
+    a.o = None if o is None else o.data_ptr()
+    a.lse = None if lse is None else lse.data_ptr()
+    return a
+
+
+def hca_decode_fp8(q, k, k_scale, v, v_scale, k_c, k_c_scale, v_c, v_c_scale, blk, window, pos, scale=None,
+                   return_lse=False, workspace=None):
+    """HCA decode over an E4M3 cache: q [B,H,d] bf16; k,v window-ring codes [B,H,window,d] uint8 with
+    scales [B,H,window]; k_c,v_c codes [B,H,Ncap,d] with scales [B,H,Ncap]; pos int64 [B].
+    Returns o [B,H,d] bf16 (and lse [B,H])."""
+    _need(q, "q", torch.bfloat16, 3)
+    for name, t in (("k", k), ("v", v), ("k_c", k_c), ("v_c", v_c)):
+        _need(t, name, torch.uint8, 4)
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale), ("k_c_scale", k_c_scale), ("v_c_scale", v_c_scale)):
+        _need(t, name, torch.float32, 3)
+    _need(pos, "pos", torch.int64, 1)
+    B, H, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
+    args = _fp8_args(q, k, k_scale, v, v_scale, k_c, k_c_scale, v_c, v_c_scale, blk, window, scale, pos, o, lse)
+    need = lib().hca_decode_fp8_workspace_size(ctypes.byref(args))
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("hca_decode_fp8", lib().hca_decode_fp8(ctypes.byref(args), _stream()))
+    return (o, lse) if return_lse else o
+
+
+def hca_decode_fp8_workspace_size(q, k_c, blk, window):
+    a = HcaDecodeFp8Args()
+    a.B, a.H, a.d = q.shape
+    a.blk, a.window, a.n_c_cap = blk, window, k_c.shape[2]
+    return lib().hca_decode_fp8_workspace_size(ctypes.byref(a))
 
 
 def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None, out=None):

@@ -27,6 +27,7 @@ SOURCES = [
     "hca_compress.hip",
     "hca_prefill.hip",
     "hca_decode.hip",
+    "hca_quant.hip",
     "dsa_indexer.hip",
     "dsa_topk.hip",
     "dsa_sparse_attn.hip",

@@ -141,9 +141,66 @@ int hca_attention_fwd(const hca_attention_args* a, hipStream_t stream) {
   const int64_t max_keys = a->n_c_cap + a->window;
   float* part_o = reinterpret_cast<float*>(a->workspace);
   float* part_lse = part_o ? part_o + BH * ns * a->d : nullptr;
-  sa::HcaDecodeParams p{a->q, a->k_c, a->v_c, a->k, a->v, a->pos, a->o, a->lse, part_o, part_lse,
+  sa::HcaDecodeParams p{a->q, a->k_c, a->v_c, a->k, a->v, nullptr, nullptr, nullptr, nullptr,
+                        a->pos, a->o, a->lse, part_o, part_lse,
                         a->B, a->H, a->n_c_cap, a->blk, a->window, sl2, ns, (max_keys + ns - 1) / ns};
   return hip_status(sa::launch_hca_decode(p, 1, (int)a->d, stream), "hca_attention_fwd decode launch");
+}
+
+// ---------------------------------------------------------------------------
+int hca_quantize_fp8(const void* x, void* codes, float* scales, int64_t rows, int64_t d, hipStream_t stream) {
+  if (rows < 0 || d <= 0) return fail(SA_ERR_SHAPE, "hca_quantize_fp8: rows must be >= 0 and d > 0");
+  if (rows == 0) return ok();
+  if (!x || !codes || !scales) return fail(SA_ERR_NULL, "hca_quantize_fp8: x, codes, scales must be non-NULL");
+  if (d % 16 != 0 || d > 4096) return fail(SA_ERR_UNSUPPORTED, "hca_quantize_fp8: d must be a multiple of 16, <= 4096");
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return fail(SA_ERR_ALIGN, "hca_quantize_fp8: pointers must be 16-byte aligned");
+  if ((rows + 3) / 4 > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "hca_quantize_fp8: too many rows");
+  sa::HcaQuantParams p{x, codes, scales, rows, d};
+  return hip_status(sa::launch_hca_quantize_fp8(p, stream), "hca_quantize_fp8 launch");
+}
+
+static int hca_fp8_check(const hca_decode_fp8_args* a) {
+  if (!a) return fail(SA_ERR_NULL, "hca_decode_fp8: args is NULL");
+  if (!a->q || !a->k_c || !a->k_c_scale || !a->v_c || !a->v_c_scale || !a->k || !a->k_scale || !a->v ||
+      !a->v_scale || !a->pos || !a->o)
+    return fail(SA_ERR_NULL, "hca_decode_fp8: q, codes, scales, pos and o must be non-NULL");
+  if (a->B <= 0 || a->H <= 0 || a->d <= 0 || a->blk <= 0 || a->window <= 0 || a->n_c_cap < 1)
+    return fail(SA_ERR_SHAPE, "hca_decode_fp8: B, H, d, blk, window and n_c_cap must be > 0");
+  if (a->d != 512) return fail(SA_ERR_UNSUPPORTED, "hca_decode_fp8: d must be 512");
+  const void* ptrs[] = {a->q, a->k_c, a->k_c_scale, a->v_c, a->v_c_scale, a->k, a->k_scale, a->v, a->v_scale, a->o, a->lse};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SA_ERR_ALIGN, "hca_decode_fp8: pointers must be 16-byte aligned");
+  return SA_OK;
+}
+
+size_t hca_decode_fp8_workspace_size(const hca_decode_fp8_args* a) {
+  if (!a || a->B <= 0 || a->H <= 0 || a->d <= 0) return 0;
+  const int64_t ns = sa::hca_decode_nsplit(a->B * a->H, a->n_c_cap + a->window);
+  return sa::hca_decode_workspace_bytes(a->B * a->H, ns, a->d);
+}
+
+int hca_decode_fp8(const hca_decode_fp8_args* a, hipStream_t stream) {
+  const int c = hca_fp8_check(a);
+  if (c != SA_OK) return c;
+  const float sl2 = resolve_scale_log2(a->scale, a->d);
+  const int64_t BH = a->B * a->H;
+  const int64_t max_keys = a->n_c_cap + a->window;
+  const int64_t ns = sa::hca_decode_nsplit(BH, max_keys);
+  const size_t need = sa::hca_decode_workspace_bytes(BH, ns, a->d);
+  if (need > 0) {
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(SA_ERR_WORKSPACE, "hca_decode_fp8: needs %zu workspace bytes, got %zu", need,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned16(a->workspace)) return fail(SA_ERR_ALIGN, "hca_decode_fp8: workspace must be 16-byte aligned");
+  }
+  if (BH * ns > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "hca_decode_fp8: grid too large");
+  float* part_o = reinterpret_cast<float*>(a->workspace);
+  float* part_lse = part_o ? part_o + BH * ns * a->d : nullptr;
+  sa::HcaDecodeParams p{a->q, a->k_c, a->v_c, a->k, a->v, a->k_c_scale, a->v_c_scale, a->k_scale, a->v_scale,
+                        a->pos, a->o, a->lse, part_o, part_lse,
+                        a->B, a->H, a->n_c_cap, a->blk, a->window, sl2, ns, (max_keys + ns - 1) / ns};
+  return hip_status(sa::launch_hca_decode(p, 2, (int)a->d, stream), "hca_decode_fp8 launch");
 }
 
 // ---------------------------------------------------------------------------

@@ -34,12 +34,23 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-template <int D>
+// kFp8: the K/V rows are E4M3 codes (one byte per dim) with one fp32 scale
+// per row; lane `part` of a key's 8 lanes then holds dims 64*part .. +63 (64
+// contiguous bytes), the codes are widened with the hardware conversion
+// (exact: every E4M3 value is an fp32 value), the dot product runs in fp32
+// and is multiplied by the K row's scale, and the V row's scale is folded
+// into the probability.  bf16 rows: lane `part` holds the 16-byte chunks
+// part, part+16, ... of the row.
+constexpr int kDecFp8Lanes = 8;  // lanes per key with the FP8 cache (more keys in flight per wave)
+
+template <int D, bool kFp8>
 __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams p) {
-  constexpr int kLanes = 16;               // lanes per key
+  constexpr int kLanes = kFp8 ? kDecFp8Lanes : 16;  // lanes per key
+  constexpr int kLaneDims = D / kLanes;             // FP8: contiguous dims per lane
   constexpr int kSlots = kWave / kLanes;   // keys per wave step
-  constexpr int kChunks = D / 8;           // 16-byte chunks per bf16 row
-  constexpr int kPer = kChunks / kLanes;   // chunks per lane
+  constexpr int kPer = D / 8 / kLanes;     // groups of 8 dims per lane
+  constexpr int kRowBytes = kFp8 ? D : 2 * D;
+  constexpr int kLoads = kRowBytes / kLanes / 16;  // 16-byte loads per lane and row
   __shared__ float sh_o[kDecWaves][D];
   __shared__ float sh_m[kDecWaves], sh_l[kDecWaves];
 
@@ -49,6 +60,10 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
   const int64_t b = bh / p.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = lane / kLanes, part = lane % kLanes;
+  // First dim of this lane's group i of 8 dims.
+  auto dim0 = [&](int i) { return kFp8 ? kLaneDims * part + 8 * i : 8 * (part + kLanes * i); };
+  // Byte offset in a row of this lane's 16-byte load j.
+  auto load_off = [&](int j) { return kFp8 ? kLaneDims * part + 16 * j : 16 * (part + kLanes * j); };
 
   int64_t t = p.pos[b];
   if (t < 0) t = 0;
@@ -59,16 +74,28 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
   const int64_t u_end = imin64(n_keys, u_begin + p.keys_per_split);
 
   const bf16_t* q = reinterpret_cast<const bf16_t*>(p.q) + bh * D;
-  const bf16_t* kc = reinterpret_cast<const bf16_t*>(p.kc) + bh * p.Ncap * D;
-  const bf16_t* vc = reinterpret_cast<const bf16_t*>(p.vc) + bh * p.Ncap * D;
-  const bf16_t* rk = reinterpret_cast<const bf16_t*>(p.rk) + bh * p.window * D;
-  const bf16_t* rv = reinterpret_cast<const bf16_t*>(p.rv) + bh * p.window * D;
+  const char* kc = reinterpret_cast<const char*>(p.kc) + bh * p.Ncap * kRowBytes;
+  const char* vc = reinterpret_cast<const char*>(p.vc) + bh * p.Ncap * kRowBytes;
+  const char* rk = reinterpret_cast<const char*>(p.rk) + bh * p.window * kRowBytes;
+  const char* rv = reinterpret_cast<const char*>(p.rv) + bh * p.window * kRowBytes;
   const int64_t win_first = t - nw + 1;  // first window position
 
-  // Query chunks part, part+16, ... as bf16 pairs.
+  // Query: bf16 pairs (bf16 cache) or fp32 (FP8 cache), dims dim0(i) .. +7.
   uint4 qc[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) qc[i] = *reinterpret_cast<const uint4*>(q + (part + kLanes * i) * 8);
+  for (int i = 0; i < kPer; ++i) qc[i] = *reinterpret_cast<const uint4*>(q + dim0(i));
+  float qf[kFp8 ? kPer * 8 : 1];
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint32_t w[4] = {qc[i].x, qc[i].y, qc[i].z, qc[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qf[8 * i + 2 * e] = bf16_to_f32(w[e] & 0xffffu);
+        qf[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    }
+  }
 
   float acc[kPer * 8];
 #pragma unroll
@@ -77,31 +104,42 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
 
   // One group: keys g0 + slot (a group of kSlots consecutive keys).
   struct Rows {
-    uint4 k[kPer], v[kPer];
+    uint4 k[kLoads], v[kLoads];
+    float ks, vs;  // row scales (FP8 cache)
   };
   auto load = [&](int64_t g0, Rows& r) __attribute__((always_inline)) {
     const int64_t u = g0 + slot;
+    r.ks = 0.f;
+    r.vs = 0.f;
     if (u < u_end) {
-      const bf16_t* krow;
-      const bf16_t* vrow;
+      const char* krow;
+      const char* vrow;
       if (u < nc) {
-        krow = kc + u * D;
-        vrow = vc + u * D;
+        krow = kc + u * kRowBytes;
+        vrow = vc + u * kRowBytes;
+        if constexpr (kFp8) {
+          r.ks = p.kc_scale[bh * p.Ncap + u];
+          r.vs = p.vc_scale[bh * p.Ncap + u];
+        }
       } else {
         const int64_t sl = (win_first + (u - nc)) % p.window;
-        krow = rk + sl * D;
-        vrow = rv + sl * D;
+        krow = rk + sl * kRowBytes;
+        vrow = rv + sl * kRowBytes;
+        if constexpr (kFp8) {
+          r.ks = p.rk_scale[bh * p.window + sl];
+          r.vs = p.rv_scale[bh * p.window + sl];
+        }
       }
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        r.k[i] = *reinterpret_cast<const uint4*>(krow + (part + kLanes * i) * 8);
-        r.v[i] = *reinterpret_cast<const uint4*>(vrow + (part + kLanes * i) * 8);
+      for (int j = 0; j < kLoads; ++j) {
+        r.k[j] = *reinterpret_cast<const uint4*>(krow + load_off(j));
+        r.v[j] = *reinterpret_cast<const uint4*>(vrow + load_off(j));
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        r.k[i] = make_uint4(0u, 0u, 0u, 0u);
-        r.v[i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < kLoads; ++j) {
+        r.k[j] = make_uint4(0u, 0u, 0u, 0u);
+        r.v[j] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
   };
@@ -109,15 +147,34 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
   auto use = [&](int64_t g0, const Rows& r) __attribute__((always_inline)) {
     const bool valid = g0 + slot < u_end;
     float dot = 0.f;
+    if constexpr (kFp8) {
+      // Load j holds dims kLaneDims*part + 16*j .. +15, four codes per word.
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      dot = dot2_bf16(qc[i].x, r.k[i].x, dot);
-      dot = dot2_bf16(qc[i].y, r.k[i].y, dot);
-      dot = dot2_bf16(qc[i].z, r.k[i].z, dot);
-      dot = dot2_bf16(qc[i].w, r.k[i].w, dot);
+      for (int j = 0; j < kLoads; ++j) {
+        const uint32_t w[4] = {r.k[j].x, r.k[j].y, r.k[j].z, r.k[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[e], false);
+          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[e], true);
+          const int d0 = 16 * j + 4 * e;
+          dot = fmaf(qf[d0], lo[0], dot);
+          dot = fmaf(qf[d0 + 1], lo[1], dot);
+          dot = fmaf(qf[d0 + 2], hi[0], dot);
+          dot = fmaf(qf[d0 + 3], hi[1], dot);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        dot = dot2_bf16(qc[i].x, r.k[i].x, dot);
+        dot = dot2_bf16(qc[i].y, r.k[i].y, dot);
+        dot = dot2_bf16(qc[i].z, r.k[i].z, dot);
+        dot = dot2_bf16(qc[i].w, r.k[i].w, dot);
+      }
     }
 #pragma unroll
     for (int off = 1; off < kLanes; off <<= 1) dot += __shfl_xor(dot, off);
+    if constexpr (kFp8) dot *= r.ks;
     const float x = valid ? dot * p.scale_log2 : -INFINITY;
     float gm = x;
 #pragma unroll
@@ -135,13 +192,31 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
 #pragma unroll
     for (int off = kLanes; off < kWave; off <<= 1) ps += __shfl_xor(ps, off);
     l += ps;
+    if constexpr (kFp8) {
+      const float pv = pr * r.vs;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
+      for (int j = 0; j < kLoads; ++j) {
+        const uint32_t w[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[i * 8 + 2 * e] = fmaf(pr, bf16_to_f32(w[e] & 0xffffu), acc[i * 8 + 2 * e]);
-        acc[i * 8 + 2 * e + 1] = fmaf(pr, __uint_as_float(w[e] & 0xffff0000u), acc[i * 8 + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e) {
+          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[e], false);
+          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[e], true);
+          const int d0 = 16 * j + 4 * e;
+          acc[d0] = fmaf(pv, lo[0], acc[d0]);
+          acc[d0 + 1] = fmaf(pv, lo[1], acc[d0 + 1]);
+          acc[d0 + 2] = fmaf(pv, hi[0], acc[d0 + 2]);
+          acc[d0 + 3] = fmaf(pv, hi[1], acc[d0 + 3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[i * 8 + 2 * e] = fmaf(pr, bf16_to_f32(w[e] & 0xffffu), acc[i * 8 + 2 * e]);
+          acc[i * 8 + 2 * e + 1] = fmaf(pr, __uint_as_float(w[e] & 0xffff0000u), acc[i * 8 + 2 * e + 1]);
+        }
       }
     }
   };
@@ -171,7 +246,7 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sh_o[wave][(part + kLanes * i) * 8 + e] = acc[i * 8 + e];
+      for (int e = 0; e < 8; ++e) sh_o[wave][dim0(i) + e] = acc[i * 8 + e];
   }
   if (lane == 0) {
     sh_m[wave] = m;
@@ -254,10 +329,13 @@ size_t hca_decode_workspace_bytes(int64_t BH, int64_t nsplit, int64_t d) {
   return (size_t)(BH * nsplit * d + BH * nsplit) * sizeof(float);
 }
 
-hipError_t launch_hca_decode(const HcaDecodeParams& p, int dtype, int d, hipStream_t stream) {
-  if (dtype != 1 || d != 512) return hipErrorInvalidValue;
+hipError_t launch_hca_decode(const HcaDecodeParams& p, int cache, int d, hipStream_t stream) {
+  if ((cache != 1 && cache != 2) || d != 512) return hipErrorInvalidValue;
   const int64_t BH = p.B * p.H;
-  hipLaunchKernelGGL(hca_decode_kernel<512>, dim3((uint32_t)(BH * p.nsplit)), dim3(kDecThreads), 0, stream, p);
+  if (cache == 2)
+    hipLaunchKernelGGL((hca_decode_kernel<512, true>), dim3((uint32_t)(BH * p.nsplit)), dim3(kDecThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((hca_decode_kernel<512, false>), dim3((uint32_t)(BH * p.nsplit)), dim3(kDecThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   hipLaunchKernelGGL(hca_decode_combine_kernel<512>, dim3((uint32_t)BH), dim3(256), 0, stream, p);

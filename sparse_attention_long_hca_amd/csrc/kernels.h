@@ -38,6 +38,11 @@ struct HcaDecodeParams {
   const void* vc;
   const void* rk;  // window ring [B,H,window,d]
   const void* rv;
+  // FP8 cache only: one fp32 scale per row of kc, vc ([B,H,Ncap]), rk, rv ([B,H,window]).
+  const float* kc_scale;
+  const float* vc_scale;
+  const float* rk_scale;
+  const float* rv_scale;
   const int64_t* pos;
   void* o;
   float* lse;
@@ -49,7 +54,17 @@ struct HcaDecodeParams {
 };
 int64_t hca_decode_nsplit(int64_t BH, int64_t max_keys);
 size_t hca_decode_workspace_bytes(int64_t BH, int64_t nsplit, int64_t d);
-hipError_t launch_hca_decode(const HcaDecodeParams& p, int dtype, int d, hipStream_t stream);
+// cache: 1 = bf16 rows, 2 = E4M3 codes with per-row scales.
+hipError_t launch_hca_decode(const HcaDecodeParams& p, int cache, int d, hipStream_t stream);
+
+// ---- hca_quantize_fp8 -------------------------------------------------------
+struct HcaQuantParams {
+  const void* x;  // [rows, d] bf16
+  void* codes;    // [rows, d] E4M3
+  float* scales;  // [rows]
+  int64_t rows, d;
+};
+hipError_t launch_hca_quantize_fp8(const HcaQuantParams& p, hipStream_t stream);
 
 // ---- dsa_indexer_scores -----------------------------------------------------
 struct DsaIndexerParams {

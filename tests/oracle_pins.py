@@ -386,4 +386,97 @@ def pin_dsa_end_to_end_k_ge_context_is_dense():
     _close(o, ref.transpose(0, 2, 1, 3), 1e-12, "k >= context")
 
 
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3 "fn") decode cache -- the library's own format reading
+# ---------------------------------------------------------------------------
+def _torch_e4m3_decode(codes):
+    import torch
+
+    return torch.from_numpy(np.asarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_e4m3_encode(x):
+    import torch
+
+    return torch.from_numpy(np.asarray(x, dtype=np.float64)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_values_are_torch_float8():
+    """Every code decodes as torch's float8_e4m3fn does (NaN for S.1111.111 only)."""
+    codes = np.arange(256)
+    got = oracle.e4m3_value(codes)
+    ref = _torch_e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "NaN codes"
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]), "E4M3 values"
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok])), "signs"
+
+
+def pin_e4m3_golden_codes():
+    """Facts of the OCP E4M3 layout: bias 7, 3 mantissa bits, subnormals m*2^-9, max 448."""
+    v = oracle.e4m3_value
+    golden = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+              0x3F: 1.875, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, want in golden.items():
+        assert v(c) == want, (hex(c), v(c), want)
+    assert np.signbit(v(0x80)) and v(0x80) == 0.0, "0x80 is -0.0"
+    assert np.isnan(v(0x7F)) and np.isnan(v(0xFF)), "S.1111.111 is NaN"
+    pos = v(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0), "codes 0x00..0x7E increase"
+
+
+def pin_e4m3_encode_round_trip_and_ties():
+    """encode(value(c)) == c for every finite code; a midpoint goes to the even code."""
+    codes = np.arange(256)
+    vals = oracle.e4m3_value(codes)
+    ok = ~np.isnan(vals)
+    assert np.array_equal(oracle.e4m3_encode(vals[ok]), codes[ok].astype(np.uint8)), "round trip"
+    # midpoints between neighbours 0x38|0x39 (1.0625) and 0x39|0x3A (1.1875), 0x00|0x01, 0x7D|0x7E
+    for x, want in ((1.0625, 0x38), (1.1875, 0x3A), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (432.0, 0x7E),
+                    (-1.0625, 0xB8), (464.0, 0x7E)):
+        assert oracle.e4m3_encode(np.array([x]))[0] == want, (x, hex(oracle.e4m3_encode(np.array([x]))[0]), hex(want))
+
+
+def pin_e4m3_encode_is_torch_conversion():
+    """Round to nearest even, as torch's float32/64 -> float8_e4m3fn conversion, over normal,
+    subnormal and midpoint values."""
+    rng = _rng(31)
+    vals = oracle.e4m3_value(np.arange(0x7F))
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([rng.uniform(-448, 448, 5000), rng.uniform(-0.03, 0.03, 5000), mids, -mids,
+                        rng.standard_normal(2000) * 10])
+    x = x[np.abs(x) <= 448]
+    assert np.array_equal(oracle.e4m3_encode(x), _torch_e4m3_encode(x)), "E4M3 rounding"
+
+
+def pin_quantize_rows_invariants():
+    """Per-row scaling: the row's largest magnitude maps to +-448, the scale is amax/448 in fp32,
+    every value is within half a step of its code, zero rows give zero codes and scale."""
+    rng = _rng(32)
+    x = (rng.standard_normal((6, 512)) * np.array([1.0, 1e-3, 50.0, 1e-6, 3.0, 0.2])[:, None]).astype(np.float32)
+    x[1, :] = 0.0
+    x[1, 7] = -2.5  # a single nonzero value
+    x[4, :] = 0.75  # constant row
+    x = np.concatenate([x, np.zeros((1, 512), np.float32)])
+    codes, scales = oracle.quantize_fp8_rows(x)
+    assert scales.dtype == np.float32 and codes.dtype == np.uint8
+    amax = np.max(np.abs(x), axis=-1)
+    assert np.array_equal(scales, (amax / np.float32(448)).astype(np.float32)), "scale = amax/448"
+    for r in range(x.shape[0]):
+        if amax[r] == 0:
+            assert np.all(codes[r] == 0) and scales[r] == 0, "zero row"
+            continue
+        j = int(np.argmax(np.abs(x[r])))
+        assert codes[r, j] in (0x7E, 0xFE), ("row max maps to 448", r, hex(codes[r, j]))
+        inv = np.float64(np.float32(448) / amax[r])
+        scaled = x[r].astype(np.float64) * inv
+        err = np.abs(oracle.e4m3_value(codes[r]) - scaled)
+        step = np.where(np.abs(scaled) >= 2.0 ** -6, np.exp2(np.floor(np.log2(np.maximum(np.abs(scaled), 2.0 ** -6))) - 3),
+                        2.0 ** -9)
+        assert np.all(err <= step / 2 + 1e-9 * np.abs(scaled)), ("half a step", r)
+    assert np.all(codes[4] == 0x7E), "constant row"
+    deq = oracle.dequantize_fp8_rows(codes, scales)
+    assert np.all(np.abs(deq - x) <= np.abs(x) * 2.0 ** -4 + scales[:, None] * 2.0 ** -9 + 1e-30), "dequantized rows"
+
+
 ALL_PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_") and callable(fn)}

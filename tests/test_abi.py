@@ -147,3 +147,51 @@ def test_sparse_attention_validation(sa):
     dec = list(args)
     dec[12] = 2048  # kk: a 4-token call with 2048 indices is split and needs a workspace
     assert L.dsa_sparse_attention_fwd(*dec) == SA_ERR_WORKSPACE
+
+
+def test_quantize_fp8_validation(sa):
+    L = sa.lib()
+    assert L.hca_quantize_fp8(None, 4096, 4096, 4, 512, None) == SA_ERR_NULL
+    assert L.hca_quantize_fp8(4096, 4096, 4096, 4, 500, None) == SA_ERR_UNSUPPORTED
+    assert L.hca_quantize_fp8(4096, 4096, 4096, -1, 512, None) == SA_ERR_SHAPE
+    assert L.hca_quantize_fp8(4100, 4096, 4096, 4, 512, None) == SA_ERR_ALIGN
+    # no rows: nothing to do, OK without touching the GPU
+    assert L.hca_quantize_fp8(None, None, None, 0, 512, None) == SA_OK
+
+
+def _fp8_args(**kw):
+    from sparse_attention_long_hca_amd._lib import HcaDecodeFp8Args
+
+    a = HcaDecodeFp8Args()
+    a.B, a.H, a.d, a.blk, a.window, a.n_c_cap = 1, 1, 512, 128, 128, 2
+    for f in ("q", "k_c", "k_c_scale", "v_c", "v_c_scale", "k", "k_scale", "v", "v_scale", "pos", "o"):
+        setattr(a, f, 4096)
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(q=None), SA_ERR_NULL),
+        (dict(k_scale=None), SA_ERR_NULL),
+        (dict(pos=None), SA_ERR_NULL),
+        (dict(B=0), SA_ERR_SHAPE),
+        (dict(n_c_cap=0), SA_ERR_SHAPE),
+        (dict(d=256), SA_ERR_UNSUPPORTED),
+        (dict(v_c_scale=4100), SA_ERR_ALIGN),
+        (dict(B=4, H=64, n_c_cap=8192, workspace=None, workspace_bytes=0), SA_ERR_WORKSPACE),
+    ],
+)
+def test_decode_fp8_validation(sa, kw, code):
+    a = _fp8_args(**kw)
+    assert sa.lib().hca_decode_fp8(ctypes.byref(a), None) == code
+    assert sa.lib().sa_last_error().decode()
+
+
+def test_decode_fp8_workspace_matches_bf16_decode(sa):
+    a = _fp8_args(B=4, H=64, n_c_cap=8192)
+    b = _hca_args(mode=1, B=4, H=64, n_c_cap=8192)
+    assert sa.lib().hca_decode_fp8_workspace_size(ctypes.byref(a)) == sa.lib().hca_attention_fwd_workspace_size(
+        ctypes.byref(b)) > 0

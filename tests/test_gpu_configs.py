@@ -85,6 +85,32 @@ def test_hca_decode_full(B, ncap, pos, sigma):
         assert max_abs_err(f64(lse[sl]), lw) <= 1e-2
 
 
+@pytest.mark.parametrize("B,ncap,pos", [(64, 1024, 131071), (4, 8192, 1048575)])
+def test_hca_decode_fp8_full(B, ncap, pos):
+    """FP8 cache at the decode configs' full sizes: GPU encoding bit-exact against the oracle on sampled
+    (b, h) rows, GPU FP8 decode against the oracle over the dequantized cache."""
+    sa = require_gpu()
+    H, d = 64, 512
+    q = synth.torch_normal((B, H, d), 1.0, torch.bfloat16, 1410, DEV)
+    cache = {n: synth.torch_normal(shape, 1.0, torch.bfloat16, 1411 + i, DEV) for i, (n, shape) in enumerate(
+        (("kc", (B, H, ncap, d)), ("vc", (B, H, ncap, d)), ("rk", (B, H, WIN, d)), ("rv", (B, H, WIN, d))))}
+    enc = {n: sa.hca_quantize_fp8(t) for n, t in cache.items()}
+    posd = torch.full((B,), pos, dtype=torch.int64, device=DEV)
+    o, lse = sa.hca_decode_fp8(q, *enc["rk"], *enc["rv"], *enc["kc"], *enc["vc"], BLK, WIN, posd, return_lse=True)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (B - 1, 63), (B // 2, 17), (1, 40)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        deq = {}
+        for n, t in cache.items():
+            want_c, want_s = oracle.quantize_fp8_rows(f64(t[sl]))
+            assert np.array_equal(enc[n][0][sl].cpu().numpy(), want_c), (n, b, h)
+            assert np.array_equal(enc[n][1][sl].cpu().numpy(), want_s), (n, b, h)
+            deq[n] = oracle.dequantize_fp8_rows(want_c, want_s)
+        ow, lw = oracle.hca_attention_decode(f64(q[sl]), deq["kc"], deq["vc"], deq["rk"], deq["rv"], [pos], BLK, WIN)
+        assert max_abs_err(f64(o[sl]), ow) <= BF16_ABS_TOL, (b, h)
+        assert max_abs_err(f64(lse[sl]), lw) <= 1e-2
+
+
 def _band_compare(got_idx, oracle_scores, k):
     """Top-k vs the oracle's float64 scores: positions within 1e-6 of the k-th score are excluded."""
     valid = np.isfinite(oracle_scores)

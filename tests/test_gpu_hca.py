@@ -147,3 +147,71 @@ def test_decode_equals_prefill_row():
         pos = torch.tensor([t], dtype=torch.int64, device=DEV)
         o_dec = sa.hca_attention_fwd(sa.HCA_DECODE, tq[:, :, t].contiguous(), ring_k, ring_v, kc, vc, blk, window, pos=pos)
         assert max_abs_err(f64(o_dec), f64(o_pre[:, :, t])) <= 1e-2, f"t={t}"
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) decode cache
+# ---------------------------------------------------------------------------
+
+
+def _fp8_rows_case():
+    """bf16 rows over many magnitudes (subnormal codes included), a zero row, a row with -0.0
+    entries, a single-nonzero row and a constant row."""
+    x = synth.np_normal((12, 512), 1.0, "bf16", 24, 0).astype(np.float64)
+    x *= np.array([1.0, 1e-3, 40.0, 1e-5, 3.0, 0.25, 1.0, 1.0, 1.0, 1.0, 7.0, 1e-2])[:, None]
+    x[6, :] = 0.0
+    x[7, :] = -0.0
+    x[7, 3] = 1.5
+    x[8, :] = 0.0
+    x[8, 100] = -3.0
+    x[9, :] = 0.625
+    x[10, :] = np.where(x[10] < 0, -1.0, 1.0) * np.exp2(np.linspace(-25, 3, 512))  # subnormal codes
+    return synth.round_to(x, "bf16")
+
+
+def test_quantize_fp8_bit_exact():
+    sa = require_gpu()
+    x = _fp8_rows_case()
+    codes, scales = sa.hca_quantize_fp8(synth.to_torch(x, "bf16", DEV))
+    want_c, want_s = oracle.quantize_fp8_rows(x)
+    got_c = codes.cpu().numpy()
+    bad = np.argwhere(got_c != want_c)
+    assert bad.size == 0, f"{bad.shape[0]} codes differ, first at {bad[:3]}: {got_c[tuple(bad[0])]:#x} vs {want_c[tuple(bad[0])]:#x}"
+    assert np.array_equal(scales.cpu().numpy(), want_s)
+
+
+def test_quantize_fp8_cache_layout():
+    """A [B,H,N,d] cache quantizes row by row (one scale per (b, h, n))."""
+    sa = require_gpu()
+    x = synth.np_normal((2, 3, 5, 512), 0.5, "bf16", 25, 0)
+    codes, scales = sa.hca_quantize_fp8(synth.to_torch(x, "bf16", DEV))
+    assert codes.shape == (2, 3, 5, 512) and scales.shape == (2, 3, 5)
+    want_c, want_s = oracle.quantize_fp8_rows(x)
+    assert np.array_equal(codes.cpu().numpy(), want_c)
+    assert np.array_equal(scales.cpu().numpy(), want_s)
+
+
+@pytest.mark.parametrize("B,H,ncap,positions", [(3, 2, 10, [0, 130, 1407]), (2, 3, 12, [5000, 127]),
+                                                 (1, 2, 2000, [256000]), (4, 1, 3, [255, 256, 383, 384])])
+def test_decode_fp8(B, H, ncap, positions):
+    """GPU-encoded cache (checked bit-exact against the oracle's encoding) -> GPU FP8 decode vs the
+    oracle's decode over the dequantized cache."""
+    sa = require_gpu()
+    blk, window, d = 128, 128, 512
+    q = synth.np_normal((B, H, d), 1.0, "bf16", 26, 0)
+    rows = {name: synth.np_normal(shape, 1.0, "bf16", 26, tid) for tid, (name, shape) in enumerate(
+        (("kc", (B, H, ncap, d)), ("vc", (B, H, ncap, d)), ("rk", (B, H, window, d)), ("rv", (B, H, window, d))),
+        start=1)}
+    enc = {n: sa.hca_quantize_fp8(synth.to_torch(a, "bf16", DEV)) for n, a in rows.items()}
+    deq = {}
+    for n, a in rows.items():
+        want_c, want_s = oracle.quantize_fp8_rows(a)
+        assert np.array_equal(enc[n][0].cpu().numpy(), want_c), n
+        assert np.array_equal(enc[n][1].cpu().numpy(), want_s), n
+        deq[n] = oracle.dequantize_fp8_rows(want_c, want_s)
+    pos = torch.tensor(positions, dtype=torch.int64, device=DEV)
+    o, lse = sa.hca_decode_fp8(synth.to_torch(q, "bf16", DEV), *enc["rk"], *enc["rv"], *enc["kc"], *enc["vc"],
+                               blk, window, pos, return_lse=True)
+    ow, lw = oracle.hca_attention_decode(q, deq["kc"], deq["vc"], deq["rk"], deq["rv"], positions, blk, window)
+    assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL
+    assert max_abs_err(f64(lse), lw) <= 1e-2

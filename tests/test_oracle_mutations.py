@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 import oracle.dsa as odsa
+import oracle.fp8 as ofp8
 import oracle.hca as ohca
 import oracle_pins
 
@@ -58,6 +59,44 @@ def _mut_compress_includes_tail(x, blk):
 
 
 _orig_attend = ohca._attend
+_orig_encode = ofp8.e4m3_encode
+
+
+def _mut_e4m3_bias8(code):
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -10, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+    return sign * np.where((e == 15) & (m == 7), np.nan, mag)
+
+
+def _mut_e4m3_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    sign = np.where(np.signbit(x), 0x80, 0)
+    a = np.abs(x)
+    _, ex = np.frexp(a)
+    e = np.where(a > 0, np.maximum(ex - 1, -6), -6)
+    n = np.floor(np.ldexp(a, -(e - 3)))
+    return (sign | (8 * (e + 7) + (n.astype(np.int64) - 8))).astype(np.uint8)
+
+
+def _mut_e4m3_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    sign = np.where(np.signbit(x), 0x80, 0)
+    a = np.abs(x)
+    _, ex = np.frexp(a)
+    e = np.where(a > 0, np.maximum(ex - 1, -6), -6)
+    n = np.floor(np.ldexp(a, -(e - 3)) + 0.5)
+    return (sign | (8 * (e + 7) + (n.astype(np.int64) - 8))).astype(np.uint8)
+
+
+def _mut_quantize_scale_inverted(x):
+    codes, scales = _orig_quantize(x)
+    with np.errstate(divide="ignore"):
+        return codes, np.where(scales > 0, np.float32(1) / scales, 0).astype(np.float32)
+
+
+_orig_quantize = ofp8.quantize_fp8_rows
 _orig_scores = odsa.dsa_indexer_scores
 _orig_topk = odsa.dsa_topk
 _orig_sparse = odsa.dsa_sparse_attention
@@ -125,6 +164,10 @@ MUTATIONS = {
     "topk_ties_high": (odsa, "dsa_topk", _mut_topk_ties_high),
     "topk_descending_output": (odsa, "dsa_topk", _mut_topk_descending_output),
     "sparse_keeps_padding": (odsa, "dsa_sparse_attention", _mut_sparse_keeps_padding),
+    "e4m3_bias8": (ofp8, "e4m3_value", _mut_e4m3_bias8),
+    "e4m3_truncate": (ofp8, "e4m3_encode", _mut_e4m3_truncate),
+    "e4m3_ties_away": (ofp8, "e4m3_encode", _mut_e4m3_ties_away),
+    "quantize_scale_inverted": (ofp8, "quantize_fp8_rows", _mut_quantize_scale_inverted),
 }
 
 
