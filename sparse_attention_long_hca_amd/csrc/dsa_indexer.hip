@@ -118,22 +118,24 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
     plim[mb] = vc ? min(base + qc_i, S - 1) : -1;
   }
 
-  // Scores of the previous tile, held in registers and stored after the next
+  // Scores of earlier tiles, held in registers and stored after the next
   // wait: on this GPU a wait for loads also waits for every earlier store
-  // of the wave, so stores issued just before a wait would stall it.
-  float held[4][4];
-  int held_s0 = -1;  // first position of the held tile (-1: nothing held)
+  // of the wave, so stores issued just before a wait would stall it.  Two
+  // slots (the prefill pipeline works on pairs of tiles).
+  float held[2][4][4];
+  int held_s0[2] = {-1, -1};  // first position of the held tile (-1: nothing held)
   // Every position of a tile is visible to every query of the wave when the
   // tile ends at or before the first query's limit (all 16 queries valid).
   const int wave_full_lim = n_mb == 4 ? min(base + iw, S - 1) : -1;
-  auto store_held = [&]() __attribute__((always_inline)) {
-    if (held_s0 < 0) return;
-    if (held_s0 + kIdxKTile - 1 <= wave_full_lim) {
+  auto store_held = [&](int slot) __attribute__((always_inline)) {
+    const int h0 = held_s0[slot];
+    if (h0 < 0) return;
+    if (h0 + kIdxKTile - 1 <= wave_full_lim) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        float* orow = out + (int64_t)(iw + mb * 4 + g) * S + held_s0 + L;
+        float* orow = out + (int64_t)(iw + mb * 4 + g) * S + h0 + L;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) orow[nb * 16] = held[mb][nb];
+        for (int nb = 0; nb < 4; ++nb) orow[nb * 16] = held[slot][mb][nb];
       }
     } else {
 #pragma unroll
@@ -142,16 +144,16 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
         float* orow = out + (int64_t)(iw + mb * 4 + g) * S;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const int s = held_s0 + nb * 16 + L;
-          if (s <= plim[mb]) orow[s] = held[mb][nb];
+          const int s = h0 + nb * 16 + L;
+          if (s <= plim[mb]) orow[s] = held[slot][mb][nb];
         }
       }
     }
   };
-  auto compute = [&](int tile, const char* buf) __attribute__((always_inline)) {
+  auto compute = [&](int tile, const char* buf, int slot) __attribute__((always_inline)) {
     const int s0 = s_begin + tile * kIdxKTile;
     if (s0 > wave_plim) {  // tile entirely after the wave's last query
-      held_s0 = -1;
+      held_s0[slot] = -1;
       return;
     }
     // All four M-blocks always run (rows past the sequence end have zero Q
@@ -181,30 +183,70 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
         float sc = 0.f;
 #pragma unroll
         for (int h = 0; h < 4; ++h) sc = fmaf(wq[mb][h], fmaxf(acc[mb][nb][h], 0.f), sc);
-        held[mb][nb] = sc;
+        held[slot][mb][nb] = sc;
       }
-    held_s0 = s0;
+    held_s0[slot] = s0;
   };
 
-  // Two-stage pipeline, unrolled by two so each buffer has a fixed role.
   const buffer_rsrc_t rsrc = make_buffer_rsrc(kI);
-  idx_stage<kWaves>(lds0, rsrc, s_begin, s_stop);
-  for (int tile = 0; tile < n_tiles; tile += 2) {
-    wait_vmcnt<0>();
-    lds_barrier();
-    if (tile + 1 < n_tiles) idx_stage<kWaves>(lds1, rsrc, s_begin + (tile + 1) * kIdxKTile, s_stop);
-    store_held();
-    compute(tile, lds0);
-    if (tile + 1 >= n_tiles) break;
-    wait_lgkmcnt0();
-    wait_vmcnt<0>();
-    lds_barrier();
-    if (tile + 2 < n_tiles) idx_stage<kWaves>(lds0, rsrc, s_begin + (tile + 2) * kIdxKTile, s_stop);
-    store_held();
-    compute(tile + 1, lds1);
-    wait_lgkmcnt0();
+  if constexpr (kWaves == 4) {
+    // Prefill: a four-stage ring worked in pairs of tiles (lds0/lds1 and
+    // lds2/lds3 alternate).  A pair's loads are issued when the previous
+    // pair's data is visible and a pair's scores are stored at the start of
+    // the next pair, so the wait before a pair -- which also waits for the
+    // wave's stores -- covers loads and stores issued a whole pair earlier.
+    __shared__ __attribute__((aligned(16))) char lds2[kIdxTileBytes];
+    __shared__ __attribute__((aligned(16))) char lds3[kIdxTileBytes];
+    auto stage_pair = [&](char* b0, char* b1, int tile) __attribute__((always_inline)) {
+      idx_stage<kWaves>(b0, rsrc, s_begin + tile * kIdxKTile, s_stop);
+      if (tile + 1 < n_tiles) idx_stage<kWaves>(b1, rsrc, s_begin + (tile + 1) * kIdxKTile, s_stop);
+    };
+    auto run_pair = [&](int tile, const char* b0, const char* b1) __attribute__((always_inline)) {
+      store_held(0);
+      store_held(1);
+      compute(tile, b0, 0);
+      if (tile + 1 < n_tiles) {
+        compute(tile + 1, b1, 1);
+      } else {
+        held_s0[1] = -1;
+      }
+    };
+    stage_pair(lds0, lds1, 0);
+    for (int tile = 0; tile < n_tiles; tile += 4) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (tile + 2 < n_tiles) stage_pair(lds2, lds3, tile + 2);
+      run_pair(tile, lds0, lds1);
+      if (tile + 2 >= n_tiles) break;
+      wait_lgkmcnt0();
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (tile + 4 < n_tiles) stage_pair(lds0, lds1, tile + 4);
+      run_pair(tile + 2, lds2, lds3);
+      wait_lgkmcnt0();
+    }
+    store_held(0);
+    store_held(1);
+  } else {
+    // Decode shapes: two stages, unrolled by two so each buffer has a fixed role.
+    idx_stage<kWaves>(lds0, rsrc, s_begin, s_stop);
+    for (int tile = 0; tile < n_tiles; tile += 2) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (tile + 1 < n_tiles) idx_stage<kWaves>(lds1, rsrc, s_begin + (tile + 1) * kIdxKTile, s_stop);
+      store_held(0);
+      compute(tile, lds0, 0);
+      if (tile + 1 >= n_tiles) break;
+      wait_lgkmcnt0();
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (tile + 2 < n_tiles) idx_stage<kWaves>(lds0, rsrc, s_begin + (tile + 2) * kIdxKTile, s_stop);
+      store_held(0);
+      compute(tile + 1, lds1, 0);
+      wait_lgkmcnt0();
+    }
+    store_held(0);
   }
-  store_held();
 }
 
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
