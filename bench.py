@@ -31,6 +31,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 T_PREFILL, H, D_HCA, BLK, WIN = 32768, 64, 512, 128, 128
 HQ, D_DSA, HI, DI, TOPK = 64, 256, 4, 128, 2048
+CSA_RATIO = 4  # CSA variant: indexer keys, K and V averaged over 4 tokens
 
 
 def parse():
@@ -189,6 +190,34 @@ def main():
             torch.cuda.synchronize()
             t = timer.time(fn, n_it)
             kernels[name] = {"ms": sum(t) / len(t)}
+
+        # The CSA variant of the MLA layer over the same token-level inputs (an
+        # extra figure, not part of the step): block-4 means of k_I, K and V,
+        # then indexer, top-2048 and sparse attention over the 8192 entries.
+        progress("CSA variant")
+        S_c = T_PREFILL // CSA_RATIO
+        kci = torch.empty((1, 1, S_c, DI), dtype=torch.bfloat16, device=dev)
+        kcd = torch.empty((1, 1, S_c, D_DSA), dtype=torch.bfloat16, device=dev)
+        vcd = torch.empty_like(kcd)
+        sc_c = torch.empty((1, T_PREFILL, S_c), dtype=torch.float32, device=dev)
+        idx_c = torch.empty((1, T_PREFILL, TOPK), dtype=torch.int32, device=dev)
+
+        def csa_step():
+            sa.hca_compress(ki[:, None], CSA_RATIO, out=kci)
+            sa.hca_compress(kd[:, None], CSA_RATIO, out=kcd)
+            sa.hca_compress(vd[:, None], CSA_RATIO, out=vcd)
+            sa.csa_indexer_scores(qi, kci[:, 0], wi, CSA_RATIO, out=sc_c)
+            sa.csa_topk(sc_c, TOPK, CSA_RATIO, out=idx_c)
+            return sa.dsa_sparse_attention_fwd(qd, kcd[:, 0], vcd[:, 0], idx_c)
+
+        for _ in range(args.warmup):
+            csa_step()
+        torch.cuda.synchronize()
+        t_c = timer.time(csa_step, max(3, args.steps))
+        ms_c = sum(t_c) / len(t_c)
+        result["csa_prefill"] = {"ms_per_layer": ms_c, "tokens_per_s": T_PREFILL / (ms_c * 1e-3), "ratio": CSA_RATIO,
+                                 "entries": S_c, "top_k": TOPK}
+        del kci, kcd, vcd, sc_c, idx_c
 
         pairs_hca = hca_pairs_per_head(T_PREFILL) * H
         pairs_dsa = dsa_pairs(T_PREFILL) * HQ
@@ -370,6 +399,7 @@ def main():
             "parallelism": "single GPU",
         },
         "decode": {k_: v_ for k_, v_ in result.items() if k_.startswith("decode")},
+        "variants": {k_: v_ for k_, v_ in result.items() if k_.startswith("csa")},
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -244,6 +244,27 @@ int dsa_topk(const float* scores, const int64_t* q_pos, int32_t* idx,
              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * CSA variant: indexer and top-k over compressed entries.
+ *
+ * The pages contrast DSA with CSA, which compresses the history by 4x and
+ * keeps the top-k of the compressed entries.  Library reading: indexer keys,
+ * K and V are block means over `ratio` consecutive tokens (hca_compress with
+ * blk = ratio), and the query at token position p_i = q_pos[b] + i (or i) sees
+ * the entries s < floor((p_i + 1) / ratio) -- the blocks that end at or
+ * before the query.  csa_indexer_scores and csa_topk are dsa_indexer_scores
+ * and dsa_topk with that rule (S = number of entries; ratio = 1 is DSA); the
+ * selected entries go to dsa_sparse_attention_fwd with the compressed K, V.
+ * Supported: as the DSA calls, 1 <= ratio <= 2^20.
+ * ------------------------------------------------------------------------ */
+int csa_indexer_scores(const void* q_idx, const void* k_idx, const float* w,
+                       const int64_t* q_pos, float* scores,
+                       int64_t B, int64_t T, int64_t S, int64_t Hi, int64_t Di, int64_t ratio,
+                       hipStream_t stream);
+int csa_topk(const float* scores, const int64_t* q_pos, int32_t* idx,
+             int64_t B, int64_t T, int64_t S, int64_t k, int64_t ratio,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * dsa_sparse_attention_fwd -- exact attention over the selected positions.
  *
  * [P1] §二.1 / [P3] §架構創新 1: core attention runs only on the top-K

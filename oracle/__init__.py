@@ -42,6 +42,8 @@ from .dsa import (
     dsa_indexer_scores,
     dsa_topk,
     dsa_sparse_attention,
+    csa_attention,
+    n_candidates,
 )
 from .fp8 import (
     e4m3_value,
@@ -60,6 +62,8 @@ __all__ = [
     "dsa_indexer_scores",
     "dsa_topk",
     "dsa_sparse_attention",
+    "csa_attention",
+    "n_candidates",
     "e4m3_value",
     "e4m3_encode",
     "quantize_fp8_rows",

@@ -19,6 +19,13 @@ Readings taken where the pages are silent:
   * the index list is returned in ascending position order, padded with -1;
   * attention is multi-query: all query heads share one K and one V row per
     position; scale = 1/sqrt(D) unless given.
+
+CSA variant (the compressed alternative the pages contrast with DSA; the
+library's reading): the indexer keys, K and V are block means over `ratio`
+consecutive tokens (4 in the pages' description), and the query at token
+position t sees the compressed entries j < floor((t+1)/ratio), i.e. the blocks
+that end at or before t.  Indexer, top-k and sparse attention then run over
+compressed entries exactly as DSA runs over positions; ratio = 1 is DSA.
 """
 
 import numpy as np
@@ -28,13 +35,19 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None):
+def n_candidates(p, ratio, S):
+    """Number of keys visible to the query at token position p: keys s < floor((p+1)/ratio), at most S."""
+    return max(0, min((p + 1) // ratio, S))
+
+
+def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None, ratio=1):
     """Indexer scores for every (query, history position) pair.
 
     q_idx: [B, T, Hi, Di]; k_idx: [B, S, Di]; w: [B, T, Hi];
     q_pos: [B] position of query row 0 (row i sits at q_pos[b] + i);
-    None means row i sits at position i.
-    Returns [B, T, S] float64; entries with s > p_i (not candidates) are NaN.
+    None means row i sits at position i.  ratio: keys are entries of `ratio`
+    tokens (CSA); 1 for DSA.
+    Returns [B, T, S] float64; entries that are not candidates are NaN.
     """
     q_idx, k_idx, w = map(_f64, (q_idx, k_idx, w))
     B, T, Hi, Di = q_idx.shape
@@ -46,19 +59,19 @@ def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None):
         dots = (q_idx[b].reshape(T * Hi, Di) @ k_idx[b].T).reshape(T, Hi, S)
         score = (w[b][:, :, None] * np.maximum(dots, 0.0)).sum(axis=1)
         for i in range(T):
-            p = base + i
-            n = min(p + 1, S)
+            n = n_candidates(base + i, ratio, S)
             out[b, i, :n] = score[i, :n]
     return out
 
 
-def dsa_topk(scores, k, q_pos=None):
+def dsa_topk(scores, k, q_pos=None, ratio=1):
     """Top-k history positions per query row.
 
-    scores: [B, T, S]; row i of batch b has candidates s <= p_i with
-    p_i = q_pos[b] + i (or i).  Selection: the first min(k, p_i+1) candidates
-    in the order (score descending, position ascending).  Returned ascending,
-    padded with -1.  Output int64 [B, T, k].
+    scores: [B, T, S]; row i of batch b sits at token position
+    p_i = q_pos[b] + i (or i) and has candidates s < n_candidates(p_i, ratio, S)
+    (s <= p_i for ratio 1).  Selection: the first min(k, n) candidates in the
+    order (score descending, position ascending).  Returned ascending, padded
+    with -1.  Output int64 [B, T, k].
     """
     scores = _f64(scores)
     B, T, S = scores.shape
@@ -66,7 +79,7 @@ def dsa_topk(scores, k, q_pos=None):
     for b in range(B):
         base = 0 if q_pos is None else int(q_pos[b])
         for i in range(T):
-            n_cand = min(base + i + 1, S)
+            n_cand = n_candidates(base + i, ratio, S)
             cand = scores[b, i, :n_cand] + 0.0  # -0.0 + 0.0 == +0.0
             pos = np.arange(n_cand)
             # lexsort: last key is primary -> score descending, then position ascending
@@ -103,3 +116,20 @@ def dsa_sparse_attention(q, k, v, idx, scale=None):
             o[b, i] = (p @ v[b, sel]) / l
             lse[b, i] = (m + np.log(l))[:, 0]
     return o, lse
+
+
+def csa_attention(q_idx, k_idx, w, q, k, v, ratio, topk, scale=None):
+    """CSA forward for one layer over token-level inputs (see the module docstring).
+
+    q_idx [B,T,Hi,Di], k_idx [B,T,Di], w [B,T,Hi], q [B,T,Hq,D], k, v [B,T,D]:
+    block means over `ratio` tokens of k_idx, k and v (complete blocks only),
+    indexer scores and top-`topk` over the visible compressed entries, sparse
+    attention over the selected entries.  Returns (o, lse, idx).
+    """
+    from .hca import hca_compress
+
+    kc_idx = hca_compress(k_idx, ratio)
+    kc, vc = hca_compress(k, ratio), hca_compress(v, ratio)
+    idx = dsa_topk(dsa_indexer_scores(q_idx, kc_idx, w, ratio=ratio), topk, ratio=ratio)
+    o, lse = dsa_sparse_attention(q, kc, vc, idx, scale)
+    return o, lse, idx

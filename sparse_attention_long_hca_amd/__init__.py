@@ -9,6 +9,8 @@ from ._lib import (
     HCA_PREFILL,
     LIB_PATH,
     SparseAttnError,
+    csa_indexer_scores,
+    csa_topk,
     dsa_indexer_scores,
     dsa_sparse_attention_fwd,
     dsa_sparse_attention_fwd_workspace_size,
@@ -29,6 +31,8 @@ __all__ = [
     "HCA_PREFILL",
     "LIB_PATH",
     "SparseAttnError",
+    "csa_indexer_scores",
+    "csa_topk",
     "dsa_indexer_scores",
     "dsa_sparse_attention_fwd",
     "dsa_sparse_attention_fwd_workspace_size",

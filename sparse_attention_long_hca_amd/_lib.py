@@ -91,6 +91,8 @@ EXPORTS = {
     "hca_decode_fp8_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HcaDecodeFp8Args)]),
     "hca_decode_fp8": (ctypes.c_int, [ctypes.POINTER(HcaDecodeFp8Args), _c_p]),
     "dsa_indexer_scores": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p] + [_c_i64] * 5 + [_c_p]),
+    "csa_indexer_scores": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p] + [_c_i64] * 6 + [_c_p]),
+    "csa_topk": (ctypes.c_int, [_c_p, _c_p, _c_p] + [_c_i64] * 5 + [_c_p, ctypes.c_size_t, _c_p]),
     "dsa_topk_workspace_size": (ctypes.c_size_t, [_c_i64] * 4),
     "dsa_topk": (ctypes.c_int, [_c_p, _c_p, _c_p] + [_c_i64] * 4 + [_c_p, ctypes.c_size_t, _c_p]),
     "dsa_sparse_attention_fwd_workspace_size": (ctypes.c_size_t, [_c_i64] * 5),
@@ -309,6 +311,47 @@ def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None, out=None):
     _check(
         "dsa_indexer_scores",
         lib().dsa_indexer_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q_pos), _ptr(out), B, T, S, Hi, Di, _stream()),
+    )
+    return out
+
+
+def csa_indexer_scores(q_idx, kc_idx, w, ratio, q_pos=None, out=None):
+    """CSA indexer: q_idx [B,T,Hi,Di] bf16 (token rows), kc_idx [B,S,Di] bf16 (entries of `ratio` tokens),
+    w [B,T,Hi] f32 -> scores [B,T,S] f32 (row i sees entries s < (q_pos + i + 1) // ratio)."""
+    _need(q_idx, "q_idx", torch.bfloat16, 4)
+    _need(kc_idx, "kc_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 3)
+    B, T, Hi, Di = q_idx.shape
+    S = kc_idx.shape[1]
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int64, 1)
+    if out is None:
+        out = torch.empty((B, T, S), dtype=torch.float32, device=q_idx.device)
+    _need(out, "out", torch.float32, 3)
+    _check(
+        "csa_indexer_scores",
+        lib().csa_indexer_scores(_ptr(q_idx), _ptr(kc_idx), _ptr(w), _ptr(q_pos), _ptr(out), B, T, S, Hi, Di, ratio,
+                                 _stream()),
+    )
+    return out
+
+
+def csa_topk(scores, k, ratio, q_pos=None, out=None, workspace=None):
+    """CSA top-k: scores [B,T,S] f32 over entries of `ratio` tokens -> idx [B,T,k] int32."""
+    _need(scores, "scores", torch.float32, 3)
+    B, T, S = scores.shape
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int64, 1)
+    if out is None:
+        out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
+    _need(out, "out", torch.int32, 3)
+    need = lib().dsa_topk_workspace_size(B, T, S, k)
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(
+        "csa_topk",
+        lib().csa_topk(_ptr(scores), _ptr(q_pos), _ptr(out), B, T, S, k, ratio, _ptr(workspace), wsb, _stream()),
     )
     return out
 

@@ -204,19 +204,31 @@ int hca_decode_fp8(const hca_decode_fp8_args* a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
+static int indexer_impl(const char* fn, const void* q_idx, const void* k_idx, const float* w, const int64_t* q_pos,
+                        float* scores, int64_t B, int64_t T, int64_t S, int64_t Hi, int64_t Di, int64_t ratio,
+                        hipStream_t stream) {
+  if (!q_idx || !k_idx || !w || !scores) return fail(SA_ERR_NULL, "%s: q_idx, k_idx, w, scores must be non-NULL", fn);
+  if (B <= 0 || T <= 0 || S <= 0 || Hi <= 0 || Di <= 0) return fail(SA_ERR_SHAPE, "%s: sizes must be > 0", fn);
+  if (ratio < 1 || ratio > ((int64_t)1 << 20)) return fail(SA_ERR_SHAPE, "%s: ratio must be in [1, 2^20]", fn);
+  if (Hi != 4 || Di != 128) return fail(SA_ERR_UNSUPPORTED, "%s: supported Hi = 4, Di = 128", fn);
+  if (S > ((int64_t)1 << 24) || T >= ((int64_t)1 << 31))
+    return fail(SA_ERR_UNSUPPORTED, "%s: S must be <= 2^24 and T < 2^31", fn);
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w) || !aligned16(scores))
+    return fail(SA_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  const int64_t nblocks = B * ((T + 63) / 64) * ((S + 1023) / 1024);
+  if (nblocks > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "%s: grid too large", fn);
+  sa::DsaIndexerParams p{q_idx, k_idx, w, q_pos, scores, B, T, S, ratio};
+  return hip_status(sa::launch_dsa_indexer(p, stream), fn);
+}
+
 int dsa_indexer_scores(const void* q_idx, const void* k_idx, const float* w, const int64_t* q_pos, float* scores,
                        int64_t B, int64_t T, int64_t S, int64_t Hi, int64_t Di, hipStream_t stream) {
-  if (!q_idx || !k_idx || !w || !scores) return fail(SA_ERR_NULL, "dsa_indexer_scores: q_idx, k_idx, w, scores must be non-NULL");
-  if (B <= 0 || T <= 0 || S <= 0 || Hi <= 0 || Di <= 0) return fail(SA_ERR_SHAPE, "dsa_indexer_scores: sizes must be > 0");
-  if (Hi != 4 || Di != 128) return fail(SA_ERR_UNSUPPORTED, "dsa_indexer_scores: supported Hi = 4, Di = 128");
-  if (S > ((int64_t)1 << 24) || T >= ((int64_t)1 << 31))
-    return fail(SA_ERR_UNSUPPORTED, "dsa_indexer_scores: S must be <= 2^24 and T < 2^31");
-  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w) || !aligned16(scores))
-    return fail(SA_ERR_ALIGN, "dsa_indexer_scores: pointers must be 16-byte aligned");
-  const int64_t nblocks = B * ((T + 63) / 64) * ((S + 1023) / 1024);
-  if (nblocks > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "dsa_indexer_scores: grid too large");
-  sa::DsaIndexerParams p{q_idx, k_idx, w, q_pos, scores, B, T, S};
-  return hip_status(sa::launch_dsa_indexer(p, stream), "dsa_indexer_scores launch");
+  return indexer_impl("dsa_indexer_scores", q_idx, k_idx, w, q_pos, scores, B, T, S, Hi, Di, 1, stream);
+}
+
+int csa_indexer_scores(const void* q_idx, const void* k_idx, const float* w, const int64_t* q_pos, float* scores,
+                       int64_t B, int64_t T, int64_t S, int64_t Hi, int64_t Di, int64_t ratio, hipStream_t stream) {
+  return indexer_impl("csa_indexer_scores", q_idx, k_idx, w, q_pos, scores, B, T, S, Hi, Di, ratio, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -225,25 +237,36 @@ size_t dsa_topk_workspace_size(int64_t B, int64_t T, int64_t S, int64_t k) {
   return sa::dsa_topk_ws_bytes(B, T, S, k);
 }
 
-int dsa_topk(const float* scores, const int64_t* q_pos, int32_t* idx, int64_t B, int64_t T, int64_t S, int64_t k,
-             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!scores || !idx) return fail(SA_ERR_NULL, "dsa_topk: scores and idx must be non-NULL");
-  if (B <= 0 || T <= 0 || S <= 0 || k <= 0) return fail(SA_ERR_SHAPE, "dsa_topk: sizes must be > 0");
-  if (k > 2048) return fail(SA_ERR_UNSUPPORTED, "dsa_topk: k must be <= 2048");
-  if (S >= (int64_t)1 << 31) return fail(SA_ERR_UNSUPPORTED, "dsa_topk: S must be < 2^31");
-  if (!aligned16(scores) || !aligned16(idx)) return fail(SA_ERR_ALIGN, "dsa_topk: pointers must be 16-byte aligned");
-  if (B * T > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "dsa_topk: too many rows");
+static int topk_impl(const char* fn, const float* scores, const int64_t* q_pos, int32_t* idx, int64_t B, int64_t T,
+                     int64_t S, int64_t k, int64_t ratio, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!scores || !idx) return fail(SA_ERR_NULL, "%s: scores and idx must be non-NULL", fn);
+  if (B <= 0 || T <= 0 || S <= 0 || k <= 0) return fail(SA_ERR_SHAPE, "%s: sizes must be > 0", fn);
+  if (ratio < 1 || ratio > ((int64_t)1 << 20)) return fail(SA_ERR_SHAPE, "%s: ratio must be in [1, 2^20]", fn);
+  if (k > 2048) return fail(SA_ERR_UNSUPPORTED, "%s: k must be <= 2048", fn);
+  if (S >= (int64_t)1 << 31) return fail(SA_ERR_UNSUPPORTED, "%s: S must be < 2^31", fn);
+  if (!aligned16(scores) || !aligned16(idx)) return fail(SA_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  if (B * T > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "%s: too many rows", fn);
   const size_t need = sa::dsa_topk_ws_bytes(B, T, S, k);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
-      return fail(SA_ERR_WORKSPACE, "dsa_topk: needs %zu workspace bytes, got %zu", need,
+      return fail(SA_ERR_WORKSPACE, "%s: needs %zu workspace bytes, got %zu", fn, need,
                   workspace ? workspace_bytes : (size_t)0);
-    if (!aligned16(workspace)) return fail(SA_ERR_ALIGN, "dsa_topk: workspace must be 16-byte aligned");
-    const int64_t nchunk = (S + 16383) / 16384;
-    if (B * T * nchunk > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "dsa_topk: grid too large");
+    if (!aligned16(workspace)) return fail(SA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+    const int64_t nchunk = (S + 4095) / 4096;  // chunk size of the multi-workgroup path
+    if (B * T * nchunk > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "%s: grid too large", fn);
   }
-  sa::DsaTopkParams p{scores, q_pos, idx, B, T, S, k, workspace};
-  return hip_status(sa::launch_dsa_topk(p, stream), "dsa_topk launch");
+  sa::DsaTopkParams p{scores, q_pos, idx, B, T, S, k, workspace, ratio};
+  return hip_status(sa::launch_dsa_topk(p, stream), fn);
+}
+
+int dsa_topk(const float* scores, const int64_t* q_pos, int32_t* idx, int64_t B, int64_t T, int64_t S, int64_t k,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return topk_impl("dsa_topk", scores, q_pos, idx, B, T, S, k, 1, workspace, workspace_bytes, stream);
+}
+
+int csa_topk(const float* scores, const int64_t* q_pos, int32_t* idx, int64_t B, int64_t T, int64_t S, int64_t k,
+             int64_t ratio, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return topk_impl("csa_topk", scores, q_pos, idx, B, T, S, k, ratio, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

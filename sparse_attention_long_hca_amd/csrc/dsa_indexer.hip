@@ -75,9 +75,18 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
 
   const int T = (int)p.T, S = (int)p.S;
   const int base = p.q_pos ? (int)p.q_pos[b] : 0;
+  // Last key visible to query row qi (token position base + qi): keys are
+  // entries of `ratio` tokens (1 = positions) and entry s is visible iff its
+  // block ends at or before the query, s < (base + qi + 1) / ratio.  -1 or
+  // less: nothing visible.
+  const int64_t ratio = p.ratio;
+  auto lim = [&](int qi) -> int {
+    const int64_t x = ((int64_t)base + qi + 1) / ratio - 1;
+    return (int)(x < S - 1 ? x : S - 1);
+  };
   const int i0 = qt * kQTile;
   const int i_last = min(i0 + kQTile - 1, T - 1);
-  const int s_end = min(S, base + i_last + 1);  // exclusive, whole workgroup
+  const int s_end = min(S, lim(i_last) + 1);  // exclusive, whole workgroup
   const int s_begin = kc * kIdxChunk;
   if (s_begin >= s_end) return;
   const int s_stop = min(s_end, s_begin + kIdxChunk);
@@ -87,7 +96,7 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   const int L = lane & 15, g = lane >> 4;
   const int iw = i0 + wave * kIdxQPerWave;                  // first query of the wave
   const int n_mb = max(0, min(4, (T - iw + 3) / 4));          // M-blocks with a valid query
-  const int wave_plim = n_mb > 0 ? min(base + min(iw + kIdxQPerWave - 1, T - 1), S - 1) : -1;
+  const int wave_plim = n_mb > 0 ? lim(min(iw + kIdxQPerWave - 1, T - 1)) : -1;
 
   const bf16_t* qI = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * T * kIdxHi * kIdxDi;
   const bf16_t* kI = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * S * kIdxDi;
@@ -115,7 +124,7 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
     const bool vc = mb < n_mb && qc_i < T;
 #pragma unroll
     for (int h = 0; h < 4; ++h) wq[mb][h] = vc ? wgt[(int64_t)qc_i * kIdxHi + h] : 0.f;
-    plim[mb] = vc ? min(base + qc_i, S - 1) : -1;
+    plim[mb] = vc ? lim(qc_i) : -1;
   }
 
   // Scores of earlier tiles, held in registers and stored after the next
@@ -126,7 +135,7 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   int held_s0[2] = {-1, -1};  // first position of the held tile (-1: nothing held)
   // Every position of a tile is visible to every query of the wave when the
   // tile ends at or before the first query's limit (all 16 queries valid).
-  const int wave_full_lim = n_mb == 4 ? min(base + iw, S - 1) : -1;
+  const int wave_full_lim = n_mb == 4 ? lim(iw) : -1;
   auto store_held = [&](int slot) __attribute__((always_inline)) {
     const int h0 = held_s0[slot];
     if (h0 < 0) return;

@@ -39,9 +39,11 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Candidates of row i: keys s < (base + i + 1) / ratio (positions s <= base + i
+// for ratio 1), at most S.
 __device__ __forceinline__ int64_t row_len(const DsaTopkParams& p, int64_t b, int64_t i) {
   const int64_t base = p.q_pos ? p.q_pos[b] : 0;
-  int64_t n = base + i + 1;
+  int64_t n = (base + i + 1) / p.ratio;
   if (n > p.S) n = p.S;
   if (n < 0) n = 0;
   return n;
@@ -863,12 +865,14 @@ hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream) {
       hipLaunchKernelGGL(dsa_topk_reg_kernel<512>, dim3((uint32_t)rows), dim3(512), 0, stream, p, (int64_t)0, p.T);
       return hipGetLastError();
     }
-    // Causal rows from position 0: row i holds min(i + 1, S) positions, so
-    // the rows that fit a smaller workgroup (kThreads * 64 positions) form
-    // contiguous ranges, one launch each.
+    // Causal rows from position 0: row i holds min((i + 1) / ratio, S)
+    // candidates, so the rows that fit a smaller workgroup (cap = kThreads * 64
+    // candidates, i.e. i < (cap + 1) * ratio - 1) form contiguous ranges, one
+    // launch each.
     auto run = [&](auto threads_tag, int64_t& i0) {
       constexpr int kThreads = decltype(threads_tag)::value;
-      const int64_t i1 = kThreads == 512 ? p.T : std::min<int64_t>(p.T, (int64_t)kThreads * kRegVec * 4);
+      const int64_t cap = (int64_t)kThreads * kRegVec * 4;
+      const int64_t i1 = kThreads == 512 ? p.T : std::min<int64_t>(p.T, (cap + 1) * p.ratio - 1);
       if (i1 > i0) {
         hipLaunchKernelGGL(dsa_topk_reg_kernel<kThreads>, dim3((uint32_t)(p.B * (i1 - i0))), dim3(kThreads), 0,
                            stream, p, i0, i1 - i0);

@@ -74,6 +74,7 @@ struct DsaIndexerParams {
   const int64_t* q_pos;
   float* scores;  // [B,T,S]
   int64_t B, T, S;
+  int64_t ratio;  // keys are entries of `ratio` tokens: row i sees keys s < (q_pos + i + 1) / ratio
 };
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream);
 
@@ -84,6 +85,7 @@ struct DsaTopkParams {
   int32_t* idx;
   int64_t B, T, S, k;
   void* ws;
+  int64_t ratio;  // as in DsaIndexerParams
 };
 size_t dsa_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k);
 hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream);

@@ -387,6 +387,67 @@ def pin_dsa_end_to_end_k_ge_context_is_dense():
 
 
 # ---------------------------------------------------------------------------
+# CSA variant: DSA over block-mean compressed entries
+# ---------------------------------------------------------------------------
+def pin_csa_bruteforce():
+    """Tiny CSA layer written out from the reading with plain loops: block means of 4 tokens,
+    entry j visible to token t iff its block ends at or before t (4j+3 <= t), scores, top-k by
+    (score desc, entry asc), softmax over the selected entries."""
+    rng = _rng(41)
+    T, r, Hi, Di, Hq, D, kk = 23, 4, 2, 4, 3, 8, 3
+    qi, ki, w = rng.standard_normal((1, T, Hi, Di)), rng.standard_normal((1, T, Di)), rng.random((1, T, Hi))
+    q, k, v = rng.standard_normal((1, T, Hq, D)), rng.standard_normal((1, T, D)), rng.standard_normal((1, T, D))
+    o, lse, idx = oracle.csa_attention(qi, ki, w, q, k, v, r, kk)
+    nb = T // r
+    mean = lambda x, j: sum(x[0, r * j + u] for u in range(r)) / r
+    kci = [mean(ki, j) for j in range(nb)]
+    kc = [mean(k, j) for j in range(nb)]
+    vc = [mean(v, j) for j in range(nb)]
+    for t in range(T):
+        vis = [j for j in range(nb) if r * j + r - 1 <= t]
+        sc = {j: sum(w[0, t, h] * max(0.0, float(qi[0, t, h] @ kci[j])) for h in range(Hi)) for j in vis}
+        sel = sorted(sorted(vis, key=lambda j: (-sc[j], j))[:kk])
+        assert list(idx[0, t][idx[0, t] >= 0]) == sel, (t, idx[0, t], sel)
+        for h in range(Hq):
+            if not sel:
+                assert np.all(o[0, t, h] == 0) and lse[0, t, h] == -np.inf
+                continue
+            logits = np.array([q[0, t, h] @ kc[j] / math.sqrt(D) for j in sel])
+            p_ = np.exp(logits - logits.max())
+            want = sum(p_[n] * vc[j] for n, j in enumerate(sel)) / p_.sum()
+            _close(o[0, t, h], want, 1e-12, "CSA output")
+            _close(lse[0, t, h], logits.max() + math.log(p_.sum()), 1e-12, "CSA lse")
+
+
+def pin_csa_ratio_one_is_dsa():
+    """ratio 1: block means of one token are the tokens, and the visible set is s <= t."""
+    rng = _rng(42)
+    T, Hi, Di, Hq, D, kk = 19, 2, 4, 2, 8, 5
+    qi, ki, w = rng.standard_normal((1, T, Hi, Di)), rng.standard_normal((1, T, Di)), rng.random((1, T, Hi))
+    q, k, v = rng.standard_normal((1, T, Hq, D)), rng.standard_normal((1, T, D)), rng.standard_normal((1, T, D))
+    o, lse, idx = oracle.csa_attention(qi, ki, w, q, k, v, 1, kk)
+    idx_d = oracle.dsa_topk(oracle.dsa_indexer_scores(qi, ki, w), kk)
+    assert np.array_equal(idx, idx_d)
+    o_d, lse_d = oracle.dsa_sparse_attention(q, k, v, idx_d)
+    _close(o, o_d, 1e-12, "ratio 1 output")
+
+
+def pin_indexer_ratio_rows_are_single_query_calls():
+    """Row t of the ratio-4 scores equals a one-query DSA call whose last position is its last visible entry."""
+    rng = _rng(43)
+    T, S, Hi, Di = 30, 7, 2, 4
+    qi, ki, w = rng.standard_normal((1, T, Hi, Di)), rng.standard_normal((1, S, Di)), rng.random((1, T, Hi))
+    sc = oracle.dsa_indexer_scores(qi, ki, w, ratio=4)
+    for t in range(T):
+        n = min((t + 1) // 4, S)
+        assert np.all(np.isnan(sc[0, t, n:])), t
+        if n == 0:
+            continue
+        one = oracle.dsa_indexer_scores(qi[:, t:t + 1], ki, w[:, t:t + 1], q_pos=[n - 1])
+        _close(sc[0, t, :n], one[0, 0, :n], 0.0, f"row {t}")
+
+
+# ---------------------------------------------------------------------------
 # FP8 (OCP E4M3 "fn") decode cache -- the library's own format reading
 # ---------------------------------------------------------------------------
 def _torch_e4m3_decode(codes):

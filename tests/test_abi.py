@@ -195,3 +195,13 @@ def test_decode_fp8_workspace_matches_bf16_decode(sa):
     b = _hca_args(mode=1, B=4, H=64, n_c_cap=8192)
     assert sa.lib().hca_decode_fp8_workspace_size(ctypes.byref(a)) == sa.lib().hca_attention_fwd_workspace_size(
         ctypes.byref(b)) > 0
+
+
+def test_csa_validation(sa):
+    L = sa.lib()
+    assert L.csa_indexer_scores(4096, 4096, 4096, None, 4096, 1, 4, 4, 4, 128, 0, None) == SA_ERR_SHAPE
+    assert L.csa_indexer_scores(None, 4096, 4096, None, 4096, 1, 4, 4, 4, 128, 4, None) == SA_ERR_NULL
+    assert L.csa_indexer_scores(4096, 4096, 4096, None, 4096, 1, 4, 4, 8, 128, 4, None) == SA_ERR_UNSUPPORTED
+    assert L.csa_topk(4096, None, 4096, 1, 4, 4, 2, 0, None, 0, None) == SA_ERR_SHAPE
+    assert L.csa_topk(None, None, 4096, 1, 4, 4, 2, 4, None, 0, None) == SA_ERR_NULL
+    assert L.csa_topk(4096, None, 4096, 4, 1, 1 << 20, 2048, 4, None, 0, None) == SA_ERR_WORKSPACE

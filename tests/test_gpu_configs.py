@@ -167,6 +167,37 @@ def test_dsa_prefill_32768_top2048(sigma):
         assert max_abs_err(f64(lse[:, i:i + 1]), lw) <= 1e-2, i
 
 
+def test_csa_prefill_32768_ratio4_top2048():
+    """CSA variant at the DSA prefill's size: block-4 means (8192 entries), indexer, top-2048 and sparse
+    attention on the GPU; sampled rows against the oracle (scores within fp32 rounding, selection
+    bit-exact on the GPU's scores, attention on the GPU's entries and cache within 2e-2)."""
+    sa = require_gpu()
+    T, ratio, kk = 32768, 4, 2048
+    S = T // ratio
+    qi, ki, w, q, k, v = _dsa_inputs(1, T, T, 1.0, 1600)
+    kci = sa.hca_compress(ki[:, None], ratio)[:, 0].contiguous()
+    kc = sa.hca_compress(k[:, None], ratio)[:, 0].contiguous()
+    vc = sa.hca_compress(v[:, None], ratio)[:, 0].contiguous()
+    sc = sa.csa_indexer_scores(qi, kci, w, ratio)
+    idx = sa.csa_topk(sc, kk, ratio)
+    o, lse = sa.dsa_sparse_attention_fwd(q, kc, vc, idx, return_lse=True)
+    torch.cuda.synchronize()
+    kci_h, kc_h, vc_h = f64(kci), f64(kc), f64(vc)
+    rows = [0, 3, 8194, 8195, 20000, T - 1] + [int(x) for x in np.random.default_rng(1601).integers(8196, T, size=4)]
+    for i in rows:
+        n = oracle.n_candidates(i, ratio, S)
+        if n == 0:  # no complete block yet: nothing selected, o = 0
+            assert (idx[0, i] == -1).all() and (o[0, i] == 0).all(), i
+            continue
+        want_sc = oracle.dsa_indexer_scores(f64(qi[:, i:i + 1]), kci_h[:, :n], f64(w[:, i:i + 1]), q_pos=[n - 1])[0, 0]
+        sc_row = sc[0, i, :n].cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(sc_row - want_sc)) <= 2e-6, i
+        got_idx = idx[0, i].cpu().numpy().astype(np.int64)
+        assert np.array_equal(got_idx, oracle.dsa_topk(sc_row.reshape(1, 1, -1), kk, q_pos=[n - 1])[0, 0]), i
+        ow, lw = oracle.dsa_sparse_attention(f64(q[:, i:i + 1]), kc_h, vc_h, got_idx.reshape(1, 1, -1))
+        assert max_abs_err(f64(o[:, i:i + 1]), ow) <= BF16_ABS_TOL, i
+
+
 def test_dsa_decode_1m():
     sa = require_gpu()
     B, S, kk = 4, 1 << 20, 2048

@@ -275,3 +275,87 @@ def test_dsa_end_to_end_k_ge_context_is_dense():
     assert np.array_equal(idx.cpu().numpy(), dense)
     ow, _ = oracle.dsa_sparse_attention(q, k, v, dense)
     assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL
+
+
+# ---------------------------------------------------------------------------
+# CSA variant: indexer, top-k and sparse attention over block-mean entries
+# ---------------------------------------------------------------------------
+
+
+def _csa_mask(B, T, S, q_pos, ratio):
+    m = np.zeros((B, T, S), dtype=bool)
+    for b in range(B):
+        base = 0 if q_pos is None else q_pos[b]
+        for i in range(T):
+            m[b, i, : oracle.n_candidates(base + i, ratio, S)] = True
+    return m
+
+
+@pytest.mark.parametrize("B,T,ratio,q_pos,kk", [(1, 700, 4, None, 64), (2, 130, 2, [400, 0], 100),
+                                                (1, 300, 16, [2000], 8), (1, 1, 4, [5003], 2048),
+                                                (1, 9, 4, None, 4)])
+def test_csa_indexer_and_topk(B, T, ratio, q_pos, kk):
+    """GPU CSA scores within fp32 rounding of the oracle, only over visible entries; GPU top-k on those
+    scores bit-exact against the oracle's selection rule with the same ratio."""
+    sa = require_gpu()
+    L = T + (0 if q_pos is None else max(q_pos))
+    S = L // ratio
+    qi, ki_tok, w = _indexer_inputs(B, T, L, 60 + T + ratio)
+    ki_tok = ki_tok[:, : S * ratio]
+    kc = sa.hca_compress(synth.to_torch(ki_tok, "bf16", DEV)[:, None], ratio)[:, 0]
+    qp = None if q_pos is None else torch.tensor(q_pos, dtype=torch.int64, device=DEV)
+    sc = sa.csa_indexer_scores(synth.to_torch(qi, "bf16", DEV), kc.contiguous(), synth.to_torch(w, "f32", DEV),
+                               ratio, q_pos=qp)
+    want = oracle.dsa_indexer_scores(qi, f64(kc), w, q_pos=q_pos, ratio=ratio)
+    m = _csa_mask(B, T, S, q_pos, ratio)
+    assert np.array_equal(np.isfinite(want), m)
+    assert np.max(np.abs(f64(sc)[m] - want[m]), initial=0.0) <= 2e-6
+    idx = sa.csa_topk(sc, kk, ratio, q_pos=qp)
+    sc_np = np.where(m, sc.cpu().numpy(), np.nan)
+    assert np.array_equal(idx.cpu().numpy(), oracle.dsa_topk(sc_np, kk, q_pos=q_pos, ratio=ratio))
+
+
+def test_csa_layer():
+    """Whole CSA layer on the GPU (block-4 means of k_I, K, V; indexer; top-k; sparse attention)
+    against the oracle: selection bit-exact on the GPU's scores, attention on the GPU's entries and
+    cache within 2e-2, and the rows that see no complete block give o = 0, lse = -inf."""
+    sa = require_gpu()
+    B, T, ratio, kk = 1, 900, 4, 128
+    qi, ki, w = _indexer_inputs(B, T, T, 70)
+    q = synth.np_normal((B, T, 64, 256), 1.0, "bf16", 71, 0)
+    k = synth.np_normal((B, T, 256), 1.0, "bf16", 71, 1)
+    v = synth.np_normal((B, T, 256), 1.0, "bf16", 71, 2)
+    t = {n: synth.to_torch(a, "bf16", DEV) for n, a in (("ki", ki), ("q", q), ("k", k), ("v", v))}
+    kci = sa.hca_compress(t["ki"][:, None], ratio)[:, 0].contiguous()
+    kc = sa.hca_compress(t["k"][:, None], ratio)[:, 0].contiguous()
+    vc = sa.hca_compress(t["v"][:, None], ratio)[:, 0].contiguous()
+    sc = sa.csa_indexer_scores(synth.to_torch(qi, "bf16", DEV), kci, synth.to_torch(w, "f32", DEV), ratio)
+    idx = sa.csa_topk(sc, kk, ratio)
+    o, lse = sa.dsa_sparse_attention_fwd(t["q"], kc, vc, idx, return_lse=True)
+    S = T // ratio
+    m = _csa_mask(B, T, S, None, ratio)
+    sc_np = np.where(m, sc.cpu().numpy(), np.nan)
+    got_idx = idx.cpu().numpy().astype(np.int64)
+    assert np.array_equal(got_idx, oracle.dsa_topk(sc_np, kk, ratio=ratio))
+    ow, lw = oracle.dsa_sparse_attention(q, f64(kc), f64(vc), got_idx)
+    assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL
+    fin = np.isfinite(lw)
+    assert np.array_equal(fin, np.isfinite(f64(lse)))
+    assert np.max(np.abs(f64(lse)[fin] - lw[fin])) <= 1e-2
+    assert not fin[0, : ratio - 1].any() and fin[0, ratio - 1:].all()
+
+
+def test_csa_topk_causal_row_classes():
+    """Long causal CSA rows: with ratio 4 the rows split over the workgroup sizes at entry counts
+    8192 and 16384, i.e. token rows 32767 and 65539; rows on both sides of the first cut."""
+    sa = require_gpu()
+    T, ratio, k = 40000, 4, 2048
+    S = T // ratio
+    sc = synth.torch_normal((1, T, S), 1.0, torch.float32, 72, DEV)
+    idx = sa.csa_topk(sc, k, ratio)
+    torch.cuda.synchronize()
+    for i in [0, 2, 3, 8194, 8195, 20000, 32766, 32767, 32768, T - 1]:
+        n = oracle.n_candidates(i, ratio, S)
+        row = sc[0, i, :n].cpu().numpy()
+        want = oracle.dsa_topk(row.reshape(1, 1, -1), k, q_pos=[n - 1])[0, 0] if n > 0 else np.full(k, -1)
+        assert np.array_equal(idx[0, i].cpu().numpy(), want), i

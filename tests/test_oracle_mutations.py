@@ -90,6 +90,10 @@ def _mut_e4m3_ties_away(x):
     return (sign | (8 * (e + 7) + (n.astype(np.int64) - 8))).astype(np.uint8)
 
 
+def _mut_csa_partial_block_visible(p, ratio, S):
+    return max(0, min(-(-(p + 1) // ratio), S))
+
+
 def _mut_quantize_scale_inverted(x):
     codes, scales = _orig_quantize(x)
     with np.errstate(divide="ignore"):
@@ -168,6 +172,7 @@ MUTATIONS = {
     "e4m3_truncate": (ofp8, "e4m3_encode", _mut_e4m3_truncate),
     "e4m3_ties_away": (ofp8, "e4m3_encode", _mut_e4m3_ties_away),
     "quantize_scale_inverted": (ofp8, "quantize_fp8_rows", _mut_quantize_scale_inverted),
+    "csa_partial_block_visible": (odsa, "n_candidates", _mut_csa_partial_block_visible),
 }
 
 
