@@ -17,6 +17,11 @@ function that uses it):
     block that straddles t-W and lie outside the window are seen by neither;
   * one softmax over the union of both key sets, logits scale*<q, key> with
     scale = 1/sqrt(d) unless given; no sink, bias or gate.
+
+Head shapes.  The plain shape has q, k, v all d = 512 wide.  [P3] §預訓練資料工程
+item 3 (FlashMask-4) names a wider query/key head than value head, qk 576 and
+v 512; every function here takes the query/key width from q and the value
+width from v, and the default scale is 1/sqrt(query/key width).
 """
 
 import numpy as np
@@ -69,7 +74,7 @@ def hca_key_set(t, blk, window, n_entries=None):
 def _attend(q, keys, vals, scale):
     """One softmax over the given keys for a batch of heads.
 
-    q: [H, d]; keys, vals: [H, n, d].  Returns (o [H, d], lse [H]).
+    q: [H, d]; keys: [H, n, d]; vals: [H, n, dv].  Returns (o [H, dv], lse [H]).
     lse is the natural-log normaliser of the scaled logits.
     """
     logits = scale * np.einsum("hd,hnd->hn", q, keys)
@@ -88,17 +93,19 @@ def hca_attention_prefill(q, k, v, kc, vc, blk, window, scale=None, rows=None):
     the most recent uncompressed tokens.  [P3] §架構創新 1: the query attends
     to all compressed history entries and the short recent window.
 
-    q, k, v: [B, H, T, d]; kc, vc: [B, H, Nc, d] (the compressed cache; for the
-    plain method Nc = T // blk and kc = hca_compress(k, blk)).
+    q, k: [B, H, T, d]; v: [B, H, T, dv]; kc: [B, H, Nc, d], vc: [B, H, Nc, dv]
+    (the compressed cache; for the plain method Nc = T // blk and
+    kc = hca_compress(k, blk)).  dv may be smaller than d (qk 576 / v 512).
     rows: iterable of query positions (default: all of 0..T-1).
-    Returns (o [B, H, len(rows), d], lse [B, H, len(rows)]) in float64.
+    Returns (o [B, H, len(rows), dv], lse [B, H, len(rows)]) in float64.
     """
     q, k, v, kc, vc = map(_f64, (q, k, v, kc, vc))
     B, H, T, d = q.shape
+    dv = v.shape[-1]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     rows = list(range(T)) if rows is None else [int(t) for t in rows]
-    o = np.zeros((B, H, len(rows), d))
+    o = np.zeros((B, H, len(rows), dv))
     lse = np.zeros((B, H, len(rows)))
     for b in range(B):
         for r, t in enumerate(rows):
@@ -117,14 +124,16 @@ def hca_attention_decode(q, kc, vc, ring_k, ring_v, pos, blk, window, scale=None
     t-window < s <= t read from a ring buffer of ``window`` slots where
     position s lives in slot s mod window.
 
-    q: [B, H, d]; kc, vc: [B, H, Nc, d]; ring_k, ring_v: [B, H, window, d].
-    Returns (o [B, H, d], lse [B, H]).
+    q: [B, H, d]; kc: [B, H, Nc, d]; vc: [B, H, Nc, dv]; ring_k: [B, H, window, d];
+    ring_v: [B, H, window, dv].
+    Returns (o [B, H, dv], lse [B, H]).
     """
     q, kc, vc, ring_k, ring_v = map(_f64, (q, kc, vc, ring_k, ring_v))
     B, H, d = q.shape
+    dv = vc.shape[-1]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
-    o = np.zeros((B, H, d))
+    o = np.zeros((B, H, dv))
     lse = np.zeros((B, H))
     for b in range(B):
         t = int(pos[b])

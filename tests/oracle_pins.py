@@ -235,6 +235,43 @@ def pin_hca_head_permutation():
     _close(op, o[:, perm], 1e-14, "head permutation")
 
 
+def _sdpa_causal_dv(q, k, v):
+    """torch CPU float64 SDPA with a value width different from the query/key width (scale 1/sqrt(qk width))."""
+    return _sdpa_causal(q, k, v)
+
+
+def pin_hca_wide_qk_dense():
+    """qk wider than v (the 576/512 shape, scaled down): blk = 1 and window >= T reduce to dense causal
+    attention, checked against torch's SDPA, which scales by 1/sqrt(query width) and allows Ev != E."""
+    rng = _rng(44)
+    B, H, T, dk, dv = 1, 2, 21, 12, 8
+    q, k = rng.standard_normal((B, H, T, dk)), rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv))
+    want = _sdpa_causal_dv(q, k, v)
+    assert want.shape == (B, H, T, dv)
+    for blk, window in ((1, 1), (1, 5), (4, T), (8, T + 3)):
+        o, _ = oracle.hca_attention_prefill(q, k, v, oracle.hca_compress(k, blk), oracle.hca_compress(v, blk), blk, window)
+        _close(o, want, 1e-12, f"wide qk blk={blk} window={window}")
+
+
+def pin_hca_wide_qk_decode_equals_prefill_row():
+    """Decode with qk wider than v equals the prefill row at the same position."""
+    rng = _rng(45)
+    B, H, T, dk, dv, blk, window = 2, 2, 29, 10, 6, 4, 5
+    q, k = rng.standard_normal((B, H, T, dk)), rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv))
+    kc, vc = oracle.hca_compress(k, blk), oracle.hca_compress(v, blk)
+    for t in (0, 4, 9, 17, 28):
+        o_pre, lse_pre = oracle.hca_attention_prefill(q, k, v, kc, vc, blk, window, rows=[t])
+        ring_k, ring_v = np.zeros((B, H, window, dk)), np.zeros((B, H, window, dv))
+        for s_ in range(max(0, t - window + 1), t + 1):
+            ring_k[:, :, s_ % window] = k[:, :, s_]
+            ring_v[:, :, s_ % window] = v[:, :, s_]
+        o_dec, lse_dec = oracle.hca_attention_decode(q[:, :, t], kc, vc, ring_k, ring_v, [t] * B, blk, window)
+        _close(o_dec, o_pre[:, :, 0], 1e-12, f"wide qk decode t={t}")
+        _close(lse_dec, lse_pre[:, :, 0], 1e-12, f"wide qk decode lse t={t}")
+
+
 # ---------------------------------------------------------------------------
 # DSA indexer
 # ---------------------------------------------------------------------------

@@ -100,6 +100,23 @@ def _mut_quantize_scale_inverted(x):
         return codes, np.where(scales > 0, np.float32(1) / scales, 0).astype(np.float32)
 
 
+_orig_prefill = ohca.hca_attention_prefill
+
+
+def _mut_prefill_scale_from_v(q, k, v, kc, vc, blk, window, scale=None, rows=None):
+    if scale is None:
+        scale = 1.0 / np.sqrt(np.shape(v)[-1])
+    return _orig_prefill(q, k, v, kc, vc, blk, window, scale, rows)
+
+
+def _mut_prefill_qk_cut_to_v(q, k, v, kc, vc, blk, window, scale=None, rows=None):
+    dv = np.shape(v)[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(np.shape(q)[-1])
+    return _orig_prefill(np.asarray(q)[..., :dv], np.asarray(k)[..., :dv], v, np.asarray(kc)[..., :dv], vc, blk, window,
+                         scale, rows)
+
+
 _orig_quantize = ofp8.quantize_fp8_rows
 _orig_scores = odsa.dsa_indexer_scores
 _orig_topk = odsa.dsa_topk
@@ -173,6 +190,8 @@ MUTATIONS = {
     "e4m3_ties_away": (ofp8, "e4m3_encode", _mut_e4m3_ties_away),
     "quantize_scale_inverted": (ofp8, "quantize_fp8_rows", _mut_quantize_scale_inverted),
     "csa_partial_block_visible": (odsa, "n_candidates", _mut_csa_partial_block_visible),
+    "prefill_scale_from_v": (ohca, "hca_attention_prefill", _mut_prefill_scale_from_v),
+    "prefill_qk_cut_to_v": (ohca, "hca_attention_prefill", _mut_prefill_qk_cut_to_v),
 }
 
 
