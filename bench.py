@@ -31,6 +31,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 T_PREFILL, H, D_HCA, BLK, WIN = 32768, 64, 512, 128, 128
 HQ, D_DSA, HI, DI, TOPK = 64, 256, 4, 128, 2048
+D_QK_WIDE = 576  # query/key width of the wider HCA head shape (value width stays D_HCA)
 CSA_RATIO = 4  # CSA variant: indexer keys, K and V averaged over 4 tokens
 
 
@@ -219,6 +220,30 @@ def main():
                                  "entries": S_c, "top_k": TOPK}
         del kci, kcd, vcd, sc_c, idx_c
 
+        # HCA attention with the wider query/key head (qk 576, v 512) over the
+        # same T = 32768, 64 heads (an extra figure, not part of the step).
+        progress("HCA qk576/v512 variant")
+        q6 = synth.torch_normal((1, H, T_PREFILL, D_QK_WIDE), sig, torch.bfloat16, 211, dev)
+        k6 = synth.torch_normal((1, H, T_PREFILL, D_QK_WIDE), sig, torch.bfloat16, 212, dev)
+        kc6 = sa.hca_compress(k6, BLK)
+
+        def k_hca_wide():
+            return sa.hca_attention_fwd(sa.HCA_PREFILL, q6, k6, v, kc6, vc, BLK, WIN)
+
+        for _ in range(args.warmup):
+            k_hca_wide()
+        torch.cuda.synchronize()
+        t_w = timer.time(k_hca_wide, max(3, args.steps))
+        ms_w = sum(t_w) / len(t_w)
+        pairs_w = hca_pairs_per_head(T_PREFILL) * H
+        bytes_w = T_PREFILL * H * (2 * D_QK_WIDE + 2 * D_HCA) * 2
+        flops_w = 2 * (D_QK_WIDE + D_HCA) * pairs_w
+        result["hca_prefill_qk576_v512"] = {
+            "ms": ms_w, "tokens_per_s": T_PREFILL / (ms_w * 1e-3), "alg_bytes": bytes_w, "alg_flops": flops_w,
+            "hbm_frac": bytes_w / (ms_w * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac": flops_w / (ms_w * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+        del q6, k6, kc6
+
         pairs_hca = hca_pairs_per_head(T_PREFILL) * H
         pairs_dsa = dsa_pairs(T_PREFILL) * HQ
         tensor_bytes = T_PREFILL * H * D_HCA * 2
@@ -399,7 +424,7 @@ def main():
             "parallelism": "single GPU",
         },
         "decode": {k_: v_ for k_, v_ in result.items() if k_.startswith("decode")},
-        "variants": {k_: v_ for k_, v_ in result.items() if k_.startswith("csa")},
+        "variants": {k_: v_ for k_, v_ in result.items() if k_.startswith(("csa", "hca_prefill_qk576"))},
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

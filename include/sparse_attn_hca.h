@@ -77,9 +77,9 @@ const char* sa_version(void);
  * x:   [B,H,n_tokens,d] with element strides (x_sb, x_sh, x_st), d contiguous.
  * out: [B,H,n_tokens/blk,d] with element strides (o_sb, o_sh, o_sn).
  * Arithmetic: fp32 sum, one division by blk, rounded (RNE) to the I/O dtype.
- * Supported: SA_F32 and SA_BF16 with d*sizeof(element) = 16*2^n bytes, at
- * most 4096 bytes (e.g. f32 d = 64, bf16 d = 256 or 512).  Strides must be
- * multiples of 16 bytes.
+ * Supported: SA_F32 and SA_BF16 with d*sizeof(element) a multiple of 16
+ * bytes, at most 4096 bytes (e.g. f32 d = 64, bf16 d = 256, 512 or 576).
+ * Strides must be multiples of 16 bytes.
  * ------------------------------------------------------------------------ */
 int hca_compress(const void* x, void* out, sa_dtype dtype,
                  int64_t B, int64_t H, int64_t n_tokens, int64_t d, int64_t blk,
@@ -100,20 +100,27 @@ int hca_compress(const void* x, void* out, sa_dtype dtype,
  *   - raw tokens t-window < s <= t (s >= 0) form the window;
  *   - one softmax over both sets with logits scale*<q,k>; no sink/bias/gate.
  *
+ * Head widths: d is the query/key width, d_v the value/output width (d_v = 0
+ * means d_v = d).  [P3] §預訓練資料工程 item 3 (FlashMask-4) names a query/key
+ * head of 576 with a value head of 512; that shape is supported beside the
+ * plain 512/512 one.
  * PREFILL (mode = HCA_PREFILL), T = seq_len:
- *   q, k, v, o: [B,H,T,d];  k_c, v_c: [B,H,n_c,d] with n_c = n_c_cap (normally
- *   T/blk, as written by hca_compress);  query row t sits at position t.
+ *   q, k: [B,H,T,d];  v, o: [B,H,T,d_v];  k_c: [B,H,n_c,d], v_c: [B,H,n_c,d_v]
+ *   with n_c = n_c_cap (normally T/blk, as written by hca_compress);  query
+ *   row t sits at position t.
  * DECODE (mode = HCA_DECODE), one query per sequence:
- *   q, o: [B,H,d];  k_c, v_c: [B,H,n_c_cap,d];  k, v: the window ring
- *   [B,H,window,d] where position s lives in slot s mod window;
- *   pos: device int64[B], the query's position (its own K/V is already in
- *   the ring).  pos values < 0 are treated as 0.
+ *   q: [B,H,d], o: [B,H,d_v];  k_c: [B,H,n_c_cap,d], v_c: [B,H,n_c_cap,d_v];
+ *   k, v: the window ring [B,H,window,d] and [B,H,window,d_v] where position
+ *   s lives in slot s mod window;  pos: device int64[B], the query's
+ *   position (its own K/V is already in the ring).  pos values < 0 are
+ *   treated as 0.
  * lse: optional (NULL to skip) fp32 [B,H,T] (prefill) or [B,H] (decode):
  *   natural-log normaliser of the scaled logits.
- * scale <= 0 selects 1/sqrt(d).
+ * scale <= 0 selects 1/sqrt(d) (the query/key width).
  * Arithmetic: bf16 inputs, fp32 accumulation and softmax, probabilities
  * rounded to bf16 for the P*V product, output rounded (RNE) to the I/O dtype.
- * Supported: SA_F32 with d = 64 (prefill); SA_BF16 with d = 512.
+ * Supported (dtype, d, d_v): prefill (SA_F32, 64, 64), (SA_BF16, 512, 512),
+ * (SA_BF16, 576, 512); decode (SA_BF16, 512, 512), (SA_BF16, 576, 512).
  * Workspace: DECODE may need split-K partials; query
  *   hca_attention_fwd_workspace_size() (0 for PREFILL).
  * ------------------------------------------------------------------------ */
@@ -138,6 +145,7 @@ typedef struct {
   float* lse;
   void* workspace;
   size_t workspace_bytes;
+  int64_t d_v;      /* value/output width; 0 = d                          */
 } hca_attention_args;
 
 size_t hca_attention_fwd_workspace_size(const hca_attention_args* args);

@@ -44,6 +44,7 @@ class HcaAttentionArgs(ctypes.Structure):
         ("lse", _c_p),
         ("workspace", _c_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("d_v", _c_i64),
     ]
 
 
@@ -192,30 +193,45 @@ def _hca_args(mode, q, k, v, k_c, v_c, blk, window, seq_len, n_c_cap, scale, pos
     a.lse = lse.data_ptr() if lse is not None else None
     a.workspace = ws.data_ptr() if ws is not None else None
     a.workspace_bytes = ws_bytes
+    a.d_v = v.shape[-1]
     return a
 
 
 def hca_attention_fwd(mode, q, k, v, k_c, v_c, blk, window, scale=None, pos=None, return_lse=False, workspace=None):
     """HCA attention.
 
-    PREFILL: q,k,v [B,H,T,d]; k_c,v_c [B,H,Nc,d].  Returns o [B,H,T,d] (and lse [B,H,T]).
-    DECODE:  q [B,H,d]; k_c,v_c [B,H,Ncap,d]; k,v = window ring [B,H,window,d];
-             pos int64 [B] on the device.  Returns o [B,H,d] (and lse [B,H]).
+    d is the query/key width (q, k, k_c), dv the value width (v, v_c, o); dv < d
+    for the qk 576 / v 512 shape.
+    PREFILL: q,k [B,H,T,d], v [B,H,T,dv]; k_c [B,H,Nc,d], v_c [B,H,Nc,dv].
+             Returns o [B,H,T,dv] (and lse [B,H,T]).
+    DECODE:  q [B,H,d]; k_c [B,H,Ncap,d], v_c [B,H,Ncap,dv]; k,v = window ring
+             [B,H,window,d] / [B,H,window,dv]; pos int64 [B] on the device.
+             Returns o [B,H,dv] (and lse [B,H]).
     """
     for name, t in (("q", q), ("k", k), ("v", v), ("k_c", k_c), ("v_c", v_c)):
         _need(t, name, dtype=q.dtype)
+    d, dv = q.shape[-1], v.shape[-1]
     if mode == HCA_PREFILL:
-        B, H, T, d = q.shape
+        B, H, T, _ = q.shape
         seq_len, n_c = T, k_c.shape[2]
+        want = {"k": (B, H, T, d), "v": (B, H, T, dv), "k_c": (B, H, n_c, d), "v_c": (B, H, n_c, dv)}
+        o_shape = (B, H, T, dv)
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if return_lse else None
     elif mode == HCA_DECODE:
         _need(pos, "pos", dtype=torch.int64, dim=1)
-        B, H, d = q.shape
+        B, H, _ = q.shape
         seq_len, n_c = 0, k_c.shape[2]
+        want = {"k": (B, H, window, d), "v": (B, H, window, dv), "k_c": (B, H, n_c, d), "v_c": (B, H, n_c, dv)}
+        if tuple(pos.shape) != (B,):
+            raise ValueError(f"pos must have shape ({B},)")
+        o_shape = (B, H, dv)
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
     else:
         raise ValueError("mode must be HCA_PREFILL or HCA_DECODE")
-    o = torch.empty_like(q)
+    for name, t in (("k", k), ("v", v), ("k_c", k_c), ("v_c", v_c)):
+        if tuple(t.shape) != want[name]:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]}")
+    o = torch.empty(o_shape, dtype=q.dtype, device=q.device)
     args = _hca_args(mode, q, k, v, k_c, v_c, blk, window, seq_len, n_c, scale, pos, o, lse, None, 0)
     need = lib().hca_attention_fwd_workspace_size(ctypes.byref(args))
     if need > 0:

@@ -62,8 +62,8 @@ int hca_compress(const void* x, void* out, sa_dtype dtype, int64_t B, int64_t H,
   if (!x || !out) return fail(SA_ERR_NULL, "hca_compress: x and out must be non-NULL");
   const int64_t es = (int64_t)elem_size(dtype);
   const int64_t chunks = d * es / 16;
-  if ((d * es) % 16 != 0 || chunks > 256 || (chunks & (chunks - 1)) != 0)
-    return fail(SA_ERR_UNSUPPORTED, "hca_compress: d*sizeof(elem) must be 16 * 2^n bytes, at most 4096 (d=%lld)",
+  if ((d * es) % 16 != 0 || chunks > 256)
+    return fail(SA_ERR_UNSUPPORTED, "hca_compress: d*sizeof(elem) must be a multiple of 16 bytes, at most 4096 (d=%lld)",
                 (long long)d);
   if (blk > (1 << 20)) return fail(SA_ERR_SHAPE, "hca_compress: blk too large");
   if (!aligned16(x) || !aligned16(out)) return fail(SA_ERR_ALIGN, "hca_compress: pointers must be 16-byte aligned");
@@ -77,19 +77,25 @@ int hca_compress(const void* x, void* out, sa_dtype dtype, int64_t B, int64_t H,
 }
 
 // ---------------------------------------------------------------------------
+static int64_t hca_dv(const hca_attention_args* a) { return a->d_v == 0 ? a->d : a->d_v; }
+
 static int hca_check(const hca_attention_args* a) {
   if (!a) return fail(SA_ERR_NULL, "hca_attention_fwd: args is NULL");
   if (a->mode != HCA_PREFILL && a->mode != HCA_DECODE) return fail(SA_ERR_SHAPE, "hca_attention_fwd: unknown mode");
   if (!a->q || !a->k || !a->v || !a->o) return fail(SA_ERR_NULL, "hca_attention_fwd: q, k, v, o must be non-NULL");
-  if (a->B <= 0 || a->H <= 0 || a->d <= 0 || a->blk <= 0 || a->window <= 0 || a->n_c_cap < 0)
-    return fail(SA_ERR_SHAPE, "hca_attention_fwd: B, H, d, blk, window must be > 0, n_c_cap >= 0");
+  if (a->B <= 0 || a->H <= 0 || a->d <= 0 || a->d_v < 0 || a->blk <= 0 || a->window <= 0 || a->n_c_cap < 0)
+    return fail(SA_ERR_SHAPE, "hca_attention_fwd: B, H, d, blk, window must be > 0, d_v, n_c_cap >= 0");
+  const int64_t dv = hca_dv(a);
+  const bool bf16_512 = a->dtype == SA_BF16 && a->d == 512 && dv == 512;
+  const bool bf16_576 = a->dtype == SA_BF16 && a->d == 576 && dv == 512;
   if (a->n_c_cap > 0 && (!a->k_c || !a->v_c))
     return fail(SA_ERR_NULL, "hca_attention_fwd: k_c, v_c must be non-NULL when n_c_cap > 0");
   if (a->mode == HCA_PREFILL) {
     if (a->seq_len <= 0) return fail(SA_ERR_SHAPE, "hca_attention_fwd: seq_len must be > 0 for PREFILL");
-    const bool sup = (a->dtype == SA_F32 && a->d == 64) || (a->dtype == SA_BF16 && a->d == 512);
+    const bool sup = (a->dtype == SA_F32 && a->d == 64 && dv == 64) || bf16_512 || bf16_576;
     if (!sup)
-      return fail(SA_ERR_UNSUPPORTED, "hca_attention_fwd PREFILL: supported (dtype, d) are (f32, 64) and (bf16, 512)");
+      return fail(SA_ERR_UNSUPPORTED,
+                  "hca_attention_fwd PREFILL: supported (dtype, d, d_v) are (f32, 64, 64), (bf16, 512, 512), (bf16, 576, 512)");
     if (a->n_c_cap > a->seq_len / a->blk)
       return fail(SA_ERR_SHAPE, "hca_attention_fwd PREFILL: n_c_cap (%lld) exceeds seq_len/blk (%lld)",
                   (long long)a->n_c_cap, (long long)(a->seq_len / a->blk));
@@ -99,8 +105,8 @@ static int hca_check(const hca_attention_args* a) {
     if (a->B * a->H * n_qt > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "hca_attention_fwd: grid too large");
   } else {
     if (!a->pos) return fail(SA_ERR_NULL, "hca_attention_fwd DECODE: pos must be non-NULL");
-    if (!(a->dtype == SA_BF16 && a->d == 512))
-      return fail(SA_ERR_UNSUPPORTED, "hca_attention_fwd DECODE: supported (dtype, d) is (bf16, 512)");
+    if (!bf16_512 && !bf16_576)
+      return fail(SA_ERR_UNSUPPORTED, "hca_attention_fwd DECODE: supported (dtype, d, d_v) are (bf16, 512, 512), (bf16, 576, 512)");
     if (a->n_c_cap < 1) return fail(SA_ERR_SHAPE, "hca_attention_fwd DECODE: n_c_cap must be >= 1");
   }
   const void* ptrs[] = {a->q, a->k, a->v, a->k_c, a->v_c, a->o, a->lse};
@@ -114,8 +120,8 @@ static int64_t hca_dec_nsplit(const hca_attention_args* a) {
 }
 
 size_t hca_attention_fwd_workspace_size(const hca_attention_args* a) {
-  if (!a || a->mode != HCA_DECODE || a->B <= 0 || a->H <= 0 || a->d <= 0) return 0;
-  return sa::hca_decode_workspace_bytes(a->B * a->H, hca_dec_nsplit(a), a->d);
+  if (!a || a->mode != HCA_DECODE || a->B <= 0 || a->H <= 0 || a->d <= 0 || a->d_v < 0) return 0;
+  return sa::hca_decode_workspace_bytes(a->B * a->H, hca_dec_nsplit(a), hca_dv(a));
 }
 
 int hca_attention_fwd(const hca_attention_args* a, hipStream_t stream) {
@@ -125,12 +131,13 @@ int hca_attention_fwd(const hca_attention_args* a, hipStream_t stream) {
   if (a->mode == HCA_PREFILL) {
     sa::HcaPrefillParams p{a->q, a->k, a->v, a->k_c, a->v_c, a->o, a->lse, a->B, a->H, a->seq_len,
                            a->n_c_cap, a->blk, a->window, sl2, (a->seq_len + 63) / 64};
-    return hip_status(sa::launch_hca_prefill(p, a->dtype == SA_BF16 ? 1 : 0, (int)a->d, stream),
+    return hip_status(sa::launch_hca_prefill(p, a->dtype == SA_BF16 ? 1 : 0, (int)a->d, (int)hca_dv(a), stream),
                       "hca_attention_fwd prefill launch");
   }
   const int64_t BH = a->B * a->H;
   const int64_t ns = hca_dec_nsplit(a);
-  const size_t need = sa::hca_decode_workspace_bytes(BH, ns, a->d);
+  const int64_t dv = hca_dv(a);
+  const size_t need = sa::hca_decode_workspace_bytes(BH, ns, dv);
   if (need > 0) {
     if (!a->workspace || a->workspace_bytes < need)
       return fail(SA_ERR_WORKSPACE, "hca_attention_fwd DECODE: needs %zu workspace bytes, got %zu", need,
@@ -140,11 +147,11 @@ int hca_attention_fwd(const hca_attention_args* a, hipStream_t stream) {
   if (BH * ns > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "hca_attention_fwd: grid too large");
   const int64_t max_keys = a->n_c_cap + a->window;
   float* part_o = reinterpret_cast<float*>(a->workspace);
-  float* part_lse = part_o ? part_o + BH * ns * a->d : nullptr;
+  float* part_lse = part_o ? part_o + BH * ns * dv : nullptr;
   sa::HcaDecodeParams p{a->q, a->k_c, a->v_c, a->k, a->v, nullptr, nullptr, nullptr, nullptr,
                         a->pos, a->o, a->lse, part_o, part_lse,
                         a->B, a->H, a->n_c_cap, a->blk, a->window, sl2, ns, (max_keys + ns - 1) / ns};
-  return hip_status(sa::launch_hca_decode(p, 1, (int)a->d, stream), "hca_attention_fwd decode launch");
+  return hip_status(sa::launch_hca_decode(p, 1, (int)a->d, (int)dv, stream), "hca_attention_fwd decode launch");
 }
 
 // ---------------------------------------------------------------------------
@@ -200,7 +207,7 @@ int hca_decode_fp8(const hca_decode_fp8_args* a, hipStream_t stream) {
   sa::HcaDecodeParams p{a->q, a->k_c, a->v_c, a->k, a->v, a->k_c_scale, a->v_c_scale, a->k_scale, a->v_scale,
                         a->pos, a->o, a->lse, part_o, part_lse,
                         a->B, a->H, a->n_c_cap, a->blk, a->window, sl2, ns, (max_keys + ns - 1) / ns};
-  return hip_status(sa::launch_hca_decode(p, 2, (int)a->d, stream), "hca_decode_fp8 launch");
+  return hip_status(sa::launch_hca_decode(p, 2, (int)a->d, (int)a->d, stream), "hca_decode_fp8 launch");
 }
 
 // ---------------------------------------------------------------------------

@@ -84,10 +84,9 @@ __device__ __forceinline__ Tile32Addr tile32_addr() {
 // Returns the raw scores: value j is key 8*(j/4) + 4q + j%4 of row l%32.
 // All LDS reads have been issued when this returns; the caller waits for
 // them (lgkmcnt) before letting the K buffer be overwritten.
-template <int D>
+template <int D, int kAhead = 4>  // kAhead: LDS operand reads in flight
 __device__ __forceinline__ f32x16_t attend_qk32(const Attn32Regs<D>& R, const char* ks, Tile32Addr ad) {
   constexpr int kSteps = D / 16;
-  constexpr int kAhead = 4;  // LDS operand reads in flight
   // Opaque copy: the derived offsets are recomputed next to their reads
   // instead of being hoisted out of the key loop into registers.
   asm volatile("" : "+v"(ad.k));

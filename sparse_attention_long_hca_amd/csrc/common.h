@@ -98,6 +98,10 @@ __device__ __forceinline__ buffer_rsrc_t make_buffer_rsrc(const void* base) {
 __device__ __forceinline__ void buffer_load_lds_16(buffer_rsrc_t rsrc, uint32_t voff, char* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 16, voff, 0, 0, 0);
 }
+// Lane i's 4 bytes at byte offset voff land at lds_wave_base + 4*i.
+__device__ __forceinline__ void buffer_load_lds_4(buffer_rsrc_t rsrc, uint32_t voff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 4, voff, 0, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // Cross-lane pairs without LDS: v_permlane16_swap / v_permlane32_swap with

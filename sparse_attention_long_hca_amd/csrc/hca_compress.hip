@@ -4,10 +4,12 @@
 // consecutive tokens become one cache entry.  The pages do not name the
 // operator; the entry is the arithmetic mean of the block's rows.
 //
-// One workgroup per output row.  Thread t reads the 16-byte chunk t % C
-// (C = chunks per row) of rows t / C, t / C + 256 / C, ... so that each wave
-// reads whole rows contiguously; the partial sums are combined through LDS in
-// a fixed order (deterministic), divided by blk and rounded to the I/O dtype.
+// One workgroup per output row.  With C = chunks (16 bytes) per row and
+// R = floor(256 / C) rows per pass, thread t < R*C reads chunk t % C of rows
+// t / C, t / C + R, ... so that each wave reads whole rows contiguously (the
+// last 256 - R*C threads idle when C does not divide 256, e.g. 72 chunks for
+// a 576-wide bf16 row); the partial sums are combined through LDS in a fixed
+// order (deterministic), divided by blk and rounded to the I/O dtype.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,11 +29,11 @@ __global__ __launch_bounds__(kCompressThreads) void hca_compress_kernel(HcaCompr
   const T* src = reinterpret_cast<const T*>(p.x) + b * p.x_sb + h * p.x_sh + n * p.blk * p.x_st;
   T* dst = reinterpret_cast<T*>(p.out) + b * p.o_sb + h * p.o_sh + n * p.o_sn;
 
-  const int chunks = (int)(p.d / kEPC);  // a power of two <= 256 (checked on the host)
+  const int chunks = (int)(p.d / kEPC);  // <= 256 (checked on the host)
   const int tid = threadIdx.x;
   const int c = tid % chunks;
-  const int r0 = tid / chunks;
   const int rstep = kCompressThreads / chunks;
+  const int r0 = tid / chunks < rstep ? tid / chunks : (int)p.blk;  // idle threads read nothing
 
   float acc[kEPC];
 #pragma unroll

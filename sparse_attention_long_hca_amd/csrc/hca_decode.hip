@@ -17,6 +17,10 @@
 // it grows by more than 2^8.  With more than one split per (batch, head) the
 // partial (o, lse) go to the workspace and a second kernel combines them in
 // split order.
+//
+// Wider query/key heads ([P3] §預訓練資料工程 item 3: qk 576 with v 512): the
+// DR dims of q and K past the value width D are spread over a key's 16 lanes,
+// 4 dims (8 bytes) each, so the extra part of a K row is one 128-byte line.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,13 +47,15 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // part, part+16, ... of the row.
 constexpr int kDecFp8Lanes = 8;  // lanes per key with the FP8 cache (more keys in flight per wave)
 
-template <int D, bool kFp8>
+template <int D, bool kFp8, int DR>
 __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams p) {
   constexpr int kLanes = kFp8 ? kDecFp8Lanes : 16;  // lanes per key
+  static_assert(DR == 0 || (!kFp8 && DR == 4 * 16), "extra query/key dims: 4 per lane of a bf16 key");
   constexpr int kLaneDims = D / kLanes;             // FP8: contiguous dims per lane
   constexpr int kSlots = kWave / kLanes;   // keys per wave step
   constexpr int kPer = D / 8 / kLanes;     // groups of 8 dims per lane
-  constexpr int kRowBytes = kFp8 ? D : 2 * D;
+  constexpr int kRowBytes = kFp8 ? D : 2 * D;        // V row; the first D dims of a K row
+  constexpr int kKRowBytes = kRowBytes + 2 * DR;     // K row pitch
   constexpr int kLoads = kRowBytes / kLanes / 16;  // 16-byte loads per lane and row
   __shared__ float sh_o[kDecWaves][D];
   __shared__ float sh_m[kDecWaves], sh_l[kDecWaves];
@@ -73,10 +79,10 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
   const int64_t u_begin = split * p.keys_per_split;
   const int64_t u_end = imin64(n_keys, u_begin + p.keys_per_split);
 
-  const bf16_t* q = reinterpret_cast<const bf16_t*>(p.q) + bh * D;
-  const char* kc = reinterpret_cast<const char*>(p.kc) + bh * p.Ncap * kRowBytes;
+  const bf16_t* q = reinterpret_cast<const bf16_t*>(p.q) + bh * (D + DR);
+  const char* kc = reinterpret_cast<const char*>(p.kc) + bh * p.Ncap * kKRowBytes;
   const char* vc = reinterpret_cast<const char*>(p.vc) + bh * p.Ncap * kRowBytes;
-  const char* rk = reinterpret_cast<const char*>(p.rk) + bh * p.window * kRowBytes;
+  const char* rk = reinterpret_cast<const char*>(p.rk) + bh * p.window * kKRowBytes;
   const char* rv = reinterpret_cast<const char*>(p.rv) + bh * p.window * kRowBytes;
   const int64_t win_first = t - nw + 1;  // first window position
 
@@ -84,6 +90,8 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
   uint4 qc[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) qc[i] = *reinterpret_cast<const uint4*>(q + dim0(i));
+  // Extra query/key dims D + 4*part .. +3.
+  const uint2 qr = DR ? *reinterpret_cast<const uint2*>(q + D + 4 * part) : make_uint2(0u, 0u);
   float qf[kFp8 ? kPer * 8 : 1];
   if constexpr (kFp8) {
 #pragma unroll
@@ -105,6 +113,7 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
   // One group: keys g0 + slot (a group of kSlots consecutive keys).
   struct Rows {
     uint4 k[kLoads], v[kLoads];
+    uint2 kr;      // extra K dims (DR > 0)
     float ks, vs;  // row scales (FP8 cache)
   };
   auto load = [&](int64_t g0, Rows& r) __attribute__((always_inline)) {
@@ -115,7 +124,7 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
       const char* krow;
       const char* vrow;
       if (u < nc) {
-        krow = kc + u * kRowBytes;
+        krow = kc + u * kKRowBytes;
         vrow = vc + u * kRowBytes;
         if constexpr (kFp8) {
           r.ks = p.kc_scale[bh * p.Ncap + u];
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
         }
       } else {
         const int64_t sl = (win_first + (u - nc)) % p.window;
-        krow = rk + sl * kRowBytes;
+        krow = rk + sl * kKRowBytes;
         vrow = rv + sl * kRowBytes;
         if constexpr (kFp8) {
           r.ks = p.rk_scale[bh * p.window + sl];
@@ -135,12 +144,14 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
         r.k[j] = *reinterpret_cast<const uint4*>(krow + load_off(j));
         r.v[j] = *reinterpret_cast<const uint4*>(vrow + load_off(j));
       }
+      r.kr = DR ? *reinterpret_cast<const uint2*>(krow + kRowBytes + 8 * part) : make_uint2(0u, 0u);
     } else {
 #pragma unroll
       for (int j = 0; j < kLoads; ++j) {
         r.k[j] = make_uint4(0u, 0u, 0u, 0u);
         r.v[j] = make_uint4(0u, 0u, 0u, 0u);
       }
+      r.kr = make_uint2(0u, 0u);
     }
   };
   constexpr float kRescaleLog2 = 8.f;
@@ -170,6 +181,10 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
         dot = dot2_bf16(qc[i].y, r.k[i].y, dot);
         dot = dot2_bf16(qc[i].z, r.k[i].z, dot);
         dot = dot2_bf16(qc[i].w, r.k[i].w, dot);
+      }
+      if constexpr (DR > 0) {
+        dot = dot2_bf16(qr.x, r.kr.x, dot);
+        dot = dot2_bf16(qr.y, r.kr.y, dot);
       }
     }
 #pragma unroll
@@ -329,13 +344,17 @@ size_t hca_decode_workspace_bytes(int64_t BH, int64_t nsplit, int64_t d) {
   return (size_t)(BH * nsplit * d + BH * nsplit) * sizeof(float);
 }
 
-hipError_t launch_hca_decode(const HcaDecodeParams& p, int cache, int d, hipStream_t stream) {
-  if ((cache != 1 && cache != 2) || d != 512) return hipErrorInvalidValue;
+hipError_t launch_hca_decode(const HcaDecodeParams& p, int cache, int d, int dv, hipStream_t stream) {
+  if ((cache != 1 && cache != 2) || dv != 512 || (d != 512 && d != 576) || (cache == 2 && d != 512))
+    return hipErrorInvalidValue;
   const int64_t BH = p.B * p.H;
+  const dim3 grid((uint32_t)(BH * p.nsplit));
   if (cache == 2)
-    hipLaunchKernelGGL((hca_decode_kernel<512, true>), dim3((uint32_t)(BH * p.nsplit)), dim3(kDecThreads), 0, stream, p);
+    hipLaunchKernelGGL((hca_decode_kernel<512, true, 0>), grid, dim3(kDecThreads), 0, stream, p);
+  else if (d == 576)
+    hipLaunchKernelGGL((hca_decode_kernel<512, false, 64>), grid, dim3(kDecThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((hca_decode_kernel<512, false>), dim3((uint32_t)(BH * p.nsplit)), dim3(kDecThreads), 0, stream, p);
+    hipLaunchKernelGGL((hca_decode_kernel<512, false, 0>), grid, dim3(kDecThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   hipLaunchKernelGGL(hca_decode_combine_kernel<512>, dim3((uint32_t)BH), dim3(256), 0, stream, p);

@@ -167,15 +167,75 @@ constexpr int kHalfD = 256;
 constexpr int kPairRows = 32;
 constexpr int kH32Waves = 4;  // 2 wave pairs: 64 queries per workgroup
 
-template <int D, int kWaves>
+// Wider query/key heads ([P3] §預訓練資料工程 item 3, FlashMask-4's qk 576 /
+// v 512): the DR = 64 query/key dims past the value width.  Half h of a wave
+// pair takes dims D + 32h .. +31 of them, two more k-steps of its partial S.
+// Their 32-key tile is 32 rows x 128 bytes in LDS, 16-byte chunk c of row r
+// at r*128 + 16*(c ^ ((r >> 1) & 7)): the operand reads of 16 lanes (rows
+// r..r+15, one chunk) then fall in 16 distinct groups of 4 banks.  It is
+// staged with 4-byte direct-to-LDS loads so that every wave issues the same
+// number of loads per tile (the waits count loads per wave).
+template <int DR, int kWaves>
+struct RopeTile {
+  static_assert(DR == 64, "8 chunks per row");
+  static constexpr int kRowBytes = 2 * DR;
+  static constexpr int kTileBytes = kBN * kRowBytes;    // 4 KB
+  static constexpr int kInstr = kTileBytes / 4 / kWave;  // 4-byte loads of one wave
+  static constexpr int kPerWave = kInstr / kWaves;
+  static_assert(kInstr % kWaves == 0, "tile must split evenly over the waves");
+  __device__ static __forceinline__ uint32_t off(int r, int c) { return (uint32_t)(r * kRowBytes + 16 * (c ^ ((r >> 1) & 7))); }
+};
+
+// Stage the extra dims of one 32-key tile: src points at dim D of row 0,
+// rowfn(r) as for stage_rows_async, kPitch the K row pitch in bytes.
+template <int DR, int kWaves, uint32_t kPitch, typename RowFn>
+__device__ __forceinline__ void stage_rope_async(char* buf, const bf16_t* src, RowFn&& rowfn) {
+  using RT = RopeTile<DR, kWaves>;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  int row[RT::kPerWave];
+#pragma unroll
+  for (int j = 0; j < RT::kPerWave; ++j) row[j] = rowfn(((j * kWaves + wave) * kWave + lane) / (RT::kRowBytes / 4));
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t off[RT::kPerWave];
+#pragma unroll
+  for (int j = 0; j < RT::kPerWave; ++j) {
+    // Dword P of the tile in LDS: row r, physical chunk pc, dword e of it.
+    const int P = (j * kWaves + wave) * kWave + lane;
+    const int r = P / (RT::kRowBytes / 4), dw = P % (RT::kRowBytes / 4);
+    const int c = (dw >> 2) ^ ((r >> 1) & 7);
+    off[j] = (uint32_t)(row[j] < 0 ? 0 : row[j]) * kPitch + (uint32_t)c * 16u + (uint32_t)(dw & 3) * 4u;
+  }
+  const buffer_rsrc_t rsrc = make_buffer_rsrc(src);
+#pragma unroll
+  for (int j = 0; j < RT::kPerWave; ++j) buffer_load_lds_4(rsrc, off[j], buf + (j * kWaves + wave) * kWave * 4);
+}
+
+// S^T += K_extra . Q_extra^T over this half's 32 extra dims (two k-steps).
+template <int DR, int kWaves>
+__device__ __forceinline__ f32x16_t rope_qk32(f32x16_t s, const i16x8_t* qr, const char* rbuf, int half) {
+  using RT = RopeTile<DR, kWaves>;
+  const int lane = threadIdx.x & 63, r = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const i16x8_t a = __builtin_bit_cast(i16x8_t, lds_read_b128(rbuf, RT::off(r, 4 * half + 2 * ks + g)));
+    s = mfma_bf16_32x32x16(a, qr[ks], s);
+  }
+  return s;
+}
+
+template <int D, int kWaves, int DR>
 __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void hca_prefill32_kernel(HcaPrefillParams p) {
   static_assert(D == 2 * kHalfD, "two halves of 256 dims");
+  static_assert(DR == 0 || DR == 64, "extra query/key dims");
+  constexpr int kQK = D + DR;  // query/key row width (elements)
   constexpr int kRows = kWaves / 2 * kPairRows;  // queries per workgroup
   using T = bf16_t;
   using GH = AttnGeom<T, kHalfD, 1>;
   constexpr int kHalfTile = GH::kTileBytes;  // 16 KB: 32 rows x 512 bytes
+  constexpr int kRopeBytes = DR > 0 ? RopeTile<(DR > 0 ? DR : 64), kWaves>::kTileBytes : 16;
   __shared__ __attribute__((aligned(16))) char kbuf[2 * kHalfTile];
   __shared__ __attribute__((aligned(16))) char vbuf[2 * kHalfTile];
+  __shared__ __attribute__((aligned(16))) char rbuf[kRopeBytes];  // extra K dims (DR > 0)
   __shared__ __attribute__((aligned(16))) char xbuf[kWaves * 16 * kWave * 4];  // partial S, 4 KB per wave
 
   const int n_qtiles = (int)p.n_qtiles;
@@ -187,11 +247,11 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   const int lane = threadIdx.x & 63;
   const int pair = wave >> 1, half = wave & 1;
 
-  const int64_t head_off = (int64_t)bh * Tn * D;
-  const T* q = reinterpret_cast<const T*>(p.q) + head_off;
-  const T* k = reinterpret_cast<const T*>(p.k) + head_off;
+  const int64_t head_off = (int64_t)bh * Tn * D, head_qk = (int64_t)bh * Tn * kQK;
+  const T* q = reinterpret_cast<const T*>(p.q) + head_qk;
+  const T* k = reinterpret_cast<const T*>(p.k) + head_qk;
   const T* v = reinterpret_cast<const T*>(p.v) + head_off;
-  const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)bh * Nc * D;
+  const T* kc = reinterpret_cast<const T*>(p.kc) + (int64_t)bh * Nc * kQK;
   const T* vc = reinterpret_cast<const T*>(p.vc) + (int64_t)bh * Nc * D;
   T* o = reinterpret_cast<T*>(p.o) + head_off;
 
@@ -202,7 +262,14 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
 
   Attn32Regs<kHalfD> R;
   // Rows past T load the last row (their results are never written).
-  load_q32<kHalfD>(R, q + (int64_t)min(tq, Tn - 1) * D + half * kHalfD);
+  const T* qrow = q + (int64_t)min(tq, Tn - 1) * kQK;
+  load_q32<kHalfD>(R, qrow + half * kHalfD);
+  i16x8_t qr[2];  // extra dims D + 32*half + 16*ks + 8*(lane/32) .. +7
+  if constexpr (DR > 0) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      qr[ks] = __builtin_bit_cast(i16x8_t, *reinterpret_cast<const uint4*>(qrow + D + 32 * half + 16 * ks + 8 * (lane >> 5)));
+  }
   const Tile32Addr ad = tile32_addr<kHalfD>();
 
   // Key stream of the tile (as in the 16-row kernel).
@@ -239,20 +306,28 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     };
   };
   // A K (or V) tile is two half-row tiles: dims [0, 256) at buf, [256, 512)
-  // at buf + kHalfTile.
-  auto issue = [&](char* buf, const T* src, int tile) __attribute__((always_inline)) {
+  // at buf + kHalfTile; K rows also give their extra dims to rbuf.
+  auto issue_k = [&](int tile) __attribute__((always_inline)) {
     const auto rf = rows_of(tile);
-    stage_rows_async<T, kHalfD, kWaves, 1, D * 2>(buf, src, rf);
-    stage_rows_async<T, kHalfD, kWaves, 1, D * 2>(buf + kHalfTile, src + kHalfD, rf);
+    const T* src = tile < n_ctiles ? kc : k;
+    stage_rows_async<T, kHalfD, kWaves, 1, kQK * 2>(kbuf, src, rf);
+    stage_rows_async<T, kHalfD, kWaves, 1, kQK * 2>(kbuf + kHalfTile, src + kHalfD, rf);
+    if constexpr (DR > 0) stage_rope_async<DR, kWaves, (uint32_t)(kQK * 2)>(rbuf, src + D, rf);
   };
-  auto issue_k = [&](int tile) { issue(kbuf, tile < n_ctiles ? kc : k, tile); };
-  auto issue_v = [&](int tile) { issue(vbuf, tile < n_ctiles ? vc : v, tile); };
+  auto issue_v = [&](int tile) __attribute__((always_inline)) {
+    const auto rf = rows_of(tile);
+    const T* src = tile < n_ctiles ? vc : v;
+    stage_rows_async<T, kHalfD, kWaves, 1, D * 2>(vbuf, src, rf);
+    stage_rows_async<T, kHalfD, kWaves, 1, D * 2>(vbuf + kHalfTile, src + kHalfD, rf);
+  };
 
   // Partial-S exchange: value j of lane l at xbuf + wave*4096 + (j/4)*1024 + l*16.
   float* xs_mine = reinterpret_cast<float*>(xbuf + wave * 4096 + lane * 16);
   const float* xs_other = reinterpret_cast<const float*>(xbuf + (wave ^ 1) * 4096 + lane * 16);
 
-  constexpr int kLoads = 2 * StageGeom<T, kHalfD, kWaves>::kPerWave;  // per K (or V) tile
+  // Loads per wave of a V tile and of a K tile (the extra dims included).
+  constexpr int kLoadsV = 2 * StageGeom<T, kHalfD, kWaves>::kPerWave;
+  constexpr int kLoadsK = kLoadsV + (DR > 0 ? RopeTile<(DR > 0 ? DR : 64), kWaves>::kPerWave : 0);
   const char* kh = kbuf + half * kHalfTile;
   const char* vh = vbuf + half * kHalfTile;
   // Same pipeline as the 16-row kernel (last tile peeled off); the partial
@@ -266,11 +341,14 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     const int lo = ctile ? 0 : win_lo - s0;
     const int hi = ctile ? vis_c - j0 - 1 : tq - s0;
 
-    wait_loads<kLoads>();  // K of this tile has landed (its V may be in flight)
-    lds_barrier();         // ... for every wave
+    wait_loads<kLoadsV>();  // K of this tile has landed (its V may be in flight)
+    lds_barrier();          // ... for every wave
     f32x16_t s;
     if (need) {
-      s = attend_qk32<kHalfD>(R, kh, ad);
+      // Two operand reads in flight instead of four leave registers for the
+      // extra dims' query part.
+      s = attend_qk32<kHalfD, (DR > 0 ? 2 : 4)>(R, kh, ad);
+      if constexpr (DR > 0) s = rope_qk32<DR, kWaves>(s, qr, rbuf, half);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         *reinterpret_cast<f32x4_t*>(xs_mine + c * 256) = f32x4_t{s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3]};
@@ -279,7 +357,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     lds_barrier();  // every wave is done reading the K tile; partial S is visible
     if constexpr (more) {
       issue_k(tile + 1);
-      wait_loads<kLoads>();  // V of this tile has landed (the next K may be in flight)
+      wait_loads<kLoadsK>();  // V of this tile has landed (the next K may be in flight)
     } else {
       wait_loads<0>();
     }
@@ -320,16 +398,25 @@ static hipError_t launch(const HcaPrefillParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_hca_prefill(const HcaPrefillParams& p, int dtype, int d, hipStream_t stream) {
-  if (dtype == 0 && d == 64) return launch<float, 64>(p, stream);
-  if (dtype == 1 && d == 512) {
-    constexpr int kWaves = kH32Waves;
-    HcaPrefillParams p32 = p;
-    p32.n_qtiles = (p.T + kWaves / 2 * kPairRows - 1) / (kWaves / 2 * kPairRows);
-    const int64_t nblocks = p.B * p.H * p32.n_qtiles;
-    hipLaunchKernelGGL((hca_prefill32_kernel<512, kWaves>), dim3((uint32_t)nblocks), dim3(kWaves * kWave), 0, stream, p32);
-    return hipGetLastError();
-  }
+template <int DR, int kWaves>
+static hipError_t launch32(const HcaPrefillParams& p, hipStream_t stream) {
+  HcaPrefillParams p32 = p;
+  p32.n_qtiles = (p.T + kWaves / 2 * kPairRows - 1) / (kWaves / 2 * kPairRows);
+  const int64_t nblocks = p.B * p.H * p32.n_qtiles;
+  hipLaunchKernelGGL((hca_prefill32_kernel<512, kWaves, DR>), dim3((uint32_t)nblocks), dim3(kWaves * kWave), 0, stream, p32);
+  return hipGetLastError();
+}
+
+// qk 576 / v 512 runs 8 waves (4 pairs, 128 queries) per workgroup: with the
+// extra-dims tile a 4-wave workgroup needs 84 KB of LDS and two of them no
+// longer fit a CU, while one 8-wave workgroup (100 KB) keeps two waves per
+// SIMD.
+constexpr int kH32WavesQK576 = 8;
+
+hipError_t launch_hca_prefill(const HcaPrefillParams& p, int dtype, int d, int dv, hipStream_t stream) {
+  if (dtype == 0 && d == 64 && dv == 64) return launch<float, 64>(p, stream);
+  if (dtype == 1 && d == 512 && dv == 512) return launch32<0, kH32Waves>(p, stream);
+  if (dtype == 1 && d == 576 && dv == 512) return launch32<64, kH32WavesQK576>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -29,7 +29,8 @@ struct HcaPrefillParams {
   float scale_log2;
   int64_t n_qtiles;
 };
-hipError_t launch_hca_prefill(const HcaPrefillParams& p, int dtype, int d, hipStream_t stream);
+// d: query/key width, dv: value/output width.
+hipError_t launch_hca_prefill(const HcaPrefillParams& p, int dtype, int d, int dv, hipStream_t stream);
 
 // ---- hca_attention_fwd, decode ----------------------------------------------
 struct HcaDecodeParams {
@@ -55,7 +56,8 @@ struct HcaDecodeParams {
 int64_t hca_decode_nsplit(int64_t BH, int64_t max_keys);
 size_t hca_decode_workspace_bytes(int64_t BH, int64_t nsplit, int64_t d);
 // cache: 1 = bf16 rows, 2 = E4M3 codes with per-row scales.
-hipError_t launch_hca_decode(const HcaDecodeParams& p, int cache, int d, hipStream_t stream);
+// d: query/key width (512 or 576), dv: value/output width (512).
+hipError_t launch_hca_decode(const HcaDecodeParams& p, int cache, int d, int dv, hipStream_t stream);
 
 // ---- hca_quantize_fp8 -------------------------------------------------------
 struct HcaQuantParams {

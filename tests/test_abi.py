@@ -77,6 +77,12 @@ def _hca_args(**kw):
         (dict(mode=1, pos=None), SA_ERR_NULL),
         (dict(mode=1, pos=4096, workspace=None, workspace_bytes=0, B=1, H=1, n_c_cap=100000), SA_ERR_WORKSPACE),
         (dict(mode=7), SA_ERR_SHAPE),
+        (dict(d=576, d_v=576), SA_ERR_UNSUPPORTED),
+        (dict(d=512, d_v=256), SA_ERR_UNSUPPORTED),
+        (dict(d=576, d_v=512, dtype=0), SA_ERR_UNSUPPORTED),
+        (dict(d=576, d_v=-1), SA_ERR_SHAPE),
+        (dict(mode=1, pos=4096, d=576, d_v=576), SA_ERR_UNSUPPORTED),
+        (dict(mode=1, pos=4096, d=64, d_v=64, dtype=0), SA_ERR_UNSUPPORTED),
     ],
 )
 def test_hca_attention_validation(sa, kw, code):
@@ -87,7 +93,11 @@ def test_hca_attention_validation(sa, kw, code):
 
 def test_hca_decode_workspace_size_positive(sa):
     a = _hca_args(mode=1, B=4, H=64, n_c_cap=8192)
-    assert sa.lib().hca_attention_fwd_workspace_size(ctypes.byref(a)) > 0
+    n = sa.lib().hca_attention_fwd_workspace_size(ctypes.byref(a))
+    assert n > 0
+    # the split partials hold value-width rows: qk 576 / v 512 needs the same workspace
+    a = _hca_args(mode=1, B=4, H=64, n_c_cap=8192, d=576, d_v=512)
+    assert sa.lib().hca_attention_fwd_workspace_size(ctypes.byref(a)) == n
     a = _hca_args(mode=0)
     assert sa.lib().hca_attention_fwd_workspace_size(ctypes.byref(a)) == 0
 

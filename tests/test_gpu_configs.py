@@ -28,10 +28,10 @@ pytestmark = pytest.mark.gpu
 BLK = WIN = 128
 
 
-def _hca_prefill_case(sa, sigma, seed):
+def _hca_prefill_case(sa, sigma, seed, dqk=512):
     T, H, d = 32768, 64, 512
-    q = synth.torch_normal((1, H, T, d), sigma, torch.bfloat16, seed, DEV)
-    k = synth.torch_normal((1, H, T, d), sigma, torch.bfloat16, seed + 1, DEV)
+    q = synth.torch_normal((1, H, T, dqk), sigma, torch.bfloat16, seed, DEV)
+    k = synth.torch_normal((1, H, T, dqk), sigma, torch.bfloat16, seed + 1, DEV)
     v = synth.torch_normal((1, H, T, d), sigma, torch.bfloat16, seed + 2, DEV)
     kc = sa.hca_compress(k, BLK)
     vc = sa.hca_compress(v, BLK)
@@ -64,15 +64,22 @@ def test_hca_prefill_32768x64x512_config_distribution():
     assert _hca_prefill_case(sa, sigma, 1300) <= BF16_ABS_TOL * sigma
 
 
-@pytest.mark.parametrize("B,ncap,pos,sigma", [(64, 1024, 131071, 1.0), (64, 1024, 131071, 512 ** -0.5),
-                                              (4, 8192, 1048575, 1.0)])
-def test_hca_decode_full(B, ncap, pos, sigma):
+def test_hca_prefill_32768x64_qk576_v512_unit_variance():
+    """The wider query/key head (qk 576, v 512) at the prefill workload's size."""
+    sa = require_gpu()
+    assert _hca_prefill_case(sa, 1.0, 1250, dqk=576) <= BF16_ABS_TOL
+
+
+@pytest.mark.parametrize("B,ncap,pos,sigma,dqk", [(64, 1024, 131071, 1.0, 512), (64, 1024, 131071, 512 ** -0.5, 512),
+                                                  (4, 8192, 1048575, 1.0, 512), (64, 1024, 131071, 1.0, 576),
+                                                  (4, 8192, 1048575, 1.0, 576)])
+def test_hca_decode_full(B, ncap, pos, sigma, dqk):
     sa = require_gpu()
     H, d = 64, 512
-    q = synth.torch_normal((B, H, d), sigma, torch.bfloat16, 1400, DEV)
-    kc = synth.torch_normal((B, H, ncap, d), sigma, torch.bfloat16, 1401, DEV)
+    q = synth.torch_normal((B, H, dqk), sigma, torch.bfloat16, 1400, DEV)
+    kc = synth.torch_normal((B, H, ncap, dqk), sigma, torch.bfloat16, 1401, DEV)
     vc = synth.torch_normal((B, H, ncap, d), sigma, torch.bfloat16, 1402, DEV)
-    rk = synth.torch_normal((B, H, WIN, d), sigma, torch.bfloat16, 1403, DEV)
+    rk = synth.torch_normal((B, H, WIN, dqk), sigma, torch.bfloat16, 1403, DEV)
     rv = synth.torch_normal((B, H, WIN, d), sigma, torch.bfloat16, 1404, DEV)
     posd = torch.full((B,), pos, dtype=torch.int64, device=DEV)
     o, lse = sa.hca_attention_fwd(sa.HCA_DECODE, q, rk, rv, kc, vc, BLK, WIN, pos=posd, return_lse=True)

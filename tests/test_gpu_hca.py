@@ -22,7 +22,8 @@ def _inputs(shape, dtype, sigma, workload):
 
 
 @pytest.mark.parametrize("dtype,d,T,blk", [("f32", 64, 1024, 128), ("f32", 64, 300, 128), ("bf16", 512, 700, 128),
-                                           ("bf16", 512, 37, 4), ("bf16", 256, 260, 128), ("f32", 64, 9, 1)])
+                                           ("bf16", 512, 37, 4), ("bf16", 256, 260, 128), ("f32", 64, 9, 1),
+                                           ("bf16", 576, 300, 128), ("bf16", 576, 50, 3)])
 def test_compress(dtype, d, T, blk):
     sa = require_gpu()
     x = synth.np_normal((2, 3, T, d), 1.0, dtype, 101, 0)
@@ -141,6 +142,88 @@ def test_decode_equals_prefill_row():
     for t in (0, 200, 511, 767, 899):
         ring_k = torch.zeros((1, 2, window, d), dtype=torch.bfloat16, device=DEV)
         ring_v = torch.zeros_like(ring_k)
+        for s in range(max(0, t - window + 1), t + 1):
+            ring_k[:, :, s % window] = tk[:, :, s]
+            ring_v[:, :, s % window] = tv[:, :, s]
+        pos = torch.tensor([t], dtype=torch.int64, device=DEV)
+        o_dec = sa.hca_attention_fwd(sa.HCA_DECODE, tq[:, :, t].contiguous(), ring_k, ring_v, kc, vc, blk, window, pos=pos)
+        assert max_abs_err(f64(o_dec), f64(o_pre[:, :, t])) <= 1e-2, f"t={t}"
+
+
+# ---------------------------------------------------------------------------
+# Query/key head wider than the value head (qk 576 / v 512)
+# ---------------------------------------------------------------------------
+
+
+def _wide_inputs(B, H, T, workload, dqk=576, dv=512):
+    q = synth.np_normal((B, H, T, dqk), 1.0, "bf16", workload, 0)
+    k = synth.np_normal((B, H, T, dqk), 1.0, "bf16", workload, 1)
+    v = synth.np_normal((B, H, T, dv), 1.0, "bf16", workload, 2)
+    return (q, k, v), [synth.to_torch(a, "bf16", DEV) for a in (q, k, v)]
+
+
+@pytest.mark.parametrize(
+    "T,blk,window,H",
+    [(700, 128, 128, 2), (1200, 128, 128, 1), (257, 128, 128, 1), (200, 4, 6, 2), (130, 1, 5, 1), (150, 16, 200, 1),
+     (1, 128, 128, 1), (333, 32, 1, 1)],
+)
+def test_prefill_qk576_v512(T, blk, window, H):
+    """qk 576 / v 512 on unit-variance inputs: max-abs <= 2e-2 against the oracle (several 128-query
+    workgroup tiles, ragged tails, blk = 1 and window >= T (dense causal), window = 1)."""
+    sa = require_gpu()
+    (q, k, v), (tq, tk, tv) = _wide_inputs(1, H, T, 30 + T + blk)
+    o, lse = _prefill_gpu(sa, tq, tk, tv, blk, window)
+    assert o.shape == (1, H, T, 512)
+    ow, lw = oracle.hca_attention_prefill(q, k, v, oracle.hca_compress(k, blk), oracle.hca_compress(v, blk), blk, window)
+    assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL
+    assert max_abs_err(f64(lse), lw) <= 1e-2
+
+
+def test_prefill_qk576_extra_dims_enter_logits():
+    """The 64 extra query/key dims change the result; with them zeroed it equals the 512-wide call at the
+    same scale (1/24), so they enter only through the logits."""
+    sa = require_gpu()
+    T, blk, window = 600, 128, 128
+    (q, k, v), (tq, tk, tv) = _wide_inputs(1, 2, T, 31)
+    o_wide = _prefill_gpu(sa, tq, tk, tv, blk, window)[0]
+    tk0 = tk.clone()
+    tk0[..., 512:] = 0
+    kc0, vc = sa.hca_compress(tk0, blk), sa.hca_compress(tv, blk)
+    o_zero = sa.hca_attention_fwd(sa.HCA_PREFILL, tq, tk0, tv, kc0, vc, blk, window)
+    o_512 = sa.hca_attention_fwd(sa.HCA_PREFILL, tq[..., :512].contiguous(), tk0[..., :512].contiguous(), tv,
+                                 kc0[..., :512].contiguous(), vc, blk, window, scale=1.0 / 24)
+    assert max_abs_err(f64(o_zero), f64(o_512)) <= 1e-2
+    assert max_abs_err(f64(o_wide), f64(o_zero)) > 1e-2
+
+
+@pytest.mark.parametrize("B,H,ncap,positions", [(3, 2, 10, [0, 130, 1407]), (2, 3, 12, [5000, 127]),
+                                                 (1, 2, 2000, [256000]), (4, 1, 3, [255, 256, 383, 384])])
+def test_decode_qk576_v512(B, H, ncap, positions):
+    sa = require_gpu()
+    blk, window = 128, 128
+    q = synth.np_normal((B, H, 576), 1.0, "bf16", 32, 0)
+    kc = synth.np_normal((B, H, ncap, 576), 1.0, "bf16", 32, 1)
+    vc = synth.np_normal((B, H, ncap, 512), 1.0, "bf16", 32, 2)
+    rk = synth.np_normal((B, H, window, 576), 1.0, "bf16", 32, 3)
+    rv = synth.np_normal((B, H, window, 512), 1.0, "bf16", 32, 4)
+    pos = torch.tensor(positions, dtype=torch.int64, device=DEV)
+    t = [synth.to_torch(a, "bf16", DEV) for a in (q, rk, rv, kc, vc)]
+    o, lse = sa.hca_attention_fwd(sa.HCA_DECODE, t[0], t[1], t[2], t[3], t[4], blk, window, pos=pos, return_lse=True)
+    assert o.shape == (B, H, 512)
+    ow, lw = oracle.hca_attention_decode(q, kc, vc, rk, rv, positions, blk, window)
+    assert max_abs_err(f64(o), ow) <= BF16_ABS_TOL
+    assert max_abs_err(f64(lse), lw) <= 1e-2
+
+
+def test_decode_equals_prefill_row_qk576():
+    sa = require_gpu()
+    T, blk, window = 900, 128, 128
+    (q, k, v), (tq, tk, tv) = _wide_inputs(1, 2, T, 33)
+    kc, vc = sa.hca_compress(tk, blk), sa.hca_compress(tv, blk)
+    o_pre = sa.hca_attention_fwd(sa.HCA_PREFILL, tq, tk, tv, kc, vc, blk, window)
+    for t in (0, 200, 511, 767, 899):
+        ring_k = torch.zeros((1, 2, window, 576), dtype=torch.bfloat16, device=DEV)
+        ring_v = torch.zeros((1, 2, window, 512), dtype=torch.bfloat16, device=DEV)
         for s in range(max(0, t - window + 1), t + 1):
             ring_k[:, :, s % window] = tk[:, :, s]
             ring_v[:, :, s % window] = tv[:, :, s]
