@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of parts: prefill,decode128k,decode1m (default all); "
+                    help="comma list of parts: prefill,variants,decode128k,decode1m (default all; variants = the CSA layer "
+                         "and the qk 576 / v 512 HCA head, run with prefill); "
                          "'copy' runs a plain 1 GiB device copy used to calibrate counter byte totals")
     return ap.parse_args()
 
@@ -107,7 +108,7 @@ def main():
     sa.lib()
     dev = "cuda:0"
     timer = Timer(torch)
-    parts = set(args.only.split(",")) if args.only else {"prefill", "decode128k", "decode1m"}
+    parts = set(args.only.split(",")) if args.only else {"prefill", "variants", "decode128k", "decode1m"}
     result = {}
     kernels = {}
     if "copy" in parts:
@@ -192,57 +193,58 @@ def main():
             t = timer.time(fn, n_it)
             kernels[name] = {"ms": sum(t) / len(t)}
 
-        # The CSA variant of the MLA layer over the same token-level inputs (an
-        # extra figure, not part of the step): block-4 means of k_I, K and V,
-        # then indexer, top-2048 and sparse attention over the 8192 entries.
-        progress("CSA variant")
-        S_c = T_PREFILL // CSA_RATIO
-        kci = torch.empty((1, 1, S_c, DI), dtype=torch.bfloat16, device=dev)
-        kcd = torch.empty((1, 1, S_c, D_DSA), dtype=torch.bfloat16, device=dev)
-        vcd = torch.empty_like(kcd)
-        sc_c = torch.empty((1, T_PREFILL, S_c), dtype=torch.float32, device=dev)
-        idx_c = torch.empty((1, T_PREFILL, TOPK), dtype=torch.int32, device=dev)
+        if "variants" in parts:
+            # The CSA variant of the MLA layer over the same token-level inputs (an
+            # extra figure, not part of the step): block-4 means of k_I, K and V,
+            # then indexer, top-2048 and sparse attention over the 8192 entries.
+            progress("CSA variant")
+            S_c = T_PREFILL // CSA_RATIO
+            kci = torch.empty((1, 1, S_c, DI), dtype=torch.bfloat16, device=dev)
+            kcd = torch.empty((1, 1, S_c, D_DSA), dtype=torch.bfloat16, device=dev)
+            vcd = torch.empty_like(kcd)
+            sc_c = torch.empty((1, T_PREFILL, S_c), dtype=torch.float32, device=dev)
+            idx_c = torch.empty((1, T_PREFILL, TOPK), dtype=torch.int32, device=dev)
 
-        def csa_step():
-            sa.hca_compress(ki[:, None], CSA_RATIO, out=kci)
-            sa.hca_compress(kd[:, None], CSA_RATIO, out=kcd)
-            sa.hca_compress(vd[:, None], CSA_RATIO, out=vcd)
-            sa.csa_indexer_scores(qi, kci[:, 0], wi, CSA_RATIO, out=sc_c)
-            sa.csa_topk(sc_c, TOPK, CSA_RATIO, out=idx_c)
-            return sa.dsa_sparse_attention_fwd(qd, kcd[:, 0], vcd[:, 0], idx_c)
+            def csa_step():
+                sa.hca_compress(ki[:, None], CSA_RATIO, out=kci)
+                sa.hca_compress(kd[:, None], CSA_RATIO, out=kcd)
+                sa.hca_compress(vd[:, None], CSA_RATIO, out=vcd)
+                sa.csa_indexer_scores(qi, kci[:, 0], wi, CSA_RATIO, out=sc_c)
+                sa.csa_topk(sc_c, TOPK, CSA_RATIO, out=idx_c)
+                return sa.dsa_sparse_attention_fwd(qd, kcd[:, 0], vcd[:, 0], idx_c)
 
-        for _ in range(args.warmup):
-            csa_step()
-        torch.cuda.synchronize()
-        t_c = timer.time(csa_step, max(3, args.steps))
-        ms_c = sum(t_c) / len(t_c)
-        result["csa_prefill"] = {"ms_per_layer": ms_c, "tokens_per_s": T_PREFILL / (ms_c * 1e-3), "ratio": CSA_RATIO,
-                                 "entries": S_c, "top_k": TOPK}
-        del kci, kcd, vcd, sc_c, idx_c
+            for _ in range(args.warmup):
+                csa_step()
+            torch.cuda.synchronize()
+            t_c = timer.time(csa_step, max(3, args.steps))
+            ms_c = sum(t_c) / len(t_c)
+            result["csa_prefill"] = {"ms_per_layer": ms_c, "tokens_per_s": T_PREFILL / (ms_c * 1e-3), "ratio": CSA_RATIO,
+                                     "entries": S_c, "top_k": TOPK}
+            del kci, kcd, vcd, sc_c, idx_c
 
-        # HCA attention with the wider query/key head (qk 576, v 512) over the
-        # same T = 32768, 64 heads (an extra figure, not part of the step).
-        progress("HCA qk576/v512 variant")
-        q6 = synth.torch_normal((1, H, T_PREFILL, D_QK_WIDE), sig, torch.bfloat16, 211, dev)
-        k6 = synth.torch_normal((1, H, T_PREFILL, D_QK_WIDE), sig, torch.bfloat16, 212, dev)
-        kc6 = sa.hca_compress(k6, BLK)
+            # HCA attention with the wider query/key head (qk 576, v 512) over the
+            # same T = 32768, 64 heads (an extra figure, not part of the step).
+            progress("HCA qk576/v512 variant")
+            q6 = synth.torch_normal((1, H, T_PREFILL, D_QK_WIDE), sig, torch.bfloat16, 211, dev)
+            k6 = synth.torch_normal((1, H, T_PREFILL, D_QK_WIDE), sig, torch.bfloat16, 212, dev)
+            kc6 = sa.hca_compress(k6, BLK)
 
-        def k_hca_wide():
-            return sa.hca_attention_fwd(sa.HCA_PREFILL, q6, k6, v, kc6, vc, BLK, WIN)
+            def k_hca_wide():
+                return sa.hca_attention_fwd(sa.HCA_PREFILL, q6, k6, v, kc6, vc, BLK, WIN)
 
-        for _ in range(args.warmup):
-            k_hca_wide()
-        torch.cuda.synchronize()
-        t_w = timer.time(k_hca_wide, max(3, args.steps))
-        ms_w = sum(t_w) / len(t_w)
-        pairs_w = hca_pairs_per_head(T_PREFILL) * H
-        bytes_w = T_PREFILL * H * (2 * D_QK_WIDE + 2 * D_HCA) * 2
-        flops_w = 2 * (D_QK_WIDE + D_HCA) * pairs_w
-        result["hca_prefill_qk576_v512"] = {
-            "ms": ms_w, "tokens_per_s": T_PREFILL / (ms_w * 1e-3), "alg_bytes": bytes_w, "alg_flops": flops_w,
-            "hbm_frac": bytes_w / (ms_w * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "mfma_frac": flops_w / (ms_w * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
-        del q6, k6, kc6
+            for _ in range(args.warmup):
+                k_hca_wide()
+            torch.cuda.synchronize()
+            t_w = timer.time(k_hca_wide, max(3, args.steps))
+            ms_w = sum(t_w) / len(t_w)
+            pairs_w = hca_pairs_per_head(T_PREFILL) * H
+            bytes_w = T_PREFILL * H * (2 * D_QK_WIDE + 2 * D_HCA) * 2
+            flops_w = 2 * (D_QK_WIDE + D_HCA) * pairs_w
+            result["hca_prefill_qk576_v512"] = {
+                "ms": ms_w, "tokens_per_s": T_PREFILL / (ms_w * 1e-3), "alg_bytes": bytes_w, "alg_flops": flops_w,
+                "hbm_frac": bytes_w / (ms_w * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "mfma_frac": flops_w / (ms_w * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+            del q6, k6, kc6
 
         pairs_hca = hca_pairs_per_head(T_PREFILL) * H
         pairs_dsa = dsa_pairs(T_PREFILL) * HQ
