@@ -153,6 +153,12 @@ def _need(t, name, dtype=None, dim=None):
         raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
 
 
+def _shape(t, name, shape):
+    """The C ABI takes sizes, not shapes: a tensor of the wrong shape would be read or written out of bounds."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def version():
     return lib().sa_version().decode()
 
@@ -165,8 +171,9 @@ def hca_compress(x, blk, out=None):
     n = T // blk
     if out is None:
         out = torch.empty((B, H, n, d), dtype=x.dtype, device=x.device)
-    if out.dim() != 4 or out.shape[-1] != d or out.stride(-1) != 1:
+    if out.dim() != 4 or out.stride(-1) != 1:
         raise ValueError("out must be [B,H,n,d] with a contiguous last dim")
+    _shape(out, "out", (B, H, n, d))
     st = _check(
         "hca_compress",
         lib().hca_compress(
@@ -262,6 +269,8 @@ def hca_quantize_fp8(x, codes=None, scales=None):
         scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
     _need(codes, "codes", torch.uint8)
     _need(scales, "scales", torch.float32)
+    _shape(codes, "codes", x.shape)
+    _shape(scales, "scales", x.shape[:-1])
     _check("hca_quantize_fp8", lib().hca_quantize_fp8(_ptr(x), _ptr(codes), _ptr(scales), rows, d, _stream()))
     return codes, scales
 
@@ -292,6 +301,12 @@ def hca_decode_fp8(q, k, k_scale, v, v_scale, k_c, k_c_scale, v_c, v_c_scale, bl
         _need(t, name, torch.float32, 3)
     _need(pos, "pos", torch.int64, 1)
     B, H, d = q.shape
+    ncap = k_c.shape[2]
+    for name, t, shape in (("k", k, (B, H, window, d)), ("v", v, (B, H, window, d)), ("k_c", k_c, (B, H, ncap, d)),
+                           ("v_c", v_c, (B, H, ncap, d)), ("k_scale", k_scale, (B, H, window)),
+                           ("v_scale", v_scale, (B, H, window)), ("k_c_scale", k_c_scale, (B, H, ncap)),
+                           ("v_c_scale", v_c_scale, (B, H, ncap)), ("pos", pos, (B,))):
+        _shape(t, name, shape)
     o = torch.empty_like(q)
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
     args = _fp8_args(q, k, k_scale, v, v_scale, k_c, k_c_scale, v_c, v_c_scale, blk, window, scale, pos, o, lse)
@@ -319,11 +334,15 @@ def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None, out=None):
     _need(w, "w", torch.float32, 3)
     B, T, Hi, Di = q_idx.shape
     S = k_idx.shape[1]
+    _shape(k_idx, "k_idx", (B, S, Di))
+    _shape(w, "w", (B, T, Hi))
     if q_pos is not None:
         _need(q_pos, "q_pos", torch.int64, 1)
+        _shape(q_pos, "q_pos", (B,))
     if out is None:
         out = torch.empty((B, T, S), dtype=torch.float32, device=q_idx.device)
     _need(out, "out", torch.float32, 3)
+    _shape(out, "out", (B, T, S))
     _check(
         "dsa_indexer_scores",
         lib().dsa_indexer_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q_pos), _ptr(out), B, T, S, Hi, Di, _stream()),
@@ -339,11 +358,15 @@ def csa_indexer_scores(q_idx, kc_idx, w, ratio, q_pos=None, out=None):
     _need(w, "w", torch.float32, 3)
     B, T, Hi, Di = q_idx.shape
     S = kc_idx.shape[1]
+    _shape(kc_idx, "kc_idx", (B, S, Di))
+    _shape(w, "w", (B, T, Hi))
     if q_pos is not None:
         _need(q_pos, "q_pos", torch.int64, 1)
+        _shape(q_pos, "q_pos", (B,))
     if out is None:
         out = torch.empty((B, T, S), dtype=torch.float32, device=q_idx.device)
     _need(out, "out", torch.float32, 3)
+    _shape(out, "out", (B, T, S))
     _check(
         "csa_indexer_scores",
         lib().csa_indexer_scores(_ptr(q_idx), _ptr(kc_idx), _ptr(w), _ptr(q_pos), _ptr(out), B, T, S, Hi, Di, ratio,
@@ -358,9 +381,11 @@ def csa_topk(scores, k, ratio, q_pos=None, out=None, workspace=None):
     B, T, S = scores.shape
     if q_pos is not None:
         _need(q_pos, "q_pos", torch.int64, 1)
+        _shape(q_pos, "q_pos", (B,))
     if out is None:
         out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
     _need(out, "out", torch.int32, 3)
+    _shape(out, "out", (B, T, k))
     need = lib().dsa_topk_workspace_size(B, T, S, k)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
@@ -382,9 +407,11 @@ def dsa_topk(scores, k, q_pos=None, out=None, workspace=None):
     B, T, S = scores.shape
     if q_pos is not None:
         _need(q_pos, "q_pos", torch.int64, 1)
+        _shape(q_pos, "q_pos", (B,))
     if out is None:
         out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
     _need(out, "out", torch.int32, 3)
+    _shape(out, "out", (B, T, k))
     need = lib().dsa_topk_workspace_size(B, T, S, k)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
@@ -409,6 +436,9 @@ def dsa_sparse_attention_fwd(q, k, v, idx, scale=None, return_lse=False, workspa
     B, T, Hq, D = q.shape
     S = k.shape[1]
     kk = idx.shape[2]
+    _shape(k, "k", (B, S, D))
+    _shape(v, "v", (B, S, D))
+    _shape(idx, "idx", (B, T, kk))
     o = torch.empty_like(q)
     lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device) if return_lse else None
     need = lib().dsa_sparse_attention_fwd_workspace_size(B, T, Hq, D, kk)

@@ -222,7 +222,11 @@ static int indexer_impl(const char* fn, const void* q_idx, const void* k_idx, co
     return fail(SA_ERR_UNSUPPORTED, "%s: S must be <= 2^24 and T < 2^31", fn);
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w) || !aligned16(scores))
     return fail(SA_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
-  const int64_t nblocks = B * ((T + 63) / 64) * ((S + 1023) / 1024);
+  // Grid of the launch: decode shapes take 128 (T <= 4) or 256 (T <= 16)
+  // positions per workgroup, prefill shapes 64 queries x 1024 positions.
+  const int64_t nblocks = T <= 4    ? B * ((S + 127) / 128)
+                          : T <= 16 ? B * ((S + 255) / 256)
+                                    : B * ((T + 63) / 64) * ((S + 1023) / 1024);
   if (nblocks > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "%s: grid too large", fn);
   sa::DsaIndexerParams p{q_idx, k_idx, w, q_pos, scores, B, T, S, ratio};
   return hip_status(sa::launch_dsa_indexer(p, stream), fn);

@@ -14,8 +14,9 @@
 // ring with direct global->LDS loads and covers a chunk of 1024 positions.
 // Workgroups are ordered chunk-major, so the query tiles that read one k_idx
 // chunk run together and find it in L2.  Prefill shapes use 4 waves (64
-// queries) per workgroup; decode shapes (T <= 16) use 1 wave per workgroup so
-// that many workgroups stream the positions in parallel.
+// queries) per workgroup; decode shapes (T <= 16) use 1 wave per workgroup
+// and short chunks of positions so that many workgroups stream them in
+// parallel (up to 4 queries: the register-operand kernel below).
 // The build compiles this file without NaN semantics (scores of finite inputs
 // are finite), which makes the ReLU a single max instruction.
 #include "common.h"
@@ -27,8 +28,11 @@ constexpr int kIdxDi = 128;
 constexpr int kIdxHi = 4;
 constexpr int kIdxQPerWave = 16;                // queries per wave (4 M-blocks)
 constexpr int kIdxKTile = 64;                   // positions per LDS tile
-constexpr int kIdxTilesPerChunk = 16;
-constexpr int kIdxChunk = kIdxTilesPerChunk * kIdxKTile;  // positions per workgroup
+constexpr int kIdxTilesPerChunk = 16;  // prefill: positions per workgroup = 16 tiles
+// Decode: 4 tiles (256 positions) per 1-wave workgroup.  At 1M positions and
+// B = 4 that is 16384 workgroups; measured against 1, 2, 8, 16 and 52 tiles
+// (one resident round), 4 is fastest.
+constexpr int kIdxDecodeTiles = 4;
 constexpr int kIdxRowBytes = kIdxDi * 2;                  // 256
 constexpr int kIdxRowChunks = kIdxRowBytes / 16;          // 16
 constexpr int kIdxTileBytes = kIdxKTile * kIdxRowBytes;   // 16 KB
@@ -55,7 +59,8 @@ __device__ __forceinline__ void idx_stage(char* buf, buffer_rsrc_t rsrc, int s0,
 }
 
 template <int kWaves>
-__global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerParams p, int n_qtiles, int n_chunks) {
+__global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerParams p, int n_qtiles, int n_chunks,
+                                                                   int chunk) {
   __shared__ __attribute__((aligned(16))) char lds0[kIdxTileBytes];
   __shared__ __attribute__((aligned(16))) char lds1[kIdxTileBytes];
   constexpr int kQTile = kWaves * kIdxQPerWave;
@@ -87,14 +92,14 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   const int i0 = qt * kQTile;
   const int i_last = min(i0 + kQTile - 1, T - 1);
   const int s_end = min(S, lim(i_last) + 1);  // exclusive, whole workgroup
-  const int s_begin = kc * kIdxChunk;
+  const int s_begin = kc * chunk;  // chunk: positions per workgroup, a multiple of the tile
   if (s_begin >= s_end) return;
-  const int s_stop = min(s_end, s_begin + kIdxChunk);
+  const int s_stop = min(s_end, s_begin + chunk);
   const int n_tiles = (s_stop - s_begin + kIdxKTile - 1) / kIdxKTile;
 
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int L = lane & 15, g = lane >> 4;
-  const int iw = i0 + wave * kIdxQPerWave;                  // first query of the wave
+  const int iw = i0 + wave * kIdxQPerWave;                   // first query of the wave
   const int n_mb = max(0, min(4, (T - iw + 3) / 4));          // M-blocks with a valid query
   const int wave_plim = n_mb > 0 ? lim(min(iw + kIdxQPerWave - 1, T - 1)) : -1;
 
@@ -134,8 +139,9 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   float held[2][4][4];
   int held_s0[2] = {-1, -1};  // first position of the held tile (-1: nothing held)
   // Every position of a tile is visible to every query of the wave when the
-  // tile ends at or before the first query's limit (all 16 queries valid).
-  const int wave_full_lim = n_mb == 4 ? lim(iw) : -1;
+  // tile ends at or before the first query's limit and all 16 of the wave's
+  // query rows exist (rows past T must not be stored).
+  const int wave_full_lim = iw + kIdxQPerWave - 1 < T ? lim(iw) : -1;
   auto store_held = [&](int slot) __attribute__((always_inline)) {
     const int h0 = held_s0[slot];
     if (h0 < 0) return;
@@ -258,18 +264,131 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   }
 }
 
+// Decode calls of up to 4 queries: one 16-row M-block (4 queries x 4 heads)
+// per wave and no LDS.  Each lane loads its MFMA B operands straight from
+// k_idx into registers: for 16-position block nb and 32-dim step ks, lane
+// (L = lane % 16, g = lane / 16) takes dims 32*ks + 8*g .. +7 of position
+// 16*nb + L, i.e. 16 bytes of a row, and a tile of 64 positions is 16 such
+// loads per lane.  Tiles are double-buffered in registers; a tile's scores
+// are stored after the next tile's loads are sent, so the wait before a tile
+// (which also covers the wave's earlier stores) finds those stores long done.
+// Without the LDS limit of the staged kernel (5 one-wave workgroups per CU)
+// eight waves per CU keep a tile each in flight.
+constexpr int kIdxDecTiles = 2;  // 64-position tiles per workgroup (1, 2, 4, 8, 16 measured: 2 is fastest)
+
+__global__ __launch_bounds__(64) void dsa_indexer_dec_kernel(DsaIndexerParams p, int n_chunks) {
+  const int b = (int)(blockIdx.x / (uint32_t)n_chunks);
+  const int kc = (int)(blockIdx.x % (uint32_t)n_chunks);
+  const int T = (int)p.T, S = (int)p.S;
+  const int base = p.q_pos ? (int)p.q_pos[b] : 0;
+  const int64_t ratio = p.ratio;
+  auto lim = [&](int qi) -> int {  // last key visible to query row qi (-1 or less: none)
+    const int64_t x = ((int64_t)base + qi + 1) / ratio - 1;
+    return (int)(x < S - 1 ? x : S - 1);
+  };
+  constexpr int kChunk = kIdxDecTiles * kIdxKTile;
+  const int s_begin = kc * kChunk;
+  const int s_end = min(S, lim(T - 1) + 1);  // exclusive
+  if (s_begin >= s_end) return;
+  const int s_stop = min(s_end, s_begin + kChunk);
+  const int n_tiles = (s_stop - s_begin + kIdxKTile - 1) / kIdxKTile;
+
+  const int lane = threadIdx.x & 63;
+  const int L = lane & 15, g = lane >> 4;
+  const bf16_t* qI = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * T * kIdxHi * kIdxDi;
+  const bf16_t* kI = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * S * kIdxDi;
+  const float* wgt = p.w + (int64_t)b * T * kIdxHi;
+  float* out = p.scores + (int64_t)b * T * S;
+
+  // A operand: row (query L/4, head L%4), dims g*8 + 32*ks (zero for rows past T).
+  i16x8_t qa[4];
+  const int qa_i = L >> 2;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (qa_i < T) {
+      const uint4 u = *reinterpret_cast<const uint4*>(qI + ((int64_t)qa_i * kIdxHi + (L & 3)) * kIdxDi + ks * 32 + g * 8);
+      qa[ks] = __builtin_bit_cast(i16x8_t, u);
+    } else {
+      qa[ks] = i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  // This lane's accumulator query is g (heads 0..3 in its four values).
+  float wq[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) wq[h] = g < T ? wgt[(int64_t)g * kIdxHi + h] : 0.f;
+  const int plim = g < T ? lim(g) : -1;
+  float* orow = out + (int64_t)g * S;
+
+  // B operands of one tile: [nb][ks], 16 bytes each.  Positions past the
+  // chunk's stop load the chunk's first row (finite, never stored).
+  auto load_tile = [&](int tile, uint4 (&bt)[4][4]) __attribute__((always_inline)) {
+    const int s0 = s_begin + tile * kIdxKTile;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int s = s0 + nb * 16 + L;
+      const bf16_t* row = kI + (int64_t)(s < s_stop ? s : s_begin) * kIdxDi + g * 8;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) bt[nb][ks] = *reinterpret_cast<const uint4*>(row + ks * 32);
+    }
+  };
+  float sc[4];
+  auto compute = [&](const uint4 (&bt)[4][4]) __attribute__((always_inline)) {
+    f32x4_t acc[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc[nb] = mfma_bf16_16x16x32(qa[ks], __builtin_bit_cast(i16x8_t, bt[nb][ks]), acc[nb]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      float x = 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) x = fmaf(wq[h], fmaxf(acc[nb][h], 0.f), x);
+      sc[nb] = x;
+    }
+  };
+  auto store = [&](int tile) __attribute__((always_inline)) {
+    const int s0 = s_begin + tile * kIdxKTile;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int s = s0 + nb * 16 + L;
+      if (s <= plim && s < s_stop) orow[s] = sc[nb];
+    }
+  };
+
+  uint4 b0[4][4], b1[4][4];
+  load_tile(0, b0);
+  for (int tile = 0; tile < n_tiles; tile += 2) {
+    if (tile + 1 < n_tiles) load_tile(tile + 1, b1);
+    compute(b0);
+    store(tile);
+    if (tile + 1 >= n_tiles) break;
+    if (tile + 2 < n_tiles) load_tile(tile + 2, b0);
+    compute(b1);
+    store(tile + 1);
+  }
+}
+
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
-  const int64_t n_chunks = (p.S + kIdxChunk - 1) / kIdxChunk;
   if (p.T <= kIdxQPerWave) {
-    const int64_t n_qtiles = 1;
-    const int64_t nblocks = p.B * n_qtiles * n_chunks;
-    hipLaunchKernelGGL(dsa_indexer_kernel<1>, dim3((uint32_t)nblocks), dim3(64), 0, stream, p, (int)n_qtiles,
-                       (int)n_chunks);
+    // Decode: one query tile, short chunks of positions.
+    if (p.T <= 4) {
+      const int64_t n_chunks = (p.S + kIdxDecTiles * kIdxKTile - 1) / (kIdxDecTiles * kIdxKTile);
+      hipLaunchKernelGGL(dsa_indexer_dec_kernel, dim3((uint32_t)(p.B * n_chunks)), dim3(64), 0, stream, p, (int)n_chunks);
+    } else {
+      const int chunk = kIdxDecodeTiles * kIdxKTile;
+      const int64_t n_chunks = (p.S + chunk - 1) / chunk;
+      hipLaunchKernelGGL(dsa_indexer_kernel<1>, dim3((uint32_t)(p.B * n_chunks)), dim3(64), 0, stream, p, 1,
+                         (int)n_chunks, chunk);
+    }
   } else {
+    const int chunk = kIdxTilesPerChunk * kIdxKTile;
+    const int64_t n_chunks = (p.S + chunk - 1) / chunk;
     const int64_t n_qtiles = (p.T + 4 * kIdxQPerWave - 1) / (4 * kIdxQPerWave);
     const int64_t nblocks = p.B * n_qtiles * n_chunks;
     hipLaunchKernelGGL(dsa_indexer_kernel<4>, dim3((uint32_t)nblocks), dim3(256), 0, stream, p, (int)n_qtiles,
-                       (int)n_chunks);
+                       (int)n_chunks, chunk);
   }
   return hipGetLastError();
 }

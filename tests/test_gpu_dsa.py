@@ -39,7 +39,8 @@ def _causal_mask(B, T, S, q_pos):
 
 @pytest.mark.parametrize("B,T,S,q_pos", [(1, 300, 300, None), (2, 70, 333, [263, 100]), (1, 1, 5000, [4999]),
                                          (2, 1, 4500, [4499, 2047]), (1, 1, 70, None),
-                                         (1, 129, 1100, [900])])
+                                         (1, 129, 1100, [900]), (2, 3, 2000, [1999, 700]), (1, 4, 300, None),
+                                         (3, 2, 129, [128, 0, 64]), (1, 9, 2500, [2400])])
 def test_indexer_random(B, T, S, q_pos):
     sa = require_gpu()
     qi, ki, w = _indexer_inputs(B, T, S, 30 + T)
@@ -50,6 +51,30 @@ def test_indexer_random(B, T, S, q_pos):
     m = _causal_mask(B, T, S, q_pos)
     got = f64(sc)
     # fp32 accumulation of 128 exact bf16 products: |err| <= ~1e-6 on O(1) scores
+    assert np.max(np.abs(got[m] - want[m])) <= 2e-6
+
+
+@pytest.mark.parametrize("B,T,S,q_pos", [(2, 14, 2000, [1500, 1200]), (2, 13, 700, [650, 300]), (2, 30, 1500, [1300, 1000]),
+                                         (1, 47, 2100, [2000]), (2, 15, 900, None)])
+def test_indexer_partial_wave_rows_stay_in_bounds(B, T, S, q_pos):
+    """A wave whose 16 query rows are not all real (13..15 left) stores nothing for the missing rows, also on
+    tiles its real rows see in full: a guard region behind the scores keeps its sentinel, entries past each
+    row's causal limit are not written, and every visible score matches the oracle (so the next batch's rows
+    were not overwritten either)."""
+    sa = require_gpu()
+    qi, ki, w = _indexer_inputs(B, T, S, 40 + T)
+    qp = None if q_pos is None else torch.tensor(q_pos, dtype=torch.int64, device=DEV)
+    n = B * T * S
+    buf = torch.full((n + 4 * S,), -7.0, dtype=torch.float32, device=DEV)
+    out = buf[:n].view(B, T, S)
+    sa.dsa_indexer_scores(synth.to_torch(qi, "bf16", DEV), synth.to_torch(ki, "bf16", DEV), synth.to_torch(w, "f32", DEV),
+                          q_pos=qp, out=out)
+    torch.cuda.synchronize()
+    assert bool((buf[n:] == -7.0).all()), "write past the end of the scores"
+    m = _causal_mask(B, T, S, q_pos)
+    got = f64(out)
+    assert np.all(got[~m] == -7.0), "write past a row's causal limit"
+    want = oracle.dsa_indexer_scores(qi, ki, w, q_pos=q_pos)
     assert np.max(np.abs(got[m] - want[m])) <= 2e-6
 
 
