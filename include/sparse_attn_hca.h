@@ -273,6 +273,34 @@ int csa_topk(const float* scores, const int64_t* q_pos, int32_t* idx,
              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * dsa_indexer_topk -- fused indexer and top-k (an extra export beside the two
+ * separate calls, which define its result).
+ *
+ * [P1] §二.1, [P3] §架構創新 1: the indexer scores every history position and
+ * only the top-k positions are kept.  This call writes exactly the idx that
+ * dsa_indexer_scores followed by dsa_topk would write for the same inputs
+ * (the same fp32 scores, score descending then position ascending, ascending
+ * output padded with -1) without writing the [B,T,S] score matrix: a sample
+ * of every 16th position sets a per-row threshold, the indexer keeps only the
+ * (key, position) pairs at or above it, and an exact selection runs over
+ * those.  Rows where the sample misjudges the threshold (fewer than k or more
+ * than 8192 candidates) are recomputed exactly by the separate kernels inside
+ * the call, so the result never depends on the sample.
+ * q_idx: [B,T,Hi,Di] bf16; k_idx: [B,S,Di] bf16; w: [B,T,Hi] fp32;
+ * q_pos: device int64[B] or NULL (as for dsa_indexer_scores);
+ * idx: [B,T,k] int32.
+ * force_fallback: 0 normally; nonzero sends every row with more than k
+ * candidates through the exact recomputation (a test of that path).
+ * Supported: Hi = 4, Di = 128, S <= 32768, 1 <= k <= 2048.
+ * Workspace: dsa_indexer_topk_workspace_size() bytes (it includes room for
+ * the candidates and for the recomputed rows' scores).
+ * ------------------------------------------------------------------------ */
+size_t dsa_indexer_topk_workspace_size(int64_t B, int64_t T, int64_t S, int64_t k);
+int dsa_indexer_topk(const void* q_idx, const void* k_idx, const float* w, const int64_t* q_pos, int32_t* idx,
+                     int64_t B, int64_t T, int64_t S, int64_t Hi, int64_t Di, int64_t k,
+                     int64_t force_fallback, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * dsa_sparse_attention_fwd -- exact attention over the selected positions.
  *
  * [P1] §二.1 / [P3] §架構創新 1: core attention runs only on the top-K

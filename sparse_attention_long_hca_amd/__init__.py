@@ -16,6 +16,8 @@ from ._lib import (
     dsa_sparse_attention_fwd_workspace_size,
     dsa_topk,
     dsa_topk_workspace_size,
+    dsa_indexer_topk,
+    dsa_indexer_topk_workspace_size,
     hca_attention_fwd,
     hca_attention_workspace_size,
     hca_compress,
@@ -38,6 +40,8 @@ __all__ = [
     "dsa_sparse_attention_fwd_workspace_size",
     "dsa_topk",
     "dsa_topk_workspace_size",
+    "dsa_indexer_topk",
+    "dsa_indexer_topk_workspace_size",
     "hca_attention_fwd",
     "hca_attention_workspace_size",
     "hca_compress",

@@ -95,6 +95,8 @@ EXPORTS = {
     "csa_indexer_scores": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p] + [_c_i64] * 6 + [_c_p]),
     "csa_topk": (ctypes.c_int, [_c_p, _c_p, _c_p] + [_c_i64] * 5 + [_c_p, ctypes.c_size_t, _c_p]),
     "dsa_topk_workspace_size": (ctypes.c_size_t, [_c_i64] * 4),
+    "dsa_indexer_topk_workspace_size": (ctypes.c_size_t, [_c_i64] * 4),
+    "dsa_indexer_topk": (ctypes.c_int, [_c_p] * 5 + [_c_i64] * 7 + [_c_p, ctypes.c_size_t, _c_p]),
     "dsa_topk": (ctypes.c_int, [_c_p, _c_p, _c_p] + [_c_i64] * 4 + [_c_p, ctypes.c_size_t, _c_p]),
     "dsa_sparse_attention_fwd_workspace_size": (ctypes.c_size_t, [_c_i64] * 5),
     "dsa_sparse_attention_fwd": (
@@ -393,6 +395,39 @@ def csa_topk(scores, k, ratio, q_pos=None, out=None, workspace=None):
     _check(
         "csa_topk",
         lib().csa_topk(_ptr(scores), _ptr(q_pos), _ptr(out), B, T, S, k, ratio, _ptr(workspace), wsb, _stream()),
+    )
+    return out
+
+
+def dsa_indexer_topk_workspace_size(B, T, S, k):
+    return lib().dsa_indexer_topk_workspace_size(B, T, S, k)
+
+
+def dsa_indexer_topk(q_idx, k_idx, w, k, q_pos=None, out=None, workspace=None, force_fallback=False):
+    """Fused indexer and top-k: the idx of dsa_topk(dsa_indexer_scores(q_idx, k_idx, w, q_pos), k, q_pos)
+    without the score matrix.  q_idx [B,T,Hi,Di] bf16, k_idx [B,S,Di] bf16, w [B,T,Hi] f32 -> idx [B,T,k] int32."""
+    _need(q_idx, "q_idx", torch.bfloat16, 4)
+    _need(k_idx, "k_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 3)
+    B, T, Hi, Di = q_idx.shape
+    S = k_idx.shape[1]
+    _shape(k_idx, "k_idx", (B, S, Di))
+    _shape(w, "w", (B, T, Hi))
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int64, 1)
+        _shape(q_pos, "q_pos", (B,))
+    if out is None:
+        out = torch.empty((B, T, k), dtype=torch.int32, device=q_idx.device)
+    _need(out, "out", torch.int32, 3)
+    _shape(out, "out", (B, T, k))
+    need = lib().dsa_indexer_topk_workspace_size(B, T, S, k)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_idx.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(
+        "dsa_indexer_topk",
+        lib().dsa_indexer_topk(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q_pos), _ptr(out), B, T, S, Hi, Di, k,
+                               1 if force_fallback else 0, _ptr(workspace), wsb, _stream()),
     )
     return out
 

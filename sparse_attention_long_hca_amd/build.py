@@ -30,6 +30,7 @@ SOURCES = [
     "hca_quant.hip",
     "dsa_indexer.hip",
     "dsa_topk.hip",
+    "dsa_fused.hip",
     "dsa_sparse_attn.hip",
 ]
 

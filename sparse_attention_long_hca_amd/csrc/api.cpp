@@ -281,6 +281,34 @@ int csa_topk(const float* scores, const int64_t* q_pos, int32_t* idx, int64_t B,
 }
 
 // ---------------------------------------------------------------------------
+size_t dsa_indexer_topk_workspace_size(int64_t B, int64_t T, int64_t S, int64_t k) {
+  if (B <= 0 || T <= 0 || S <= 0 || k <= 0) return 0;
+  return sa::dsa_indexer_topk_ws_bytes(B, T, S, k);
+}
+
+int dsa_indexer_topk(const void* q_idx, const void* k_idx, const float* w, const int64_t* q_pos, int32_t* idx,
+                     int64_t B, int64_t T, int64_t S, int64_t Hi, int64_t Di, int64_t k, int64_t force_fallback,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dsa_indexer_topk";
+  if (!q_idx || !k_idx || !w || !idx) return fail(SA_ERR_NULL, "%s: q_idx, k_idx, w, idx must be non-NULL", fn);
+  if (B <= 0 || T <= 0 || S <= 0 || Hi <= 0 || Di <= 0 || k <= 0) return fail(SA_ERR_SHAPE, "%s: sizes must be > 0", fn);
+  if (Hi != 4 || Di != 128) return fail(SA_ERR_UNSUPPORTED, "%s: supported Hi = 4, Di = 128", fn);
+  if (S > 32768) return fail(SA_ERR_UNSUPPORTED, "%s: S must be <= 32768", fn);
+  if (k > 2048) return fail(SA_ERR_UNSUPPORTED, "%s: k must be <= 2048", fn);
+  if (B * T > 0x7fffffffLL || B * ((T + 63) / 64) * ((S + 1023) / 1024) > 0x7fffffffLL)
+    return fail(SA_ERR_SHAPE, "%s: too many rows", fn);
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w) || !aligned16(idx))
+    return fail(SA_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  const size_t need = sa::dsa_indexer_topk_ws_bytes(B, T, S, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(SA_ERR_WORKSPACE, "%s: needs %zu workspace bytes, got %zu", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(SA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  sa::DsaIndexerTopkParams p{q_idx, k_idx, w, q_pos, idx, B, T, S, k, workspace, force_fallback != 0 ? 1 : 0};
+  return hip_status(sa::launch_dsa_indexer_topk(p, stream), fn);
+}
+
+// ---------------------------------------------------------------------------
 size_t dsa_sparse_attention_fwd_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t D, int64_t kk) {
   if (B <= 0 || T <= 0 || Hq <= 0 || D <= 0 || kk <= 0) return 0;
   return sa::dsa_sparse_workspace_bytes(B * T, sa::dsa_sparse_nsplit(B * T, kk), Hq, D);

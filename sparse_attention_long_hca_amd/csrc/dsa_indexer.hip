@@ -21,6 +21,7 @@
 // are finite), which makes the ReLU a single max instruction.
 #include "common.h"
 #include "kernels.h"
+#include "select_util.h"
 
 namespace sa {
 
@@ -58,7 +59,8 @@ __device__ __forceinline__ void idx_stage(char* buf, buffer_rsrc_t rsrc, int s0,
   }
 }
 
-template <int kWaves>
+// kEmit: candidate mode (see DsaIndexerParams) instead of storing scores.
+template <int kWaves, bool kEmit>
 __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerParams p, int n_qtiles, int n_chunks,
                                                                    int chunk) {
   __shared__ __attribute__((aligned(16))) char lds0[kIdxTileBytes];
@@ -91,6 +93,16 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   };
   const int i0 = qt * kQTile;
   const int i_last = min(i0 + kQTile - 1, T - 1);
+  if (p.row_flag) {  // row filter: run only for a tile that holds a flagged row
+    __shared__ uint32_t any_row;
+    if (threadIdx.x == 0) any_row = 0u;
+    __syncthreads();
+    if (*p.any_flag != 0u && (int)threadIdx.x < kQTile && i0 + (int)threadIdx.x < T &&
+        p.row_flag[(int64_t)b * T + i0 + threadIdx.x] != 0u)
+      any_row = 1u;
+    __syncthreads();
+    if (any_row == 0u) return;
+  }
   const int s_end = min(S, lim(i_last) + 1);  // exclusive, whole workgroup
   const int s_begin = kc * chunk;  // chunk: positions per workgroup, a multiple of the tile
   if (s_begin >= s_end) return;
@@ -142,7 +154,66 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   // tile ends at or before the first query's limit and all 16 of the wave's
   // query rows exist (rows past T must not be stored).
   const int wave_full_lim = iw + kIdxQPerWave - 1 < T ? lim(iw) : -1;
+  // Candidate mode: the threshold of each of this lane's accumulator rows
+  // (0 for rows that keep every position, which emit nothing).
+  uint32_t thr[4];
+  bool emit_row[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int qi = iw + mb * 4 + g;
+    emit_row[mb] = kEmit && qi < T && plim[mb] + 1 > (int)p.topk;
+    thr[mb] = emit_row[mb] ? p.thresh[(int64_t)b * T + qi] : 0u;
+  }
+  auto emit_held = [&](int slot) __attribute__((always_inline)) {
+    const int h0 = held_s0[slot];
+    if (h0 < 0) return;
+    // Lanes 16g .. 16g + 15 hold a row's 64 positions of the tile (per
+    // M-block).  Counts and in-row offsets for all four rows first, then the
+    // four slot reservations (one atomic per row and tile) back to back, so
+    // the wave waits for one round trip, then the stores.
+    uint32_t fl[4], incl[4], total[4], base[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      fl[mb] = 0u;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int s = h0 + nb * 16 + L;
+        fl[mb] |= (emit_row[mb] && s <= plim[mb] && score_key(held[slot][mb][nb]) >= thr[mb]) ? (1u << nb) : 0u;
+      }
+      const uint32_t mine = (uint32_t)__popc(fl[mb]);
+      uint32_t x = mine;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off, 16);
+        if (L >= off) x += y;
+      }
+      incl[mb] = x - mine;  // exclusive
+      total[mb] = __shfl(x, 15, 16);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int64_t row = (int64_t)b * T + iw + mb * 4 + g;
+      base[mb] = (L == 0 && total[mb] > 0u) ? atomicAdd(&p.cnt[row], total[mb]) : 0u;
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int64_t row = (int64_t)b * T + iw + mb * 4 + g;
+      uint32_t slot_i = __shfl(base[mb], 0, 16) + incl[mb];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if (fl[mb] & (1u << nb)) {
+          if (slot_i < (uint32_t)p.cap)
+            p.cand[row * p.cap + slot_i] = make_uint2(score_key(held[slot][mb][nb]), (uint32_t)(h0 + nb * 16 + L));
+          ++slot_i;
+        }
+      }
+    }
+  };
   auto store_held = [&](int slot) __attribute__((always_inline)) {
+    if constexpr (kEmit) {
+      emit_held(slot);
+      return;
+    }
     const int h0 = held_s0[slot];
     if (h0 < 0) return;
     if (h0 + kIdxKTile - 1 <= wave_full_lim) {
@@ -373,22 +444,31 @@ __global__ __launch_bounds__(64) void dsa_indexer_dec_kernel(DsaIndexerParams p,
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
   if (p.T <= kIdxQPerWave) {
     // Decode: one query tile, short chunks of positions.
-    if (p.T <= 4) {
+    // (Candidate mode and filtered launches take the staged kernel.)
+    if (p.T <= 4 && !p.cand && !p.row_flag) {
       const int64_t n_chunks = (p.S + kIdxDecTiles * kIdxKTile - 1) / (kIdxDecTiles * kIdxKTile);
       hipLaunchKernelGGL(dsa_indexer_dec_kernel, dim3((uint32_t)(p.B * n_chunks)), dim3(64), 0, stream, p, (int)n_chunks);
     } else {
       const int chunk = kIdxDecodeTiles * kIdxKTile;
       const int64_t n_chunks = (p.S + chunk - 1) / chunk;
-      hipLaunchKernelGGL(dsa_indexer_kernel<1>, dim3((uint32_t)(p.B * n_chunks)), dim3(64), 0, stream, p, 1,
-                         (int)n_chunks, chunk);
+      if (p.cand)
+        hipLaunchKernelGGL((dsa_indexer_kernel<1, true>), dim3((uint32_t)(p.B * n_chunks)), dim3(64), 0, stream, p, 1,
+                           (int)n_chunks, chunk);
+      else
+        hipLaunchKernelGGL((dsa_indexer_kernel<1, false>), dim3((uint32_t)(p.B * n_chunks)), dim3(64), 0, stream, p, 1,
+                           (int)n_chunks, chunk);
     }
   } else {
     const int chunk = kIdxTilesPerChunk * kIdxKTile;
     const int64_t n_chunks = (p.S + chunk - 1) / chunk;
     const int64_t n_qtiles = (p.T + 4 * kIdxQPerWave - 1) / (4 * kIdxQPerWave);
     const int64_t nblocks = p.B * n_qtiles * n_chunks;
-    hipLaunchKernelGGL(dsa_indexer_kernel<4>, dim3((uint32_t)nblocks), dim3(256), 0, stream, p, (int)n_qtiles,
-                       (int)n_chunks, chunk);
+    if (p.cand)
+      hipLaunchKernelGGL((dsa_indexer_kernel<4, true>), dim3((uint32_t)nblocks), dim3(256), 0, stream, p, (int)n_qtiles,
+                         (int)n_chunks, chunk);
+    else
+      hipLaunchKernelGGL((dsa_indexer_kernel<4, false>), dim3((uint32_t)nblocks), dim3(256), 0, stream, p,
+                         (int)n_qtiles, (int)n_chunks, chunk);
   }
   return hipGetLastError();
 }

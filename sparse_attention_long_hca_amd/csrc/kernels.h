@@ -77,6 +77,19 @@ struct DsaIndexerParams {
   float* scores;  // [B,T,S]
   int64_t B, T, S;
   int64_t ratio;  // keys are entries of `ratio` tokens: row i sees keys s < (q_pos + i + 1) / ratio
+  // Candidate mode (cand != NULL; ratio 1): no scores are stored; every row
+  // with more than topk visible positions appends (order-preserving key,
+  // position) of each score whose key is >= thresh[row] to cand[row*cap ..]
+  // and counts them in cnt[row] (appends past cap are dropped, the count
+  // still grows).
+  const uint32_t* thresh;
+  uint32_t* cnt;
+  uint2* cand;
+  int64_t cap, topk;
+  // Row filter (row_flag != NULL): nothing runs unless *any_flag != 0, and a
+  // workgroup runs only if one of its rows has row_flag[row] != 0.
+  const uint32_t* row_flag;
+  const uint32_t* any_flag;
 };
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream);
 
@@ -88,9 +101,26 @@ struct DsaTopkParams {
   int64_t B, T, S, k;
   void* ws;
   int64_t ratio;  // as in DsaIndexerParams
+  // Row filter as in DsaIndexerParams (rows of at most 32768 positions).
+  const uint32_t* row_flag;
+  const uint32_t* any_flag;
 };
 size_t dsa_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k);
 hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream);
+
+// ---- dsa_indexer_topk (fused) -------------------------------------------------
+struct DsaIndexerTopkParams {
+  const void* q;   // [B,T,4,128] bf16
+  const void* k;   // [B,S,128] bf16
+  const float* w;  // [B,T,4]
+  const int64_t* q_pos;
+  int32_t* idx;    // [B,T,topk]
+  int64_t B, T, S, topk;
+  void* ws;
+  int force_fallback;
+};
+size_t dsa_indexer_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k);
+hipError_t launch_dsa_indexer_topk(const DsaIndexerTopkParams& p, hipStream_t stream);
 
 // ---- dsa_sparse_attention_fwd -----------------------------------------------
 struct DsaSparseParams {

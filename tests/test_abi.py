@@ -215,3 +215,22 @@ def test_csa_validation(sa):
     assert L.csa_topk(4096, None, 4096, 1, 4, 4, 2, 0, None, 0, None) == SA_ERR_SHAPE
     assert L.csa_topk(None, None, 4096, 1, 4, 4, 2, 4, None, 0, None) == SA_ERR_NULL
     assert L.csa_topk(4096, None, 4096, 4, 1, 1 << 20, 2048, 4, None, 0, None) == SA_ERR_WORKSPACE
+
+
+def test_indexer_topk_validation(sa):
+    L = sa.lib()
+    ws = 4096
+    big = 1 << 40
+    # null, shape, unsupported, alignment, workspace
+    assert L.dsa_indexer_topk(None, 4096, 4096, None, 4096, 1, 4, 4, 4, 128, 2, 0, ws, big, None) == SA_ERR_NULL
+    assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 0, 4, 4, 128, 2, 0, ws, big, None) == SA_ERR_SHAPE
+    assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 4, 40000, 4, 128, 2, 0, ws, big, None) == SA_ERR_UNSUPPORTED
+    assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 4, 4, 4, 128, 4096, 0, ws, big, None) == SA_ERR_UNSUPPORTED
+    assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 4, 4, 8, 128, 2, 0, ws, big, None) == SA_ERR_UNSUPPORTED
+    assert L.dsa_indexer_topk(4100, 4096, 4096, None, 4096, 1, 4, 4, 4, 128, 2, 0, ws, big, None) == SA_ERR_ALIGN
+    assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 4, 4, 4, 128, 2, 0, None, 0, None) == SA_ERR_WORKSPACE
+    need = L.dsa_indexer_topk_workspace_size(1, 4, 4, 2)
+    assert need > 0
+    assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 4, 4, 4, 128, 2, 0, ws, need - 1, None) == SA_ERR_WORKSPACE
+    # the workspace holds the candidates (8192 per row, 8 bytes) and the recomputed rows' scores
+    assert L.dsa_indexer_topk_workspace_size(1, 32768, 32768, 2048) >= 32768 * (8192 * 8 + 32768 * 4)

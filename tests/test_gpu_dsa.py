@@ -303,6 +303,54 @@ def test_dsa_end_to_end_k_ge_context_is_dense():
 
 
 # ---------------------------------------------------------------------------
+# Fused indexer -> top-k: exactly the separate calls' selection
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("B,T,S,kk,q_pos,grid", [(1, 300, 300, 64, None, False), (2, 70, 333, 32, [263, 100], False),
+                                                  (1, 1, 5000, 2048, [4999], False), (1, 2000, 2000, 128, None, False),
+                                                  (1, 4096, 4096, 2048, None, False), (2, 17, 3000, 100, [2900, 1500], False),
+                                                  (1, 3, 1000, 16, [999], False), (2, 9, 2100, 7, [2000, 30], False),
+                                                  (1, 700, 700, 64, None, True), (1, 1500, 1500, 1, None, False),
+                                                  (1, 33, 10, 4, None, False)])
+@pytest.mark.parametrize("force", [False, True])
+def test_indexer_topk_equals_separate_calls(B, T, S, kk, q_pos, grid, force):
+    """dsa_indexer_topk returns exactly dsa_topk(dsa_indexer_scores(...)): several chunks, ragged sizes,
+    per-batch q_pos, decode-sized calls, integer-grid inputs (heavy ties), k = 1, S < 16 (no samples);
+    force=True sends every long row through the exact recomputation instead of the candidates."""
+    sa = require_gpu()
+    qi, ki, w = _indexer_inputs(B, T, S, 50 + T, grid=grid)
+    tqi, tki, tw = synth.to_torch(qi, "bf16", DEV), synth.to_torch(ki, "bf16", DEV), synth.to_torch(w, "f32", DEV)
+    qp = None if q_pos is None else torch.tensor(q_pos, dtype=torch.int64, device=DEV)
+    want = sa.dsa_topk(sa.dsa_indexer_scores(tqi, tki, tw, q_pos=qp), kk, q_pos=qp)
+    got = sa.dsa_indexer_topk(tqi, tki, tw, kk, q_pos=qp, force_fallback=force)
+    assert torch.equal(got, want)
+
+
+def test_indexer_topk_32768_top2048():
+    """Fused call at the prefill workload's size: identical to the separate calls on every row, and on
+    sampled rows equal to the oracle's selection outside the 1e-6 tie band."""
+    sa = require_gpu()
+    T, kk = 32768, 2048
+    qi = synth.torch_normal((1, T, 4, 128), 128 ** -0.5, torch.bfloat16, 1700, DEV)
+    ki = synth.torch_normal((1, T, 128), 128 ** -0.5, torch.bfloat16, 1701, DEV)
+    w = synth.torch_uniform((1, T, 4), 1702, DEV)
+    got = sa.dsa_indexer_topk(qi, ki, w, kk)
+    sc = sa.dsa_indexer_scores(qi, ki, w)
+    want = sa.dsa_topk(sc, kk)
+    assert torch.equal(got, want)
+    del sc
+    for i in (2047, 2048, 5000, 20000, T - 1):
+        n = i + 1
+        ws = oracle.dsa_indexer_scores(f64(qi[:, i:i + 1]), f64(ki[:, :n]), f64(w[:, i:i + 1]), q_pos=[i])[0, 0]
+        kth = np.sort(ws)[::-1][kk - 1]
+        band = np.abs(ws - kth) <= 1e-6
+        sel = set(got[0, i].cpu().numpy().tolist()) - {-1}
+        want_sel = set(np.argsort(-ws, kind="stable")[:kk].tolist())
+        assert {s_ for s_ in sel if not band[s_]} == {s_ for s_ in want_sel if not band[s_]}, i
+
+
+# ---------------------------------------------------------------------------
 # CSA variant: indexer, top-k and sparse attention over block-mean entries
 # ---------------------------------------------------------------------------
 
