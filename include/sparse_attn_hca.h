@@ -284,7 +284,7 @@ int csa_topk(const float* scores, const int64_t* q_pos, int32_t* idx,
  * of every 16th position sets a per-row threshold, the indexer keeps only the
  * (key, position) pairs at or above it, and an exact selection runs over
  * those.  Rows where the sample misjudges the threshold (fewer than k or more
- * than 8192 candidates) are recomputed exactly by the separate kernels inside
+ * than 4096 candidates) are recomputed exactly by the separate kernels inside
  * the call, so the result never depends on the sample.
  * q_idx: [B,T,Hi,Di] bf16; k_idx: [B,S,Di] bf16; w: [B,T,Hi] fp32;
  * q_pos: device int64[B] or NULL (as for dsa_indexer_scores);

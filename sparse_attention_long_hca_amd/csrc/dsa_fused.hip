@@ -10,18 +10,20 @@
 //      indexer in its ratio-16 mode, whose visibility rule (entry j visible
 //      to position p iff 16j + 15 <= p) is exactly "sampled position <= p".
 //   2. Threshold: per row, the r-th largest sampled key (r = k/16 plus a
-//      margin of six standard deviations), or 0 when the row has at most r
-//      samples.
-//   3. Candidates: the indexer runs in candidate mode and appends (key,
-//      position) of every score whose key is >= the row's threshold; its
-//      scores are the same fp32 values as in dsa_indexer_scores (same code,
-//      same order of accumulation).
+//      margin of five standard deviations) cut to its top 16 bits, or 0 when
+//      the row has at most r samples.
+//   3. Candidates: the indexer runs in candidate mode and writes (key,
+//      position) of every score whose key is >= the row's threshold, per
+//      chunk of positions into the row's segment for that chunk; its scores
+//      are the same fp32 values as in dsa_indexer_scores (same code, same
+//      order of accumulation).
 //   4. Select: if a row has at least k and at most kCap candidates, the k-th
 //      largest key K over them is the k-th largest of the row (at least k
 //      keys lie above the threshold, so every key of the top k, ties of K
-//      included, is a candidate).  Rounds of key histograms find K exactly;
-//      positions with key > K and the lowest `need` positions with key == K
-//      are marked in an LDS bitmap and written in ascending order.
+//      included, is a candidate).  Rounds of key histograms narrow the key
+//      interval holding K; positions with larger keys and the lowest `need`
+//      positions with key K are marked in an LDS bitmap and written in
+//      ascending order.
 //   5. Exact fallback: rows with fewer than k or more than kCap candidates
 //      (the sample misjudged them) are flagged; the plain indexer and top-k
 //      then run for the flagged rows only (every workgroup of those launches
@@ -33,28 +35,34 @@
 namespace sa {
 
 constexpr int kSample = 16;     // sample stride (positions)
-constexpr int64_t kCap = 8192;  // candidates kept per row
-constexpr int kSelThreads = 256;
-constexpr int kSelPer = (int)(kCap / kSelThreads);  // candidates per thread
+constexpr int64_t kCap = 4096;  // most candidates the select step holds per row
+constexpr int kSelPer = (int)(kCap / 64);           // candidates per lane (one wave per row)
 constexpr int kMaxS = 32768;                        // bitmap of the select step
 constexpr int kThrPer = 2048 / 64;                  // sampled keys per lane (S / 16 <= 2048)
 
-// Sample rank for k: k/16 rounded up, plus six standard deviations of a
-// binomial count of that mean, plus a constant.
+// Sample rank for k: k/16 rounded up, plus five standard deviations of a
+// binomial count of that mean, plus a constant.  At k = 2048 (rank 196) a row
+// has about 3136 candidates, and fewer than k or more than kCap of them only
+// at four to five standard deviations of the sample.
 __host__ __device__ inline int fused_rank(int64_t k) {
   const int m = (int)((k + kSample - 1) / kSample);
   int sd = 1;
   while (sd * sd < m) ++sd;
-  return m + 6 * sd + 8;
+  return m + 5 * sd + 8;
 }
 
+constexpr int kMaxSeg = 128;  // chunks of the candidate launch per row (S / 256 at most)
+
 struct FusedLayout {
-  size_t ks, sscore, thresh, cnt, fail, anyf, cand, fb, total;
+  size_t ks, sscore, thresh, cnt, fail, anyf, cand, total;
 };
 
+// The exact fallback's scores ([rows, S] fp32) reuse the candidate area
+// ([rows, S] pairs): they are written after the select step has read it.
 static FusedLayout fused_layout(int64_t B, int64_t T, int64_t S) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int64_t Ss = S / kSample, rows = B * T;
+  const int64_t nseg = (S + dsa_indexer_chunk(T) - 1) / dsa_indexer_chunk(T);
   FusedLayout L;
   size_t off = 0;
   L.ks = off;
@@ -64,15 +72,13 @@ static FusedLayout fused_layout(int64_t B, int64_t T, int64_t S) {
   L.thresh = off;
   off += al((size_t)rows * 4);
   L.cnt = off;
-  off += al((size_t)rows * 4);
+  off += al((size_t)(rows * nseg) * 4);
   L.fail = off;
   off += al((size_t)rows * 4);
   L.anyf = off;
   off += 256;
   L.cand = off;
-  off += al((size_t)(rows * kCap) * 8);
-  L.fb = off;
-  off += al((size_t)(rows * S) * 4);
+  off += al((size_t)(rows * S) * 8);
   L.total = off;
   return L;
 }
@@ -86,11 +92,11 @@ struct FusedPtrs {
   const bf16_t* ks;
   const float* sscore;
   uint32_t* thresh;
-  uint32_t* cnt;
+  const uint32_t* cnt;  // [rows, nseg]
   uint32_t* fail;
   uint32_t* anyf;
-  const uint2* cand;
-  int64_t Ss;
+  const uint2* cand;  // [rows, S]: segment c at c * chunk
+  int64_t Ss, chunk, nseg;
 };
 
 // ks[b, j] = k[b, 16j + 15]: 16 threads per 256-byte row.
@@ -103,19 +109,21 @@ __global__ __launch_bounds__(256) void fused_sample_kernel(const bf16_t* k, bf16
   reinterpret_cast<uint4*>(ks + r * 128)[c] = *src;
 }
 
-// One wave per row: clears the row's count and flag, and writes the
-// threshold key (0: every visible position is a candidate).
+// One wave per row: clears the row's fallback flag, and writes the
+// threshold key (0: every visible position is a candidate).  The threshold is
+// the r-th largest sampled key cut to its top 16 bits (two rounds of 256-bin
+// histograms over the key's top two bytes), so at least r sampled keys reach
+// it; exactness never depends on it (the select step checks the counts).
 __global__ __launch_bounds__(256) void fused_thresh_kernel(DsaIndexerTopkParams p, FusedPtrs f) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][256];
   const int lane = threadIdx.x & 63;
+  uint32_t* hist = hist_all[threadIdx.x >> 6];
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (blockIdx.x == 0 && threadIdx.x == 0) *f.anyf = 0u;
   if (row >= p.B * p.T) return;
   const int64_t b = row / p.T, i = row % p.T;
   const int64_t base = p.q_pos ? p.q_pos[b] : 0;
-  if (lane == 0) {
-    f.cnt[row] = 0u;
-    f.fail[row] = 0u;
-  }
+  if (lane == 0) f.fail[row] = 0u;
   int64_t n = base + i + 1;
   n = n < p.S ? n : p.S;
   uint32_t V = 0u;
@@ -131,33 +139,44 @@ __global__ __launch_bounds__(256) void fused_thresh_kernel(DsaIndexerTopkParams 
 #pragma unroll
       for (int t = 0; t < kThrPer; ++t) {
         const int64_t j = lane + 64 * t;
-        kv[t] = j < ns ? score_key(ss[j]) : 0u;  // 0: absent (below every threshold tried)
+        kv[t] = j < ns ? score_key(ss[j]) : 0u;
       }
-      // Largest V with at least r keys >= V, bit by bit from the top.
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t tv = V | (1u << bit);
-        uint32_t c = 0;
+      reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+      wave_lds_sync();
 #pragma unroll
-        for (int t = 0; t < kThrPer; ++t) c += kv[t] >= tv ? 1u : 0u;
-        if (wave_sum_u32(c) >= r) V = tv;
-      }
+      for (int t = 0; t < kThrPer; ++t)
+        if (lane + 64 * t < ns) atomicAdd(&hist[kv[t] >> 24], 1u);
+      wave_lds_sync();
+      uint32_t d1, above, cnt;
+      wave_top_bin256(hist, r, &d1, &above, &cnt);
+      wave_lds_sync();
+      reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+      wave_lds_sync();
+#pragma unroll
+      for (int t = 0; t < kThrPer; ++t)
+        if (lane + 64 * t < ns && (kv[t] >> 24) == d1) atomicAdd(&hist[(kv[t] >> 16) & 255u], 1u);
+      wave_lds_sync();
+      uint32_t d2;
+      wave_top_bin256(hist, r - above, &d2, &above, &cnt);
+      V = (d1 << 24) | (d2 << 16);
     }
   }
   if (lane == 0) f.thresh[row] = V;
 }
 
-// One workgroup per row: the exact k-th largest candidate key K by rounds of
-// histograms over the key interval [lo, hi] (first [threshold, max]; 2048
-// bins of 2^shift keys, each round at least 1024 times narrower, one-key
-// bins end it), then the kept positions in an LDS bitmap, written in order.
-__global__ __launch_bounds__(kSelThreads) void fused_select_kernel(DsaIndexerTopkParams p, FusedPtrs f) {
-  constexpr int kBinsSel = 2048;
-  __shared__ uint32_t hist[kBinsSel];
-  __shared__ uint32_t sel[kMaxS / 32];
-  __shared__ uint32_t tie[kMaxS / 32];
-  __shared__ uint32_t scratch[32];
-  __shared__ uint32_t res[4];
-  const int tid = threadIdx.x;
+// One wave per row.  The row's candidates stay in registers (keys, and
+// positions packed two per register).  Rounds of 256-bin histograms over the
+// key interval [lo, hi] (first [threshold, max]) narrow it to the bin where
+// the count from the top reaches k, until the interval holds exactly the
+// keys still needed or a single key.  Keys above the interval are kept; of
+// the keys in it, all when their count is what is needed, else (one key,
+// tied) the lowest positions.  Kept positions are marked in an LDS bitmap
+// and written in ascending order.
+__global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p, FusedPtrs f) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+  __shared__ __attribute__((aligned(16))) uint32_t bm[kMaxS / 32];
+  __shared__ uint32_t pre[kMaxSeg + 1];
+  const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int64_t b = row / p.T, i = row % p.T;
   const int64_t base = p.q_pos ? p.q_pos[b] : 0;
@@ -166,102 +185,139 @@ __global__ __launch_bounds__(kSelThreads) void fused_select_kernel(DsaIndexerTop
   const int k = (int)p.topk;
   int32_t* out = p.idx + row * p.topk;
   if (n <= k) {  // every visible position
-    for (int j = tid; j < k; j += kSelThreads) out[j] = j < n ? j : -1;
+    for (int j = lane; j < k; j += 64) out[j] = j < n ? j : -1;
     return;
   }
-  const uint32_t c = f.cnt[row];
+  // The row's candidates: segments 0 .. nseg-1 (one per chunk holding a
+  // visible position), concatenated; pre[s] = candidates before segment s.
+  const int nseg = (int)((n + f.chunk - 1) / f.chunk);
+  uint32_t c = 0u;
+  for (int s0 = 0; s0 < nseg; s0 += 64) {
+    const int si = s0 + lane;
+    const uint32_t v = si < nseg ? f.cnt[row * f.nseg + si] : 0u;
+    const uint32_t incl = wave_incl_scan(v) + c;
+    if (si < nseg) pre[si + 1] = incl;
+    c = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  }
+  if (lane == 0) pre[0] = 0u;
   if (c < (uint32_t)k || c > (uint32_t)kCap) {  // the exact fallback writes this row
-    if (tid == 0) {
+    if (lane == 0) {
       f.fail[row] = 1u;
       atomicOr(f.anyf, 1u);
     }
     return;
   }
-  const uint2* cr = f.cand + row * kCap;
-  uint32_t kv[kSelPer], ps[kSelPer];
+  wave_lds_sync();
+  const uint2* cr = f.cand + row * p.S;
+  uint32_t kv[kSelPer], pp[kSelPer / 2];
   uint32_t mx = 0u;
+  int seg = 0;  // this lane's segment; entries j of it lie in [seg_lo, seg_hi)
+  uint32_t seg_lo = 0u, seg_hi = pre[1];
 #pragma unroll
   for (int t = 0; t < kSelPer; ++t) {
-    const uint32_t j = (uint32_t)(tid + kSelThreads * t);
-    const uint2 e = j < c ? cr[j] : make_uint2(0u, 0u);
-    kv[t] = e.x;
-    ps[t] = e.y;
-    mx = max(mx, e.x);
+    if ((t & 1) == 0) pp[t >> 1] = 0u;
+    kv[t] = 0u;
+    if (64 * t < (int)c) {
+      const uint32_t j = (uint32_t)(lane + 64 * t);
+      if (j < c) {
+        while (j >= seg_hi) {
+          ++seg;
+          seg_lo = seg_hi;
+          seg_hi = pre[seg + 1];
+        }
+        const uint2 e = cr[(int64_t)seg * f.chunk + (j - seg_lo)];
+        kv[t] = e.x;
+        pp[t >> 1] |= (e.y & 0xffffu) << (16 * (t & 1));
+        mx = max(mx, e.x);
+      }
+    }
   }
-  mx = wave_max_u32(mx);
-  if ((tid & 63) == 0) scratch[tid >> 6] = mx;
-  __syncthreads();
-  uint32_t hi = 0u;
-#pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) hi = max(hi, scratch[w]);
-  __syncthreads();
-  // Every candidate key is >= the row's threshold; absent slots hold 0 and
-  // fall outside [lo, hi] (lo >= 1 whenever a real key is 0 never occurs).
-  uint32_t lo = f.thresh[row];
+  auto valid = [&](int t) __attribute__((always_inline)) { return lane + 64 * t < (int)c; };
+  auto pos = [&](int t) __attribute__((always_inline)) { return (pp[t >> 1] >> (16 * (t & 1))) & 0xffffu; };
+  uint32_t hi = wave_max_u32(mx);
+  uint32_t lo = f.thresh[row];  // every candidate key is in [lo, hi]
   uint32_t need = (uint32_t)k;  // keys still to take from [lo, hi]
-  while (lo < hi) {
-    const uint32_t range = hi - lo, sh = bin_shift(range);
-    for (int j = tid; j < kBinsSel; j += kSelThreads) hist[j] = 0u;
-    __syncthreads();
+  uint32_t in_range = c;        // candidate keys in [lo, hi]
+  while (lo < hi && in_range != need) {
+    const uint32_t range = hi - lo, sh = bin_shift256(range);
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_sync();
 #pragma unroll
     for (int t = 0; t < kSelPer; ++t) {
-      const uint32_t d = kv[t] - lo;  // wraps for keys below lo (and absent slots when lo > 0)
-      if (tid + kSelThreads * t < (int)c && d <= range) atomicAdd(&hist[d >> sh], 1u);
+      if (64 * t < (int)c) {
+        const uint32_t d = kv[t] - lo;  // wraps for keys below lo
+        if (valid(t) && d <= range) atomicAdd(&hist[d >> sh], 1u);
+      }
     }
-    __syncthreads();
-    select_bin(hist, kBinsSel, need, scratch, &res[0], &res[1]);
-    const uint32_t bsel = uniform_u32(res[0]);
-    need -= uniform_u32(res[1]);
+    wave_lds_sync();
+    uint32_t bsel, above;
+    wave_top_bin256(hist, need, &bsel, &above, &in_range);
+    wave_lds_sync();
+    need -= above;
     hi = lo + min(range, (bsel << sh) | ((1u << sh) - 1u));
     lo = lo + (bsel << sh);
-    __syncthreads();
   }
-  const uint32_t K = lo;  // k-th largest key; `need` copies of it are taken
-  for (int w = tid; w < kMaxS / 32; w += kSelThreads) {
-    sel[w] = 0u;
-    tie[w] = 0u;
+  const bool take_range = in_range == need;
+#pragma unroll
+  for (int q = 0; q < kMaxS / 32 / 256; ++q) reinterpret_cast<uint4*>(bm)[lane + 64 * q] = make_uint4(0u, 0u, 0u, 0u);
+  wave_lds_sync();
+  if (!take_range) {
+    // A single key K = lo = hi with more copies than needed: mark them, then
+    // keep the `need` lowest.  Lane l owns words 16l .. 16l + 15.
+#pragma unroll
+    for (int t = 0; t < kSelPer; ++t) {
+      if (64 * t < (int)c) {
+        if (valid(t) && kv[t] == lo) atomicOr(&bm[pos(t) >> 5], 1u << (pos(t) & 31u));
+      }
+    }
+    wave_lds_sync();
+    constexpr int kOwn = kMaxS / 32 / 64;
+    uint32_t w[kOwn], tc = 0u;
+#pragma unroll
+    for (int u = 0; u < kOwn; ++u) {
+      w[u] = bm[kOwn * lane + u];
+      tc += (uint32_t)__popc(w[u]);
+    }
+    uint32_t rank = wave_incl_scan(tc) - tc;  // copies at lower positions
+#pragma unroll
+    for (int u = 0; u < kOwn; ++u) {
+      const uint32_t pc = (uint32_t)__popc(w[u]);
+      if (rank >= need) {
+        w[u] = 0u;
+      } else if (rank + pc > need) {
+        uint32_t keep = 0u, x = w[u];
+        for (uint32_t m = need - rank; m > 0u; --m) {
+          const uint32_t low = x & (~x + 1u);
+          keep |= low;
+          x ^= low;
+        }
+        w[u] = keep;
+      }
+      rank += pc;
+      bm[kOwn * lane + u] = w[u];
+    }
+    wave_lds_sync();
   }
-  __syncthreads();
 #pragma unroll
   for (int t = 0; t < kSelPer; ++t) {
-    if (tid + kSelThreads * t < (int)c) {
-      const uint32_t bit = 1u << (ps[t] & 31u);
-      if (kv[t] > K) atomicOr(&sel[ps[t] >> 5], bit);
-      else if (kv[t] == K) atomicOr(&tie[ps[t] >> 5], bit);
+    if (64 * t < (int)c) {
+      if (valid(t) && (kv[t] > hi || (take_range && kv[t] >= lo))) atomicOr(&bm[pos(t) >> 5], 1u << (pos(t) & 31u));
     }
   }
-  __syncthreads();
-  // Thread t owns bitmap words 4t .. 4t+3 (positions 128t .. 128t+127, in order).
-  constexpr int kWords = kMaxS / 32 / kSelThreads;
-  uint32_t tc = 0;
-#pragma unroll
-  for (int u = 0; u < kWords; ++u) tc += (uint32_t)__popc(tie[kWords * tid + u]);
-  uint32_t tot;
-  uint32_t rank = block_inclusive_scan(tc, scratch, tot) - tc;  // copies of K at lower positions
-#pragma unroll
-  for (int u = 0; u < kWords; ++u) {
-    uint32_t w = tie[kWords * tid + u], add = 0u;
-    while (w != 0u && rank < need) {
-      const uint32_t low = w & (~w + 1u);
-      add |= low;
-      w ^= low;
-      ++rank;
-    }
-    sel[kWords * tid + u] |= add;
-  }
-  __syncthreads();
-  uint32_t sc = 0;
-#pragma unroll
-  for (int u = 0; u < kWords; ++u) sc += (uint32_t)__popc(sel[kWords * tid + u]);
-  uint32_t o = block_inclusive_scan(sc, scratch, tot) - sc;
-#pragma unroll
-  for (int u = 0; u < kWords; ++u) {
-    uint32_t w = sel[kWords * tid + u];
+  wave_lds_sync();
+  // Output: 64 words (2048 positions) per step, one word per lane.
+  const int nw = (int)((n + 31) / 32);
+  uint32_t o_base = 0u;
+  for (int cw = 0; cw < nw; cw += 64) {
+    uint32_t w = cw + lane < nw ? bm[cw + lane] : 0u;
+    const uint32_t pc = (uint32_t)__popc(w);
+    const uint32_t incl = wave_incl_scan(pc);
+    uint32_t o = o_base + incl - pc;
     while (w != 0u) {
-      const int bpos = __ffs((int)w) - 1;
-      out[o++] = (kWords * tid + u) * 32 + bpos;
+      out[o++] = (cw + lane) * 32 + (__ffs((int)w) - 1);
       w &= w - 1u;
     }
+    o_base += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
   }
 }
 
@@ -273,12 +329,14 @@ hipError_t launch_dsa_indexer_topk(const DsaIndexerTopkParams& p, hipStream_t st
   f.ks = reinterpret_cast<const bf16_t*>(ws + L.ks);
   f.sscore = reinterpret_cast<const float*>(ws + L.sscore);
   f.thresh = reinterpret_cast<uint32_t*>(ws + L.thresh);
-  f.cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
+  f.cnt = reinterpret_cast<const uint32_t*>(ws + L.cnt);
   f.fail = reinterpret_cast<uint32_t*>(ws + L.fail);
   f.anyf = reinterpret_cast<uint32_t*>(ws + L.anyf);
   f.cand = reinterpret_cast<const uint2*>(ws + L.cand);
   f.Ss = Ss;
-  float* fb = reinterpret_cast<float*>(ws + L.fb);
+  f.chunk = dsa_indexer_chunk(p.T);
+  f.nseg = (p.S + f.chunk - 1) / f.chunk;
+  float* fb = reinterpret_cast<float*>(ws + L.cand);
   hipError_t e;
 
   // 1. Sampled scores (ratio-16 visibility).
@@ -299,7 +357,7 @@ hipError_t launch_dsa_indexer_topk(const DsaIndexerTopkParams& p, hipStream_t st
     sp.ratio = kSample;
     if ((e = launch_dsa_indexer(sp, stream)) != hipSuccess) return e;
   }
-  // 2. Thresholds (also clears counts and flags).
+  // 2. Thresholds (also clears the fallback flags).
   hipLaunchKernelGGL(fused_thresh_kernel, dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, stream, p, f);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 3. Candidates.
@@ -314,13 +372,12 @@ hipError_t launch_dsa_indexer_topk(const DsaIndexerTopkParams& p, hipStream_t st
   ep.S = p.S;
   ep.ratio = 1;
   ep.thresh = f.thresh;
-  ep.cnt = f.cnt;
+  ep.cnt = const_cast<uint32_t*>(f.cnt);
   ep.cand = const_cast<uint2*>(f.cand);
-  ep.cap = kCap;
   ep.topk = p.topk;
   if ((e = launch_dsa_indexer(ep, stream)) != hipSuccess) return e;
   // 4. Exact selection over the candidates.
-  hipLaunchKernelGGL(fused_select_kernel, dim3((uint32_t)rows), dim3(kSelThreads), 0, stream, p, f);
+  hipLaunchKernelGGL(fused_select_kernel, dim3((uint32_t)rows), dim3(64), 0, stream, p, f);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 5. Exact fallback for flagged rows (every workgroup returns at once when none is).
   DsaIndexerParams fp{};

@@ -154,59 +154,50 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   // tile ends at or before the first query's limit and all 16 of the wave's
   // query rows exist (rows past T must not be stored).
   const int wave_full_lim = iw + kIdxQPerWave - 1 < T ? lim(iw) : -1;
-  // Candidate mode: the threshold of each of this lane's accumulator rows
-  // (0 for rows that keep every position, which emit nothing).
+  // Candidate mode: the threshold of each of this lane's accumulator rows.
+  // Rows that emit nothing (past the end, or keeping every visible position)
+  // get 0xffffffff, which no finite or infinite score's key reaches.
   uint32_t thr[4];
-  bool emit_row[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int qi = iw + mb * 4 + g;
-    emit_row[mb] = kEmit && qi < T && plim[mb] + 1 > (int)p.topk;
-    thr[mb] = emit_row[mb] ? p.thresh[(int64_t)b * T + qi] : 0u;
+    const bool emit_row = kEmit && qi < T && plim[mb] + 1 > (int)p.topk;
+    thr[mb] = emit_row ? p.thresh[(int64_t)b * T + qi] : 0xffffffffu;
   }
+  // Candidates of this workgroup's chunk go to the rows' segments for the
+  // chunk (cand[row][s_begin ..], room for every position of the chunk), so
+  // slots come from a running count per row (uniform over the row's 16
+  // lanes) and no atomics are needed; the counts are written at the end.
+  uint32_t c_run[4] = {0u, 0u, 0u, 0u};
   auto emit_held = [&](int slot) __attribute__((always_inline)) {
     const int h0 = held_s0[slot];
     if (h0 < 0) return;
-    // Lanes 16g .. 16g + 15 hold a row's 64 positions of the tile (per
-    // M-block).  Counts and in-row offsets for all four rows first, then the
-    // four slot reservations (one atomic per row and tile) back to back, so
-    // the wave waits for one round trip, then the stores.
-    uint32_t fl[4], incl[4], total[4], base[4];
+    // Lanes 16g .. 16g + 15 hold a row's 64 positions of the tile (per M-block).
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      fl[mb] = 0u;
+      uint32_t fl = 0u;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int s = h0 + nb * 16 + L;
-        fl[mb] |= (emit_row[mb] && s <= plim[mb] && score_key(held[slot][mb][nb]) >= thr[mb]) ? (1u << nb) : 0u;
+        fl |= (s <= plim[mb] && score_key(held[slot][mb][nb]) >= thr[mb]) ? (1u << nb) : 0u;
       }
-      const uint32_t mine = (uint32_t)__popc(fl[mb]);
+      const uint32_t mine = (uint32_t)__popc(fl);
       uint32_t x = mine;
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) {
         const uint32_t y = __shfl_up(x, off, 16);
         if (L >= off) x += y;
       }
-      incl[mb] = x - mine;  // exclusive
-      total[mb] = __shfl(x, 15, 16);
-    }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int64_t row = (int64_t)b * T + iw + mb * 4 + g;
-      base[mb] = (L == 0 && total[mb] > 0u) ? atomicAdd(&p.cnt[row], total[mb]) : 0u;
-    }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int64_t row = (int64_t)b * T + iw + mb * 4 + g;
-      uint32_t slot_i = __shfl(base[mb], 0, 16) + incl[mb];
+      uint2* seg = p.cand + ((int64_t)b * T + iw + mb * 4 + g) * S + s_begin;
+      uint32_t slot_i = c_run[mb] + x - mine;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        if (fl[mb] & (1u << nb)) {
-          if (slot_i < (uint32_t)p.cap)
-            p.cand[row * p.cap + slot_i] = make_uint2(score_key(held[slot][mb][nb]), (uint32_t)(h0 + nb * 16 + L));
+        if (fl & (1u << nb)) {
+          seg[slot_i] = make_uint2(score_key(held[slot][mb][nb]), (uint32_t)(h0 + nb * 16 + L));
           ++slot_i;
         }
       }
+      c_run[mb] += (uint32_t)__shfl(x, 15, 16);
     }
   };
   auto store_held = [&](int slot) __attribute__((always_inline)) {
@@ -333,6 +324,13 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
     }
     store_held(0);
   }
+  if constexpr (kEmit) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int qi = iw + mb * 4 + g;
+      if (L == 0 && qi < T) p.cnt[((int64_t)b * T + qi) * n_chunks + kc] = c_run[mb];
+    }
+  }
 }
 
 // Decode calls of up to 4 queries: one 16-row M-block (4 queries x 4 heads)
@@ -439,6 +437,10 @@ __global__ __launch_bounds__(64) void dsa_indexer_dec_kernel(DsaIndexerParams p,
     compute(b1);
     store(tile + 1);
   }
+}
+
+int64_t dsa_indexer_chunk(int64_t T) {
+  return T <= kIdxQPerWave ? (int64_t)kIdxDecodeTiles * kIdxKTile : (int64_t)kIdxTilesPerChunk * kIdxKTile;
 }
 
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {

@@ -77,21 +77,25 @@ struct DsaIndexerParams {
   float* scores;  // [B,T,S]
   int64_t B, T, S;
   int64_t ratio;  // keys are entries of `ratio` tokens: row i sees keys s < (q_pos + i + 1) / ratio
-  // Candidate mode (cand != NULL; ratio 1): no scores are stored; every row
-  // with more than topk visible positions appends (order-preserving key,
-  // position) of each score whose key is >= thresh[row] to cand[row*cap ..]
-  // and counts them in cnt[row] (appends past cap are dropped, the count
-  // still grows).
+  // Candidate mode (cand != NULL; ratio 1): no scores are stored.  Positions
+  // are worked in chunks of dsa_indexer_chunk(T); for every row with more
+  // than topk visible positions, the workgroup of chunk c writes (order-
+  // preserving key, position) of each score whose key is >= thresh[row] to
+  // cand[row*S + c*chunk ..] (room for the whole chunk) and their number to
+  // cnt[row*n_chunks + c], n_chunks = ceil(S / chunk); rows keeping every
+  // visible position write count 0.  Every chunk holding a visible position
+  // of a row writes that row's count.
   const uint32_t* thresh;
   uint32_t* cnt;
   uint2* cand;
-  int64_t cap, topk;
+  int64_t topk;
   // Row filter (row_flag != NULL): nothing runs unless *any_flag != 0, and a
   // workgroup runs only if one of its rows has row_flag[row] != 0.
   const uint32_t* row_flag;
   const uint32_t* any_flag;
 };
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream);
+int64_t dsa_indexer_chunk(int64_t T);  // positions per workgroup for T queries
 
 // ---- dsa_topk ---------------------------------------------------------------
 struct DsaTopkParams {

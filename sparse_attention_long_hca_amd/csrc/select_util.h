@@ -41,6 +41,45 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), 63);
 }
 
+// Orders this wave's earlier LDS accesses before its later ones for the
+// compiler (the hardware executes one wave's LDS instructions in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// One wave, 256 bins in LDS (16-byte aligned): the bin where the count from
+// the top reaches need (1 <= need <= total).  *bin, *above (count in higher
+// bins) and *count (the bin's count) are uniform over the wave.
+__device__ __forceinline__ void wave_top_bin256(const uint32_t* hist, uint32_t need, uint32_t* bin, uint32_t* above,
+                                                uint32_t* count) {
+  const int lane = threadIdx.x & 63;
+  const uint4 v = reinterpret_cast<const uint4*>(hist)[63 - lane];  // lane 0 holds the top four bins
+  const uint32_t cs[4] = {v.w, v.z, v.y, v.x};
+  const uint32_t s = v.x + v.y + v.z + v.w;
+  const uint32_t incl = wave_incl_scan(s);
+  const int src = __ffsll((unsigned long long)__ballot(incl >= need)) - 1;
+  uint32_t ab = incl - s, b = 0u, a = 0u, c = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (ab < need && ab + cs[j] >= need) {
+      b = (uint32_t)(4 * (63 - lane) + 3 - j);
+      a = ab;
+      c = cs[j];
+    }
+    ab += cs[j];
+  }
+  *bin = (uint32_t)__builtin_amdgcn_readlane((int)b, src);
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)a, src);
+  *count = (uint32_t)__builtin_amdgcn_readlane((int)c, src);
+}
+
+// Bin width exponent for 256 bins over an interval of (range + 1) keys.
+__device__ __forceinline__ uint32_t bin_shift256(uint32_t range) {
+  const int bits = 32 - __clz((int)range);
+  return bits > 8 ? (uint32_t)(bits - 8) : 0u;
+}
+
 // Bin width exponent for an interval of (range + 1) keys: bins of 2^shift
 // keys with range >> shift in [1024, 2047] (or shift 0 for small ranges).
 __device__ __forceinline__ uint32_t bin_shift(uint32_t range) {
