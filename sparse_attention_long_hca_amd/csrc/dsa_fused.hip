@@ -10,7 +10,7 @@
 //      indexer in its ratio-16 mode, whose visibility rule (entry j visible
 //      to position p iff 16j + 15 <= p) is exactly "sampled position <= p".
 //   2. Threshold: per row, the r-th largest sampled key (r = k/16 plus a
-//      margin of five standard deviations) cut to its top 16 bits, or 0 when
+//      margin of 4.5 standard deviations) cut to its top 16 bits, or 0 when
 //      the row has at most r samples.
 //   3. Candidates: the indexer runs in candidate mode and writes (key,
 //      position) of every score whose key is >= the row's threshold, per
@@ -40,15 +40,16 @@ constexpr int kSelPer = (int)(kCap / 64);           // candidates per lane (one 
 constexpr int kMaxS = 32768;                        // bitmap of the select step
 constexpr int kThrPer = 2048 / 64;                  // sampled keys per lane (S / 16 <= 2048)
 
-// Sample rank for k: k/16 rounded up, plus five standard deviations of a
-// binomial count of that mean, plus a constant.  At k = 2048 (rank 196) a row
-// has about 3136 candidates, and fewer than k or more than kCap of them only
-// at four to five standard deviations of the sample.
+// Sample rank for k: k/16 rounded up, plus four and a half standard
+// deviations of a binomial count of that mean, plus a constant.  At k = 2048
+// (rank 190) a row has about 3040 candidates; with scores independent of
+// position, fewer than k or (pads included) more than kCap of them take
+// about 4.5 standard deviations of the sample either way.
 __host__ __device__ inline int fused_rank(int64_t k) {
   const int m = (int)((k + kSample - 1) / kSample);
   int sd = 1;
   while (sd * sd < m) ++sd;
-  return m + 5 * sd + 8;
+  return m + (9 * sd + 1) / 2 + 8;
 }
 
 constexpr int kMaxSeg = 128;  // chunks of the candidate launch per row (S / 256 at most)
@@ -189,18 +190,20 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
     return;
   }
   // The row's candidates: segments 0 .. nseg-1 (one per chunk holding a
-  // visible position), concatenated; pre[s] = candidates before segment s.
+  // visible position), each padded to an even length, concatenated;
+  // pre[s] = entries before segment s.
   const int nseg = (int)((n + f.chunk - 1) / f.chunk);
-  uint32_t c = 0u;
+  uint32_t c = 0u, cp = 0u;  // candidates; entries with pads
   for (int s0 = 0; s0 < nseg; s0 += 64) {
     const int si = s0 + lane;
     const uint32_t v = si < nseg ? f.cnt[row * f.nseg + si] : 0u;
-    const uint32_t incl = wave_incl_scan(v) + c;
+    const uint32_t incl = wave_incl_scan((v + 1u) & ~1u) + cp;
     if (si < nseg) pre[si + 1] = incl;
-    c = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    cp = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    c += wave_sum_u32(v);
   }
   if (lane == 0) pre[0] = 0u;
-  if (c < (uint32_t)k || c > (uint32_t)kCap) {  // the exact fallback writes this row
+  if (c < (uint32_t)k || cp > (uint32_t)kCap) {  // the exact fallback writes this row
     if (lane == 0) {
       f.fail[row] = 1u;
       atomicOr(f.anyf, 1u);
@@ -208,32 +211,39 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
     return;
   }
   wave_lds_sync();
+  // Lane l takes entry pairs m = l + 64u (entries 2m, 2m + 1; a pair never
+  // straddles segments) with one 16-byte load: keys to kv[2u], kv[2u + 1],
+  // positions to ps[2u], ps[2u + 1].  Nothing loaded is used before the loop
+  // ends, so the loads are all in flight together.  Lanes past the end load
+  // the last pair again; `valid` excludes them, and the pads.
   const uint2* cr = f.cand + row * p.S;
-  uint32_t kv[kSelPer], pp[kSelPer / 2];
-  uint32_t mx = 0u;
+  uint32_t kv[kSelPer], ps[kSelPer];
   int seg = 0;  // this lane's segment; entries j of it lie in [seg_lo, seg_hi)
   uint32_t seg_lo = 0u, seg_hi = pre[1];
 #pragma unroll
-  for (int t = 0; t < kSelPer; ++t) {
-    if ((t & 1) == 0) pp[t >> 1] = 0u;
-    kv[t] = 0u;
-    if (64 * t < (int)c) {
-      const uint32_t j = (uint32_t)(lane + 64 * t);
-      if (j < c) {
-        while (j >= seg_hi) {
-          ++seg;
-          seg_lo = seg_hi;
-          seg_hi = pre[seg + 1];
-        }
-        const uint2 e = cr[(int64_t)seg * f.chunk + (j - seg_lo)];
-        kv[t] = e.x;
-        pp[t >> 1] |= (e.y & 0xffffu) << (16 * (t & 1));
-        mx = max(mx, e.x);
+  for (int u = 0; u < kSelPer / 2; ++u) {
+    kv[2 * u] = kv[2 * u + 1] = ps[2 * u] = ps[2 * u + 1] = 0u;
+    if (128 * u < (int)cp) {
+      const uint32_t j = min((uint32_t)(2 * (lane + 64 * u)), cp - 2u);
+      while (j >= seg_hi) {
+        ++seg;
+        seg_lo = seg_hi;
+        seg_hi = pre[seg + 1];
       }
+      const uint4 e = *reinterpret_cast<const uint4*>(cr + (int64_t)seg * f.chunk + (j - seg_lo));
+      kv[2 * u] = e.x;
+      ps[2 * u] = e.y;
+      kv[2 * u + 1] = e.z;
+      ps[2 * u + 1] = e.w;
     }
   }
-  auto valid = [&](int t) __attribute__((always_inline)) { return lane + 64 * t < (int)c; };
-  auto pos = [&](int t) __attribute__((always_inline)) { return (pp[t >> 1] >> (16 * (t & 1))) & 0xffffu; };
+  auto valid = [&](int t) __attribute__((always_inline)) {
+    return 2 * (lane + 64 * (t >> 1)) < (int)cp && kv[t] != 0u;
+  };
+  auto pos = [&](int t) __attribute__((always_inline)) { return ps[t]; };
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int t = 0; t < kSelPer; ++t) mx = max(mx, valid(t) ? kv[t] : 0u);
   uint32_t hi = wave_max_u32(mx);
   uint32_t lo = f.thresh[row];  // every candidate key is in [lo, hi]
   uint32_t need = (uint32_t)k;  // keys still to take from [lo, hi]
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
     wave_lds_sync();
 #pragma unroll
     for (int t = 0; t < kSelPer; ++t) {
-      if (64 * t < (int)c) {
+      if (128 * (t >> 1) < (int)cp) {
         const uint32_t d = kv[t] - lo;  // wraps for keys below lo
         if (valid(t) && d <= range) atomicAdd(&hist[d >> sh], 1u);
       }
@@ -266,7 +276,7 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
     // keep the `need` lowest.  Lane l owns words 16l .. 16l + 15.
 #pragma unroll
     for (int t = 0; t < kSelPer; ++t) {
-      if (64 * t < (int)c) {
+      if (128 * (t >> 1) < (int)cp) {
         if (valid(t) && kv[t] == lo) atomicOr(&bm[pos(t) >> 5], 1u << (pos(t) & 31u));
       }
     }
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
   }
 #pragma unroll
   for (int t = 0; t < kSelPer; ++t) {
-    if (64 * t < (int)c) {
+    if (128 * (t >> 1) < (int)cp) {
       if (valid(t) && (kv[t] > hi || (take_range && kv[t] >= lo))) atomicOr(&bm[pos(t) >> 5], 1u << (pos(t) & 31u));
     }
   }

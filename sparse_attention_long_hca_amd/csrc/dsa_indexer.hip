@@ -325,10 +325,16 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
     store_held(0);
   }
   if constexpr (kEmit) {
+    // Counts, and a pad entry (key 0) after an odd count: segments hold
+    // whole pairs.
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int qi = iw + mb * 4 + g;
-      if (L == 0 && qi < T) p.cnt[((int64_t)b * T + qi) * n_chunks + kc] = c_run[mb];
+      if (L == 0 && qi < T) {
+        const int64_t row = (int64_t)b * T + qi;
+        p.cnt[row * n_chunks + kc] = c_run[mb];
+        if (c_run[mb] & 1u) p.cand[row * S + s_begin + c_run[mb]] = make_uint2(0u, 0u);
+      }
     }
   }
 }

@@ -81,8 +81,9 @@ struct DsaIndexerParams {
   // are worked in chunks of dsa_indexer_chunk(T); for every row with more
   // than topk visible positions, the workgroup of chunk c writes (order-
   // preserving key, position) of each score whose key is >= thresh[row] to
-  // cand[row*S + c*chunk ..] (room for the whole chunk) and their number to
-  // cnt[row*n_chunks + c], n_chunks = ceil(S / chunk); rows keeping every
+  // cand[row*S + c*chunk ..] (room for the whole chunk), their number to
+  // cnt[row*n_chunks + c] (n_chunks = ceil(S / chunk)), and after an odd
+  // number a pad entry (0, 0) (no score has key 0).  Rows keeping every
   // visible position write count 0.  Every chunk holding a visible position
   // of a row writes that row's count.
   const uint32_t* thresh;
