@@ -6,8 +6,10 @@ A step is one prefill pass of the hybrid layer pair over T = 32768 tokens:
   HCA layer (64 heads, d = 512, bf16):  hca_compress(K), hca_compress(V),
                                         hca_attention_fwd(PREFILL)
   MLA-DSA layer (64 query heads sharing one 256-wide KV head):
-                                        dsa_indexer_scores -> dsa_topk(2048)
+                                        dsa_indexer_topk(2048)
                                         -> dsa_sparse_attention_fwd
+(dsa_indexer_topk writes the same indices as dsa_indexer_scores followed by
+dsa_topk; the line also times that pair and checks the two agree.)
 `value` is prefill tokens/s of that step (inputs resident in HBM).  The same
 JSON line carries decode microseconds per step for the 128K context
 (batch 64) and the 1M context (batch 4, HCA layer + MLA-DSA layer), per-kernel
@@ -142,6 +144,9 @@ def main():
         vd = synth.torch_normal((1, T_PREFILL, D_DSA), 1.0 / 16, torch.bfloat16, 406, dev)
         scores = torch.empty((1, T_PREFILL, T_PREFILL), dtype=torch.float32, device=dev)
         idx = torch.empty((1, T_PREFILL, TOPK), dtype=torch.int32, device=dev)
+        idx_sep = torch.empty_like(idx)
+        wsf = torch.empty(sa.dsa_indexer_topk_workspace_size(1, T_PREFILL, T_PREFILL, TOPK), dtype=torch.uint8,
+                          device=dev)
         torch.cuda.synchronize()
 
         def k_compress():
@@ -155,7 +160,10 @@ def main():
             sa.dsa_indexer_scores(qi, ki, wi, out=scores)
 
         def k_topk():
-            sa.dsa_topk(scores, TOPK, out=idx)
+            sa.dsa_topk(scores, TOPK, out=idx_sep)
+
+        def k_indexer_topk():
+            sa.dsa_indexer_topk(qi, ki, wi, TOPK, out=idx, workspace=wsf)
 
         def k_sparse():
             return sa.dsa_sparse_attention_fwd(qd, kd, vd, idx)
@@ -163,8 +171,7 @@ def main():
         def step():
             k_compress()
             k_hca()
-            k_indexer()
-            k_topk()
+            k_indexer_topk()
             k_sparse()
 
         progress("prefill warmup")
@@ -183,15 +190,17 @@ def main():
         per = {
             "hca_compress_kv": (k_compress, None),
             "hca_attention_prefill": (k_hca, None),
+            "dsa_indexer_topk": (k_indexer_topk, None),
+            "dsa_sparse_attention": (k_sparse, None),
             "dsa_indexer_scores": (k_indexer, None),
             "dsa_topk": (k_topk, None),
-            "dsa_sparse_attention": (k_sparse, None),
         }
         for name, (fn, _) in per.items():
             fn()
             torch.cuda.synchronize()
             t = timer.time(fn, n_it)
             kernels[name] = {"ms": sum(t) / len(t)}
+        kernels["dsa_indexer_topk"]["equals_separate"] = bool(torch.equal(idx, idx_sep))
 
         if "variants" in parts:
             # The CSA variant of the MLA layer over the same token-level inputs (an
@@ -256,6 +265,8 @@ def main():
         kernels["dsa_indexer_scores"]["alg_flop"] = 2 * HI * DI * causal
         kernels["dsa_indexer_scores"]["alg_bytes"] = 4 * causal + T_PREFILL * (HI * DI * 2 + DI * 2 + HI * 4)
         kernels["dsa_topk"]["alg_bytes"] = 4 * causal + 4 * T_PREFILL * TOPK
+        kernels["dsa_indexer_topk"]["alg_flop"] = 2 * HI * DI * causal
+        kernels["dsa_indexer_topk"]["alg_bytes"] = T_PREFILL * (HI * DI * 2 + DI * 2 + HI * 4) + 4 * T_PREFILL * TOPK
         kernels["dsa_sparse_attention"]["alg_flop"] = 4 * D_DSA * pairs_dsa
         kernels["dsa_sparse_attention"]["alg_bytes"] = 2 * T_PREFILL * HQ * D_DSA * 2 + 4 * T_PREFILL * TOPK + 2 * T_PREFILL * D_DSA * 2
         kernels["dsa_sparse_attention"]["gathered_bytes"] = pairs_dsa // HQ * D_DSA * 2 * 2
@@ -267,7 +278,7 @@ def main():
             if "alg_flop" in kd_:
                 kd_["TFLOPs"] = kd_["alg_flop"] / s_ / 1e12
                 kd_["mfma_frac"] = kd_["TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
-        del q, k, v, kc, vc, qi, ki, wi, qd, kd, vd, scores, idx
+        del q, k, v, kc, vc, qi, ki, wi, qd, kd, vd, scores, idx, idx_sep, wsf
         torch.cuda.empty_cache()
 
     # -------------------------------------------------------------------
@@ -384,7 +395,7 @@ def main():
     # -------------------------------------------------------------------
     roofline = None
     if "prefill" in result:
-        pk = {n: kernels[n] for n in ("hca_compress_kv", "hca_attention_prefill", "dsa_indexer_scores", "dsa_topk",
+        pk = {n: kernels[n] for n in ("hca_compress_kv", "hca_attention_prefill", "dsa_indexer_topk",
                                       "dsa_sparse_attention")}
         dom = max(pk, key=lambda n: pk[n]["ms"])
         kd_ = pk[dom]

@@ -59,10 +59,14 @@ __device__ __forceinline__ void idx_stage(char* buf, buffer_rsrc_t rsrc, int s0,
   }
 }
 
-// kEmit: candidate mode (see DsaIndexerParams) instead of storing scores.
-template <int kWaves, bool kEmit>
+// kMode: kIdxScores stores the scores; kIdxCand runs candidate mode (see
+// DsaIndexerParams); kIdxFiltered stores the scores of the query tiles that
+// hold a flagged row only (the row filter).
+constexpr int kIdxScores = 0, kIdxCand = 1, kIdxFiltered = 2;
+template <int kWaves, int kMode>
 __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerParams p, int n_qtiles, int n_chunks,
                                                                    int chunk) {
+  constexpr bool kEmit = kMode == kIdxCand;
   __shared__ __attribute__((aligned(16))) char lds0[kIdxTileBytes];
   __shared__ __attribute__((aligned(16))) char lds1[kIdxTileBytes];
   constexpr int kQTile = kWaves * kIdxQPerWave;
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   };
   const int i0 = qt * kQTile;
   const int i_last = min(i0 + kQTile - 1, T - 1);
-  if (p.row_flag) {  // row filter: run only for a tile that holds a flagged row
+  if constexpr (kMode == kIdxFiltered) {  // run only for a tile that holds a flagged row
     __shared__ uint32_t any_row;
     if (threadIdx.x == 0) any_row = 0u;
     __syncthreads();
@@ -459,24 +463,29 @@ hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
     } else {
       const int chunk = kIdxDecodeTiles * kIdxKTile;
       const int64_t n_chunks = (p.S + chunk - 1) / chunk;
+      const dim3 grid((uint32_t)(p.B * n_chunks));
       if (p.cand)
-        hipLaunchKernelGGL((dsa_indexer_kernel<1, true>), dim3((uint32_t)(p.B * n_chunks)), dim3(64), 0, stream, p, 1,
-                           (int)n_chunks, chunk);
+        hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxCand>), grid, dim3(64), 0, stream, p, 1, (int)n_chunks, chunk);
+      else if (p.row_flag)
+        hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxFiltered>), grid, dim3(64), 0, stream, p, 1, (int)n_chunks, chunk);
       else
-        hipLaunchKernelGGL((dsa_indexer_kernel<1, false>), dim3((uint32_t)(p.B * n_chunks)), dim3(64), 0, stream, p, 1,
-                           (int)n_chunks, chunk);
+        hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxScores>), grid, dim3(64), 0, stream, p, 1, (int)n_chunks, chunk);
     }
   } else {
     const int chunk = kIdxTilesPerChunk * kIdxKTile;
     const int64_t n_chunks = (p.S + chunk - 1) / chunk;
     const int64_t n_qtiles = (p.T + 4 * kIdxQPerWave - 1) / (4 * kIdxQPerWave);
     const int64_t nblocks = p.B * n_qtiles * n_chunks;
+    const dim3 grid((uint32_t)nblocks);
     if (p.cand)
-      hipLaunchKernelGGL((dsa_indexer_kernel<4, true>), dim3((uint32_t)nblocks), dim3(256), 0, stream, p, (int)n_qtiles,
+      hipLaunchKernelGGL((dsa_indexer_kernel<4, kIdxCand>), grid, dim3(256), 0, stream, p, (int)n_qtiles, (int)n_chunks,
+                         chunk);
+    else if (p.row_flag)
+      hipLaunchKernelGGL((dsa_indexer_kernel<4, kIdxFiltered>), grid, dim3(256), 0, stream, p, (int)n_qtiles,
                          (int)n_chunks, chunk);
     else
-      hipLaunchKernelGGL((dsa_indexer_kernel<4, false>), dim3((uint32_t)nblocks), dim3(256), 0, stream, p,
-                         (int)n_qtiles, (int)n_chunks, chunk);
+      hipLaunchKernelGGL((dsa_indexer_kernel<4, kIdxScores>), grid, dim3(256), 0, stream, p, (int)n_qtiles,
+                         (int)n_chunks, chunk);
   }
   return hipGetLastError();
 }

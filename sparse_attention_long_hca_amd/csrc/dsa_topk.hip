@@ -79,7 +79,8 @@ constexpr int kCandCap = kWave;              // ranked pairwise by one wave
 
 
 // Rows i0 .. i0 + ni - 1 of every batch entry, one workgroup each.
-template <int kThreads>
+// kFilter: only rows with row_flag[row] != 0 run (and none unless *any_flag).
+template <int kThreads, bool kFilter>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void dsa_topk_reg_kernel(
     DsaTopkParams p, int64_t i0, int64_t ni) {
   constexpr int kRegThreads = kThreads;
@@ -100,7 +101,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int64_t lid = blockIdx.x;
   const int64_t b = lid / ni, i = i0 + lid % ni;
   const int64_t row = b * p.T + i;
-  if (p.row_flag && (*p.any_flag == 0u || p.row_flag[row] == 0u)) return;  // row filter
+  if constexpr (kFilter) {
+    if (*p.any_flag == 0u || p.row_flag[row] == 0u) return;
+  }
   const int n = (int)row_len(p, b, i);
   const int k = (int)p.k;
   int32_t* out = p.idx + row * p.k;
@@ -749,7 +752,10 @@ hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream) {
   const int64_t rows = p.B * p.T;
   if (p.S <= kRegRow) {
     if (p.q_pos) {  // row lengths are on the device: one size fits all
-      hipLaunchKernelGGL(dsa_topk_reg_kernel<512>, dim3((uint32_t)rows), dim3(512), 0, stream, p, (int64_t)0, p.T);
+      if (p.row_flag)
+        hipLaunchKernelGGL((dsa_topk_reg_kernel<512, true>), dim3((uint32_t)rows), dim3(512), 0, stream, p, (int64_t)0, p.T);
+      else
+        hipLaunchKernelGGL((dsa_topk_reg_kernel<512, false>), dim3((uint32_t)rows), dim3(512), 0, stream, p, (int64_t)0, p.T);
       return hipGetLastError();
     }
     // Causal rows from position 0: row i holds min((i + 1) / ratio, S)
@@ -761,8 +767,11 @@ hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream) {
       const int64_t cap = (int64_t)kThreads * kRegVec * 4;
       const int64_t i1 = kThreads == 512 ? p.T : std::min<int64_t>(p.T, (cap + 1) * p.ratio - 1);
       if (i1 > i0) {
-        hipLaunchKernelGGL(dsa_topk_reg_kernel<kThreads>, dim3((uint32_t)(p.B * (i1 - i0))), dim3(kThreads), 0,
-                           stream, p, i0, i1 - i0);
+        const dim3 grid((uint32_t)(p.B * (i1 - i0)));
+        if (p.row_flag)
+          hipLaunchKernelGGL((dsa_topk_reg_kernel<kThreads, true>), grid, dim3(kThreads), 0, stream, p, i0, i1 - i0);
+        else
+          hipLaunchKernelGGL((dsa_topk_reg_kernel<kThreads, false>), grid, dim3(kThreads), 0, stream, p, i0, i1 - i0);
         i0 = i1;
       }
     };
