@@ -42,6 +42,7 @@ from .dsa import (
     dsa_indexer_scores,
     dsa_topk,
     dsa_sparse_attention,
+    dsa_sparse_attention_bwd,
     csa_attention,
     n_candidates,
 )
@@ -62,6 +63,7 @@ __all__ = [
     "dsa_indexer_scores",
     "dsa_topk",
     "dsa_sparse_attention",
+    "dsa_sparse_attention_bwd",
     "csa_attention",
     "n_candidates",
     "e4m3_value",

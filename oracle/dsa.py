@@ -118,6 +118,49 @@ def dsa_sparse_attention(q, k, v, idx, scale=None):
     return o, lse
 
 
+def dsa_sparse_attention_bwd(q, k, v, idx, do, scale=None):
+    """Gradients of dsa_sparse_attention for an upstream gradient do of o.
+
+    The pages train these layers ([P1] §二.1 notes DSA's training speed) but
+    print no backward formula; this is the chain rule applied to the forward's
+    definition, entry by entry of idx (an entry listed twice counts twice).
+    The selection idx is discrete and receives no gradient.  Per row, with
+    the row's entries s_1..s_n, K = k[s_j], V = v[s_j]:
+      P  = softmax_j(scale * q_h . k_{s_j})      (the forward's weights)
+      dP = do_h . v_{s_j}
+      dS = P * (dP - sum_j P dP)                 (softmax derivative)
+      dq_h        = scale * sum_j dS_hj k_{s_j}
+      dk[s_j]    += scale * sum_h dS_hj q_h
+      dv[s_j]    += sum_h P_hj do_h
+    Returns (dq [B, T, Hq, D], dk [B, S, D], dv [B, S, D]) in float64; rows
+    without an entry contribute nothing.
+    """
+    q, k, v, do = map(_f64, (q, k, v, do))
+    B, T, Hq, D = q.shape
+    S = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    dq = np.zeros((B, T, Hq, D))
+    dk = np.zeros((B, S, D))
+    dv = np.zeros((B, S, D))
+    for b in range(B):
+        for i in range(T):
+            sel = idx[b, i]
+            sel = sel[sel >= 0]
+            if sel.size == 0:
+                continue
+            kr, vr = k[b, sel], v[b, sel]
+            logits = scale * (q[b, i] @ kr.T)  # [Hq, n]
+            p = np.exp(logits - logits.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = do[b, i] @ vr.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[b, i] = scale * (ds @ kr)
+            np.add.at(dk[b], sel, scale * (ds.T @ q[b, i]))
+            np.add.at(dv[b], sel, p.T @ do[b, i])
+    return dq, dk, dv
+
+
 def csa_attention(q_idx, k_idx, w, q, k, v, ratio, topk, scale=None):
     """CSA forward for one layer over token-level inputs (see the module docstring).
 

@@ -408,6 +408,63 @@ def pin_sparse_identity_support():
         _close(w[sel], p / p.sum(), 1e-12, "identity-V weights")
 
 
+def _sparse_bwd_case(seed, B, T, S, Hq, D, kk):
+    rng = _rng(seed)
+    q = rng.standard_normal((B, T, Hq, D))
+    k = rng.standard_normal((B, S, D))
+    v = rng.standard_normal((B, S, D))
+    do = rng.standard_normal((B, T, Hq, D))
+    idx = np.stack([np.stack([rng.choice(S, kk, replace=False) for _ in range(T)]) for _ in range(B)])
+    return q, k, v, do, idx
+
+
+def pin_sparse_bwd_finite_differences():
+    """Every gradient entry equals a central difference of the forward oracle's loss sum(do * o)
+    (the forward is pinned on its own); padding, a repeated entry and an empty row included."""
+    q, k, v, do, idx = _sparse_bwd_case(31, 1, 4, 9, 2, 3, 4)
+    idx[0, 1, 2] = -1
+    idx[0, 2, 3] = idx[0, 2, 0]  # one position listed twice
+    idx[0, 3] = -1               # empty row
+    dq, dk, dv = oracle.dsa_sparse_attention_bwd(q, k, v, idx, do)
+    loss = lambda q_, k_, v_: float((oracle.dsa_sparse_attention(q_, k_, v_, idx)[0] * do).sum())
+    h = 1e-6
+    for name, x, g in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
+        fd = np.zeros_like(x)
+        for j in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[j] += h
+            xm[j] -= h
+            args_p = [xp if a is x else a for a in (q, k, v)]
+            args_m = [xm if a is x else a for a in (q, k, v)]
+            fd[j] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        _close(g, fd, 1e-7, f"{name} vs central differences")
+
+
+def pin_sparse_bwd_sum_identities():
+    """Softmax weights sum to 1 and their derivative rows sum to 0: summed over positions, dk is 0
+    and dv is the sum of do over every (token, head) whose row has an entry."""
+    q, k, v, do, idx = _sparse_bwd_case(32, 2, 5, 11, 3, 4, 5)
+    idx[1, 2] = -1
+    dq, dk, dv = oracle.dsa_sparse_attention_bwd(q, k, v, idx, do)
+    live = (idx >= 0).any(axis=2)
+    _close(dk.sum(axis=1), np.zeros((2, 4)), 1e-12, "sum of dk")
+    _close(dv.sum(axis=1), (do * live[:, :, None, None]).sum(axis=(1, 2)), 1e-12, "sum of dv")
+    assert np.all(dq[1, 2] == 0), "empty row has no dq"
+
+
+def pin_sparse_bwd_single_entry():
+    """One entry per row: its weight is 1 for any logits, so dq = 0, dk = 0 and dv[s] collects
+    the row's do summed over heads."""
+    q, k, v, do, idx = _sparse_bwd_case(33, 1, 3, 6, 2, 4, 1)
+    idx[0, :, 0] = [4, 1, 4]
+    dq, dk, dv = oracle.dsa_sparse_attention_bwd(q, k, v, idx, do)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    ref = np.zeros((6, 4))
+    for t, s in enumerate([4, 1, 4]):
+        ref[s] += do[0, t].sum(axis=0)
+    _close(dv[0], ref, 1e-14, "single-entry dv")
+
+
 def pin_dsa_end_to_end_k_ge_context_is_dense():
     rng = _rng(18)
     T, Hi, Di, Hq, D = 14, 2, 4, 3, 8

@@ -121,6 +121,7 @@ _orig_quantize = ofp8.quantize_fp8_rows
 _orig_scores = odsa.dsa_indexer_scores
 _orig_topk = odsa.dsa_topk
 _orig_sparse = odsa.dsa_sparse_attention
+_orig_sparse_bwd = odsa.dsa_sparse_attention_bwd
 
 
 def _mut_scores_no_relu(q_idx, k_idx, w, q_pos=None):
@@ -173,6 +174,40 @@ def _mut_sparse_keeps_padding(q, k, v, idx, scale=None):
     return _orig_sparse(q, k, v, idx, scale)
 
 
+def _sparse_bwd_parts(q, k, v, idx, do, scale, ds_fn, dk_scale, dv_from_ds):
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    B, T, Hq, D = q.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(B):
+        for i in range(T):
+            sel = idx[b, i][idx[b, i] >= 0]
+            if sel.size == 0:
+                continue
+            lg = scale * (q[b, i] @ k[b, sel].T)
+            p = np.exp(lg - lg.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            ds = ds_fn(p, do[b, i] @ v[b, sel].T)
+            dq[b, i] = scale * ds @ k[b, sel]
+            np.add.at(dk[b], sel, dk_scale(scale) * (ds.T @ q[b, i]))
+            np.add.at(dv[b], sel, (ds if dv_from_ds else p).T @ do[b, i])
+    return dq, dk, dv
+
+
+def _mut_sparse_bwd_no_rowsum(q, k, v, idx, do, scale=None):
+    return _sparse_bwd_parts(q, k, v, idx, do, scale, lambda p, dp: p * dp, lambda s: s, False)
+
+
+def _mut_sparse_bwd_dk_unscaled(q, k, v, idx, do, scale=None):
+    return _sparse_bwd_parts(q, k, v, idx, do, scale, lambda p, dp: p * (dp - (p * dp).sum(1, keepdims=True)),
+                             lambda s: 1.0, False)
+
+
+def _mut_sparse_bwd_dv_from_ds(q, k, v, idx, do, scale=None):
+    return _sparse_bwd_parts(q, k, v, idx, do, scale, lambda p, dp: p * (dp - (p * dp).sum(1, keepdims=True)),
+                             lambda s: s, True)
+
+
 MUTATIONS = {
     "visible_off_by_one": (ohca, "hca_visible_blocks", _mut_visible_off_by_one),
     "window_one_short": (ohca, "hca_window_range", _mut_window_one_short),
@@ -185,6 +220,9 @@ MUTATIONS = {
     "topk_ties_high": (odsa, "dsa_topk", _mut_topk_ties_high),
     "topk_descending_output": (odsa, "dsa_topk", _mut_topk_descending_output),
     "sparse_keeps_padding": (odsa, "dsa_sparse_attention", _mut_sparse_keeps_padding),
+    "sparse_bwd_no_rowsum": (odsa, "dsa_sparse_attention_bwd", _mut_sparse_bwd_no_rowsum),
+    "sparse_bwd_dk_unscaled": (odsa, "dsa_sparse_attention_bwd", _mut_sparse_bwd_dk_unscaled),
+    "sparse_bwd_dv_from_ds": (odsa, "dsa_sparse_attention_bwd", _mut_sparse_bwd_dv_from_ds),
     "e4m3_bias8": (ofp8, "e4m3_value", _mut_e4m3_bias8),
     "e4m3_truncate": (ofp8, "e4m3_encode", _mut_e4m3_truncate),
     "e4m3_ties_away": (ofp8, "e4m3_encode", _mut_e4m3_ties_away),
