@@ -328,6 +328,35 @@ int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v,
                              int64_t kk, float scale, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * dsa_sparse_attention_bwd -- gradients of dsa_sparse_attention_fwd.
+ *
+ * [P1] §二.1 / [P3] §架構創新 1 define the forward (exact attention over the
+ * selected positions); the pages train these layers but print no backward
+ * formula, so this is the chain rule of the forward's definition, entry by
+ * entry of idx (an entry listed twice counts twice; skipped entries and the
+ * selection itself get no gradient).  With P the forward's weights over the
+ * row's entries, rebuilt from lse, and D_h = sum_d d_o[h,d] * o[h,d]:
+ *   dq[b,i,h]   = scale * sum_j P_hj (d_o[h].v[s_j] - D_h) k[s_j]
+ *   dk[b,s_j]  += scale * sum_h P_hj (d_o[h].v[s_j] - D_h) q[b,i,h]
+ *   dv[b,s_j]  += sum_h P_hj d_o[b,i,h]
+ * q, o, d_o: [B,T,Hq,D] bf16 (o and lse as written by the forward call with
+ * the same q, k, v, idx, scale); k, v: [B,S,D] bf16; idx: [B,T,kk] int32;
+ * lse: fp32 [B,T,Hq], required.  Outputs (fp32, written by the call): dq
+ * [B,T,Hq,D]; dk, dv [B,S,D] (the call zeroes them, then accumulates; the
+ * order of the additions is not fixed, so the last bits can differ between
+ * runs).  scale <= 0 -> 1/sqrt(D).  Arithmetic: bf16 inputs, fp32 dot
+ * products, weights and sums.
+ * Supported: SA_BF16, D = 256, Hq = 64, 1 <= kk <= 2048, S <= 2^23.
+ * Errors: SA_ERR_NULL (any pointer NULL), SA_ERR_SHAPE, SA_ERR_UNSUPPORTED,
+ * SA_ERR_ALIGN (every pointer 16-byte aligned), SA_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+int dsa_sparse_attention_bwd(const void* q, const void* k, const void* v, const int32_t* idx,
+                             const void* o, const float* lse, const void* d_o,
+                             float* dq, float* dk, float* dv, sa_dtype dtype,
+                             int64_t B, int64_t T, int64_t S, int64_t Hq, int64_t D, int64_t kk,
+                             float scale, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

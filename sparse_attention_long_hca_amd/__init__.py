@@ -12,6 +12,7 @@ from ._lib import (
     csa_indexer_scores,
     csa_topk,
     dsa_indexer_scores,
+    dsa_sparse_attention_bwd,
     dsa_sparse_attention_fwd,
     dsa_sparse_attention_fwd_workspace_size,
     dsa_topk,
@@ -37,6 +38,7 @@ __all__ = [
     "csa_topk",
     "dsa_indexer_scores",
     "dsa_sparse_attention_fwd",
+    "dsa_sparse_attention_bwd",
     "dsa_sparse_attention_fwd_workspace_size",
     "dsa_topk",
     "dsa_topk_workspace_size",

@@ -103,6 +103,10 @@ EXPORTS = {
         ctypes.c_int,
         [_c_p] * 6 + [ctypes.c_int] + [_c_i64] * 6 + [ctypes.c_float, _c_p, ctypes.c_size_t, _c_p],
     ),
+    "dsa_sparse_attention_bwd": (
+        ctypes.c_int,
+        [_c_p] * 10 + [ctypes.c_int] + [_c_i64] * 6 + [ctypes.c_float, _c_p],
+    ),
 }
 
 
@@ -488,3 +492,38 @@ def dsa_sparse_attention_fwd(q, k, v, idx, scale=None, return_lse=False, workspa
         ),
     )
     return (o, lse) if return_lse else o
+
+
+def dsa_sparse_attention_bwd(q, k, v, idx, o, lse, do, scale=None):
+    """Gradients of dsa_sparse_attention_fwd for the upstream gradient do of o.
+
+    q, o, do [B,T,Hq,D] bf16; k, v [B,S,D] bf16; idx [B,T,kk] int32; lse [B,T,Hq] fp32 (o and lse
+    from the forward call) -> (dq [B,T,Hq,D], dk [B,S,D], dv [B,S,D]) fp32.
+    """
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(idx, "idx", torch.int32, 3)
+    _need(o, "o", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(do, "do", torch.bfloat16, 4)
+    B, T, Hq, D = q.shape
+    S = k.shape[1]
+    kk = idx.shape[2]
+    _shape(k, "k", (B, S, D))
+    _shape(v, "v", (B, S, D))
+    _shape(idx, "idx", (B, T, kk))
+    _shape(o, "o", (B, T, Hq, D))
+    _shape(lse, "lse", (B, T, Hq))
+    _shape(do, "do", (B, T, Hq, D))
+    dq = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, S, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, S, D), dtype=torch.float32, device=q.device)
+    _check(
+        "dsa_sparse_attention_bwd",
+        lib().dsa_sparse_attention_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            SA_BF16, B, T, S, Hq, D, kk, 0.0 if scale is None else float(scale), _stream(),
+        ),
+    )
+    return dq, dk, dv

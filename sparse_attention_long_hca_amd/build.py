@@ -32,6 +32,7 @@ SOURCES = [
     "dsa_topk.hip",
     "dsa_fused.hip",
     "dsa_sparse_attn.hip",
+    "dsa_sparse_bwd.hip",
 ]
 
 COMMON_FLAGS = [

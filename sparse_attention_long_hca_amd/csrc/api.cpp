@@ -345,4 +345,25 @@ int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v, const 
   return hip_status(sa::launch_dsa_sparse(p, (int)D, (int)Hq, stream), "dsa_sparse_attention_fwd launch");
 }
 
+int dsa_sparse_attention_bwd(const void* q, const void* k, const void* v, const int32_t* idx, const void* o,
+                             const float* lse, const void* d_o, float* dq, float* dk, float* dv, sa_dtype dtype,
+                             int64_t B, int64_t T, int64_t S, int64_t Hq, int64_t D, int64_t kk, float scale,
+                             hipStream_t stream) {
+  if (!q || !k || !v || !idx || !o || !lse || !d_o || !dq || !dk || !dv)
+    return fail(SA_ERR_NULL, "dsa_sparse_attention_bwd: every pointer must be non-NULL");
+  if (B <= 0 || T <= 0 || S <= 0 || Hq <= 0 || D <= 0 || kk <= 0)
+    return fail(SA_ERR_SHAPE, "dsa_sparse_attention_bwd: sizes must be > 0");
+  if (dtype != SA_BF16 || D != 256 || Hq != 64)
+    return fail(SA_ERR_UNSUPPORTED, "dsa_sparse_attention_bwd: supported dtype bf16, D = 256, Hq = 64");
+  if (kk > 2048) return fail(SA_ERR_UNSUPPORTED, "dsa_sparse_attention_bwd: kk must be <= 2048");
+  if (S > ((int64_t)1 << 23)) return fail(SA_ERR_UNSUPPORTED, "dsa_sparse_attention_bwd: S must be <= 2^23");
+  if (B * T > 0x7fffffffLL) return fail(SA_ERR_SHAPE, "dsa_sparse_attention_bwd: too many tokens");
+  const void* ptrs[] = {q, k, v, idx, o, lse, d_o, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(SA_ERR_ALIGN, "dsa_sparse_attention_bwd: pointers must be 16-byte aligned");
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  sa::DsaSparseBwdParams p{q, k, v, idx, o, lse, d_o, dq, dk, dv, B, T, S, kk, sc, resolve_scale_log2(scale, D)};
+  return hip_status(sa::launch_dsa_sparse_bwd(p, stream), "dsa_sparse_attention_bwd launch");
+}
+
 }  // extern "C"

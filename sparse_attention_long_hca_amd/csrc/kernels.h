@@ -145,4 +145,21 @@ int64_t dsa_sparse_nsplit(int64_t BT, int64_t kk);
 size_t dsa_sparse_workspace_bytes(int64_t BT, int64_t nsplit, int64_t hq, int64_t d);
 hipError_t launch_dsa_sparse(const DsaSparseParams& p, int d, int hq, hipStream_t stream);
 
+// ---- dsa_sparse_bwd -----------------------------------------------------------
+struct DsaSparseBwdParams {
+  const void* q;  // [B,T,64,256] bf16
+  const void* k;  // [B,S,256]
+  const void* v;
+  const int32_t* idx;  // [B,T,kk]
+  const void* o;       // forward output [B,T,64,256] bf16
+  const float* lse;    // forward log-sum-exp [B,T,64] (natural log)
+  const void* dout;    // [B,T,64,256] bf16
+  float* dq;           // [B,T,64,256]
+  float* dk;           // [B,S,256] (zeroed, then accumulated)
+  float* dv;
+  int64_t B, T, S, kk;
+  float scale, scale_log2;
+};
+hipError_t launch_dsa_sparse_bwd(const DsaSparseBwdParams& p, hipStream_t stream);
+
 }  // namespace sa

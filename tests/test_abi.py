@@ -235,3 +235,20 @@ def test_indexer_topk_validation(sa):
     # the workspace holds a candidate slot (8 bytes) per row and position; the
     # recomputed rows' scores reuse that area
     assert L.dsa_indexer_topk_workspace_size(1, 32768, 32768, 2048) >= 32768 * 32768 * 8
+
+
+def test_sparse_attention_bwd_validation(sa):
+    L = sa.lib()
+    # q, k, v, idx, o, lse, d_o, dq, dk, dv, dtype, B, T, S, Hq, D, kk, scale, stream
+    # (never called with valid arguments on the CPU)
+    args = [4096] * 10 + [1, 1, 4, 16, 64, 256, 32, 0.0, None]
+    for i in range(10):
+        bad = list(args)
+        bad[i] = None
+        assert L.dsa_sparse_attention_bwd(*bad) == SA_ERR_NULL
+    for i, val, err in ((15, 128, SA_ERR_UNSUPPORTED), (14, 32, SA_ERR_UNSUPPORTED), (16, 4096, SA_ERR_UNSUPPORTED),
+                        (10, 0, SA_ERR_UNSUPPORTED), (12, 0, SA_ERR_SHAPE), (13, 0, SA_ERR_SHAPE),
+                        (13, (1 << 23) + 1, SA_ERR_UNSUPPORTED), (7, 4100, SA_ERR_ALIGN)):
+        bad = list(args)
+        bad[i] = val
+        assert L.dsa_sparse_attention_bwd(*bad) == err, (i, val)
