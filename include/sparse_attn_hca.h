@@ -344,18 +344,22 @@ int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v,
  * the same q, k, v, idx, scale); k, v: [B,S,D] bf16; idx: [B,T,kk] int32;
  * lse: fp32 [B,T,Hq], required.  Outputs (fp32, written by the call): dq
  * [B,T,Hq,D]; dk, dv [B,S,D] (the call zeroes them, then accumulates; the
- * order of the additions is not fixed, so the last bits can differ between
- * runs).  scale <= 0 -> 1/sqrt(D).  Arithmetic: bf16 inputs, fp32 dot
+ * order of the additions per position is not fixed, so the last bits can
+ * differ between runs).  scale <= 0 -> 1/sqrt(D).  Arithmetic: bf16 inputs, fp32 dot
  * products, weights and sums.
  * Supported: SA_BF16, D = 256, Hq = 64, 1 <= kk <= 2048, S <= 2^23.
+ * Workspace: dsa_sparse_attention_bwd_workspace_size(B, T, S, kk) bytes,
+ * 16-byte aligned (per-entry dk / dv rows of up to 1024 tokens at a time and
+ * an inverse index of their entries: about 4.3 GB at kk = 2048).
  * Errors: SA_ERR_NULL (any pointer NULL), SA_ERR_SHAPE, SA_ERR_UNSUPPORTED,
- * SA_ERR_ALIGN (every pointer 16-byte aligned), SA_ERR_HIP.
+ * SA_ERR_ALIGN (every pointer 16-byte aligned), SA_ERR_WORKSPACE, SA_ERR_HIP.
  * ------------------------------------------------------------------------ */
+size_t dsa_sparse_attention_bwd_workspace_size(int64_t B, int64_t T, int64_t S, int64_t kk);
 int dsa_sparse_attention_bwd(const void* q, const void* k, const void* v, const int32_t* idx,
                              const void* o, const float* lse, const void* d_o,
                              float* dq, float* dk, float* dv, sa_dtype dtype,
                              int64_t B, int64_t T, int64_t S, int64_t Hq, int64_t D, int64_t kk,
-                             float scale, hipStream_t stream);
+                             float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,7 @@ from ._lib import (
     csa_topk,
     dsa_indexer_scores,
     dsa_sparse_attention_bwd,
+    dsa_sparse_attention_bwd_workspace_size,
     dsa_sparse_attention_fwd,
     dsa_sparse_attention_fwd_workspace_size,
     dsa_topk,
@@ -39,6 +40,7 @@ __all__ = [
     "dsa_indexer_scores",
     "dsa_sparse_attention_fwd",
     "dsa_sparse_attention_bwd",
+    "dsa_sparse_attention_bwd_workspace_size",
     "dsa_sparse_attention_fwd_workspace_size",
     "dsa_topk",
     "dsa_topk_workspace_size",

@@ -103,9 +103,10 @@ EXPORTS = {
         ctypes.c_int,
         [_c_p] * 6 + [ctypes.c_int] + [_c_i64] * 6 + [ctypes.c_float, _c_p, ctypes.c_size_t, _c_p],
     ),
+    "dsa_sparse_attention_bwd_workspace_size": (ctypes.c_size_t, [_c_i64] * 4),
     "dsa_sparse_attention_bwd": (
         ctypes.c_int,
-        [_c_p] * 10 + [ctypes.c_int] + [_c_i64] * 6 + [ctypes.c_float, _c_p],
+        [_c_p] * 10 + [ctypes.c_int] + [_c_i64] * 6 + [ctypes.c_float, _c_p, ctypes.c_size_t, _c_p],
     ),
 }
 
@@ -494,7 +495,11 @@ def dsa_sparse_attention_fwd(q, k, v, idx, scale=None, return_lse=False, workspa
     return (o, lse) if return_lse else o
 
 
-def dsa_sparse_attention_bwd(q, k, v, idx, o, lse, do, scale=None):
+def dsa_sparse_attention_bwd_workspace_size(B, T, S, kk):
+    return lib().dsa_sparse_attention_bwd_workspace_size(B, T, S, kk)
+
+
+def dsa_sparse_attention_bwd(q, k, v, idx, o, lse, do, scale=None, workspace=None):
     """Gradients of dsa_sparse_attention_fwd for the upstream gradient do of o.
 
     q, o, do [B,T,Hq,D] bf16; k, v [B,S,D] bf16; idx [B,T,kk] int32; lse [B,T,Hq] fp32 (o and lse
@@ -519,11 +524,15 @@ def dsa_sparse_attention_bwd(q, k, v, idx, o, lse, do, scale=None):
     dq = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
     dk = torch.empty((B, S, D), dtype=torch.float32, device=q.device)
     dv = torch.empty((B, S, D), dtype=torch.float32, device=q.device)
+    need = lib().dsa_sparse_attention_bwd_workspace_size(B, T, S, kk)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check(
         "dsa_sparse_attention_bwd",
         lib().dsa_sparse_attention_bwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-            SA_BF16, B, T, S, Hq, D, kk, 0.0 if scale is None else float(scale), _stream(),
+            SA_BF16, B, T, S, Hq, D, kk, 0.0 if scale is None else float(scale), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(),
         ),
     )
     return dq, dk, dv

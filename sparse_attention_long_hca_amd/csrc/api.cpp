@@ -345,10 +345,15 @@ int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v, const 
   return hip_status(sa::launch_dsa_sparse(p, (int)D, (int)Hq, stream), "dsa_sparse_attention_fwd launch");
 }
 
+size_t dsa_sparse_attention_bwd_workspace_size(int64_t B, int64_t T, int64_t S, int64_t kk) {
+  if (B <= 0 || T <= 0 || S <= 0 || kk <= 0) return 0;
+  return sa::dsa_sparse_bwd_ws_bytes(B, T, S, kk);
+}
+
 int dsa_sparse_attention_bwd(const void* q, const void* k, const void* v, const int32_t* idx, const void* o,
                              const float* lse, const void* d_o, float* dq, float* dk, float* dv, sa_dtype dtype,
                              int64_t B, int64_t T, int64_t S, int64_t Hq, int64_t D, int64_t kk, float scale,
-                             hipStream_t stream) {
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k || !v || !idx || !o || !lse || !d_o || !dq || !dk || !dv)
     return fail(SA_ERR_NULL, "dsa_sparse_attention_bwd: every pointer must be non-NULL");
   if (B <= 0 || T <= 0 || S <= 0 || Hq <= 0 || D <= 0 || kk <= 0)
@@ -361,8 +366,15 @@ int dsa_sparse_attention_bwd(const void* q, const void* k, const void* v, const 
   const void* ptrs[] = {q, k, v, idx, o, lse, d_o, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(SA_ERR_ALIGN, "dsa_sparse_attention_bwd: pointers must be 16-byte aligned");
+  if (B * S >= 0xffffffffLL) return fail(SA_ERR_SHAPE, "dsa_sparse_attention_bwd: B*S must be < 2^32 - 1");
+  const size_t need = sa::dsa_sparse_bwd_ws_bytes(B, T, S, kk);
+  if (!workspace || workspace_bytes < need)
+    return fail(SA_ERR_WORKSPACE, "dsa_sparse_attention_bwd: needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(SA_ERR_ALIGN, "dsa_sparse_attention_bwd: workspace must be 16-byte aligned");
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
-  sa::DsaSparseBwdParams p{q, k, v, idx, o, lse, d_o, dq, dk, dv, B, T, S, kk, sc, resolve_scale_log2(scale, D)};
+  sa::DsaSparseBwdParams p{q, k, v, idx, o, lse, d_o, dq, dk, dv, B, T, S, kk, sc, resolve_scale_log2(scale, D),
+                           workspace, 0, nullptr, nullptr};
   return hip_status(sa::launch_dsa_sparse_bwd(p, stream), "dsa_sparse_attention_bwd launch");
 }
 

@@ -16,11 +16,16 @@
 // rows gathered into LDS.  Every thread computes S and dP for one row and four
 // heads (bf16 dot2 into fp32), then P and dS go to LDS; dQ accumulates in
 // registers (one head, 64 dims per thread); the tile's dK and dV rows are
-// summed over the 64 heads in the workgroup and added to the fp32 outputs with
-// atomics (several tokens select the same position).  Vector ALU arithmetic:
-// a first, plain version of the backward.
+// summed over the 64 heads in the workgroup and written, one row per (token,
+// entry), to G and H in the workspace.  Several tokens select the same
+// position, so dk and dv are then summed per position: tokens are taken in
+// chunks; per chunk a counting sort lists each position's (token, entry)
+// rows, and one workgroup per position adds them into dk and dv (each output
+// row has one owner and chunks run in order, so no floating-point atomics).
+// Vector ALU arithmetic: a first, plain version of the backward.
 #include "common.h"
 #include "kernels.h"
+#include "select_util.h"
 
 namespace sa {
 
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(kBwThreads) void dsa_sparse_bwd_kernel(DsaSparseBwd
   __shared__ float dsum[kBwH];  // D_h
 
   const int t = threadIdx.x;
-  const int64_t tok = blockIdx.x;  // b*T + i
+  const int64_t tok = p.tok0 + blockIdx.x;  // b*T + i
   const int64_t b = tok / p.T;
   const int kk = (int)p.kk;
   const bf16_t* q = reinterpret_cast<const bf16_t*>(p.q) + tok * kBwH * kBwD;
@@ -175,12 +180,12 @@ __global__ __launch_bounds__(kBwThreads) void dsa_sparse_bwd_kernel(DsaSparseBwd
           bw_axpy8(av, wv, *reinterpret_cast<const uint4*>(dr));
           bw_axpy8(av + 8, wv, *reinterpret_cast<const uint4*>(dr + 16));
         }
-        float* dkr = p.dk + (b * p.S + s) * kBwD + c * 16;
-        float* dvr = p.dv + (b * p.S + s) * kBwD + c * 16;
+        const int64_t row = ((int64_t)blockIdx.x * kk + tile * kBwTK + j) * kBwD + c * 16;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          unsafeAtomicAdd(dkr + i, ak[i] * p.scale);
-          unsafeAtomicAdd(dvr + i, av[i]);
+        for (int i = 0; i < 16; i += 4) {
+          *reinterpret_cast<float4*>(p.g + row + i) =
+              make_float4(ak[i] * p.scale, ak[i + 1] * p.scale, ak[i + 2] * p.scale, ak[i + 3] * p.scale);
+          *reinterpret_cast<float4*>(p.hh + row + i) = make_float4(av[i], av[i + 1], av[i + 2], av[i + 3]);
         }
       }
     }
@@ -193,15 +198,113 @@ __global__ __launch_bounds__(kBwThreads) void dsa_sparse_bwd_kernel(DsaSparseBwd
         make_float4(dq[4 * u] * p.scale, dq[4 * u + 1] * p.scale, dq[4 * u + 2] * p.scale, dq[4 * u + 3] * p.scale);
 }
 
-hipError_t launch_dsa_sparse_bwd(const DsaSparseBwdParams& p, hipStream_t stream) {
-  const int64_t n4 = p.B * p.S * kBwD / 4;
+// Inverse index of one chunk of tokens: entry e = (token - tok0) * kk + j.
+__global__ __launch_bounds__(256) void dsa_sparse_bwd_count_kernel(DsaSparseBwdParams p, int64_t ntok, uint32_t* cnt) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= ntok * p.kk) return;
+  const int64_t tok = p.tok0 + e / p.kk;
+  const int32_t s = p.idx[tok * p.kk + e % p.kk];
+  if (s >= 0 && s < p.S) atomicAdd(&cnt[(tok / p.T) * p.S + s], 1u);
+}
+
+// Exclusive offsets of the counts (one workgroup): off[0..n], cursor = off.
+__global__ __launch_bounds__(1024) void dsa_sparse_bwd_scan_kernel(const uint32_t* cnt, uint32_t* off, uint32_t* cursor,
+                                                                   int64_t n) {
+  __shared__ uint32_t scratch[32];
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t i0 = threadIdx.x * per, i1 = min(n, i0 + per);
+  uint32_t local = 0;
+  for (int64_t i = i0; i < i1; ++i) local += cnt[i];
+  uint32_t tot;
+  uint32_t run = block_inclusive_scan(local, scratch, tot) - local;
+  for (int64_t i = i0; i < i1; ++i) {
+    off[i] = run;
+    cursor[i] = run;
+    run += cnt[i];
+  }
+  if (threadIdx.x == 0) off[n] = tot;
+}
+
+__global__ __launch_bounds__(256) void dsa_sparse_bwd_fill_kernel(DsaSparseBwdParams p, int64_t ntok, uint32_t* cursor,
+                                                                  uint32_t* list) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= ntok * p.kk) return;
+  const int64_t tok = p.tok0 + e / p.kk;
+  const int32_t s = p.idx[tok * p.kk + e % p.kk];
+  if (s >= 0 && s < p.S) list[atomicAdd(&cursor[(tok / p.T) * p.S + s], 1u)] = (uint32_t)e;
+}
+
+// One workgroup per key row, one thread per dim: dk[r] += sum of the chunk's
+// G rows listed for r (dv likewise from H).
+__global__ __launch_bounds__(kBwD) void dsa_sparse_bwd_reduce_kernel(DsaSparseBwdParams p, const uint32_t* off,
+                                                                     const uint32_t* list) {
+  const int64_t r = blockIdx.x;  // b*S + s
+  const uint32_t e0 = off[r], e1 = off[r + 1];
+  if (e0 == e1) return;
+  const int d = threadIdx.x;
+  float ak = 0.f, av = 0.f;
+  uint32_t e = e0;
+  for (; e + 4 <= e1; e += 4) {
+    float gk[4], gv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = (int64_t)list[e + u] * kBwD + d;
+      gk[u] = p.g[row];
+      gv[u] = p.hh[row];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ak += gk[u];
+      av += gv[u];
+    }
+  }
+  for (; e < e1; ++e) {
+    const int64_t row = (int64_t)list[e] * kBwD + d;
+    ak += p.g[row];
+    av += p.hh[row];
+  }
+  p.dk[r * kBwD + d] += ak;
+  p.dv[r * kBwD + d] += av;
+}
+
+int64_t dsa_sparse_bwd_chunk(int64_t BT) { return BT < 1024 ? BT : 1024; }
+
+size_t dsa_sparse_bwd_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t kk) {
+  const int64_t tc = dsa_sparse_bwd_chunk(B * T), keys = B * S;
+  auto al = [](int64_t x) { return (size_t)((x + 63) & ~(int64_t)63); };  // 256-byte multiples of 4-byte words
+  return 4 * (2 * al(tc * kk * kBwD) + al(tc * kk) + 3 * al(keys + 1));
+}
+
+hipError_t launch_dsa_sparse_bwd(DsaSparseBwdParams p, hipStream_t stream) {
+  const int64_t BT = p.B * p.T, keys = p.B * p.S, tc = dsa_sparse_bwd_chunk(BT);
+  auto al = [](int64_t x) { return (x + 63) & ~(int64_t)63; };
+  float* w = reinterpret_cast<float*>(p.ws);
+  p.g = w;
+  p.hh = p.g + al(tc * p.kk * kBwD);
+  uint32_t* list = reinterpret_cast<uint32_t*>(p.hh + al(tc * p.kk * kBwD));
+  uint32_t* cnt = list + al(tc * p.kk);
+  uint32_t* off = cnt + al(keys + 1);
+  uint32_t* cursor = off + al(keys + 1);
+  const int64_t n4 = keys * kBwD / 4;
   const uint32_t zb = (uint32_t)std::min<int64_t>((n4 + 255) / 256, 4096);
   hipLaunchKernelGGL(dsa_sparse_bwd_zero_kernel, dim3(zb), dim3(256), 0, stream, reinterpret_cast<float4*>(p.dk), n4);
   hipLaunchKernelGGL(dsa_sparse_bwd_zero_kernel, dim3(zb), dim3(256), 0, stream, reinterpret_cast<float4*>(p.dv), n4);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dsa_sparse_bwd_kernel, dim3((uint32_t)(p.B * p.T)), dim3(kBwThreads), 0, stream, p);
-  return hipGetLastError();
+  const int64_t c4 = al(keys + 1) / 4;  // the counts, zeroed per chunk as float4 words
+  const uint32_t cb = (uint32_t)std::min<int64_t>((c4 + 255) / 256, 4096);
+  for (int64_t tok0 = 0; tok0 < BT; tok0 += tc) {
+    const int64_t ntok = std::min<int64_t>(tc, BT - tok0);
+    p.tok0 = tok0;
+    const uint32_t eb = (uint32_t)((ntok * p.kk + 255) / 256);
+    hipLaunchKernelGGL(dsa_sparse_bwd_zero_kernel, dim3(cb), dim3(256), 0, stream, reinterpret_cast<float4*>(cnt), c4);
+    hipLaunchKernelGGL(dsa_sparse_bwd_count_kernel, dim3(eb), dim3(256), 0, stream, p, ntok, cnt);
+    hipLaunchKernelGGL(dsa_sparse_bwd_scan_kernel, dim3(1), dim3(1024), 0, stream, cnt, off, cursor, keys);
+    hipLaunchKernelGGL(dsa_sparse_bwd_fill_kernel, dim3(eb), dim3(256), 0, stream, p, ntok, cursor, list);
+    hipLaunchKernelGGL(dsa_sparse_bwd_kernel, dim3((uint32_t)ntok), dim3(kBwThreads), 0, stream, p);
+    hipLaunchKernelGGL(dsa_sparse_bwd_reduce_kernel, dim3((uint32_t)keys), dim3(kBwD), 0, stream, p, off, list);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace sa

@@ -159,7 +159,14 @@ struct DsaSparseBwdParams {
   float* dv;
   int64_t B, T, S, kk;
   float scale, scale_log2;
+  void* ws;            // dsa_sparse_bwd_ws_bytes()
+  // Set by the launcher per chunk of tokens: the first token, and the
+  // per-entry dK / dV rows of the chunk ([tokens, kk, 256] fp32).
+  int64_t tok0;
+  float* g;
+  float* hh;
 };
-hipError_t launch_dsa_sparse_bwd(const DsaSparseBwdParams& p, hipStream_t stream);
+size_t dsa_sparse_bwd_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t kk);
+hipError_t launch_dsa_sparse_bwd(DsaSparseBwdParams p, hipStream_t stream);
 
 }  // namespace sa

@@ -239,9 +239,9 @@ def test_indexer_topk_validation(sa):
 
 def test_sparse_attention_bwd_validation(sa):
     L = sa.lib()
-    # q, k, v, idx, o, lse, d_o, dq, dk, dv, dtype, B, T, S, Hq, D, kk, scale, stream
-    # (never called with valid arguments on the CPU)
-    args = [4096] * 10 + [1, 1, 4, 16, 64, 256, 32, 0.0, None]
+    # q, k, v, idx, o, lse, d_o, dq, dk, dv, dtype, B, T, S, Hq, D, kk, scale, workspace, bytes, stream
+    # (never called with valid arguments on the CPU: the workspace check comes last)
+    args = [4096] * 10 + [1, 1, 4, 16, 64, 256, 32, 0.0, 4096, 0, None]
     for i in range(10):
         bad = list(args)
         bad[i] = None
@@ -252,3 +252,8 @@ def test_sparse_attention_bwd_validation(sa):
         bad = list(args)
         bad[i] = val
         assert L.dsa_sparse_attention_bwd(*bad) == err, (i, val)
+    need = L.dsa_sparse_attention_bwd_workspace_size(1, 4, 16, 32)
+    assert need > 0
+    assert L.dsa_sparse_attention_bwd(*args) == SA_ERR_WORKSPACE
+    # at 32768 tokens x top-2048: per-entry dk and dv rows of 1024 tokens (2 x 2 GiB) plus the index
+    assert 2 * 1024 * 2048 * 256 * 4 <= L.dsa_sparse_attention_bwd_workspace_size(1, 32768, 32768, 2048) < 5 * 2 ** 30
