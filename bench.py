@@ -110,7 +110,7 @@ def main():
     sa.lib()
     dev = "cuda:0"
     timer = Timer(torch)
-    parts = set(args.only.split(",")) if args.only else {"prefill", "variants", "decode128k", "decode1m"}
+    parts = set(args.only.split(",")) if args.only else {"prefill", "variants", "backward", "decode128k", "decode1m"}
     result = {}
     kernels = {}
     if "copy" in parts:
@@ -201,6 +201,30 @@ def main():
             t = timer.time(fn, n_it)
             kernels[name] = {"ms": sum(t) / len(t)}
         kernels["dsa_indexer_topk"]["equals_separate"] = bool(torch.equal(idx, idx_sep))
+
+        if "backward" in parts:
+            # Backward of the DSA sparse attention over the step's selection (an extra
+            # figure, not part of the step): upstream gradient N(0,1) bf16.
+            progress("DSA backward")
+            do_ = synth.torch_normal((1, T_PREFILL, HQ, D_DSA), 1.0, torch.bfloat16, 407, dev)
+            o_f, lse_f = sa.dsa_sparse_attention_fwd(qd, kd, vd, idx, return_lse=True)
+            wsb = torch.empty(sa.dsa_sparse_attention_bwd_workspace_size(1, T_PREFILL, T_PREFILL, TOPK),
+                              dtype=torch.uint8, device=dev)
+
+            def k_bwd():
+                return sa.dsa_sparse_attention_bwd(qd, kd, vd, idx, o_f, lse_f, do_, workspace=wsb)
+
+            k_bwd()
+            torch.cuda.synchronize()
+            t = timer.time(k_bwd, 2)
+            ms_b = sum(t) / len(t)
+            flop_b = 10 * D_DSA * dsa_pairs(T_PREFILL) * HQ
+            result["dsa_sparse_attention_bwd"] = {
+                "ms": ms_b, "alg_flop": flop_b, "TFLOPs": flop_b / (ms_b * 1e-3) / 1e12,
+                "mfma_frac": flop_b / (ms_b * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                "workload": "dq, dk, dv of the MLA-DSA sparse attention, T=32768, top-2048, 64 heads x 256"}
+            del do_, o_f, lse_f, wsb
+            torch.cuda.empty_cache()
 
         if "variants" in parts:
             # The CSA variant of the MLA layer over the same token-level inputs (an
@@ -438,6 +462,7 @@ def main():
         },
         "decode": {k_: v_ for k_, v_ in result.items() if k_.startswith("decode")},
         "variants": {k_: v_ for k_, v_ in result.items() if k_.startswith(("csa", "hca_prefill_qk576"))},
+        "backward": {k_: v_ for k_, v_ in result.items() if k_.startswith("dsa_sparse_attention_bwd")},
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
