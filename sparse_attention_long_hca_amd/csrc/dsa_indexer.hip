@@ -186,12 +186,13 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
         fl |= (s <= plim[mb] && score_key(held[slot][mb][nb]) >= thr[mb]) ? (1u << nb) : 0u;
       }
       const uint32_t mine = (uint32_t)__popc(fl);
+      // Inclusive scan over the row's 16 lanes (one DPP row): row_shr 1, 2, 4, 8,
+      // lanes shifted in from outside the row read 0.
       uint32_t x = mine;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, 16);
-        if (L >= off) x += y;
-      }
+      x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true);
+      x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);
+      x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);
+      x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);
       uint2* seg = p.cand + ((int64_t)b * T + iw + mb * 4 + g) * S + s_begin;
       uint32_t slot_i = c_run[mb] + x - mine;
 #pragma unroll
