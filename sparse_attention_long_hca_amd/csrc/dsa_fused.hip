@@ -69,7 +69,7 @@ static FusedLayout fused_layout(int64_t B, int64_t T, int64_t S) {
   L.ks = off;
   off += al((size_t)(B * Ss) * 256);
   L.sscore = off;
-  off += al((size_t)(rows * Ss) * 4);
+  off += al((size_t)(rows * Ss) * 2);
   L.thresh = off;
   off += al((size_t)rows * 4);
   L.cnt = off;
@@ -91,7 +91,7 @@ size_t dsa_indexer_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k) {
 
 struct FusedPtrs {
   const bf16_t* ks;
-  const float* sscore;
+  const uint16_t* skey;  // [rows, Ss]: top 16 bits of the sampled scores' keys
   uint32_t* thresh;
   const uint32_t* cnt;  // [rows, nseg]
   uint32_t* fail;
@@ -135,12 +135,12 @@ __global__ __launch_bounds__(256) void fused_thresh_kernel(DsaIndexerTopkParams 
     ns = ns < f.Ss ? ns : f.Ss;
     const uint32_t r = (uint32_t)fused_rank(p.topk);
     if (ns > (int64_t)r) {
-      const float* ss = f.sscore + row * f.Ss;
+      const uint16_t* ss = f.skey + row * f.Ss;
       uint32_t kv[kThrPer];
 #pragma unroll
       for (int t = 0; t < kThrPer; ++t) {
         const int64_t j = lane + 64 * t;
-        kv[t] = j < ns ? score_key(ss[j]) : 0u;
+        kv[t] = j < ns ? (uint32_t)ss[j] << 16 : 0u;  // the key's top 16 bits: all the threshold uses
       }
       reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
       wave_lds_sync();
@@ -337,7 +337,7 @@ hipError_t launch_dsa_indexer_topk(const DsaIndexerTopkParams& p, hipStream_t st
   const int64_t Ss = p.S / kSample, rows = p.B * p.T;
   FusedPtrs f;
   f.ks = reinterpret_cast<const bf16_t*>(ws + L.ks);
-  f.sscore = reinterpret_cast<const float*>(ws + L.sscore);
+  f.skey = reinterpret_cast<const uint16_t*>(ws + L.sscore);
   f.thresh = reinterpret_cast<uint32_t*>(ws + L.thresh);
   f.cnt = reinterpret_cast<const uint32_t*>(ws + L.cnt);
   f.fail = reinterpret_cast<uint32_t*>(ws + L.fail);
@@ -360,7 +360,7 @@ hipError_t launch_dsa_indexer_topk(const DsaIndexerTopkParams& p, hipStream_t st
     sp.k = f.ks;
     sp.w = p.w;
     sp.q_pos = p.q_pos;
-    sp.scores = const_cast<float*>(f.sscore);
+    sp.keys16 = const_cast<uint16_t*>(f.skey);
     sp.B = p.B;
     sp.T = p.T;
     sp.S = Ss;

@@ -61,8 +61,9 @@ __device__ __forceinline__ void idx_stage(char* buf, buffer_rsrc_t rsrc, int s0,
 
 // kMode: kIdxScores stores the scores; kIdxCand runs candidate mode (see
 // DsaIndexerParams); kIdxFiltered stores the scores of the query tiles that
-// hold a flagged row only (the row filter).
-constexpr int kIdxScores = 0, kIdxCand = 1, kIdxFiltered = 2;
+// hold a flagged row only (the row filter); kIdxKeys16 stores the top 16 bits
+// of each score's order-preserving key instead of the score.
+constexpr int kIdxScores = 0, kIdxCand = 1, kIdxFiltered = 2, kIdxKeys16 = 3;
 template <int kWaves, int kMode>
 __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerParams p, int n_qtiles, int n_chunks,
                                                                    int chunk) {
@@ -212,6 +213,20 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
     }
     const int h0 = held_s0[slot];
     if (h0 < 0) return;
+    if constexpr (kMode == kIdxKeys16) {
+      uint16_t* out16 = p.keys16 + (int64_t)b * T * S;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        // Rows past the sequence end have plim = -1: nothing is stored.
+        uint16_t* orow = out16 + (int64_t)(iw + mb * 4 + g) * S;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int s = h0 + nb * 16 + L;
+          if (s <= plim[mb]) orow[s] = (uint16_t)(score_key(held[slot][mb][nb]) >> 16);
+        }
+      }
+      return;
+    }
     if (h0 + kIdxKTile - 1 <= wave_full_lim) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
@@ -458,7 +473,7 @@ hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
   if (p.T <= kIdxQPerWave) {
     // Decode: one query tile, short chunks of positions.
     // (Candidate mode and filtered launches take the staged kernel.)
-    if (p.T <= 4 && !p.cand && !p.row_flag) {
+    if (p.T <= 4 && !p.cand && !p.row_flag && !p.keys16) {
       const int64_t n_chunks = (p.S + kIdxDecTiles * kIdxKTile - 1) / (kIdxDecTiles * kIdxKTile);
       hipLaunchKernelGGL(dsa_indexer_dec_kernel, dim3((uint32_t)(p.B * n_chunks)), dim3(64), 0, stream, p, (int)n_chunks);
     } else {
@@ -469,6 +484,8 @@ hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxCand>), grid, dim3(64), 0, stream, p, 1, (int)n_chunks, chunk);
       else if (p.row_flag)
         hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxFiltered>), grid, dim3(64), 0, stream, p, 1, (int)n_chunks, chunk);
+      else if (p.keys16)
+        hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxKeys16>), grid, dim3(64), 0, stream, p, 1, (int)n_chunks, chunk);
       else
         hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxScores>), grid, dim3(64), 0, stream, p, 1, (int)n_chunks, chunk);
     }
@@ -483,6 +500,9 @@ hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
                          chunk);
     else if (p.row_flag)
       hipLaunchKernelGGL((dsa_indexer_kernel<4, kIdxFiltered>), grid, dim3(256), 0, stream, p, (int)n_qtiles,
+                         (int)n_chunks, chunk);
+    else if (p.keys16)
+      hipLaunchKernelGGL((dsa_indexer_kernel<4, kIdxKeys16>), grid, dim3(256), 0, stream, p, (int)n_qtiles,
                          (int)n_chunks, chunk);
     else
       hipLaunchKernelGGL((dsa_indexer_kernel<4, kIdxScores>), grid, dim3(256), 0, stream, p, (int)n_qtiles,

@@ -90,6 +90,9 @@ struct DsaIndexerParams {
   uint32_t* cnt;
   uint2* cand;
   int64_t topk;
+  // Key mode (keys16 != NULL): instead of scores, keys16[b,i,s] (same layout)
+  // receives the top 16 bits of the score's order-preserving key.
+  uint16_t* keys16;
   // Row filter (row_flag != NULL): nothing runs unless *any_flag != 0, and a
   // workgroup runs only if one of its rows has row_flag[row] != 0.
   const uint32_t* row_flag;
