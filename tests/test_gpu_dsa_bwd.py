@@ -112,3 +112,42 @@ def test_sparse_bwd_4096_sums_and_sampled_rows():
         err = max_abs_err(f64(dq[:, i:i + 1]), rq)
         print(f"dq row {i}: max abs err {err:.3e} (largest sampled |dq| {mag:.3e})", flush=True)
         assert err <= REL_TOL["dq"] * mag, i
+
+
+def test_sparse_bwd_32768_top2048_sums_and_sampled_rows():
+    """The bench's configuration: T = S = 32768, top-2048 chosen by the indexer and top-k, inputs
+    N(0,1)/16 and do N(0,1).  The sum identities over every position and dq of sampled rows
+    against the oracle row by row."""
+    sa = require_gpu()
+    T, kk = 32768, 2048
+    qi = synth.torch_normal((1, T, 4, 128), 128 ** -0.5, torch.bfloat16, 401, DEV)
+    ki = synth.torch_normal((1, T, 128), 128 ** -0.5, torch.bfloat16, 402, DEV)
+    wi = synth.torch_uniform((1, T, 4), 403, DEV)
+    idx = sa.dsa_indexer_topk(qi, ki, wi, kk)
+    del qi, ki, wi
+    q = synth.torch_normal((1, T, 64, 256), 1.0 / 16, torch.bfloat16, 404, DEV)
+    k = synth.torch_normal((1, T, 256), 1.0 / 16, torch.bfloat16, 405, DEV)
+    v = synth.torch_normal((1, T, 256), 1.0 / 16, torch.bfloat16, 406, DEV)
+    do = synth.torch_normal((1, T, 64, 256), 1.0, torch.bfloat16, 407, DEV)
+    o, lse = sa.dsa_sparse_attention_fwd(q, k, v, idx, return_lse=True)
+    dq, dk, dv = sa.dsa_sparse_attention_bwd(q, k, v, idx, o, lse, do)
+    dk64, dv64 = dk.double(), dv.double()
+    err_k = float(dk64.sum(dim=1).abs().max())
+    mag_k = float(dk64.abs().sum(dim=1).max())
+    err_v = float((dv64.sum(dim=1) - do.double().sum(dim=(1, 2))).abs().max())
+    mag_v = float(dv64.abs().sum(dim=1).max())
+    print(f"sum dk: {err_k:.3e} vs {mag_k:.3e}; sum dv: {err_v:.3e} vs {mag_v:.3e}", flush=True)
+    assert err_k <= REL_TOL["dk"] * mag_k
+    assert err_v <= REL_TOL["dv"] * mag_v  # every row has at least one entry
+    kn, vn = f64(k), f64(v)
+    rows = [0, 1, 2047, 2048, 16384, 32767]
+    refs = []
+    for i in rows:
+        r = oracle.dsa_sparse_attention_bwd(f64(q[:, i:i + 1]), kn, vn, idx[:, i:i + 1].cpu().numpy().astype(np.int64),
+                                            f64(do[:, i:i + 1]))
+        refs.append(r[0])
+    mag = max(float(np.abs(r).max()) for r in refs)
+    for i, rq in zip(rows, refs):
+        err = max_abs_err(f64(dq[:, i:i + 1]), rq)
+        print(f"dq row {i}: max abs err {err:.3e} (largest sampled |dq| {mag:.3e})", flush=True)
+        assert err <= REL_TOL["dq"] * mag, i
