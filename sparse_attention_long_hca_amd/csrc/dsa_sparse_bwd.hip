@@ -17,7 +17,9 @@
 // heads (bf16 dot2 into fp32), then P and dS go to LDS; dQ accumulates in
 // registers (one head, 64 dims per thread); the tile's dK and dV rows are
 // summed over the 64 heads in the workgroup and written, one row per (token,
-// entry), to G and H in the workspace.  Several tokens select the same
+// entry), to G and H in the workspace.  The dQ, dK and dV sums take two rows
+// or two heads per bf16 dot2, with dS and P rounded to bf16 (as the forward
+// rounds P for its P*V product).  Several tokens select the same
 // position, so dk and dv are then summed per position: tokens are taken in
 // chunks; per chunk a counting sort lists each position's (token, entry)
 // rows, and one workgroup per position adds them into dk and dv (each output
@@ -46,15 +48,20 @@ __device__ __forceinline__ float bw_dot8(uint4 a, uint4 b, float c) {
   return c;
 }
 
-// acc[0..7] += w * (8 bf16 of u)
-__device__ __forceinline__ void bw_axpy8(float* acc, float w, uint4 u) {
-  const uint32_t x[4] = {u.x, u.y, u.z, u.w};
+// Two bf16 rows a, b (8 values each) interleaved into pairs (a_e, b_e), then
+// acc[e] += a_e * w.x + b_e * w.y for the bf16 pair w: one dot2 per value.
+__device__ __forceinline__ void bw_pair8(float* acc, uint32_t w2, uint4 a, uint4 b) {
+  const uint32_t xa[4] = {a.x, a.y, a.z, a.w}, xb[4] = {b.x, b.y, b.z, b.w};
+  const bf16x2_t w = __builtin_bit_cast(bf16x2_t, w2);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    acc[2 * i] = fmaf(w, bf16_to_f32(x[i] & 0xffffu), acc[2 * i]);
-    acc[2 * i + 1] = fmaf(w, bf16_to_f32(x[i] >> 16), acc[2 * i + 1]);
+    const uint32_t lo = (xa[i] & 0xffffu) | (xb[i] << 16);
+    const uint32_t hi = (xa[i] >> 16) | (xb[i] & 0xffff0000u);
+    acc[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo), w, acc[2 * i], false);
+    acc[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi), w, acc[2 * i + 1], false);
   }
 }
+
 }  // namespace
 
 __global__ __launch_bounds__(256) void dsa_sparse_bwd_zero_kernel(float4* p, int64_t n4) {
@@ -156,12 +163,15 @@ __global__ __launch_bounds__(kBwThreads) void dsa_sparse_bwd_kernel(DsaSparseBwd
       }
     }
     __syncthreads();
-    // dQ (head hq, dims 64cq .. 64cq+63) += dS * K.
-    for (int j = 0; j < kBwTK; ++j) {
-      const float w = dst[j * kBwPP + hq];
+    // dQ (head hq, dims 64cq .. 64cq+63) += dS * K, two rows per dot2 (dS
+    // rounded to bf16, as P is for the forward's P*V product).
+    for (int j = 0; j < kBwTK; j += 2) {
+      const uint32_t w2 = pack_bf16x2(dst[j * kBwPP + hq], dst[(j + 1) * kBwPP + hq]);
       const char* kr = ks + j * kBwRowB + cq * 128;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) bw_axpy8(dq + 8 * u, w, *reinterpret_cast<const uint4*>(kr + u * 16));
+      for (int u = 0; u < 8; ++u)
+        bw_pair8(dq + 8 * u, w2, *reinterpret_cast<const uint4*>(kr + u * 16),
+                 *reinterpret_cast<const uint4*>(kr + kBwRowB + u * 16));
     }
     {
       // dK and dV of row j, dims 16c .. 16c+15, summed over the 64 heads.
@@ -171,14 +181,18 @@ __global__ __launch_bounds__(kBwThreads) void dsa_sparse_bwd_kernel(DsaSparseBwd
         float ak[16], av[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) ak[i] = av[i] = 0.f;
-        for (int h = 0; h < kBwH; ++h) {
-          const float wk = dst[j * kBwPP + h], wv = pt[j * kBwPP + h];
+        // Two heads per dot2 (dS and P rounded to bf16).
+        for (int h = 0; h < kBwH; h += 2) {
+          const uint32_t wk2 = pack_bf16x2(dst[j * kBwPP + h], dst[j * kBwPP + h + 1]);
+          const uint32_t wv2 = pack_bf16x2(pt[j * kBwPP + h], pt[j * kBwPP + h + 1]);
           const char* qr = qs + h * kBwRowB + c * 32;
           const char* dr = dos + h * kBwRowB + c * 32;
-          bw_axpy8(ak, wk, *reinterpret_cast<const uint4*>(qr));
-          bw_axpy8(ak + 8, wk, *reinterpret_cast<const uint4*>(qr + 16));
-          bw_axpy8(av, wv, *reinterpret_cast<const uint4*>(dr));
-          bw_axpy8(av + 8, wv, *reinterpret_cast<const uint4*>(dr + 16));
+          bw_pair8(ak, wk2, *reinterpret_cast<const uint4*>(qr), *reinterpret_cast<const uint4*>(qr + kBwRowB));
+          bw_pair8(ak + 8, wk2, *reinterpret_cast<const uint4*>(qr + 16),
+                   *reinterpret_cast<const uint4*>(qr + kBwRowB + 16));
+          bw_pair8(av, wv2, *reinterpret_cast<const uint4*>(dr), *reinterpret_cast<const uint4*>(dr + kBwRowB));
+          bw_pair8(av + 8, wv2, *reinterpret_cast<const uint4*>(dr + 16),
+                   *reinterpret_cast<const uint4*>(dr + kBwRowB + 16));
         }
         const int64_t row = ((int64_t)blockIdx.x * kk + tile * kBwTK + j) * kBwD + c * 16;
 #pragma unroll

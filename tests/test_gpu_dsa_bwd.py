@@ -2,13 +2,13 @@
 
 The kernel works from the forward's bf16 output o and fp32 log-sum-exp and accumulates in fp32;
 the oracle rebuilds everything in float64 from the same bf16 inputs.  Tolerances, as a fraction
-of the output's largest magnitude:
-  * dv = sum P do involves neither o nor D_h: only fp32 accumulation and the fp32 weights rebuilt
-    from lse, so 1e-4 (measured: about 1e-6);
+of the output's largest magnitude, 1e-2 for each gradient:
   * dq and dk go through dS = P (dP - D_h) with D_h = sum_d do*o taken from the forward's o, which
     carries bf16 rounding (of P in the PV product and of o itself, each relative 2^-9 = 2e-3); the
-    error of D_h is of that order relative to dP, and passes to dS, dq and dk, so 1e-2 (measured:
-    up to 2.2e-3).
+    error of D_h is of that order relative to dP and passes to dS, dq and dk;
+  * the kernel rounds dS and P to bf16 (relative 2^-9) for the dq, dk and dv sums, as the forward
+    rounds P for its PV product; summed over many terms of either sign these errors stay of that
+    order (measured: dq, dk up to 2.2e-3 before this rounding; dv about 1e-6 without it).
 """
 
 import numpy as np
@@ -21,7 +21,7 @@ from gpu_util import DEV, f64, max_abs_err, require_gpu
 
 pytestmark = pytest.mark.gpu
 
-REL_TOL = {"dq": 1e-2, "dk": 1e-2, "dv": 1e-4}
+REL_TOL = {"dq": 1e-2, "dk": 1e-2, "dv": 1e-2}
 
 
 def _inputs(B, T, S, seed):
