@@ -58,8 +58,13 @@ struct FusedLayout {
   size_t ks, sscore, thresh, cnt, fail, anyf, cand, total;
 };
 
-// The exact fallback's scores ([rows, S] fp32) reuse the candidate area
-// ([rows, S] pairs): they are written after the select step has read it.
+// Candidate rows are pitched at Sp = S rounded up to even: a row whose last
+// chunk is all candidates with an odd length puts its pad entry at index S,
+// which then stays in the row, and every row starts 16-byte aligned (the
+// select step loads entry pairs as 16 bytes).  The exact fallback's scores
+// ([rows, S] fp32) reuse the candidate area ([rows, Sp] pairs): they are
+// written after the select step has read it.
+static int64_t cand_pitch(int64_t S) { return (S + 1) & ~(int64_t)1; }
 static FusedLayout fused_layout(int64_t B, int64_t T, int64_t S) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int64_t Ss = S / kSample, rows = B * T;
@@ -79,7 +84,7 @@ static FusedLayout fused_layout(int64_t B, int64_t T, int64_t S) {
   L.anyf = off;
   off += 256;
   L.cand = off;
-  off += al((size_t)(rows * S) * 8);
+  off += al((size_t)(rows * cand_pitch(S)) * 8);
   L.total = off;
   return L;
 }
@@ -96,8 +101,8 @@ struct FusedPtrs {
   const uint32_t* cnt;  // [rows, nseg]
   uint32_t* fail;
   uint32_t* anyf;
-  const uint2* cand;  // [rows, S]: segment c at c * chunk
-  int64_t Ss, chunk, nseg;
+  const uint2* cand;  // [rows, Sp]: segment c at c * chunk
+  int64_t Ss, chunk, nseg, pitch;
 };
 
 // ks[b, j] = k[b, 16j + 15]: 16 threads per 256-byte row.
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
   // positions to ps[2u], ps[2u + 1].  Nothing loaded is used before the loop
   // ends, so the loads are all in flight together.  Lanes past the end load
   // the last pair again; `valid` excludes them, and the pads.
-  const uint2* cr = f.cand + row * p.S;
+  const uint2* cr = f.cand + row * f.pitch;
   uint32_t kv[kSelPer], ps[kSelPer];
   int seg = 0;  // this lane's segment; entries j of it lie in [seg_lo, seg_hi)
   uint32_t seg_lo = 0u, seg_hi = pre[1];
@@ -346,6 +351,7 @@ hipError_t launch_dsa_indexer_topk(const DsaIndexerTopkParams& p, hipStream_t st
   f.Ss = Ss;
   f.chunk = dsa_indexer_chunk(p.T);
   f.nseg = (p.S + f.chunk - 1) / f.chunk;
+  f.pitch = cand_pitch(p.S);
   float* fb = reinterpret_cast<float*>(ws + L.cand);
   hipError_t e;
 
@@ -384,6 +390,7 @@ hipError_t launch_dsa_indexer_topk(const DsaIndexerTopkParams& p, hipStream_t st
   ep.thresh = f.thresh;
   ep.cnt = const_cast<uint32_t*>(f.cnt);
   ep.cand = const_cast<uint2*>(f.cand);
+  ep.cand_pitch = f.pitch;
   ep.topk = p.topk;
   if ((e = launch_dsa_indexer(ep, stream)) != hipSuccess) return e;
   // 4. Exact selection over the candidates.

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
       x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);
       x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);
       x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);
-      uint2* seg = p.cand + ((int64_t)b * T + iw + mb * 4 + g) * S + s_begin;
+      uint2* seg = p.cand + ((int64_t)b * T + iw + mb * 4 + g) * p.cand_pitch + s_begin;
       uint32_t slot_i = c_run[mb] + x - mine;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
       if (L == 0 && qi < T) {
         const int64_t row = (int64_t)b * T + qi;
         p.cnt[row * n_chunks + kc] = c_run[mb];
-        if (c_run[mb] & 1u) p.cand[row * S + s_begin + c_run[mb]] = make_uint2(0u, 0u);
+        if (c_run[mb] & 1u) p.cand[row * p.cand_pitch + s_begin + c_run[mb]] = make_uint2(0u, 0u);
       }
     }
   }

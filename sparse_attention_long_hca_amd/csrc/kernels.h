@@ -81,14 +81,17 @@ struct DsaIndexerParams {
   // are worked in chunks of dsa_indexer_chunk(T); for every row with more
   // than topk visible positions, the workgroup of chunk c writes (order-
   // preserving key, position) of each score whose key is >= thresh[row] to
-  // cand[row*S + c*chunk ..] (room for the whole chunk), their number to
-  // cnt[row*n_chunks + c] (n_chunks = ceil(S / chunk)), and after an odd
-  // number a pad entry (0, 0) (no score has key 0).  Rows keeping every
-  // visible position write count 0.  Every chunk holding a visible position
-  // of a row writes that row's count.
+  // cand[row*cand_pitch + c*chunk ..] (room for the whole chunk), their
+  // number to cnt[row*n_chunks + c] (n_chunks = ceil(S / chunk)), and after
+  // an odd number a pad entry (0, 0) (no score has key 0).  cand_pitch is S
+  // rounded up to even, so the pad after an all-candidate last chunk of odd
+  // length stays inside the row.  Rows keeping every visible position write
+  // count 0.  Every chunk holding a visible position of a row writes that
+  // row's count.
   const uint32_t* thresh;
   uint32_t* cnt;
   uint2* cand;
+  int64_t cand_pitch;
   int64_t topk;
   // Key mode (keys16 != NULL): instead of scores, keys16[b,i,s] (same layout)
   // receives the top 16 bits of the score's order-preserving key.

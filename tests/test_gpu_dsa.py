@@ -327,6 +327,33 @@ def test_indexer_topk_equals_separate_calls(B, T, S, kk, q_pos, grid, force):
     assert torch.equal(got, want)
 
 
+@pytest.mark.parametrize("B,T,S,kk,q_pos,zero_w", [(2, 64, 1025, 64, [961, 500], True), (2, 64, 1025, 64, [961, 900], False),
+                                                    (2, 64, 301, 64, [237, 100], False), (2, 64, 301, 64, [237, 100], True),
+                                                    (3, 40, 2049, 32, [2009, 1999, 7], True)])
+def test_indexer_topk_odd_width_all_candidate_rows(B, T, S, kk, q_pos, zero_w):
+    """Odd S with rows that see every position: the last chunk of a row can be all candidates with an odd
+    length (its pad entry then sits at index S of the row), followed by the next row's segments.  w = 0 makes
+    every score 0.0, so every visible position is a candidate; S = 301 rows keep every position through a
+    zero threshold (too few samples).  The result must equal the separate calls and, for w = 0, the lowest
+    positions (ties go to the lower position)."""
+    sa = require_gpu()
+    qi, ki, w = _indexer_inputs(B, T, S, 70 + S)
+    if zero_w:
+        w = np.zeros_like(w)
+    tqi, tki, tw = synth.to_torch(qi, "bf16", DEV), synth.to_torch(ki, "bf16", DEV), synth.to_torch(w, "f32", DEV)
+    qp = torch.tensor(q_pos, dtype=torch.int64, device=DEV)
+    want = sa.dsa_topk(sa.dsa_indexer_scores(tqi, tki, tw, q_pos=qp), kk, q_pos=qp)
+    got = sa.dsa_indexer_topk(tqi, tki, tw, kk, q_pos=qp)
+    assert torch.equal(got, want)
+    if zero_w:
+        exp = np.full((B, T, kk), -1)
+        for b in range(B):
+            for i in range(T):
+                n = min(S, q_pos[b] + i + 1)
+                exp[b, i, : min(n, kk)] = np.arange(min(n, kk))
+        assert np.array_equal(got.cpu().numpy(), exp)
+
+
 def test_indexer_topk_32768_top2048():
     """Fused call at the prefill workload's size: identical to the separate calls on every row, and on
     sampled rows equal to the oracle's selection outside the 1e-6 tie band."""

@@ -17,13 +17,18 @@ import oracle_pins
 
 
 def _run_all_pins():
-    failed = []
+    """(pins whose assertions fail, pins that raised anything else).  Only an AssertionError counts
+    as a catch: a mutant that merely crashes a pin (a wrong signature, an empty key set) is not
+    detected by that pin."""
+    failed, crashed = [], []
     for name, fn in sorted(oracle_pins.ALL_PINS.items()):
         try:
             fn()
-        except Exception:  # a wrong result or a crash both count as caught
+        except AssertionError:
             failed.append(name)
-    return failed
+        except Exception as e:  # noqa: BLE001 -- recorded, never counted as a catch
+            crashed.append(f"{name}: {type(e).__name__}")
+    return failed, crashed
 
 
 def _mut_visible_off_by_one(t, blk, window):
@@ -124,7 +129,7 @@ _orig_sparse = odsa.dsa_sparse_attention
 _orig_sparse_bwd = odsa.dsa_sparse_attention_bwd
 
 
-def _mut_scores_no_relu(q_idx, k_idx, w, q_pos=None):
+def _mut_scores_no_relu(q_idx, k_idx, w, q_pos=None, ratio=1):
     q_idx, k_idx, w = (np.asarray(a, dtype=np.float64) for a in (q_idx, k_idx, w))
     B, T, Hi, Di = q_idx.shape
     S = k_idx.shape[1]
@@ -134,24 +139,24 @@ def _mut_scores_no_relu(q_idx, k_idx, w, q_pos=None):
         dots = np.einsum("thd,sd->ths", q_idx[b], k_idx[b])
         score = (w[b][:, :, None] * dots).sum(axis=1)
         for i in range(T):
-            n = min(base + i + 1, S)
+            n = odsa.n_candidates(base + i, ratio, S)
             out[b, i, :n] = score[i, :n]
     return out
 
 
-def _mut_scores_weights_reversed(q_idx, k_idx, w, q_pos=None):
+def _mut_scores_weights_reversed(q_idx, k_idx, w, q_pos=None, ratio=1):
     w = np.asarray(w)[:, :, ::-1]
-    return _orig_scores(q_idx, k_idx, w, q_pos)
+    return _orig_scores(q_idx, k_idx, w, q_pos, ratio)
 
 
-def _mut_topk_ties_high(scores, k, q_pos=None):
+def _mut_topk_ties_high(scores, k, q_pos=None, ratio=1):
     scores = np.asarray(scores, dtype=np.float64)
     B, T, S = scores.shape
     idx = np.full((B, T, k), -1, dtype=np.int64)
     for b in range(B):
         base = 0 if q_pos is None else int(q_pos[b])
         for i in range(T):
-            n = min(base + i + 1, S)
+            n = odsa.n_candidates(base + i, ratio, S)
             cand = scores[b, i, :n] + 0.0
             order = np.lexsort((-np.arange(n), -cand))
             sel = np.sort(order[: min(k, n)])
@@ -159,8 +164,8 @@ def _mut_topk_ties_high(scores, k, q_pos=None):
     return idx
 
 
-def _mut_topk_descending_output(scores, k, q_pos=None):
-    idx = _orig_topk(scores, k, q_pos)
+def _mut_topk_descending_output(scores, k, q_pos=None, ratio=1):
+    idx = _orig_topk(scores, k, q_pos, ratio)
     out = idx.copy()
     for b in range(idx.shape[0]):
         for i in range(idx.shape[1]):
@@ -240,5 +245,5 @@ def test_pins_catch_mutation(mutation, monkeypatch):
     # the package namespace re-exports the public functions: patch it too
     if hasattr(oracle, attr):
         monkeypatch.setattr(oracle, attr, fn)
-    failed = _run_all_pins()
-    assert failed, f"no pin caught mutation {mutation}"
+    failed, crashed = _run_all_pins()
+    assert failed, f"no pin's assertion caught mutation {mutation} (crashed: {crashed})"
