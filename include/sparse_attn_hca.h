@@ -15,8 +15,10 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
- *    library never allocates device memory and keeps no pointer after a call
- *    returns.  Buffers must stay alive until the enqueued work has finished.
+ *    library never allocates device memory (its one static array, the scratch
+ *    of hca_attention_fwd_noalloc, is part of the loaded code object) and
+ *    keeps no pointer after a call returns.  Buffers must stay alive until
+ *    the enqueued work has finished.
  *  - Every call only enqueues work on the given stream (NULL = the default
  *    stream) and never synchronises.  Results are deterministic: the same
  *    inputs give bit-identical outputs on every run.
@@ -150,6 +152,25 @@ typedef struct {
 
 size_t hca_attention_fwd_workspace_size(const hca_attention_args* args);
 int hca_attention_fwd(const hca_attention_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * hca_attention_fwd_noalloc -- hca_attention_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Same arguments, validation, kernels and results as hca_attention_fwd;
+ * args->workspace and args->workspace_bytes are ignored.  DECODE calls keep
+ * their split-K partials in a static device array of the library (8 MiB per
+ * GPU, held until the process ends; every supported decode shape needs at
+ * most about 6.3 MB of it); a call needing more returns SA_ERR_WORKSPACE.
+ * PREFILL needs no scratch.  The call allocates nothing; its first call on a
+ * device looks up the array's address there (hipGetSymbolAddress) and keeps
+ * it.  Every call on one GPU shares that array and every decode call writes
+ * all of the partials it reads, so nothing needs clearing between calls, but
+ * calls that overlap on one GPU (concurrent streams or threads) race on it and
+ * must be serialised by the caller.
+ * ------------------------------------------------------------------------ */
+int hca_attention_fwd_noalloc(const hca_attention_args* args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * FP8 decode cache (an extension: the pages fix no cache format).

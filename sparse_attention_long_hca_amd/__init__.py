@@ -21,6 +21,7 @@ from ._lib import (
     dsa_indexer_topk,
     dsa_indexer_topk_workspace_size,
     hca_attention_fwd,
+    hca_attention_fwd_noalloc,
     hca_attention_workspace_size,
     hca_compress,
     hca_decode_fp8,
@@ -47,6 +48,7 @@ __all__ = [
     "dsa_indexer_topk",
     "dsa_indexer_topk_workspace_size",
     "hca_attention_fwd",
+    "hca_attention_fwd_noalloc",
     "hca_attention_workspace_size",
     "hca_compress",
     "hca_decode_fp8",

@@ -88,6 +88,7 @@ EXPORTS = {
     "hca_compress": (ctypes.c_int, [_c_p, _c_p, ctypes.c_int] + [_c_i64] * 11 + [_c_p]),
     "hca_attention_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HcaAttentionArgs)]),
     "hca_attention_fwd": (ctypes.c_int, [ctypes.POINTER(HcaAttentionArgs), _c_p]),
+    "hca_attention_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(HcaAttentionArgs), _c_p]),
     "hca_quantize_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p]),
     "hca_decode_fp8_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HcaDecodeFp8Args)]),
     "hca_decode_fp8": (ctypes.c_int, [ctypes.POINTER(HcaDecodeFp8Args), _c_p]),
@@ -211,7 +212,8 @@ def _hca_args(mode, q, k, v, k_c, v_c, blk, window, seq_len, n_c_cap, scale, pos
     return a
 
 
-def hca_attention_fwd(mode, q, k, v, k_c, v_c, blk, window, scale=None, pos=None, return_lse=False, workspace=None):
+def hca_attention_fwd(mode, q, k, v, k_c, v_c, blk, window, scale=None, pos=None, return_lse=False, workspace=None,
+                      _noalloc=False):
     """HCA attention.
 
     d is the query/key width (q, k, k_c), dv the value width (v, v_c, o); dv < d
@@ -247,6 +249,9 @@ def hca_attention_fwd(mode, q, k, v, k_c, v_c, blk, window, scale=None, pos=None
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]}")
     o = torch.empty(o_shape, dtype=q.dtype, device=q.device)
     args = _hca_args(mode, q, k, v, k_c, v_c, blk, window, seq_len, n_c, scale, pos, o, lse, None, 0)
+    if _noalloc:
+        _check("hca_attention_fwd_noalloc", lib().hca_attention_fwd_noalloc(ctypes.byref(args), _stream()))
+        return (o, lse) if return_lse else o
     need = lib().hca_attention_fwd_workspace_size(ctypes.byref(args))
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -255,6 +260,13 @@ def hca_attention_fwd(mode, q, k, v, k_c, v_c, blk, window, scale=None, pos=None
         args.workspace_bytes = workspace.numel() * workspace.element_size()
     _check("hca_attention_fwd", lib().hca_attention_fwd(ctypes.byref(args), _stream()))
     return (o, lse) if return_lse else o
+
+
+def hca_attention_fwd_noalloc(mode, q, k, v, k_c, v_c, blk, window, scale=None, pos=None, return_lse=False):
+    """hca_attention_fwd through the allocation-free entry point: the library's static scratch holds the
+    decode split partials (the outputs o and lse are still allocated here, by torch)."""
+    return hca_attention_fwd(mode, q, k, v, k_c, v_c, blk, window, scale=scale, pos=pos, return_lse=return_lse,
+                             _noalloc=True)
 
 
 def hca_attention_workspace_size(mode, q, k_c, blk, window):

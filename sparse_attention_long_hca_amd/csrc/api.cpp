@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "sparse_attn_hca.h"
 #include "kernels.h"
@@ -152,6 +153,74 @@ int hca_attention_fwd(const hca_attention_args* a, hipStream_t stream) {
                         a->pos, a->o, a->lse, part_o, part_lse,
                         a->B, a->H, a->n_c_cap, a->blk, a->window, sl2, ns, (max_keys + ns - 1) / ns};
   return hip_status(sa::launch_hca_decode(p, 1, (int)a->d, (int)dv, stream), "hca_attention_fwd decode launch");
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free HCA attention: the decode split partials go to `scratch`, a
+// file-scope device array (each GPU the library runs on holds its own copy
+// until the process ends) instead of a caller workspace.  Host code never
+// passes the array's name to a kernel: the device address is looked up once
+// per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+}  // extern "C"
+
+static constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on device dev, looked up on the first call for
+// that device with dev current.
+int scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_HIP, "hca_attention_fwd_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || !p)
+      return fail(SA_ERR_HIP, "hca_attention_fwd_noalloc: scratch address on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int hca_attention_fwd_noalloc(const hca_attention_args* a, hipStream_t stream) {
+  const int c = hca_check(a);
+  if (c != SA_OK) return c;
+  hca_attention_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (a->mode == HCA_DECODE) {
+    const size_t need = sa::hca_decode_workspace_bytes(a->B * a->H, hca_dec_nsplit(a), hca_dv(a));
+    if (need > kScratchBytes)
+      return fail(SA_ERR_WORKSPACE, "hca_attention_fwd_noalloc: needs %zu scratch bytes, the static limit is %zu", need,
+                  kScratchBytes);
+    if (need > 0) {
+      int dev = 0;
+      const hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+      if (e != hipSuccess) return hip_status(e, "hca_attention_fwd_noalloc: stream device");
+      void* ptr = nullptr;
+      const int r = scratch_on(dev, &ptr);
+      if (r != SA_OK) return r;
+      b.workspace = ptr;
+      b.workspace_bytes = kScratchBytes;
+    }
+  }
+  return hca_attention_fwd(&b, stream);
 }
 
 // ---------------------------------------------------------------------------
