@@ -1,4 +1,4 @@
-"""Float64 CPU oracle for the HCA + MLA-DSA forward pass.
+"""Float64 CPU oracle for the HCA + MLA-DSA forward pass (and its backward).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link this package: only the tests, the smoke check and the benchmark's CPU
@@ -37,6 +37,9 @@ from .hca import (
     hca_key_set,
     hca_attention_prefill,
     hca_attention_decode,
+    hca_attention_bwd,
+    hca_compress_bwd,
+    hca_layer_bwd,
 )
 from .dsa import (
     dsa_indexer_scores,
@@ -60,6 +63,9 @@ __all__ = [
     "hca_key_set",
     "hca_attention_prefill",
     "hca_attention_decode",
+    "hca_attention_bwd",
+    "hca_compress_bwd",
+    "hca_layer_bwd",
     "dsa_indexer_scores",
     "dsa_topk",
     "dsa_sparse_attention",

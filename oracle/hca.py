@@ -143,3 +143,71 @@ def hca_attention_decode(q, kc, vc, ring_k, ring_v, pos, blk, window, scale=None
         vals = np.concatenate([vc[b][:, cj], ring_v[b][:, slots]], axis=1)
         o[b], lse[b] = _attend(q[b], keys, vals, scale)
     return o, lse
+
+
+def hca_attention_bwd(q, k, v, kc, vc, blk, window, do, scale=None):
+    """Gradients of hca_attention_prefill (every row) for an upstream gradient do of o.
+
+    The pages train the HCA layers (FlashMask-4, [P3] §預訓練資料工程 item 3, ships
+    a backward pass) but print no backward formula; this is the chain rule of
+    the forward's definition.  Per row t, with the row's keys (visible
+    compressed entries, then the window positions) and P the forward's
+    softmax weights over them:
+      dP = do_t . value,   dS = P * (dP - sum P dP)      (softmax derivative)
+      dq_t          = scale * sum dS * key
+      d(key)       += scale * dS * q_t      (into dkc for an entry, dk for a window token)
+      d(value)     += P * do_t              (into dvc, dv likewise)
+    q, k: [B, H, T, d]; v, do: [B, H, T, dv]; kc: [B, H, Nc, d]; vc: [B, H, Nc, dv],
+    treated as independent inputs.  Returns (dq, dk, dv, dkc, dvc) in float64:
+    dk, dv hold only the window path; the path through the compression is
+    hca_compress_bwd(dkc) (hca_layer_bwd adds both).
+    """
+    q, k, v, kc, vc, do = map(_f64, (q, k, v, kc, vc, do))
+    B, H, T, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    dkc, dvc = np.zeros(kc.shape), np.zeros(vc.shape)
+    for b in range(B):
+        for t in range(T):
+            cj, rs = hca_key_set(t, blk, window, n_entries=kc.shape[2])
+            nc = cj.size
+            keys = np.concatenate([kc[b][:, cj], k[b][:, rs]], axis=1)  # [H, n, d]
+            vals = np.concatenate([vc[b][:, cj], v[b][:, rs]], axis=1)  # [H, n, dv]
+            logits = scale * np.einsum("hd,hnd->hn", q[b, :, t], keys)
+            p = np.exp(logits - logits.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = np.einsum("hd,hnd->hn", do[b, :, t], vals)
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[b, :, t] = scale * np.einsum("hn,hnd->hd", ds, keys)
+            dkey = scale * ds[:, :, None] * q[b, :, t][:, None, :]  # [H, n, d]
+            dval = p[:, :, None] * do[b, :, t][:, None, :]          # [H, n, dv]
+            dkc[b][:, cj] += dkey[:, :nc]
+            dvc[b][:, cj] += dval[:, :nc]
+            dk[b][:, rs] += dkey[:, nc:]
+            dv[b][:, rs] += dval[:, nc:]
+    return dq, dk, dv, dkc, dvc
+
+
+def hca_compress_bwd(dxc, blk, T):
+    """Gradient of hca_compress: entry j is the mean of tokens j*blk .. j*blk+blk-1, so each of
+    them receives dxc[j] / blk; trailing tokens of an incomplete block receive nothing.
+
+    dxc: [..., Nc, d] with Nc <= T // blk  ->  [..., T, d]
+    """
+    dxc = _f64(dxc)
+    nc, d = dxc.shape[-2], dxc.shape[-1]
+    out = np.zeros(dxc.shape[:-2] + (T, d))
+    for j in range(nc):
+        out[..., j * blk: (j + 1) * blk, :] = dxc[..., j: j + 1, :] / blk
+    return out
+
+
+def hca_layer_bwd(q, k, v, blk, window, do, scale=None):
+    """Gradients of the whole HCA layer (K and V compressed with hca_compress, then
+    hca_attention_prefill) with respect to the raw q, k, v: the window path plus the
+    compression path.  Returns (dq, dk, dv, dkc, dvc) in float64."""
+    T = np.shape(k)[-2]
+    kc, vc = hca_compress(k, blk), hca_compress(v, blk)
+    dq, dk, dv, dkc, dvc = hca_attention_bwd(q, k, v, kc, vc, blk, window, do, scale)
+    return dq, dk + hca_compress_bwd(dkc, blk, T), dv + hca_compress_bwd(dvc, blk, T), dkc, dvc

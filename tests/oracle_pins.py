@@ -235,6 +235,100 @@ def pin_hca_head_permutation():
     _close(op, o[:, perm], 1e-14, "head permutation")
 
 
+def _sdpa_causal_grads(q, k, v, do):
+    """Dense causal attention's gradients (dq, dk, dv) for upstream do, from torch's CPU float64
+    autograd of its library routine.  q,k,v,do: [B,H,T,d]."""
+    import torch
+    import torch.nn.functional as F
+
+    tq, tk, tv = (torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True) for a in (q, k, v))
+    o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    o.backward(torch.from_numpy(np.ascontiguousarray(do, dtype=np.float64)))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def _central_diff(loss, args, which, h=1e-6):
+    """Central differences of loss(*args) with respect to args[which], entry by entry."""
+    x = args[which]
+    fd = np.zeros_like(x)
+    for j in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[j] += h
+        xm[j] -= h
+        fd[j] = (loss(*[xp if i == which else a for i, a in enumerate(args)]) -
+                 loss(*[xm if i == which else a for i, a in enumerate(args)])) / (2 * h)
+    return fd
+
+
+def pin_hca_bwd_finite_differences():
+    """Every gradient of hca_attention_bwd (q, the window path of k and v, and the compressed
+    entries kc, vc as independent inputs) equals a central difference of the forward oracle's
+    loss sum(do * o); a query/key width above the value width, rows with no visible entry, rows
+    with a gap between entries and window, and an entry past every query's reach included."""
+    rng = _rng(61)
+    B, H, T, d, dv, blk, window = 1, 2, 11, 3, 2, 2, 3
+    q, k = rng.standard_normal((B, H, T, d)), rng.standard_normal((B, H, T, d))
+    v, do = rng.standard_normal((B, H, T, dv)), rng.standard_normal((B, H, T, dv))
+    kc, vc = rng.standard_normal((B, H, T // blk, d)), rng.standard_normal((B, H, T // blk, dv))
+    got = oracle.hca_attention_bwd(q, k, v, kc, vc, blk, window, do)
+
+    def loss(q_, k_, v_, kc_, vc_):
+        return float((oracle.hca_attention_prefill(q_, k_, v_, kc_, vc_, blk, window)[0] * do).sum())
+
+    args = [q, k, v, kc, vc]
+    for i, name in enumerate(("dq", "dk", "dv", "dkc", "dvc")):
+        _close(got[i], _central_diff(loss, args, i), 1e-7, f"{name} vs central differences")
+    # entry 4 (tokens 8, 9) is visible from t = 12 on: no query sees it
+    assert np.all(got[3][:, :, 4] == 0) and np.all(got[4][:, :, 4] == 0), "unreached entry has a gradient"
+
+
+def pin_hca_layer_bwd_finite_differences():
+    """hca_layer_bwd's dk, dv (window path plus the block mean's 1/blk spread; the ragged tail gets
+    the window path only) equal central differences of the whole layer, compression included."""
+    rng = _rng(62)
+    # (13, 3, 4): the last entry is out of every query's reach; (14, 3, 1): it is seen, next to a
+    # two-token tail that must get the window path only.
+    for T, blk, window in ((13, 3, 4), (14, 3, 1)):
+        B, H, d = 1, 2, 3
+        q, k, v, do = (rng.standard_normal((B, H, T, d)) for _ in range(4))
+        dq, dk, dv, _, _ = oracle.hca_layer_bwd(q, k, v, blk, window, do)
+
+        def loss(q_, k_, v_):
+            o = oracle.hca_attention_prefill(q_, k_, v_, oracle.hca_compress(k_, blk), oracle.hca_compress(v_, blk),
+                                             blk, window)[0]
+            return float((o * do).sum())
+
+        for i, (name, g) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
+            _close(g, _central_diff(loss, [q, k, v], i), 1e-7, f"T={T} window={window} layer {name} vs central differences")
+
+
+def pin_hca_layer_bwd_blk1_is_dense_causal():
+    """blk = 1 (any window): the layer is dense causal attention, so its gradients are those of
+    torch's float64 SDPA; window >= T: no entry is visible (dkc = dvc = 0) and the same holds."""
+    rng = _rng(63)
+    B, H, T, d = 2, 2, 17, 5
+    q, k, v, do = (rng.standard_normal((B, H, T, d)) for _ in range(4))
+    want = _sdpa_causal_grads(q, k, v, do)
+    for blk, window in ((1, 1), (1, 4), (1, 30), (4, T), (16, T + 5)):
+        dq, dk, dv, dkc, dvc = oracle.hca_layer_bwd(q, k, v, blk, window, do)
+        for name, g, w in (("dq", dq, want[0]), ("dk", dk, want[1]), ("dv", dv, want[2])):
+            _close(g, w, 1e-12, f"blk={blk} window={window} {name}")
+        if window >= T:
+            assert not dkc.any() and not dvc.any(), "window >= T: no entry gradient"
+
+
+def pin_hca_bwd_sum_identities():
+    """The softmax derivative sums to 0 over a row's keys and the weights sum to 1: summed over
+    keys (window tokens and entries), dk is 0 and dv is the sum of do over the rows."""
+    rng = _rng(64)
+    B, H, T, d, blk, window = 2, 3, 40, 4, 4, 6
+    q, k, v, do = (rng.standard_normal((B, H, T, d)) for _ in range(4))
+    kc, vc = oracle.hca_compress(k, blk), oracle.hca_compress(v, blk)
+    dq, dk, dv, dkc, dvc = oracle.hca_attention_bwd(q, k, v, kc, vc, blk, window, do)
+    _close(dk.sum(axis=2) + dkc.sum(axis=2), np.zeros((B, H, d)), 1e-12, "sum of dk")
+    _close(dv.sum(axis=2) + dvc.sum(axis=2), do.sum(axis=2), 1e-12, "sum of dv")
+
+
 def _sdpa_causal_dv(q, k, v):
     """torch CPU float64 SDPA with a value width different from the query/key width (scale 1/sqrt(qk width))."""
     return _sdpa_causal(q, k, v)

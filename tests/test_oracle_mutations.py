@@ -213,6 +213,66 @@ def _mut_sparse_bwd_dv_from_ds(q, k, v, idx, do, scale=None):
                              lambda s: s, True)
 
 
+_orig_hca_bwd = ohca.hca_attention_bwd
+
+
+def _hca_bwd_variant(q, k, v, kc, vc, blk, window, do, scale, ds_fn, entry_scale, dval_from_ds):
+    q, k, v, kc, vc, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, kc, vc, do))
+    B, H, T, d = q.shape
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    dkc, dvc = np.zeros(kc.shape), np.zeros(vc.shape)
+    for b in range(B):
+        for t in range(T):
+            cj, rs = ohca.hca_key_set(t, blk, window, n_entries=kc.shape[2])
+            nc = cj.size
+            keys = np.concatenate([kc[b][:, cj], k[b][:, rs]], axis=1)
+            vals = np.concatenate([vc[b][:, cj], v[b][:, rs]], axis=1)
+            lg = scale * np.einsum("hd,hnd->hn", q[b, :, t], keys)
+            p = np.exp(lg - lg.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            ds = ds_fn(p, np.einsum("hd,hnd->hn", do[b, :, t], vals))
+            dq[b, :, t] = scale * np.einsum("hn,hnd->hd", ds, keys)
+            dkey = ds[:, :, None] * q[b, :, t][:, None, :]
+            dval = (ds if dval_from_ds else p)[:, :, None] * do[b, :, t][:, None, :]
+            dkc[b][:, cj] += entry_scale(scale) * dkey[:, :nc]
+            dvc[b][:, cj] += dval[:, :nc]
+            dk[b][:, rs] += scale * dkey[:, nc:]
+            dv[b][:, rs] += dval[:, nc:]
+    return dq, dk, dv, dkc, dvc
+
+
+def _ds_ok(p, dp):
+    return p * (dp - (p * dp).sum(axis=1, keepdims=True))
+
+
+def _mut_hca_bwd_no_rowsum(q, k, v, kc, vc, blk, window, do, scale=None):
+    return _hca_bwd_variant(q, k, v, kc, vc, blk, window, do, scale, lambda p, dp: p * dp, lambda s: s, False)
+
+
+def _mut_hca_bwd_entry_unscaled(q, k, v, kc, vc, blk, window, do, scale=None):
+    return _hca_bwd_variant(q, k, v, kc, vc, blk, window, do, scale, _ds_ok, lambda s: 1.0, False)
+
+
+def _mut_hca_bwd_dv_from_ds(q, k, v, kc, vc, blk, window, do, scale=None):
+    return _hca_bwd_variant(q, k, v, kc, vc, blk, window, do, scale, _ds_ok, lambda s: s, True)
+
+
+def _mut_compress_bwd_no_divisor(dxc, blk, T):
+    return _orig_compress_bwd(dxc, blk, T) * blk
+
+
+def _mut_compress_bwd_into_tail(dxc, blk, T):
+    out = _orig_compress_bwd(dxc, blk, T)
+    nc = np.shape(dxc)[-2]
+    if nc * blk < T:
+        out[..., nc * blk:, :] = np.asarray(dxc, dtype=np.float64)[..., -1:, :] / blk
+    return out
+
+
+_orig_compress_bwd = ohca.hca_compress_bwd
+
+
 MUTATIONS = {
     "visible_off_by_one": (ohca, "hca_visible_blocks", _mut_visible_off_by_one),
     "window_one_short": (ohca, "hca_window_range", _mut_window_one_short),
@@ -235,6 +295,11 @@ MUTATIONS = {
     "csa_partial_block_visible": (odsa, "n_candidates", _mut_csa_partial_block_visible),
     "prefill_scale_from_v": (ohca, "hca_attention_prefill", _mut_prefill_scale_from_v),
     "prefill_qk_cut_to_v": (ohca, "hca_attention_prefill", _mut_prefill_qk_cut_to_v),
+    "hca_bwd_no_rowsum": (ohca, "hca_attention_bwd", _mut_hca_bwd_no_rowsum),
+    "hca_bwd_entry_unscaled": (ohca, "hca_attention_bwd", _mut_hca_bwd_entry_unscaled),
+    "hca_bwd_dv_from_ds": (ohca, "hca_attention_bwd", _mut_hca_bwd_dv_from_ds),
+    "compress_bwd_no_divisor": (ohca, "hca_compress_bwd", _mut_compress_bwd_no_divisor),
+    "compress_bwd_into_tail": (ohca, "hca_compress_bwd", _mut_compress_bwd_into_tail),
 }
 
 
