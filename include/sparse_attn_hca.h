@@ -154,6 +154,68 @@ size_t hca_attention_fwd_workspace_size(const hca_attention_args* args);
 int hca_attention_fwd(const hca_attention_args* args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * hca_attention_bwd -- gradients of HCA prefill (an extension: the pages
+ * train the HCA layers -- [P3] §預訓練資料工程 item 3, FlashMask-4 has a
+ * backward pass -- but print no backward formula).
+ *
+ * The chain rule of hca_attention_fwd's definition (PREFILL, every row).  Per
+ * query t with its keys (visible compressed entries, then the window), P the
+ * forward's weights rebuilt from lse and D_t = sum_d d_o[t,d] * o[t,d]:
+ *   dS = P * (d_o[t] . value - D_t)
+ *   dq[t]      = scale * sum dS * key
+ *   d(key)    += scale * dS * q[t]      (entry j -> dk_c[j], window s -> dk[s])
+ *   d(value)  += P * d_o[t]             (dv_c, dv likewise)
+ * When through_compress != 0, k_c and v_c are taken to be hca_compress(k)
+ * and hca_compress(v) with the same blk, and dk, dv also receive the
+ * compression path: every token s of a complete block j < n_c gets
+ * dk_c[j] / blk and dv_c[j] / blk (the gradient of the whole layer with
+ * respect to the raw k, v).  dk_c, dv_c are always the gradients with
+ * respect to the compressed entries as inputs of their own.
+ * q, k, v, o, d_o: [B,H,T,d] bf16 (o and lse as written by hca_attention_fwd
+ * for the same inputs); k_c, v_c: [B,H,n_c,d] bf16; lse: fp32 [B,H,T]
+ * (natural log), required.  Outputs, fp32, every element written: dq, dk,
+ * dv [B,H,T,d]; dk_c, dv_c [B,H,n_c,d] (may be NULL when n_c == 0).
+ * scale <= 0 selects 1/sqrt(d).  Arithmetic: bf16 inputs, fp32 products and
+ * sums; P and dS rounded to bf16 for the dq, dk, dv products (as the forward
+ * rounds P for its P*V product).  Results are deterministic (fixed-order
+ * sums, no atomics).
+ * Supported: SA_BF16, d = 512, n_c <= T / blk, T < 2^24.
+ * Workspace: hca_attention_bwd_workspace_size() bytes, 16-byte aligned (the
+ * P and dS blocks of every (32 queries, 32 keys) tile pair -- about 3.4 GB
+ * at T = 32768, 64 heads -- and partial sums of the compressed entries).
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_ALIGN,
+ * SA_ERR_WORKSPACE, SA_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  sa_dtype dtype;
+  int64_t B, H, d;
+  int64_t blk;       /* compression block                                   */
+  int64_t window;    /* uncompressed recent window                          */
+  int64_t seq_len;   /* T                                                   */
+  int64_t n_c;       /* entries in k_c / v_c                                */
+  int64_t through_compress; /* nonzero: add dk_c/blk, dv_c/blk into dk, dv */
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* k_c;
+  const void* v_c;
+  const void* o;
+  const void* d_o;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dk_c;
+  float* dv_c;
+  void* workspace;
+  size_t workspace_bytes;
+} hca_attention_bwd_args;
+
+size_t hca_attention_bwd_workspace_size(const hca_attention_bwd_args* args);
+int hca_attention_bwd(const hca_attention_bwd_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * hca_attention_fwd_noalloc -- hca_attention_fwd for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).

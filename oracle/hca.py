@@ -145,7 +145,7 @@ def hca_attention_decode(q, kc, vc, ring_k, ring_v, pos, blk, window, scale=None
     return o, lse
 
 
-def hca_attention_bwd(q, k, v, kc, vc, blk, window, do, scale=None):
+def hca_attention_bwd(q, k, v, kc, vc, blk, window, do, scale=None, rows=None):
     """Gradients of hca_attention_prefill (every row) for an upstream gradient do of o.
 
     The pages train the HCA layers (FlashMask-4, [P3] §預訓練資料工程 item 3, ships
@@ -161,6 +161,9 @@ def hca_attention_bwd(q, k, v, kc, vc, blk, window, do, scale=None):
     treated as independent inputs.  Returns (dq, dk, dv, dkc, dvc) in float64:
     dk, dv hold only the window path; the path through the compression is
     hca_compress_bwd(dkc) (hca_layer_bwd adds both).
+    rows: the query rows whose terms are summed (default: every row); dq of
+    the other rows is left 0 and dk, dv, dkc, dvc hold only the listed rows'
+    contributions (complete for a position s when rows covers s .. s+window-1).
     """
     q, k, v, kc, vc, do = map(_f64, (q, k, v, kc, vc, do))
     B, H, T, d = q.shape
@@ -168,8 +171,9 @@ def hca_attention_bwd(q, k, v, kc, vc, blk, window, do, scale=None):
         scale = 1.0 / np.sqrt(d)
     dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
     dkc, dvc = np.zeros(kc.shape), np.zeros(vc.shape)
+    rows = range(T) if rows is None else [int(t) for t in rows]
     for b in range(B):
-        for t in range(T):
+        for t in rows:
             cj, rs = hca_key_set(t, blk, window, n_entries=kc.shape[2])
             nc = cj.size
             keys = np.concatenate([kc[b][:, cj], k[b][:, rs]], axis=1)  # [H, n, d]

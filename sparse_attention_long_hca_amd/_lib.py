@@ -74,6 +74,36 @@ class HcaDecodeFp8Args(ctypes.Structure):
     ]
 
 
+class HcaAttentionBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("B", _c_i64),
+        ("H", _c_i64),
+        ("d", _c_i64),
+        ("blk", _c_i64),
+        ("window", _c_i64),
+        ("seq_len", _c_i64),
+        ("n_c", _c_i64),
+        ("through_compress", _c_i64),
+        ("scale", ctypes.c_float),
+        ("q", _c_p),
+        ("k", _c_p),
+        ("v", _c_p),
+        ("k_c", _c_p),
+        ("v_c", _c_p),
+        ("o", _c_p),
+        ("d_o", _c_p),
+        ("lse", _c_p),
+        ("dq", _c_p),
+        ("dk", _c_p),
+        ("dv", _c_p),
+        ("dk_c", _c_p),
+        ("dv_c", _c_p),
+        ("workspace", _c_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class SparseAttnError(RuntimeError):
     def __init__(self, fn, status, msg):
         super().__init__(f"{fn} failed with status {status}: {msg}")
@@ -89,6 +119,8 @@ EXPORTS = {
     "hca_attention_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HcaAttentionArgs)]),
     "hca_attention_fwd": (ctypes.c_int, [ctypes.POINTER(HcaAttentionArgs), _c_p]),
     "hca_attention_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(HcaAttentionArgs), _c_p]),
+    "hca_attention_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HcaAttentionBwdArgs)]),
+    "hca_attention_bwd": (ctypes.c_int, [ctypes.POINTER(HcaAttentionBwdArgs), _c_p]),
     "hca_quantize_fp8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p]),
     "hca_decode_fp8_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(HcaDecodeFp8Args)]),
     "hca_decode_fp8": (ctypes.c_int, [ctypes.POINTER(HcaDecodeFp8Args), _c_p]),
@@ -275,6 +307,47 @@ def hca_attention_workspace_size(mode, q, k_c, blk, window):
     a.B, a.H, a.d = q.shape[0], q.shape[1], q.shape[-1]
     a.blk, a.window, a.n_c_cap = blk, window, k_c.shape[2]
     return lib().hca_attention_fwd_workspace_size(ctypes.byref(a))
+
+
+def hca_attention_bwd(q, k, v, k_c, v_c, o, lse, do, blk, window, scale=None, through_compress=True, workspace=None):
+    """Gradients of HCA prefill: q, k, v, o, do [B,H,T,d] bf16; k_c, v_c [B,H,Nc,d] bf16; lse [B,H,T] fp32
+    (o and lse from hca_attention_fwd).  Returns (dq, dk, dv, dk_c, dv_c), fp32; with through_compress dk and
+    dv include the block mean's path (dk_c/blk, dv_c/blk on every token of a complete block)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("k_c", k_c), ("v_c", v_c), ("o", o), ("do", do)):
+        _need(t, name, dtype=q.dtype)
+    _need(lse, "lse", dtype=torch.float32)
+    B, H, T, d = q.shape
+    n_c = k_c.shape[2]
+    for name, t, shp in (("k", k, (B, H, T, d)), ("v", v, (B, H, T, d)), ("o", o, (B, H, T, d)), ("do", do, (B, H, T, d)),
+                         ("k_c", k_c, (B, H, n_c, d)), ("v_c", v_c, (B, H, n_c, d)), ("lse", lse, (B, H, T))):
+        _shape(t, name, shp)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty((B, H, T, d), **f32), torch.empty((B, H, T, d), **f32), torch.empty((B, H, T, d), **f32)
+    dkc, dvc = torch.empty((B, H, n_c, d), **f32), torch.empty((B, H, n_c, d), **f32)
+    a = HcaAttentionBwdArgs()
+    a.dtype = _dtype_code(q)
+    a.B, a.H, a.d, a.blk, a.window, a.seq_len, a.n_c = B, H, d, blk, window, T, n_c
+    a.through_compress = 1 if through_compress else 0
+    a.scale = 0.0 if scale is None else float(scale)
+    a.q, a.k, a.v, a.o, a.d_o, a.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr()
+    a.k_c = k_c.data_ptr() if n_c > 0 else None
+    a.v_c = v_c.data_ptr() if n_c > 0 else None
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.dk_c = dkc.data_ptr() if n_c > 0 else None
+    a.dv_c = dvc.data_ptr() if n_c > 0 else None
+    need = lib().hca_attention_bwd_workspace_size(ctypes.byref(a))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("hca_attention_bwd", lib().hca_attention_bwd(ctypes.byref(a), _stream()))
+    return dq, dk, dv, dkc, dvc
+
+
+def hca_attention_bwd_workspace_size(B, H, T, n_c, window):
+    a = HcaAttentionBwdArgs()
+    a.dtype, a.B, a.H, a.d, a.blk, a.window, a.seq_len, a.n_c = SA_BF16, B, H, 512, 1, window, T, n_c
+    return lib().hca_attention_bwd_workspace_size(ctypes.byref(a))
 
 
 def hca_quantize_fp8(x, codes=None, scales=None):

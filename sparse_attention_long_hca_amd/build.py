@@ -33,6 +33,7 @@ SOURCES = [
     "dsa_fused.hip",
     "dsa_sparse_attn.hip",
     "dsa_sparse_bwd.hip",
+    "hca_bwd.hip",
 ]
 
 COMMON_FLAGS = [
@@ -43,13 +44,18 @@ COMMON_FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # Keep MFMA accumulators in ordinary VGPRs: the attention loops rescale
-    # and read them with VALU ops, and splitting them across the two register
-    # files makes the compiler copy every accumulator at each loop iteration.
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]
+
+# Keep MFMA accumulators in ordinary VGPRs: the attention loops rescale and
+# read them with VALU ops, and splitting them across the two register files
+# makes the compiler copy every accumulator at each loop iteration.  The
+# backward passes' gradient accumulators are only ever MFMA operands (no
+# rescaling) and need more than 256 registers per wave with everything else,
+# so those files let the compiler place them in the accumulation registers.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+NO_VGPR_FORM = {"hca_bwd.hip"}
 
 
 def hipcc():
@@ -70,7 +76,8 @@ SOURCE_FLAGS = {
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc()] + lang + COMMON_FLAGS + SOURCE_FLAGS.get(src, []) + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+    form = [] if src in NO_VGPR_FORM else VGPR_FORM
+    cmd = [hipcc()] + lang + COMMON_FLAGS + form + SOURCE_FLAGS.get(src, []) + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; that note is harmless.
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)

@@ -156,6 +156,75 @@ int hca_attention_fwd(const hca_attention_args* a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
+static int hca_bwd_check(const hca_attention_bwd_args* a) {
+  if (!a) return fail(SA_ERR_NULL, "hca_attention_bwd: args is NULL");
+  if (a->B <= 0 || a->H <= 0 || a->d <= 0 || a->blk <= 0 || a->window <= 0 || a->seq_len <= 0 || a->n_c < 0)
+    return fail(SA_ERR_SHAPE, "hca_attention_bwd: B, H, d, blk, window, seq_len must be > 0 and n_c >= 0");
+  if (a->dtype != SA_BF16 || a->d != 512)
+    return fail(SA_ERR_UNSUPPORTED, "hca_attention_bwd: supported is (bf16, d = 512)");
+  if (a->n_c > a->seq_len / a->blk)
+    return fail(SA_ERR_SHAPE, "hca_attention_bwd: n_c (%lld) exceeds seq_len/blk (%lld)", (long long)a->n_c,
+                (long long)(a->seq_len / a->blk));
+  if (a->seq_len >= ((int64_t)1 << 24) || a->window >= ((int64_t)1 << 24))
+    return fail(SA_ERR_SHAPE, "hca_attention_bwd: seq_len and window must be < 2^24");
+  if (!a->q || !a->k || !a->v || !a->o || !a->d_o || !a->lse || !a->dq || !a->dk || !a->dv)
+    return fail(SA_ERR_NULL, "hca_attention_bwd: q, k, v, o, d_o, lse, dq, dk, dv must be non-NULL");
+  if (a->n_c > 0 && (!a->k_c || !a->v_c || !a->dk_c || !a->dv_c))
+    return fail(SA_ERR_NULL, "hca_attention_bwd: k_c, v_c, dk_c, dv_c must be non-NULL when n_c > 0");
+  const int64_t ntq = (a->seq_len + 31) / 32, nslot = (a->n_c + 31) / 32 + (a->window + 30) / 32 + 1;
+  if (ntq * nslot * 4096 >= ((int64_t)1 << 32))
+    return fail(SA_ERR_SHAPE, "hca_attention_bwd: (seq_len/32) * (n_c/32 + window/32) too large (per-head weight blocks "
+                              "must stay below 4 GiB)");
+  const int64_t BH = a->B * a->H;
+  if (BH * ((ntq + 1) / 2) > 0x7fffffffLL || BH * a->n_c > 0x7fffffffLL)
+    return fail(SA_ERR_SHAPE, "hca_attention_bwd: grid too large");
+  const void* ptrs[] = {a->q, a->k, a->v, a->k_c, a->v_c, a->o, a->d_o, a->lse, a->dq, a->dk, a->dv, a->dk_c, a->dv_c};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SA_ERR_ALIGN, "hca_attention_bwd: pointers must be 16-byte aligned");
+  return SA_OK;
+}
+
+size_t hca_attention_bwd_workspace_size(const hca_attention_bwd_args* a) {
+  if (!a || a->B <= 0 || a->H <= 0 || a->seq_len <= 0 || a->n_c < 0 || a->window <= 0) return 0;
+  return sa::hca_bwd_ws_bytes(a->B, a->H, a->seq_len, a->n_c, a->window);
+}
+
+int hca_attention_bwd(const hca_attention_bwd_args* a, hipStream_t stream) {
+  const int c = hca_bwd_check(a);
+  if (c != SA_OK) return c;
+  const size_t need = sa::hca_bwd_ws_bytes(a->B, a->H, a->seq_len, a->n_c, a->window);
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(SA_ERR_WORKSPACE, "hca_attention_bwd: needs %zu workspace bytes, got %zu", need,
+                a->workspace ? a->workspace_bytes : (size_t)0);
+  if (!aligned16(a->workspace)) return fail(SA_ERR_ALIGN, "hca_attention_bwd: workspace must be 16-byte aligned");
+  sa::HcaBwdParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.kc = a->k_c;
+  p.vc = a->v_c;
+  p.o = a->o;
+  p.dout = a->d_o;
+  p.lse = a->lse;
+  p.dq = a->dq;
+  p.dk = a->dk;
+  p.dv = a->dv;
+  p.dkc = a->dk_c;
+  p.dvc = a->dv_c;
+  p.B = a->B;
+  p.H = a->H;
+  p.T = a->seq_len;
+  p.Nc = a->n_c;
+  p.blk = a->blk;
+  p.window = a->window;
+  p.spread = a->through_compress != 0 ? 1 : 0;
+  p.scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->d);
+  p.scale_log2 = p.scale * 1.4426950408889634f;
+  p.blocks = reinterpret_cast<uint16_t*>(a->workspace);
+  return hip_status(sa::launch_hca_bwd(p, stream), "hca_attention_bwd launch");
+}
+
+// ---------------------------------------------------------------------------
 // Allocation-free HCA attention: the decode split partials go to `scratch`, a
 // file-scope device array (each GPU the library runs on holds its own copy
 // until the process ends) instead of a caller workspace.  Host code never

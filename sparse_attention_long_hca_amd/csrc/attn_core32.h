@@ -85,7 +85,17 @@ __device__ __forceinline__ Tile32Addr tile32_addr() {
 // All LDS reads have been issued when this returns; the caller waits for
 // them (lgkmcnt) before letting the K buffer be overwritten.
 template <int D, int kAhead = 4>  // kAhead: LDS operand reads in flight
+__device__ __forceinline__ f32x16_t qk32_ops(const i16x8_t* qb, const char* ks, Tile32Addr ad);
+
+template <int D, int kAhead = 4>  // kAhead: LDS operand reads in flight
 __device__ __forceinline__ f32x16_t attend_qk32(const Attn32Regs<D>& R, const char* ks, Tile32Addr ad) {
+  return qk32_ops<D, kAhead>(R.q, ks, ad);
+}
+
+// The same product with the B operand given as registers: S^T = K . Q^T for
+// qb[n] = this lane's Q^T operand of k-step n (row l%32, dims 16n + 8q .. +7).
+template <int D, int kAhead>
+__device__ __forceinline__ f32x16_t qk32_ops(const i16x8_t* qb, const char* ks, Tile32Addr ad) {
   constexpr int kSteps = D / 16;
   // Opaque copy: the derived offsets are recomputed next to their reads
   // instead of being hoisted out of the key loop into registers.
@@ -102,11 +112,49 @@ __device__ __forceinline__ f32x16_t attend_qk32(const Attn32Regs<D>& R, const ch
 #pragma unroll
   for (int n = 0; n < kSteps; ++n) {
     __builtin_amdgcn_sched_barrier(0);
-    s = mfma_bf16_32x32x16(ka[n % kAhead], R.q[n], s);
+    s = mfma_bf16_32x32x16(ka[n % kAhead], qb[n], s);
     if (n + kAhead < kSteps) ka[n % kAhead] = kread(n + kAhead);
   }
   __builtin_amdgcn_sched_barrier(0);
   return s;
+}
+
+// Probabilities (or any weights) of one tile in the S^T accumulator layout ->
+// the B operand of the P.V product.  The contraction over the tile's 32 keys
+// is two k-steps of 16 whose k-slots map to keys 16*st + 4q + {0..3, 8..11}:
+// exactly the values this lane holds, in order, so no shuffles are needed.
+__device__ __forceinline__ void pack_p32(const f32x16_t& s, i16x8_t pf[2]) {
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const uint4 u = make_uint4(pack_bf16x2(s[8 * st + 0], s[8 * st + 1]), pack_bf16x2(s[8 * st + 2], s[8 * st + 3]),
+                               pack_bf16x2(s[8 * st + 4], s[8 * st + 5]), pack_bf16x2(s[8 * st + 6], s[8 * st + 7]));
+    pf[st] = __builtin_bit_cast(i16x8_t, u);
+  }
+}
+
+// acc[i] += V^T[dims 32*(nb0+i) .. +31] . P^T for i < NB, with V a 32-row
+// tile of 256-dim rows in LDS (read transposed) and pf from pack_p32.
+template <int NB, int kAhead = 2>
+__device__ __forceinline__ void pv32_acc(f32x16_t* acc, const i16x8_t pf[2], const char* vs, Tile32Addr ad, int nb0) {
+  constexpr int kPairs = NB * 2;  // (dims block, key half)
+  asm volatile("" : "+v"(ad.v0), "+v"(ad.v1));
+  auto vread = [&](int i) -> i16x8_t {
+    const int nb = nb0 + (i >> 1), st = i & 1;
+    const uint32_t x = 64u * (uint32_t)(nb & 3), c = 256u * (uint32_t)(nb >> 2) + 8192u * (uint32_t)st;
+    const i16x4_t lo = lds_read_tr16_b64(vs + ((ad.v0 ^ x) + c));
+    const i16x4_t hi = lds_read_tr16_b64(vs + ((ad.v1 ^ x) + c));
+    return i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  i16x8_t va[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) va[i] = vread(i);
+#pragma unroll
+  for (int i = 0; i < kPairs; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    acc[i >> 1] = mfma_bf16_32x32x16(va[i % kAhead], pf[i & 1], acc[i >> 1]);
+    if (i + kAhead < kPairs) va[i % kAhead] = vread(i + kAhead);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Online-softmax update and O^T += V^T . P^T for one tile, given its logits
@@ -114,7 +162,6 @@ __device__ __forceinline__ f32x16_t attend_qk32(const Attn32Regs<D>& R, const ch
 // lane's maximum of them.
 template <int D>
 __device__ __forceinline__ void softmax_pv32(Attn32Regs<D>& R, f32x16_t s, float mx, const char* vs, Tile32Addr ad) {
-  constexpr int kPairs = D / 32 * 2;  // (dims block, key half)
   constexpr int kAhead = 2;  // pairs of LDS reads in flight (register budget)
   asm volatile("" : "+v"(ad.v0), "+v"(ad.v1));
 
@@ -141,33 +188,9 @@ __device__ __forceinline__ void softmax_pv32(Attn32Regs<D>& R, f32x16_t s, float
   rs = sum_xor32(rs);
   R.l += rs;
 
-  // The contraction over the tile's 32 keys is two k-steps of 16 whose
-  // k-slots map to keys 16*st + 4q + {0..3, 8..11}: exactly the values this
-  // lane holds, in order, so P needs no shuffles.
   i16x8_t pf[2];
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const uint4 u = make_uint4(pack_bf16x2(s[8 * st + 0], s[8 * st + 1]), pack_bf16x2(s[8 * st + 2], s[8 * st + 3]),
-                               pack_bf16x2(s[8 * st + 4], s[8 * st + 5]), pack_bf16x2(s[8 * st + 6], s[8 * st + 7]));
-    pf[st] = __builtin_bit_cast(i16x8_t, u);
-  }
-  auto vread = [&](int i) -> i16x8_t {
-    const int nb = i >> 1, st = i & 1;
-    const uint32_t x = 64u * (uint32_t)(nb & 3), c = 256u * (uint32_t)(nb >> 2) + 8192u * (uint32_t)st;
-    const i16x4_t lo = lds_read_tr16_b64(vs + ((ad.v0 ^ x) + c));
-    const i16x4_t hi = lds_read_tr16_b64(vs + ((ad.v1 ^ x) + c));
-    return i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
-  i16x8_t va[kAhead];
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i) va[i] = vread(i);
-#pragma unroll
-  for (int i = 0; i < kPairs; ++i) {
-    __builtin_amdgcn_sched_barrier(0);
-    R.o[i >> 1] = mfma_bf16_32x32x16(va[i % kAhead], pf[i & 1], R.o[i >> 1]);
-    if (i + kAhead < kPairs) va[i % kAhead] = vread(i + kAhead);
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  pack_p32(s, pf);
+  pv32_acc<D / 32, kAhead>(R.o, pf, vs, ad, 0);
 }
 
 // Mask, online-softmax update and O^T += V^T . P^T for the tile whose raw

@@ -59,6 +59,35 @@ size_t hca_decode_workspace_bytes(int64_t BH, int64_t nsplit, int64_t d);
 // d: query/key width (512 or 576), dv: value/output width (512).
 hipError_t launch_hca_decode(const HcaDecodeParams& p, int cache, int d, int dv, hipStream_t stream);
 
+// ---- hca_attention_bwd (prefill) --------------------------------------------
+// Stored weights: for every (32-query tile tq, key tile) pair of the forward's
+// key stream, the 32 x 32 blocks of P and dS (bf16, [key][query] with the
+// query columns permuted as hca_bwd_col()), slot jt < nct for compressed
+// entry tile jt, slot nct + u for raw tile tq - nr + 1 + u.
+struct HcaBwdParams {
+  const void* q;   // [B,H,T,512] bf16
+  const void* k;
+  const void* v;
+  const void* kc;  // [B,H,Nc,512]
+  const void* vc;
+  const void* o;   // forward output
+  const void* dout;
+  const float* lse;  // [B,H,T] natural log
+  float* dq;   // [B,H,T,512]
+  float* dk;
+  float* dv;
+  float* dkc;  // [B,H,Nc,512]
+  float* dvc;
+  int64_t B, H, T, Nc, blk, window;
+  int64_t spread;  // nonzero: dk, dv also get dkc/blk, dvc/blk (the block mean's gradient)
+  float scale, scale_log2;
+  uint16_t* blocks;  // [B*H, ntq, nslot, 2, 32, 32] + one trash block pair
+  float* part;       // [nchunk, B*H, Nc, 2, 512] compressed partial dK, dV
+  int64_t ntq, nct, nr, nslot, nchunk;
+};
+size_t hca_bwd_ws_bytes(int64_t B, int64_t H, int64_t T, int64_t Nc, int64_t window);
+hipError_t launch_hca_bwd(HcaBwdParams p, hipStream_t stream);
+
 // ---- hca_quantize_fp8 -------------------------------------------------------
 struct HcaQuantParams {
   const void* x;  // [rows, d] bf16
