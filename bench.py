@@ -226,6 +226,33 @@ def main():
             del do_, o_f, lse_f, wsb
             torch.cuda.empty_cache()
 
+            # Backward of the HCA layer over the step's inputs (an extra figure, not part
+            # of the step): dq, dk, dv through the window and the block mean, dk_c, dv_c.
+            progress("HCA backward")
+            k_compress()
+            o_h, lse_h = sa.hca_attention_fwd(sa.HCA_PREFILL, q, k, v, kc, vc, BLK, WIN, return_lse=True)
+            do_h = synth.torch_normal((1, H, T_PREFILL, D_HCA), 1.0, torch.bfloat16, 208, dev)
+            wsh = torch.empty(sa.hca_attention_bwd_workspace_size(1, H, T_PREFILL, T_PREFILL // BLK, WIN),
+                              dtype=torch.uint8, device=dev)
+
+            def k_hbwd():
+                return sa.hca_attention_bwd(q, k, v, kc, vc, o_h, lse_h, do_h, BLK, WIN, workspace=wsh)
+
+            k_hbwd()
+            torch.cuda.synchronize()
+            t = timer.time(k_hbwd, max(3, args.steps))
+            ms_h = sum(t) / len(t)
+            flop_h = 10 * D_HCA * hca_pairs_per_head(T_PREFILL) * H
+            bytes_h = T_PREFILL * H * D_HCA * (5 * 2 + 3 * 4) + 2 * (T_PREFILL // BLK) * H * D_HCA * (2 + 4)
+            result["hca_attention_bwd"] = {
+                "ms": ms_h, "alg_flop": flop_h, "TFLOPs": flop_h / (ms_h * 1e-3) / 1e12,
+                "mfma_frac": flop_h / (ms_h * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, "alg_bytes": bytes_h,
+                "hbm_frac": bytes_h / (ms_h * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "workload": "dq, dk, dv (window and block-mean paths), dk_c, dv_c of the HCA layer, T=32768, "
+                            "64 heads x 512, block 128, window 128"}
+            del o_h, lse_h, do_h, wsh
+            torch.cuda.empty_cache()
+
         if "variants" in parts:
             # The CSA variant of the MLA layer over the same token-level inputs (an
             # extra figure, not part of the step): block-4 means of k_I, K and V,
@@ -462,7 +489,7 @@ def main():
         },
         "decode": {k_: v_ for k_, v_ in result.items() if k_.startswith("decode")},
         "variants": {k_: v_ for k_, v_ in result.items() if k_.startswith(("csa", "hca_prefill_qk576"))},
-        "backward": {k_: v_ for k_, v_ in result.items() if k_.startswith("dsa_sparse_attention_bwd")},
+        "backward": {k_: v_ for k_, v_ in result.items() if k_.endswith("_bwd")},
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -425,15 +425,19 @@ int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v,
  *   dv[b,s_j]  += sum_h P_hj d_o[b,i,h]
  * q, o, d_o: [B,T,Hq,D] bf16 (o and lse as written by the forward call with
  * the same q, k, v, idx, scale); k, v: [B,S,D] bf16; idx: [B,T,kk] int32;
- * lse: fp32 [B,T,Hq], required.  Outputs (fp32, written by the call): dq
- * [B,T,Hq,D]; dk, dv [B,S,D] (the call zeroes them, then accumulates; the
- * order of the additions per position is not fixed, so the last bits can
- * differ between runs).  scale <= 0 -> 1/sqrt(D).  Arithmetic: bf16 inputs, fp32 dot
- * products, weights and sums.
- * Supported: SA_BF16, D = 256, Hq = 64, 1 <= kk <= 2048, S <= 2^23.
+ * lse: fp32 [B,T,Hq], required.  Outputs (fp32, every element written): dq
+ * [B,T,Hq,D]; dk, dv [B,S,D].  scale <= 0 -> 1/sqrt(D).
+ * Arithmetic: bf16 inputs, fp32 products and sums; P and dS rounded to bf16
+ * for the dq, dk, dv products (as the forward rounds P for its P*V
+ * product), and each entry's dk and dv rows (sums over the heads) rounded to
+ * bf16 before they are added per position in fp32.  Deterministic: the
+ * entries of a position are added in ascending (token, entry) order, chunk
+ * after chunk, with no floating-point atomics.
+ * Supported: SA_BF16, D = 256, Hq = 64, 1 <= kk <= 2048, S <= 2^23,
+ * B*S < 2^32 - 1.
  * Workspace: dsa_sparse_attention_bwd_workspace_size(B, T, S, kk) bytes,
- * 16-byte aligned (per-entry dk / dv rows of up to 1024 tokens at a time and
- * an inverse index of their entries: about 4.3 GB at kk = 2048).
+ * 16-byte aligned (for chunks of up to 2048 tokens: the P and dS blocks,
+ * each entry's dk / dv rows and an inverse index: about 5.4 GB at kk = 2048).
  * Errors: SA_ERR_NULL (any pointer NULL), SA_ERR_SHAPE, SA_ERR_UNSUPPORTED,
  * SA_ERR_ALIGN (every pointer 16-byte aligned), SA_ERR_WORKSPACE, SA_ERR_HIP.
  * ------------------------------------------------------------------------ */

@@ -55,7 +55,7 @@ COMMON_FLAGS = [
 # rescaling) and need more than 256 registers per wave with everything else,
 # so those files let the compiler place them in the accumulation registers.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-NO_VGPR_FORM = {"hca_bwd.hip"}
+NO_VGPR_FORM = {"hca_bwd.hip", "dsa_sparse_bwd.hip"}
 
 
 def hipcc():

@@ -511,8 +511,24 @@ int dsa_sparse_attention_bwd(const void* q, const void* k, const void* v, const 
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(SA_ERR_ALIGN, "dsa_sparse_attention_bwd: workspace must be 16-byte aligned");
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
-  sa::DsaSparseBwdParams p{q, k, v, idx, o, lse, d_o, dq, dk, dv, B, T, S, kk, sc, resolve_scale_log2(scale, D),
-                           workspace, 0, nullptr, nullptr};
+  sa::DsaSparseBwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.idx = idx;
+  p.o = o;
+  p.lse = lse;
+  p.dout = d_o;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.B = B;
+  p.T = T;
+  p.S = S;
+  p.kk = kk;
+  p.scale = sc;
+  p.scale_log2 = resolve_scale_log2(scale, D);
+  p.ws = workspace;
   return hip_status(sa::launch_dsa_sparse_bwd(p, stream), "dsa_sparse_attention_bwd launch");
 }
 

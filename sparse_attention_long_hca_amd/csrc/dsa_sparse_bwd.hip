@@ -11,21 +11,25 @@
 //   dq_h += scale * dS * k_s,  dk[s] += scale * sum_h dS * q_h,
 //   dv[s] += sum_h P * dO_h.
 //
-// One workgroup (256 threads) per token.  Q and dO of the token sit in LDS
-// (bf16); the index list is walked in tiles of 16 rows, each tile's K and V
-// rows gathered into LDS.  Every thread computes S and dP for one row and four
-// heads (bf16 dot2 into fp32), then P and dS go to LDS; dQ accumulates in
-// registers (one head, 64 dims per thread); the tile's dK and dV rows are
-// summed over the 64 heads in the workgroup and written, one row per (token,
-// entry), to G and H in the workspace.  The dQ, dK and dV sums take two rows
-// or two heads per bf16 dot2, with dS and P rounded to bf16 (as the forward
-// rounds P for its P*V product).  Several tokens select the same
-// position, so dk and dv are then summed per position: tokens are taken in
-// chunks; per chunk a counting sort lists each position's (token, entry)
-// rows, and one workgroup per position adds them into dk and dv (each output
-// row has one owner and chunks run in order, so no floating-point atomics).
-// Vector ALU arithmetic: a first, plain version of the backward.
-#include "common.h"
+// Tokens are taken in chunks; per chunk, every contraction on 32x32x16 bf16
+// MFMA and no floating-point atomics:
+//  1. dsa_bwd_ds_kernel, one workgroup (2 waves x 32 heads) per token, the
+//     forward's tiling: entry tiles of 32 gathered K/V rows, S^T = K Q^T and
+//     dP^T = V dO^T, P and dS, dQ^T += K^T dS^T; each tile's P and dS (bf16)
+//     are stored as 32x32 blocks (entries x heads of one wave).
+//  2. dsa_bwd_contrib_kernel, one workgroup (4 waves x 64 dims) per token:
+//     for each entry tile, dK^T = Q^T dS and dV^T = dO^T P over the 64 heads
+//     (Q and dO staged in LDS and read transposed, the blocks as the B
+//     operand): one dK row and one dV row per entry (bf16).
+//  3. The inverse index of the chunk's entries (integer counts, a scan, a
+//     fill in arbitrary order), then dsa_bwd_reduce_kernel: one workgroup per
+//     key row sorts its segment's entry ids in LDS and adds the entries' rows
+//     in ascending (token, entry) order into dk and dv.  Chunks run in order,
+//     so every output element is summed in a fixed order and the result is
+//     bit-identical from run to run.
+#include <type_traits>
+
+#include "attn_core32.h"
 #include "kernels.h"
 #include "select_util.h"
 
@@ -34,34 +38,18 @@ namespace sa {
 namespace {
 constexpr int kBwH = 64;         // query heads
 constexpr int kBwD = 256;        // head width
-constexpr int kBwTK = 16;        // index-list rows per tile
-constexpr int kBwThreads = 256;
 constexpr int kBwMaxK = 2048;
-constexpr int kBwRowB = kBwD * 2 + 16;  // LDS pitch of a bf16 row: consecutive rows start 4 banks apart
-constexpr int kBwPP = kBwH + 1;         // pitch (floats) of the P and dS tiles
+constexpr int kBlkE = 32 * 32;   // one stored block (P or dS of 32 entries x 32 heads)
+constexpr int kSortCap = 4096;   // segment length sorted in LDS; longer ones take the ordered scan
+constexpr int64_t kChunkTokens = 2048;
 
-__device__ __forceinline__ float bw_dot8(uint4 a, uint4 b, float c) {
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), c, false);
-  return c;
-}
+// Column of head x (0..31) within a stored block: bits 2 and 3 swapped, so
+// that the 8 heads a lane needs for one k-step of the contribution product
+// (16st + 4q + {0..3, 8..11}, the k-slot order of the transposing LDS read)
+// are 16 contiguous bytes of the entry's row.
+__device__ __forceinline__ int bw_col(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-// Two bf16 rows a, b (8 values each) interleaved into pairs (a_e, b_e), then
-// acc[e] += a_e * w.x + b_e * w.y for the bf16 pair w: one dot2 per value.
-__device__ __forceinline__ void bw_pair8(float* acc, uint32_t w2, uint4 a, uint4 b) {
-  const uint32_t xa[4] = {a.x, a.y, a.z, a.w}, xb[4] = {b.x, b.y, b.z, b.w};
-  const bf16x2_t w = __builtin_bit_cast(bf16x2_t, w2);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = (xa[i] & 0xffffu) | (xb[i] << 16);
-    const uint32_t hi = (xa[i] >> 16) | (xb[i] & 0xffff0000u);
-    acc[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo), w, acc[2 * i], false);
-    acc[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi), w, acc[2 * i + 1], false);
-  }
-}
-
+__host__ __device__ __forceinline__ int64_t bw_ntile(int64_t kk) { return (kk + 31) / 32; }
 }  // namespace
 
 __global__ __launch_bounds__(256) void dsa_sparse_bwd_zero_kernel(float4* p, int64_t n4) {
@@ -69,156 +57,271 @@ __global__ __launch_bounds__(256) void dsa_sparse_bwd_zero_kernel(float4* p, int
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-__global__ __launch_bounds__(kBwThreads) void dsa_sparse_bwd_kernel(DsaSparseBwdParams p) {
-  __shared__ __attribute__((aligned(16))) char qs[kBwH * kBwRowB];
-  __shared__ __attribute__((aligned(16))) char dos[kBwH * kBwRowB];
-  __shared__ __attribute__((aligned(16))) char ks[kBwTK * kBwRowB];
-  __shared__ __attribute__((aligned(16))) char vs[kBwTK * kBwRowB];
-  __shared__ float pt[kBwTK * kBwPP];
-  __shared__ float dst[kBwTK * kBwPP];
+// ---------------------------------------------------------------------------
+// Pass 1: dq and the P / dS blocks.  One workgroup per token: wave w holds Q,
+// dO (B operands, 256 dims) and dQ^T of heads 32w .. 32w + 31.  K tiles are
+// double buffered, V single (the next one is sent once dP has read it).  Every
+// tile issues the same loads and stores on every wave, so the waits count
+// exactly (the prologue's stores go to a discard block).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void dsa_bwd_ds_kernel(DsaSparseBwdParams p) {
+  using T = bf16_t;
+  using G = AttnGeom<T, kBwD, 1>;
+  constexpr int kWaves = 2;
+  __shared__ __attribute__((aligned(16))) char kl[2][G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char vl[G::kTileBytes];
   __shared__ int32_t sidx[kBwMaxK];
-  __shared__ float lse2[kBwH];  // log-sum-exp in log2 units
-  __shared__ float dsum[kBwH];  // D_h
 
-  const int t = threadIdx.x;
-  const int64_t tok = p.tok0 + blockIdx.x;  // b*T + i
+  const int64_t tl = blockIdx.x;  // token within the chunk
+  const int64_t tok = p.tok0 + tl;
   const int64_t b = tok / p.T;
+  const int wave = wave_id(), lane = threadIdx.x & 63, qh = lane >> 5;
+  const int h = wave * 32 + (lane & 31);
   const int kk = (int)p.kk;
-  const bf16_t* q = reinterpret_cast<const bf16_t*>(p.q) + tok * kBwH * kBwD;
-  const bf16_t* dO = reinterpret_cast<const bf16_t*>(p.dout) + tok * kBwH * kBwD;
-  const bf16_t* o = reinterpret_cast<const bf16_t*>(p.o) + tok * kBwH * kBwD;
-  const bf16_t* kb = reinterpret_cast<const bf16_t*>(p.k) + b * p.S * kBwD;
-  const bf16_t* vb = reinterpret_cast<const bf16_t*>(p.v) + b * p.S * kBwD;
+  const int ntile = (int)bw_ntile(p.kk);
+  const int64_t S = p.S;
+  const T* kb = reinterpret_cast<const T*>(p.k) + b * S * kBwD;
+  const T* vb = reinterpret_cast<const T*>(p.v) + b * S * kBwD;
 
-  // Q and dO rows -> LDS (32 chunks of 16 bytes per row); the index list with
-  // skipped entries and the tail of the last tile set to -1.
-  for (int e = t; e < kBwH * 32; e += kBwThreads) {
-    const int r = e >> 5, c = e & 31;
-    *reinterpret_cast<uint4*>(qs + r * kBwRowB + c * 16) = reinterpret_cast<const uint4*>(q)[e];
-    *reinterpret_cast<uint4*>(dos + r * kBwRowB + c * 16) = reinterpret_cast<const uint4*>(dO)[e];
-  }
-  const int kk_pad = (kk + kBwTK - 1) / kBwTK * kBwTK;
-  for (int n = t; n < kk_pad; n += kBwThreads) {
+  for (int n = threadIdx.x; n < 32 * ntile; n += 128) {
     const int32_t s = n < kk ? p.idx[tok * kk + n] : -1;
-    sidx[n] = (s >= 0 && s < p.S) ? s : -1;
+    sidx[n] = (s >= 0 && s < S) ? s : -1;
   }
+  // Q, dO of head h as B operands (k-step n: dims 16n + 8q .. +7), D_h.
+  i16x8_t qb[16], db[16];
+  float dpart = 0.f;
   {
-    // D_h from the forward's output (four threads per head, 64 dims each).
-    const int h = t >> 2, c = t & 3;
-    float acc = 0.f;
+    const int64_t row = (tok * kBwH + h) * kBwD + 8 * qh;
+    const T* qr = reinterpret_cast<const T*>(p.q) + row;
+    const T* dr = reinterpret_cast<const T*>(p.dout) + row;
+    const T* orr = reinterpret_cast<const T*>(p.o) + row;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      acc = bw_dot8(reinterpret_cast<const uint4*>(o + h * kBwD + c * 64)[u],
-                    reinterpret_cast<const uint4*>(dO + h * kBwD + c * 64)[u], acc);
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    if (c == 0) {
-      dsum[h] = acc;
-      lse2[h] = p.lse[tok * kBwH + h] * kLog2e;
+    for (int n = 0; n < 16; ++n) {
+      qb[n] = __builtin_bit_cast(i16x8_t, *reinterpret_cast<const uint4*>(qr + 16 * n));
+      const uint4 du = *reinterpret_cast<const uint4*>(dr + 16 * n);
+      db[n] = __builtin_bit_cast(i16x8_t, du);
+      const uint4 ou = *reinterpret_cast<const uint4*>(orr + 16 * n);
+      const uint32_t a[4] = {du.x, du.y, du.z, du.w}, c[4] = {ou.x, ou.y, ou.z, ou.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[e]), __builtin_bit_cast(bf16x2_t, c[e]),
+                                                dpart, false);
     }
   }
-  __syncthreads();
+  const float Dh = sum_xor32(dpart);
+  const float lse2 = p.lse[tok * kBwH + h] * kLog2e;
+  const Tile32Addr ad = tile32_addr<kBwD>();
 
-  const int hq = t >> 2, cq = t & 3;  // dQ: head, 64-dim chunk
-  float dq[64];
+  auto rows_of = [&](int t) {
+    const int32_t* trow = sidx + 32 * t;
+    return [=](int r) -> int { return trow[r]; };
+  };
+  auto issue_k = [&](int t) { stage_rows_async<T, kBwD, kWaves, 1>(kl[t & 1], kb, rows_of(t)); };
+  auto issue_v = [&](int t) { stage_rows_async<T, kBwD, kWaves, 1>(vl, vb, rows_of(t)); };
+  constexpr int kLd = StageGeom<T, kBwD, kWaves>::kPerWave;  // loads per wave of a K (or V) tile
+  constexpr int kSt = 32;                                    // block stores per wave and tile
+
+  uint16_t* const blk_tok = p.blocks + tl * ntile * 4 * kBlkE;
+  uint16_t* const discard = p.blocks + p.ntok * ntile * 4 * kBlkE;
+  const int col = bw_col(lane & 31);
+  auto store_block = [&](uint16_t* base, const f32x16_t& x) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 64; ++i) dq[i] = 0.f;
-  const int n_tiles = kk_pad / kBwTK;
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int32_t* trow = sidx + tile * kBwTK;
-    // K and V rows of the tile -> LDS (zeros for skipped entries).
-    for (int e = t; e < kBwTK * 32; e += kBwThreads) {
-      const int r = e >> 5, c = e & 31;
-      const int32_t s = trow[r];
-      uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
-      if (s >= 0) {
-        kv = reinterpret_cast<const uint4*>(kb + (int64_t)s * kBwD)[c];
-        vv = reinterpret_cast<const uint4*>(vb + (int64_t)s * kBwD)[c];
-      }
-      *reinterpret_cast<uint4*>(ks + r * kBwRowB + c * 16) = kv;
-      *reinterpret_cast<uint4*>(vs + r * kBwRowB + c * 16) = vv;
+    for (int j = 0; j < 16; ++j) {
+      const int e = 8 * (j >> 2) + 4 * qh + (j & 3);
+      base[e * 32 + col] = (uint16_t)(pack_bf16x2(x[j], 0.f) & 0xffffu);
     }
-    __syncthreads();
-    {
-      // S and dP of row j for heads 4g .. 4g+3, then P and dS.
-      const int j = t & 15, g = t >> 4;
-      float sa_[4] = {0.f, 0.f, 0.f, 0.f}, pa[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int c = 0; c < 32; ++c) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(ks + j * kBwRowB + c * 16);
-        const uint4 vv = *reinterpret_cast<const uint4*>(vs + j * kBwRowB + c * 16);
+  };
+  f32x16_t dqa[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int h = 4 * g + i;
-          sa_[i] = bw_dot8(*reinterpret_cast<const uint4*>(qs + h * kBwRowB + c * 16), kv, sa_[i]);
-          pa[i] = bw_dot8(*reinterpret_cast<const uint4*>(dos + h * kBwRowB + c * 16), vv, pa[i]);
-        }
-      }
-      const bool live = trow[j] >= 0;
+  for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 4 * g + i;
-        const float pr = live ? fast_exp2(sa_[i] * p.scale_log2 - lse2[h]) : 0.f;
-        pt[j * kBwPP + h] = pr;
-        dst[j * kBwPP + h] = pr * (pa[i] - dsum[h]);
-      }
+    for (int j = 0; j < 16; ++j) dqa[nb][j] = 0.f;
+  f32x16_t zero16;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) zero16[j] = 0.f;
+
+  wait_vmcnt<0>();  // Q, dO, O, lse and the index list are in
+  __syncthreads();  // sidx
+  issue_k(0);
+  issue_v(0);
+  // Two blocks' worth of stores to distinct addresses (identical stores to one
+  // address could be merged, and the waits would then miscount).
+  store_block(discard, zero16);
+  store_block(discard + 2 * kBlkE, zero16);
+
+  auto step = [&](int t, auto more_tag) __attribute__((always_inline)) {
+    constexpr bool more = decltype(more_tag)::value;
+    const char* kt = kl[t & 1];
+    if constexpr (more) {
+      issue_k(t + 1);
+      wait_vmcnt<kLd + kSt + kLd>();  // K(t) landed: V(t), stores(t - 1), K(t + 1) may be in flight
+    } else {
+      wait_vmcnt<kLd + kSt>();
     }
-    __syncthreads();
-    // dQ (head hq, dims 64cq .. 64cq+63) += dS * K, two rows per dot2 (dS
-    // rounded to bf16, as P is for the forward's P*V product).
-    for (int j = 0; j < kBwTK; j += 2) {
-      const uint32_t w2 = pack_bf16x2(dst[j * kBwPP + hq], dst[(j + 1) * kBwPP + hq]);
-      const char* kr = ks + j * kBwRowB + cq * 128;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        bw_pair8(dq + 8 * u, w2, *reinterpret_cast<const uint4*>(kr + u * 16),
-                 *reinterpret_cast<const uint4*>(kr + kBwRowB + u * 16));
+    lds_barrier();
+    f32x16_t s = qk32_ops<kBwD, 4>(qb, kt, ad);
+    if constexpr (more) {
+      wait_vmcnt<kSt + kLd>();  // V(t) landed
+    } else {
+      wait_vmcnt<kSt>();
     }
-    {
-      // dK and dV of row j, dims 16c .. 16c+15, summed over the 64 heads.
-      const int j = t >> 4, c = t & 15;
-      const int32_t s = trow[j];
-      if (s >= 0) {
-        float ak[16], av[16];
+    lds_barrier();
+    f32x16_t dp = qk32_ops<kBwD, 4>(db, vl, ad);
+    const uint32_t mask = (uint32_t)(__ballot(sidx[32 * t + (lane & 31)] >= 0) & 0xffffffffull);
+    wait_lgkmcnt0();
+    lds_barrier();  // both waves are done reading V(t)
+    if constexpr (more) issue_v(t + 1);
+    const uint32_t kbits = mask >> (4 * qh);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ak[i] = av[i] = 0.f;
-        // Two heads per dot2 (dS and P rounded to bf16).
-        for (int h = 0; h < kBwH; h += 2) {
-          const uint32_t wk2 = pack_bf16x2(dst[j * kBwPP + h], dst[j * kBwPP + h + 1]);
-          const uint32_t wv2 = pack_bf16x2(pt[j * kBwPP + h], pt[j * kBwPP + h + 1]);
-          const char* qr = qs + h * kBwRowB + c * 32;
-          const char* dr = dos + h * kBwRowB + c * 32;
-          bw_pair8(ak, wk2, *reinterpret_cast<const uint4*>(qr), *reinterpret_cast<const uint4*>(qr + kBwRowB));
-          bw_pair8(ak + 8, wk2, *reinterpret_cast<const uint4*>(qr + 16),
-                   *reinterpret_cast<const uint4*>(qr + kBwRowB + 16));
-          bw_pair8(av, wv2, *reinterpret_cast<const uint4*>(dr), *reinterpret_cast<const uint4*>(dr + kBwRowB));
-          bw_pair8(av + 8, wv2, *reinterpret_cast<const uint4*>(dr + 16),
-                   *reinterpret_cast<const uint4*>(dr + kBwRowB + 16));
-        }
-        const int64_t row = ((int64_t)blockIdx.x * kk + tile * kBwTK + j) * kBwD + c * 16;
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-          *reinterpret_cast<float4*>(p.g + row + i) =
-              make_float4(ak[i] * p.scale, ak[i + 1] * p.scale, ak[i + 2] * p.scale, ak[i + 3] * p.scale);
-          *reinterpret_cast<float4*>(p.hh + row + i) = make_float4(av[i], av[i + 1], av[i + 2], av[i + 3]);
-        }
-      }
+    for (int j = 0; j < 16; ++j) {
+      const float pr = (kbits & (1u << (8 * (j >> 2) + (j & 3)))) ? fast_exp2(s[j] * p.scale_log2 - lse2) : 0.f;
+      s[j] = pr;
+      dp[j] = pr * (dp[j] - Dh);
     }
-    __syncthreads();  // the next tile overwrites K, V, P and dS
-  }
-  float* dqr = p.dq + (tok * kBwH + hq) * kBwD + cq * 64;
+    i16x8_t pf[2];
+    pack_p32(dp, pf);
+    pv32_acc<8, 2>(dqa, pf, kt, ad, 0);
+    wait_lgkmcnt0();
+    uint16_t* bt = blk_tok + (int64_t)t * 4 * kBlkE + wave * kBlkE;
+    store_block(bt, s);              // P:  tensor 0
+    store_block(bt + 2 * kBlkE, dp); // dS: tensor 1
+    lds_barrier();  // both waves are done with K(t)
+  };
+  for (int t = 0; t + 1 < ntile; ++t) step(t, std::true_type{});
+  step(ntile - 1, std::false_type{});
+
+  float* dqr = p.dq + (tok * kBwH + h) * kBwD;
 #pragma unroll
-  for (int u = 0; u < 16; ++u)
-    reinterpret_cast<float4*>(dqr)[u] =
-        make_float4(dq[4 * u] * p.scale, dq[4 * u + 1] * p.scale, dq[4 * u + 2] * p.scale, dq[4 * u + 3] * p.scale);
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<float4*>(dqr + 32 * nb + 8 * m + 4 * qh) =
+          make_float4(dqa[nb][4 * m] * p.scale, dqa[nb][4 * m + 1] * p.scale, dqa[nb][4 * m + 2] * p.scale,
+                      dqa[nb][4 * m + 3] * p.scale);
 }
 
+// ---------------------------------------------------------------------------
+// Pass 2: each entry's dK and dV rows.  One workgroup of 4 waves per token:
+// Q and dO (64 heads x 256 dims, as two 32-head tiles each) are staged once;
+// the blocks of each entry tile are staged double buffered; wave w computes
+// dims [64w, 64w + 64) of dK^T = Q^T dS and dV^T = dO^T P (contraction over
+// the 64 heads: two tiles x two k-steps) and stores them as bf16 rows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dsa_bwd_contrib_kernel(DsaSparseBwdParams p) {
+  using T = bf16_t;
+  using G = AttnGeom<T, kBwD, 1>;
+  constexpr int kWaves = 4;
+  constexpr int kTile = G::kTileBytes;  // 16 KB
+  __shared__ __attribute__((aligned(16))) char qs[2][kTile];
+  __shared__ __attribute__((aligned(16))) char dos[2][kTile];
+  __shared__ __attribute__((aligned(16))) char bl[2][4 * 2 * kBlkE];  // 4 blocks of 2 KB per stage
+
+  const int64_t tl = blockIdx.x;
+  const int64_t tok = p.tok0 + tl;
+  const int wave = wave_id(), lane = threadIdx.x & 63, qh = lane >> 5;
+  const int kk = (int)p.kk;
+  const int ntile = (int)bw_ntile(p.kk);
+  const T* qt = reinterpret_cast<const T*>(p.q) + tok * kBwH * kBwD;
+  const T* dt = reinterpret_cast<const T*>(p.dout) + tok * kBwH * kBwD;
+  auto ident = [](int r) -> int { return r; };
+#pragma unroll
+  for (int hw = 0; hw < 2; ++hw) {
+    stage_rows_async<T, kBwD, kWaves, 1>(qs[hw], qt + hw * 32 * kBwD, ident);
+    stage_rows_async<T, kBwD, kWaves, 1>(dos[hw], dt + hw * 32 * kBwD, ident);
+  }
+  // Blocks of tile t: four 2 KB blocks (tensor e, head half hw) at (2e + hw) * 2 KB;
+  // 16-byte chunk c of block row r at chunk c ^ ((r >> 2) & 3).  Wave w loads
+  // the 1 KB halves 2w and 2w + 1.
+  const buffer_rsrc_t brs = make_buffer_rsrc(p.blocks + tl * ntile * 4 * kBlkE);
+  auto stage_blocks = [&](int st, int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = 2 * wave + i, blk4 = u >> 1, hb = u & 1;
+      const int r = 16 * hb + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
+      const uint32_t off = (uint32_t)(((int64_t)t * 4 + blk4) * kBlkE * 2) + (uint32_t)(r * 64 + c * 16);
+      buffer_load_lds_16(brs, off, bl[st] + blk4 * 2 * kBlkE + hb * 1024);
+    }
+  };
+  const Tile32Addr ad = tile32_addr<kBwD>();
+  const int br = lane & 31;
+  uint32_t boff[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) boff[st] = (uint32_t)(br * 64 + 16 * ((2 * st + qh) ^ ((br >> 2) & 3)));
+  const int nb0 = 2 * wave;
+  uint16_t* const discard_k = p.gk + p.ntok * p.kk * kBwD;
+  uint16_t* const discard_v = p.gv + p.ntok * p.kk * kBwD;
+  constexpr int kLd = 2, kSt = 16;
+
+  stage_blocks(0, 0);
+  // Discard stores so that every tile sees the same outstanding operations,
+  // each to its own address (identical stores to one address could be merged,
+  // and the waits would then miscount).
+#pragma unroll
+  for (int i = 0; i < kSt / 2; ++i) {
+    *reinterpret_cast<uint2*>(discard_k + i * kBwD + 4 * lane) = make_uint2(0u, 0u);
+    *reinterpret_cast<uint2*>(discard_v + i * kBwD + 4 * lane) = make_uint2(0u, 0u);
+  }
+
+  for (int t = 0; t < ntile; ++t) {
+    if (t + 1 < ntile) {
+      stage_blocks((t + 1) & 1, t + 1);
+      wait_vmcnt<kSt + kLd>();
+    } else {
+      wait_vmcnt<kSt>();
+    }
+    lds_barrier();
+    f32x16_t ak[2], av[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ak[nb][j] = av[nb][j] = 0.f;
+    const char* b0 = bl[t & 1];
+#pragma unroll
+    for (int hw = 0; hw < 2; ++hw) {
+      i16x8_t bp[2], bd[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        bp[st] = __builtin_bit_cast(i16x8_t, lds_read_b128(b0 + hw * 2 * kBlkE, boff[st]));
+        bd[st] = __builtin_bit_cast(i16x8_t, lds_read_b128(b0 + (2 + hw) * 2 * kBlkE, boff[st]));
+      }
+      pv32_acc<2, 2>(ak, bd, qs[hw], ad, nb0);
+      pv32_acc<2, 2>(av, bp, dos[hw], ad, nb0);
+    }
+    wait_lgkmcnt0();
+    // Lane: entry 32t + l%32, dims 64w + 32nb + 8m + 4q .. +3.
+    const int j = 32 * t + (lane & 31);
+    const int64_t e = tl * kk + j;
+    uint16_t* rk = j < kk ? p.gk + e * kBwD : discard_k;
+    uint16_t* rv = j < kk ? p.gv + e * kBwD : discard_v;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int d = 32 * (nb0 + nb) + 8 * m + 4 * qh;
+        *reinterpret_cast<uint2*>(rk + d) =
+            make_uint2(pack_bf16x2(ak[nb][4 * m] * p.scale, ak[nb][4 * m + 1] * p.scale),
+                       pack_bf16x2(ak[nb][4 * m + 2] * p.scale, ak[nb][4 * m + 3] * p.scale));
+        *reinterpret_cast<uint2*>(rv + d) = make_uint2(pack_bf16x2(av[nb][4 * m], av[nb][4 * m + 1]),
+                                                       pack_bf16x2(av[nb][4 * m + 2], av[nb][4 * m + 3]));
+      }
+    lds_barrier();  // the stage's buffer is free for the load two tiles on
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Inverse index of one chunk of tokens: entry e = (token - tok0) * kk + j.
-__global__ __launch_bounds__(256) void dsa_sparse_bwd_count_kernel(DsaSparseBwdParams p, int64_t ntok, uint32_t* cnt) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= ntok * p.kk) return;
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t bw_key(const DsaSparseBwdParams& p, int64_t e) {
   const int64_t tok = p.tok0 + e / p.kk;
   const int32_t s = p.idx[tok * p.kk + e % p.kk];
-  if (s >= 0 && s < p.S) atomicAdd(&cnt[(tok / p.T) * p.S + s], 1u);
+  return (s >= 0 && s < p.S) ? (tok / p.T) * p.S + s : -1;
+}
+
+__global__ __launch_bounds__(256) void dsa_sparse_bwd_count_kernel(DsaSparseBwdParams p, uint32_t* cnt) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= p.ntok * p.kk) return;
+  const int64_t key = bw_key(p, e);
+  if (key >= 0) atomicAdd(&cnt[key], 1u);
 }
 
 // Exclusive offsets of the counts (one workgroup): off[0..n], cursor = off.
@@ -239,82 +342,163 @@ __global__ __launch_bounds__(1024) void dsa_sparse_bwd_scan_kernel(const uint32_
   if (threadIdx.x == 0) off[n] = tot;
 }
 
-__global__ __launch_bounds__(256) void dsa_sparse_bwd_fill_kernel(DsaSparseBwdParams p, int64_t ntok, uint32_t* cursor,
-                                                                  uint32_t* list) {
+// Segment slots in arbitrary order: the reduce step orders each segment.
+__global__ __launch_bounds__(256) void dsa_sparse_bwd_fill_kernel(DsaSparseBwdParams p, uint32_t* cursor) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= ntok * p.kk) return;
-  const int64_t tok = p.tok0 + e / p.kk;
-  const int32_t s = p.idx[tok * p.kk + e % p.kk];
-  if (s >= 0 && s < p.S) list[atomicAdd(&cursor[(tok / p.T) * p.S + s], 1u)] = (uint32_t)e;
+  if (e >= p.ntok * p.kk) return;
+  const int64_t key = bw_key(p, e);
+  if (key >= 0) p.list[atomicAdd(&cursor[key], 1u)] = (uint32_t)e;
 }
 
-// One workgroup per key row, one thread per dim: dk[r] += sum of the chunk's
-// G rows listed for r (dv likewise from H).
-__global__ __launch_bounds__(kBwD) void dsa_sparse_bwd_reduce_kernel(DsaSparseBwdParams p, const uint32_t* off,
-                                                                     const uint32_t* list) {
-  const int64_t r = blockIdx.x;  // b*S + s
-  const uint32_t e0 = off[r], e1 = off[r + 1];
-  if (e0 == e1) return;
-  const int d = threadIdx.x;
-  float ak = 0.f, av = 0.f;
-  uint32_t e = e0;
-  for (; e + 4 <= e1; e += 4) {
-    float gk[4], gv[4];
+// ---------------------------------------------------------------------------
+// dk[key] += the chunk's dK rows of the key's entries, in ascending entry
+// order (dv likewise).  One workgroup per key row (grid-stride), one thread
+// per dim.  Segments of up to kSortCap entries are sorted in LDS (bitonic);
+// a longer segment (an index list with many repeated positions) is ordered
+// by scanning the chunk's entries in order instead.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dsa_sparse_bwd_reduce_kernel(DsaSparseBwdParams p, int64_t nkeys) {
+  __shared__ uint32_t ids[kSortCap];
+  __shared__ uint32_t wtot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d = tid;
+  auto row_sum = [&](int m, float& ak, float& av) __attribute__((always_inline)) {
+    int r = 0;
+    for (; r + 8 <= m; r += 8) {
+      float xk[8], xv[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t row = (int64_t)list[e + u] * kBwD + d;
-      gk[u] = p.g[row];
-      gv[u] = p.hh[row];
-    }
+      for (int u = 0; u < 8; ++u) {
+        const int64_t row = (int64_t)ids[r + u] * kBwD + d;
+        xk[u] = bf16_to_f32(p.gk[row]);
+        xv[u] = bf16_to_f32(p.gv[row]);
+      }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ak += gk[u];
-      av += gv[u];
+      for (int u = 0; u < 8; ++u) {
+        ak += xk[u];
+        av += xv[u];
+      }
     }
+    for (; r < m; ++r) {
+      const int64_t row = (int64_t)ids[r] * kBwD + d;
+      ak += bf16_to_f32(p.gk[row]);
+      av += bf16_to_f32(p.gv[row]);
+    }
+  };
+  for (int64_t key = blockIdx.x; key < nkeys; key += gridDim.x) {
+    const uint32_t e0 = p.off[key], n = p.off[key + 1] - e0;
+    if (n == 0) continue;
+    float ak = 0.f, av = 0.f;
+    if (n <= (uint32_t)kSortCap) {
+      uint32_t np2 = 1;
+      while (np2 < n) np2 <<= 1;
+      for (uint32_t i = tid; i < np2; i += 256) ids[i] = i < n ? p.list[e0 + i] : 0xffffffffu;
+      __syncthreads();
+      for (uint32_t k2 = 2; k2 <= np2; k2 <<= 1) {
+        for (uint32_t j = k2 >> 1; j > 0; j >>= 1) {
+          for (uint32_t i = tid; i < np2; i += 256) {
+            const uint32_t ixj = i ^ j;
+            if (ixj > i) {
+              const uint32_t a = ids[i], c = ids[ixj];
+              if ((a > c) == ((i & k2) == 0)) {
+                ids[i] = c;
+                ids[ixj] = a;
+              }
+            }
+          }
+          __syncthreads();
+        }
+      }
+      row_sum((int)n, ak, av);
+    } else {
+      // Ordered scan: the chunk's entries 256 at a time, matches appended in order.
+      const int64_t ne = p.ntok * p.kk;
+      for (int64_t base = 0; base < ne; base += 256) {
+        const int64_t e = base + tid;
+        const bool match = e < ne && bw_key(p, e) == key;
+        const uint64_t bal = __ballot(match);
+        const uint32_t rank = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wtot[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        uint32_t before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          before += w < wave ? wtot[w] : 0u;
+          total += wtot[w];
+        }
+        if (match) ids[before + rank] = (uint32_t)e;
+        __syncthreads();
+        row_sum((int)total, ak, av);
+        __syncthreads();
+      }
+    }
+    p.dk[key * kBwD + d] += ak;
+    p.dv[key * kBwD + d] += av;
+    __syncthreads();  // ids is reused by the next key
   }
-  for (; e < e1; ++e) {
-    const int64_t row = (int64_t)list[e] * kBwD + d;
-    ak += p.g[row];
-    av += p.hh[row];
-  }
-  p.dk[r * kBwD + d] += ak;
-  p.dv[r * kBwD + d] += av;
 }
 
-int64_t dsa_sparse_bwd_chunk(int64_t BT) { return BT < 1024 ? BT : 1024; }
+int64_t dsa_sparse_bwd_chunk(int64_t BT) { return BT < kChunkTokens ? BT : kChunkTokens; }
 
-size_t dsa_sparse_bwd_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t kk) {
+namespace {
+struct BwdLayout {
+  size_t blocks, gk, gv, list, cnt, off, cursor, total;
+};
+BwdLayout bwd_layout(int64_t B, int64_t T, int64_t S, int64_t kk) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int64_t tc = dsa_sparse_bwd_chunk(B * T), keys = B * S;
-  auto al = [](int64_t x) { return (size_t)((x + 63) & ~(int64_t)63); };  // 256-byte multiples of 4-byte words
-  return 4 * (2 * al(tc * kk * kBwD) + al(tc * kk) + 3 * al(keys + 1));
+  BwdLayout L;
+  size_t off = 0;
+  L.blocks = off;
+  off += al((size_t)(tc * bw_ntile(kk) + 1) * 4 * kBlkE * 2);  // + a discard tile
+  L.gk = off;
+  off += al((size_t)(tc * kk + 8) * kBwD * 2);  // + 8 discard rows
+  L.gv = off;
+  off += al((size_t)(tc * kk + 8) * kBwD * 2);
+  L.list = off;
+  off += al((size_t)(tc * kk) * 4);
+  L.cnt = off;
+  off += al((size_t)(keys + 1) * 4);
+  L.off = off;
+  off += al((size_t)(keys + 1) * 4);
+  L.cursor = off;
+  off += al((size_t)(keys + 1) * 4);
+  L.total = off;
+  return L;
 }
+}  // namespace
+
+size_t dsa_sparse_bwd_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t kk) { return bwd_layout(B, T, S, kk).total; }
 
 hipError_t launch_dsa_sparse_bwd(DsaSparseBwdParams p, hipStream_t stream) {
   const int64_t BT = p.B * p.T, keys = p.B * p.S, tc = dsa_sparse_bwd_chunk(BT);
-  auto al = [](int64_t x) { return (x + 63) & ~(int64_t)63; };
-  float* w = reinterpret_cast<float*>(p.ws);
-  p.g = w;
-  p.hh = p.g + al(tc * p.kk * kBwD);
-  uint32_t* list = reinterpret_cast<uint32_t*>(p.hh + al(tc * p.kk * kBwD));
-  uint32_t* cnt = list + al(tc * p.kk);
-  uint32_t* off = cnt + al(keys + 1);
-  uint32_t* cursor = off + al(keys + 1);
+  const BwdLayout L = bwd_layout(p.B, p.T, p.S, p.kk);
+  char* w = reinterpret_cast<char*>(p.ws);
+  p.blocks = reinterpret_cast<uint16_t*>(w + L.blocks);
+  p.gk = reinterpret_cast<uint16_t*>(w + L.gk);
+  p.gv = reinterpret_cast<uint16_t*>(w + L.gv);
+  p.list = reinterpret_cast<uint32_t*>(w + L.list);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
+  uint32_t* off = reinterpret_cast<uint32_t*>(w + L.off);
+  uint32_t* cursor = reinterpret_cast<uint32_t*>(w + L.cursor);
+  p.off = off;
   const int64_t n4 = keys * kBwD / 4;
   const uint32_t zb = (uint32_t)std::min<int64_t>((n4 + 255) / 256, 4096);
   hipLaunchKernelGGL(dsa_sparse_bwd_zero_kernel, dim3(zb), dim3(256), 0, stream, reinterpret_cast<float4*>(p.dk), n4);
   hipLaunchKernelGGL(dsa_sparse_bwd_zero_kernel, dim3(zb), dim3(256), 0, stream, reinterpret_cast<float4*>(p.dv), n4);
-  const int64_t c4 = al(keys + 1) / 4;  // the counts, zeroed per chunk as float4 words
+  const int64_t c4 = ((keys + 1 + 63) & ~(int64_t)63) / 4;  // the counts, zeroed per chunk as float4 words
   const uint32_t cb = (uint32_t)std::min<int64_t>((c4 + 255) / 256, 4096);
+  const uint32_t rb = (uint32_t)std::min<int64_t>(keys, 65536);
   for (int64_t tok0 = 0; tok0 < BT; tok0 += tc) {
-    const int64_t ntok = std::min<int64_t>(tc, BT - tok0);
     p.tok0 = tok0;
-    const uint32_t eb = (uint32_t)((ntok * p.kk + 255) / 256);
+    p.ntok = std::min<int64_t>(tc, BT - tok0);
+    const uint32_t eb = (uint32_t)((p.ntok * p.kk + 255) / 256);
     hipLaunchKernelGGL(dsa_sparse_bwd_zero_kernel, dim3(cb), dim3(256), 0, stream, reinterpret_cast<float4*>(cnt), c4);
-    hipLaunchKernelGGL(dsa_sparse_bwd_count_kernel, dim3(eb), dim3(256), 0, stream, p, ntok, cnt);
+    hipLaunchKernelGGL(dsa_sparse_bwd_count_kernel, dim3(eb), dim3(256), 0, stream, p, cnt);
     hipLaunchKernelGGL(dsa_sparse_bwd_scan_kernel, dim3(1), dim3(1024), 0, stream, cnt, off, cursor, keys);
-    hipLaunchKernelGGL(dsa_sparse_bwd_fill_kernel, dim3(eb), dim3(256), 0, stream, p, ntok, cursor, list);
-    hipLaunchKernelGGL(dsa_sparse_bwd_kernel, dim3((uint32_t)ntok), dim3(kBwThreads), 0, stream, p);
-    hipLaunchKernelGGL(dsa_sparse_bwd_reduce_kernel, dim3((uint32_t)keys), dim3(kBwD), 0, stream, p, off, list);
+    hipLaunchKernelGGL(dsa_sparse_bwd_fill_kernel, dim3(eb), dim3(256), 0, stream, p, cursor);
+    hipLaunchKernelGGL(dsa_bwd_ds_kernel, dim3((uint32_t)p.ntok), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(dsa_bwd_contrib_kernel, dim3((uint32_t)p.ntok), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(dsa_sparse_bwd_reduce_kernel, dim3(rb), dim3(256), 0, stream, p, keys);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -190,16 +190,21 @@ struct DsaSparseBwdParams {
   const float* lse;    // forward log-sum-exp [B,T,64] (natural log)
   const void* dout;    // [B,T,64,256] bf16
   float* dq;           // [B,T,64,256]
-  float* dk;           // [B,S,256] (zeroed, then accumulated)
+  float* dk;           // [B,S,256] (zeroed, then accumulated chunk by chunk)
   float* dv;
   int64_t B, T, S, kk;
   float scale, scale_log2;
   void* ws;            // dsa_sparse_bwd_ws_bytes()
-  // Set by the launcher per chunk of tokens: the first token, and the
-  // per-entry dK / dV rows of the chunk ([tokens, kk, 256] fp32).
-  int64_t tok0;
-  float* g;
-  float* hh;
+  // Set by the launcher per chunk of tokens [tok0, tok0 + ntok): the chunk's
+  // P / dS blocks, per-entry dK / dV rows (bf16, entry e = (token - tok0) * kk
+  // + j), and the inverse index (segment of key b*S + s: list[off[key] ..
+  // off[key + 1]), entry ids in arbitrary order).
+  int64_t tok0, ntok;
+  uint16_t* blocks;  // [ntok, kk/32 tiles, 2 tensors, 2 head halves, 32, 32]
+  uint16_t* gk;      // [ntok * kk, 256]
+  uint16_t* gv;
+  uint32_t* list;
+  const uint32_t* off;
 };
 size_t dsa_sparse_bwd_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t kk);
 hipError_t launch_dsa_sparse_bwd(DsaSparseBwdParams p, hipStream_t stream);

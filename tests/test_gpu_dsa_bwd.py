@@ -1,14 +1,18 @@
 """Backward of the DSA sparse attention (dsa_sparse_attention_bwd) against the float64 oracle.
 
-The kernel works from the forward's bf16 output o and fp32 log-sum-exp and accumulates in fp32;
-the oracle rebuilds everything in float64 from the same bf16 inputs.  Tolerances, as a fraction
-of the output's largest magnitude, 1e-2 for each gradient:
-  * dq and dk go through dS = P (dP - D_h) with D_h = sum_d do*o taken from the forward's o, which
-    carries bf16 rounding (of P in the PV product and of o itself, each relative 2^-9 = 2e-3); the
-    error of D_h is of that order relative to dP and passes to dS, dq and dk;
-  * the kernel rounds dS and P to bf16 (relative 2^-9) for the dq, dk and dv sums, as the forward
-    rounds P for its PV product; summed over many terms of either sign these errors stay of that
-    order (measured: dq, dk up to 2.2e-3 before this rounding; dv about 1e-6 without it).
+The GPU works from the forward's bf16 output o and fp32 log-sum-exp; the oracle rebuilds everything in
+float64 from the same bf16 inputs.  Tolerance: an element-wise bound derived from the roundings the
+kernels make, computed in float64 beside the reference (per token, from the exact weights P, their
+derivative dS = P (dP - D) and D = sum P dP):
+  * D_h comes from the forward's bf16 output o: dS is off by P |dD_h|, dD_h = do_h . (o_gpu - o_exact)
+    computed exactly here;
+  * P and dS are rounded to bf16 (relative 2^-9) for the dq, dk, dv products (2^-8 covers it with room);
+  * P is rebuilt from fp32 scores and the forward's fp32 log-sum-exp (relative 1e-5 covers it);
+  * each entry's dk and dv rows are rounded to bf16 (relative 2^-9) before the per-position sums.
+So with e_hj = P |dD_h| + 2^-8 |dS| + 1e-5 P (|dP| + |D|): |error of dq_h| <= scale sum_j e_hj |k_j|,
+|error of dk[s]| <= sum over the entries at s of (scale sum_h e_hj |q_h| + 2^-9 |dk row|), and
+|error of dv[s]| <= sum over the entries at s of ((2^-8 + 1e-5) sum_h P_hj |do_h| + 2^-9 |dv row|).
+Checked with a margin of 2 and an absolute floor of 1e-6 of the reference's largest magnitude.
 """
 
 import numpy as np
@@ -17,17 +21,17 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DEV, f64, max_abs_err, require_gpu
+from gpu_util import DEV, f64, require_gpu
 
 pytestmark = pytest.mark.gpu
 
-REL_TOL = {"dq": 1e-2, "dk": 1e-2, "dv": 1e-2}
+U = 2.0 ** -8
 
 
-def _inputs(B, T, S, seed):
-    q = synth.np_normal((B, T, 64, 256), 1.0, "bf16", seed, 0)
-    k = synth.np_normal((B, S, 256), 1.0, "bf16", seed, 1)
-    v = synth.np_normal((B, S, 256), 1.0, "bf16", seed, 2)
+def _inputs(B, T, S, seed, sigma=1.0):
+    q = synth.np_normal((B, T, 64, 256), sigma, "bf16", seed, 0)
+    k = synth.np_normal((B, S, 256), sigma, "bf16", seed, 1)
+    v = synth.np_normal((B, S, 256), sigma, "bf16", seed, 2)
     do = synth.np_normal((B, T, 64, 256), 1.0, "bf16", seed, 3)
     return q, k, v, do
 
@@ -43,31 +47,83 @@ def _causal_idx(B, T, S, kk, g):
     return idx
 
 
+def _token_terms(q_i, k_b, v_b, o_i, do_i, sel, scale):
+    """Float64 terms of one token: (dq_i, per-entry dk rows, dv rows) and their error bounds."""
+    K, V = k_b[sel], v_b[sel]
+    lg = scale * (q_i @ K.T)
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dp = do_i @ V.T
+    D = (p * dp).sum(axis=1, keepdims=True)
+    ds = p * (dp - D)
+    dD = np.abs((do_i * (o_i - p @ V)).sum(axis=1, keepdims=True))
+    e = p * dD + U * np.abs(ds) + 1e-5 * p * (np.abs(dp) + np.abs(D))
+    ck, cv = scale * (ds.T @ q_i), p.T @ do_i
+    eq = scale * (e @ np.abs(K))
+    ek = scale * (e.T @ np.abs(q_i)) + 2.0 ** -9 * np.abs(ck)
+    ev = (U + 1e-5) * (p.T @ np.abs(do_i)) + 2.0 ** -9 * np.abs(cv)
+    return scale * (ds @ K), ck, cv, eq, ek, ev
+
+
+def _bounds(q, k, v, o_gpu, do, idx, scale=None):
+    """Element-wise error bounds (dq, dk, dv) for the whole call (float64)."""
+    q, k, v, o_gpu, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, o_gpu, do))
+    B, T, Hq, D = q.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    eq, ek, ev = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(B):
+        for i in range(T):
+            sel = idx[b, i][(idx[b, i] >= 0) & (idx[b, i] < k.shape[1])]
+            if sel.size == 0:
+                continue
+            _, _, _, eq[b, i], eki, evi = _token_terms(q[b, i], k[b], v[b], o_gpu[b, i], do[b, i], sel, scale)
+            np.add.at(ek[b], sel, eki)
+            np.add.at(ev[b], sel, evi)
+    return eq, ek, ev
+
+
+def _check(name, got, ref, bound):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    floor = 1e-6 * max(float(np.abs(ref).max()), 1e-30)
+    worst = float(np.max(err / (2 * bound + floor)))
+    print(f"  {name}: max abs err {err.max():.3e}, max |ref| {np.abs(ref).max():.3e}, "
+          f"worst err / (2 bound + floor) {worst:.3f}", flush=True)
+    assert worst <= 1.0, f"{name}: error above the derived bound ({worst:.3f})"
+
+
 def _gpu(sa, q, k, v, do, idx):
     t = lambda a: synth.to_torch(a, "bf16", DEV)
     ti = torch.from_numpy(idx.astype(np.int32)).to(DEV)
     tq, tk, tv = t(q), t(k), t(v)
     o, lse = sa.dsa_sparse_attention_fwd(tq, tk, tv, ti, return_lse=True)
-    return sa.dsa_sparse_attention_bwd(tq, tk, tv, ti, o, lse, t(do))
+    dq, dk, dv = sa.dsa_sparse_attention_bwd(tq, tk, tv, ti, o, lse, t(do))
+    torch.cuda.synchronize()
+    return f64(dq), f64(dk), f64(dv), f64(o)
 
 
-def _check(got, ref, what):
-    err = max_abs_err(f64(got), ref)
-    scale = float(np.abs(ref).max())
-    print(f"{what}: max abs err {err:.3e}, max |ref| {scale:.3e}", flush=True)
-    assert err <= REL_TOL[what.split()[0]] * scale, what
+def _compare_all(sa, q, k, v, do, idx):
+    dq, dk, dv, o = _gpu(sa, q, k, v, do, idx)
+    S = k.shape[1]
+    clean = np.where((idx >= 0) & (idx < S), idx, -1)
+    rq, rk, rv = oracle.dsa_sparse_attention_bwd(q, k, v, clean, do)
+    eq, ek, ev = _bounds(q, k, v, o, do, clean)
+    _check("dq", dq, rq, eq)
+    _check("dk", dk, rk, ek)
+    _check("dv", dv, rv, ev)
+    return dq
 
 
-@pytest.mark.parametrize("B,T,S,kk", [(1, 40, 100, 48), (2, 9, 300, 21), (1, 20, 2100, 2048), (1, 33, 33, 16)])
+@pytest.mark.parametrize("B,T,S,kk", [(1, 40, 100, 48), (2, 9, 300, 21), (1, 20, 2100, 2048), (1, 33, 33, 16),
+                                      (2, 1500, 1600, 64)])
 def test_sparse_bwd_matches_oracle(B, T, S, kk):
+    """Element-wise against the oracle; (2, 1500, 1600, 64) has 3000 tokens, so two chunks of the
+    per-position sums (2048 tokens each) and a batch boundary inside the first chunk."""
     sa = require_gpu()
+    print(f"[dsa_bwd] B={B} T={T} S={S} kk={kk}", flush=True)
     q, k, v, do = _inputs(B, T, S, 60 + kk)
     idx = _causal_idx(B, T, S, kk, np.random.default_rng(61 + kk))
-    dq, dk, dv = _gpu(sa, q, k, v, do, idx)
-    rq, rk, rv = oracle.dsa_sparse_attention_bwd(q, k, v, idx, do)
-    _check(dq, rq, "dq")
-    _check(dk, rk, "dk")
-    _check(dv, rv, "dv")
+    _compare_all(sa, q, k, v, do, idx)
 
 
 def test_sparse_bwd_padding_duplicates_and_empty_rows():
@@ -80,44 +136,70 @@ def test_sparse_bwd_padding_duplicates_and_empty_rows():
     idx[0, 1, 10:12] = [42, 43]
     idx[0, 3, :] = np.arange(kk)
     idx[0, 4, :] = np.arange(kk) + 80
-    dq, dk, dv = _gpu(sa, q, k, v, do, idx)
-    clean = np.where((idx >= 0) & (idx < S), idx, -1)
-    rq, rk, rv = oracle.dsa_sparse_attention_bwd(q, k, v, clean, do)
-    _check(dq, rq, "dq")
-    _check(dk, rk, "dk")
-    _check(dv, rv, "dv")
-    assert torch.all(dq[0, 2] == 0)
+    dq = _compare_all(sa, q, k, v, do, idx)
+    assert np.all(dq[0, 2] == 0)
 
 
-def test_sparse_bwd_4096_sums_and_sampled_rows():
-    """T = S = 4096, k = 2048: the sum identities of the gradients (sum of dk = 0, sum of dv = sum
-    of do over the rows with an entry) and dq of sampled rows against the oracle row by row."""
+def test_sparse_bwd_long_segment_of_one_position():
+    """One position listed 8192 times within a chunk (every entry of 64 tokens is position 5, most of
+    another position 9): more entries than the per-position sort holds, so the ordered scan adds them."""
     sa = require_gpu()
-    B, T, S, kk = 1, 4096, 4096, 2048
-    g = np.random.default_rng(63)
-    q, k, v, do = _inputs(B, T, S, 64)
-    idx = _causal_idx(B, T, S, kk, g)
-    dq, dk, dv = _gpu(sa, q, k, v, do, idx)
-    dk64, dv64 = f64(dk), f64(dv)
-    _check_sum = lambda got, want, mag, what: (print(f"{what}: {np.abs(got - want).max():.3e} vs {mag:.3e}"),
-                                              np.abs(got - want).max() <= REL_TOL[what.split()[1]] * mag)
-    # sum of dk: each row's dS sums to D_h-error terms only, so its sum is small against sum |dk|
-    assert _check_sum(dk64.sum(axis=1), 0.0, np.abs(dk64).sum(axis=1).max(), "sum dk")[1]
-    want_v = do.astype(np.float64).sum(axis=(1, 2))
-    assert _check_sum(dv64.sum(axis=1), want_v, np.abs(dv64).sum(axis=1).max(), "sum dv")[1]
-    rows = [0, 1, 2047, 2048, 3000, 4095]  # row 0 has one entry: its dq is exactly 0
-    refs = [oracle.dsa_sparse_attention_bwd(q[:, i:i + 1], k, v, idx[:, i:i + 1], do[:, i:i + 1])[0] for i in rows]
-    mag = max(float(np.abs(r).max()) for r in refs)
-    for i, rq in zip(rows, refs):
-        err = max_abs_err(f64(dq[:, i:i + 1]), rq)
-        print(f"dq row {i}: max abs err {err:.3e} (largest sampled |dq| {mag:.3e})", flush=True)
-        assert err <= REL_TOL["dq"] * mag, i
+    B, T, S, kk = 1, 64, 40, 128
+    q, k, v, do = _inputs(B, T, S, 65)
+    idx = np.full((B, T, kk), 5, dtype=np.int64)
+    idx[0, 10:20, 1::2] = 9
+    idx[0, 30, -3:] = -1
+    _compare_all(sa, q, k, v, do, idx)
 
 
-def test_sparse_bwd_32768_top2048_sums_and_sampled_rows():
-    """The bench's configuration: T = S = 32768, top-2048 chosen by the indexer and top-k, inputs
-    N(0,1)/16 and do N(0,1).  The sum identities over every position and dq of sampled rows
-    against the oracle row by row."""
+def test_sparse_bwd_bit_reproducible():
+    """Entries are added per position in ascending (token, entry) order: two runs give identical bits."""
+    sa = require_gpu()
+    B, T, S, kk = 2, 2500, 2600, 256
+    q, k, v, do = _inputs(B, T, S, 66)
+    idx = _causal_idx(B, T, S, kk, np.random.default_rng(67))
+    t = lambda a: synth.to_torch(a, "bf16", DEV)
+    ti = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    tq, tk, tv, tdo = t(q), t(k), t(v), t(do)
+    o, lse = sa.dsa_sparse_attention_fwd(tq, tk, tv, ti, return_lse=True)
+    a = sa.dsa_sparse_attention_bwd(tq, tk, tv, ti, o, lse, tdo)
+    b = sa.dsa_sparse_attention_bwd(tq, tk, tv, ti, o, lse, tdo)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def _sampled_check(q, k, v, o, do, idx, dq, dk, dv, rows, positions, scale):
+    """dq of sampled rows, and dk, dv at sampled positions from every token that lists them."""
+    B = q.shape[0]
+    kn, vn = f64(k), f64(v)
+    idx_np = idx.cpu().numpy().astype(np.int64)
+    for i in rows:
+        qi, oi, doi = f64(q[0, i]), f64(o[0, i]), f64(do[0, i])
+        sel = idx_np[0, i][idx_np[0, i] >= 0]
+        rq, _, _, eq, _, _ = _token_terms(qi, kn[0], vn[0], oi, doi, sel, scale)
+        _check(f"dq row {i}", f64(dq[0, i]), rq, eq)
+    for s in positions:
+        toks = np.nonzero((idx_np[0] == s).any(axis=1))[0]
+        rk, rv, ek, ev = (np.zeros(256) for _ in range(4))
+        for i in toks:
+            sel = idx_np[0, i][idx_np[0, i] >= 0]
+            _, ck, cv, _, eki, evi = _token_terms(f64(q[0, i]), kn[0], vn[0], f64(o[0, i]), f64(do[0, i]), sel, scale)
+            m = sel == s
+            rk += ck[m].sum(axis=0)
+            rv += cv[m].sum(axis=0)
+            ek += eki[m].sum(axis=0)
+            ev += evi[m].sum(axis=0)
+        print(f"  position {s}: listed by {toks.size} tokens", flush=True)
+        _check(f"dk[{s}]", f64(dk[0, s]), rk, ek)
+        _check(f"dv[{s}]", f64(dv[0, s]), rv, ev)
+
+
+@pytest.mark.parametrize("sigma", [1.0, 1.0 / 16])
+def test_sparse_bwd_32768_top2048(sigma):
+    """The bench's configuration: T = S = 32768, top-2048 chosen by the indexer and top-k, inputs at unit
+    variance and at the workload's N(0,1)/16, do N(0,1).  dq of sampled rows and dk, dv at sampled
+    positions (every token that lists them, found from the index) against the oracle within the derived
+    bound, and the sum identities over every position."""
     sa = require_gpu()
     T, kk = 32768, 2048
     qi = synth.torch_normal((1, T, 4, 128), 128 ** -0.5, torch.bfloat16, 401, DEV)
@@ -125,29 +207,18 @@ def test_sparse_bwd_32768_top2048_sums_and_sampled_rows():
     wi = synth.torch_uniform((1, T, 4), 403, DEV)
     idx = sa.dsa_indexer_topk(qi, ki, wi, kk)
     del qi, ki, wi
-    q = synth.torch_normal((1, T, 64, 256), 1.0 / 16, torch.bfloat16, 404, DEV)
-    k = synth.torch_normal((1, T, 256), 1.0 / 16, torch.bfloat16, 405, DEV)
-    v = synth.torch_normal((1, T, 256), 1.0 / 16, torch.bfloat16, 406, DEV)
+    q = synth.torch_normal((1, T, 64, 256), sigma, torch.bfloat16, 404, DEV)
+    k = synth.torch_normal((1, T, 256), sigma, torch.bfloat16, 405, DEV)
+    v = synth.torch_normal((1, T, 256), sigma, torch.bfloat16, 406, DEV)
     do = synth.torch_normal((1, T, 64, 256), 1.0, torch.bfloat16, 407, DEV)
     o, lse = sa.dsa_sparse_attention_fwd(q, k, v, idx, return_lse=True)
     dq, dk, dv = sa.dsa_sparse_attention_bwd(q, k, v, idx, o, lse, do)
+    torch.cuda.synchronize()
     dk64, dv64 = dk.double(), dv.double()
-    err_k = float(dk64.sum(dim=1).abs().max())
-    mag_k = float(dk64.abs().sum(dim=1).max())
-    err_v = float((dv64.sum(dim=1) - do.double().sum(dim=(1, 2))).abs().max())
-    mag_v = float(dv64.abs().sum(dim=1).max())
-    print(f"sum dk: {err_k:.3e} vs {mag_k:.3e}; sum dv: {err_v:.3e} vs {mag_v:.3e}", flush=True)
-    assert err_k <= REL_TOL["dk"] * mag_k
-    assert err_v <= REL_TOL["dv"] * mag_v  # every row has at least one entry
-    kn, vn = f64(k), f64(v)
+    err_k = float((dk64.sum(dim=1).abs() / dk64.abs().sum(dim=1)).max())
+    err_v = float(((dv64.sum(dim=1) - do.double().sum(dim=(1, 2))).abs() / dv64.abs().sum(dim=1)).max())
+    print(f"sigma {sigma}: |sum dk| / mass {err_k:.3e}; |sum dv - sum do| / mass {err_v:.3e}", flush=True)
+    assert err_k <= 1e-2 and err_v <= 1e-3  # every row has at least one entry
     rows = [0, 1, 2047, 2048, 16384, 32767]
-    refs = []
-    for i in rows:
-        r = oracle.dsa_sparse_attention_bwd(f64(q[:, i:i + 1]), kn, vn, idx[:, i:i + 1].cpu().numpy().astype(np.int64),
-                                            f64(do[:, i:i + 1]))
-        refs.append(r[0])
-    mag = max(float(np.abs(r).max()) for r in refs)
-    for i, rq in zip(rows, refs):
-        err = max_abs_err(f64(dq[:, i:i + 1]), rq)
-        print(f"dq row {i}: max abs err {err:.3e} (largest sampled |dq| {mag:.3e})", flush=True)
-        assert err <= REL_TOL["dq"] * mag, i
+    positions = [32500, 32000, 31000, 28000]
+    _sampled_check(q, k, v, o, do, idx, dq, dk, dv, rows, positions, 1.0 / 16)
