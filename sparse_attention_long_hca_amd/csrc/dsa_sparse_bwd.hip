@@ -68,7 +68,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   using T = bf16_t;
   using G = AttnGeom<T, kBwD, 1>;
   constexpr int kWaves = 2;
-  __shared__ __attribute__((aligned(16))) char kl[2][G::kTileBytes];
+  // Two K buffers as separate arrays, and a tile loop unrolled by two so that
+  // every load and read names its buffer at compile time (with a computed
+  // index the compiler would wait for every load before any LDS read).
+  __shared__ __attribute__((aligned(16))) char kl0[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char kl1[G::kTileBytes];
   __shared__ __attribute__((aligned(16))) char vl[G::kTileBytes];
   __shared__ int32_t sidx[kBwMaxK];
 
@@ -116,7 +120,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int32_t* trow = sidx + 32 * t;
     return [=](int r) -> int { return trow[r]; };
   };
-  auto issue_k = [&](int t) { stage_rows_async<T, kBwD, kWaves, 1>(kl[t & 1], kb, rows_of(t)); };
+  auto issue_k = [&](int t, char* buf) { stage_rows_async<T, kBwD, kWaves, 1>(buf, kb, rows_of(t)); };
   auto issue_v = [&](int t) { stage_rows_async<T, kBwD, kWaves, 1>(vl, vb, rows_of(t)); };
   constexpr int kLd = StageGeom<T, kBwD, kWaves>::kPerWave;  // loads per wave of a K (or V) tile
   constexpr int kSt = 32;                                    // block stores per wave and tile
@@ -142,18 +146,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   wait_vmcnt<0>();  // Q, dO, O, lse and the index list are in
   __syncthreads();  // sidx
-  issue_k(0);
+  issue_k(0, kl0);
   issue_v(0);
   // Two blocks' worth of stores to distinct addresses (identical stores to one
   // address could be merged, and the waits would then miscount).
   store_block(discard, zero16);
   store_block(discard + 2 * kBlkE, zero16);
 
-  auto step = [&](int t, auto more_tag) __attribute__((always_inline)) {
+  auto step = [&](int t, auto more_tag, auto buf_tag) __attribute__((always_inline)) {
     constexpr bool more = decltype(more_tag)::value;
-    const char* kt = kl[t & 1];
+    constexpr int buf = decltype(buf_tag)::value;  // t & 1
+    const char* kt = buf == 0 ? kl0 : kl1;
     if constexpr (more) {
-      issue_k(t + 1);
+      issue_k(t + 1, buf == 0 ? kl1 : kl0);
       wait_vmcnt<kLd + kSt + kLd>();  // K(t) landed: V(t), stores(t - 1), K(t + 1) may be in flight
     } else {
       wait_vmcnt<kLd + kSt>();
@@ -187,8 +192,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     store_block(bt + 2 * kBlkE, dp); // dS: tensor 1
     lds_barrier();  // both waves are done with K(t)
   };
-  for (int t = 0; t + 1 < ntile; ++t) step(t, std::true_type{});
-  step(ntile - 1, std::false_type{});
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  int t = 0;
+  for (; t + 2 < ntile; t += 2) {
+    step(t, std::true_type{}, B0{});
+    step(t + 1, std::true_type{}, B1{});
+  }
+  if (t + 1 < ntile) {
+    step(t, std::true_type{}, B0{});
+    step(t + 1, std::false_type{}, B1{});
+  } else {
+    step(t, std::false_type{}, B0{});
+  }
 
   float* dqr = p.dq + (tok * kBwH + h) * kBwD;
 #pragma unroll

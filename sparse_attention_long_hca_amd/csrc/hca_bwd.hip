@@ -81,7 +81,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   using GH = AttnGeom<T, kBwdHD, 1>;
   constexpr int kWaves = 4;
   constexpr int kHalfTile = GH::kTileBytes;  // 16 KB: 32 rows x 512 bytes
-  __shared__ __attribute__((aligned(16))) char kbuf[2][2 * kHalfTile];
+  // Two K buffers as separate arrays, and a tile loop unrolled by two so that
+  // every load and read names its buffer at compile time (with a computed
+  // index the compiler would wait for every load before any LDS read).
+  __shared__ __attribute__((aligned(16))) char kbuf0[2 * kHalfTile];
+  __shared__ __attribute__((aligned(16))) char kbuf1[2 * kHalfTile];
   __shared__ __attribute__((aligned(16))) char vbuf[2 * kHalfTile];
   __shared__ __attribute__((aligned(16))) char xbuf[kWaves * 8192];  // partial S^T, dP^T per wave
   __shared__ float dsh[kWaves][32];
@@ -162,10 +166,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       return x <= last ? x : -1;
     };
   };
-  auto issue_k = [&](int tile) __attribute__((always_inline)) {
+  auto issue_k = [&](int tile, char* dst) __attribute__((always_inline)) {
     const auto rf = rows_of(tile);
     const T* src = tile < n_ct ? kc : k;
-    char* dst = kbuf[tile & 1];
     stage_rows_async<T, kBwdHD, kWaves, 1, kBwdD * 2>(dst, src, rf);
     stage_rows_async<T, kBwdHD, kWaves, 1, kBwdD * 2>(dst + kHalfTile, src + kBwdHD, rf);
   };
@@ -208,20 +211,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int j = 0; j < 16; ++j) zero16[j] = 0.f;
   if (n_tiles > 0) {
-    issue_k(0);
+    issue_k(0, kbuf0);
     issue_v(0);
     store_block(discard + half * kBlkElems, zero16);
   }
 
-  auto step = [&](int tile, auto more_tag) __attribute__((always_inline)) {
+  auto step = [&](int tile, auto more_tag, auto buf_tag) __attribute__((always_inline)) {
     constexpr bool more = decltype(more_tag)::value;
+    constexpr int buf = decltype(buf_tag)::value;  // tile & 1
     const bool ct = tile < n_ct;
     const int jt = tile, r = r_lo + tile - n_ct;
     const bool need = pvalid && (ct ? jt < n_ct_p : (r >= r_lo_p && r <= tqi));
     const int slot = ct ? jt : nct + (r - tqi + nr - 1);
-    const char* kt = kbuf[tile & 1] + half * kHalfTile;
+    const char* kt = (buf == 0 ? kbuf0 : kbuf1) + half * kHalfTile;
     if constexpr (more) {
-      issue_k(tile + 1);
+      issue_k(tile + 1, buf == 0 ? kbuf1 : kbuf0);
       wait_vmcnt<kLd + kSt + kLd>();  // K(tile) landed: V(tile), stores(tile - 1), K(tile + 1) may be in flight
     } else {
       wait_vmcnt<kLd + kSt>();
@@ -272,9 +276,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     store_block(dst, half == 0 ? s : dp);
     lds_barrier();  // every wave is done with K(tile) and the partials
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
   if (n_tiles > 0) {
-    for (int tile = 0; tile + 1 < n_tiles; ++tile) step(tile, std::true_type{});
-    step(n_tiles - 1, std::false_type{});
+    int tile = 0;
+    for (; tile + 2 < n_tiles; tile += 2) {
+      step(tile, std::true_type{}, B0{});
+      step(tile + 1, std::true_type{}, B1{});
+    }
+    if (tile + 1 < n_tiles) {
+      step(tile, std::true_type{}, B0{});
+      step(tile + 1, std::false_type{}, B1{});
+    } else {
+      step(tile, std::false_type{}, B0{});
+    }
   }
   if (qvalid) {
     float* dqr = p.dq + head + (int64_t)tq * kBwdD + half * kBwdHD;
