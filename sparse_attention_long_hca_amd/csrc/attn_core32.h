@@ -134,7 +134,10 @@ __device__ __forceinline__ void pack_p32(const f32x16_t& s, i16x8_t pf[2]) {
 
 // acc[i] += V^T[dims 32*(nb0+i) .. +31] . P^T for i < NB, with V a 32-row
 // tile of 256-dim rows in LDS (read transposed) and pf from pack_p32.
-template <int NB, int kAhead = 2>
+// kOutT: the same product with the MFMA operands swapped, which gives the
+// transposed block (acc[i] += P . V[:, dims 32*(nb0+i) ..]): lane l then
+// holds dim 32*(nb0+i) + l%32 of rows 8*(j/4) + 4q + j%4.
+template <int NB, int kAhead = 2, bool kOutT = false>
 __device__ __forceinline__ void pv32_acc(f32x16_t* acc, const i16x8_t pf[2], const char* vs, Tile32Addr ad, int nb0) {
   constexpr int kPairs = NB * 2;  // (dims block, key half)
   asm volatile("" : "+v"(ad.v0), "+v"(ad.v1));
@@ -151,7 +154,10 @@ __device__ __forceinline__ void pv32_acc(f32x16_t* acc, const i16x8_t pf[2], con
 #pragma unroll
   for (int i = 0; i < kPairs; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    acc[i >> 1] = mfma_bf16_32x32x16(va[i % kAhead], pf[i & 1], acc[i >> 1]);
+    if constexpr (kOutT)
+      acc[i >> 1] = mfma_bf16_32x32x16(pf[i & 1], va[i % kAhead], acc[i >> 1]);
+    else
+      acc[i >> 1] = mfma_bf16_32x32x16(va[i % kAhead], pf[i & 1], acc[i >> 1]);
     if (i + kAhead < kPairs) va[i % kAhead] = vread(i + kAhead);
   }
   __builtin_amdgcn_sched_barrier(0);

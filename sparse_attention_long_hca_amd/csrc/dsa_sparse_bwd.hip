@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nb0 = 2 * wave;
   uint16_t* const discard_k = p.gk + p.ntok * p.kk * kBwD;
   uint16_t* const discard_v = p.gv + p.ntok * p.kk * kBwD;
-  constexpr int kLd = 2, kSt = 16;
+  constexpr int kLd = 2, kSt = 32;
 
   stage_blocks(0, 0);
   // Discard stores so that every tile sees the same outstanding operations,
@@ -274,8 +274,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // and the waits would then miscount).
 #pragma unroll
   for (int i = 0; i < kSt / 2; ++i) {
-    *reinterpret_cast<uint2*>(discard_k + i * kBwD + 4 * lane) = make_uint2(0u, 0u);
-    *reinterpret_cast<uint2*>(discard_v + i * kBwD + 4 * lane) = make_uint2(0u, 0u);
+    *reinterpret_cast<uint32_t*>(discard_k + 2 * i * kBwD + 2 * lane) = 0u;
+    *reinterpret_cast<uint32_t*>(discard_v + 2 * i * kBwD + 2 * lane) = 0u;
   }
 
   for (int t = 0; t < ntile; ++t) {
@@ -300,25 +300,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bp[st] = __builtin_bit_cast(i16x8_t, lds_read_b128(b0 + hw * 2 * kBlkE, boff[st]));
         bd[st] = __builtin_bit_cast(i16x8_t, lds_read_b128(b0 + (2 + hw) * 2 * kBlkE, boff[st]));
       }
-      pv32_acc<2, 2>(ak, bd, qs[hw], ad, nb0);
-      pv32_acc<2, 2>(av, bp, dos[hw], ad, nb0);
+      pv32_acc<2, 2, true>(ak, bd, qs[hw], ad, nb0);
+      pv32_acc<2, 2, true>(av, bp, dos[hw], ad, nb0);
     }
     wait_lgkmcnt0();
-    // Lane: entry 32t + l%32, dims 64w + 32nb + 8m + 4q .. +3.
-    const int j = 32 * t + (lane & 31);
-    const int64_t e = tl * kk + j;
-    uint16_t* rk = j < kk ? p.gk + e * kBwD : discard_k;
-    uint16_t* rv = j < kk ? p.gv + e * kBwD : discard_v;
+    // Lane l holds dim 64w + 32nb + l%32 of entries 32t + 8(j/4) + 4q + j%4.
+    // Values j and j+1 (entries E, E+1) are paired across lanes l, l^1: the
+    // even lane stores dims (l, l+1) of entry E, the odd lane dims (l-1, l)
+    // of entry E+1, so every store writes 64 contiguous bytes of 4 rows.
+    const bool odd = lane & 1;
+    const int dcol = 64 * wave + (lane & 30);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int d = 32 * (nb0 + nb) + 8 * m + 4 * qh;
-        *reinterpret_cast<uint2*>(rk + d) =
-            make_uint2(pack_bf16x2(ak[nb][4 * m] * p.scale, ak[nb][4 * m + 1] * p.scale),
-                       pack_bf16x2(ak[nb][4 * m + 2] * p.scale, ak[nb][4 * m + 3] * p.scale));
-        *reinterpret_cast<uint2*>(rv + d) = make_uint2(pack_bf16x2(av[nb][4 * m], av[nb][4 * m + 1]),
-                                                       pack_bf16x2(av[nb][4 * m + 2], av[nb][4 * m + 3]));
+      for (int j = 0; j < 16; j += 2) {
+        const int jj = 32 * t + 8 * (j >> 2) + 4 * qh + (j & 3) + (odd ? 1 : 0);
+        const int64_t e = tl * kk + jj;
+        const bool live = jj < kk;
+        const float k0 = ak[nb][j] * p.scale, k1 = ak[nb][j + 1] * p.scale;
+        const float kx = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? k0 : k1), 0xb1, 0xf, 0xf, false));
+        const float v0 = av[nb][j], v1 = av[nb][j + 1];
+        const float vx = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? v0 : v1), 0xb1, 0xf, 0xf, false));
+        const int d = dcol + 32 * nb;
+        uint16_t* rk = (live ? p.gk + e * kBwD : discard_k) + d;
+        uint16_t* rv = (live ? p.gv + e * kBwD : discard_v) + d;
+        *reinterpret_cast<uint32_t*>(rk) = odd ? pack_bf16x2(kx, k1) : pack_bf16x2(k0, kx);
+        *reinterpret_cast<uint32_t*>(rv) = odd ? pack_bf16x2(vx, v1) : pack_bf16x2(v0, vx);
       }
     lds_barrier();  // the stage's buffer is free for the load two tiles on
   }
@@ -467,9 +474,9 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t S, int64_t kk) {
   L.blocks = off;
   off += al((size_t)(tc * bw_ntile(kk) + 1) * 4 * kBlkE * 2);  // + a discard tile
   L.gk = off;
-  off += al((size_t)(tc * kk + 8) * kBwD * 2);  // + 8 discard rows
+  off += al((size_t)(tc * kk + 32) * kBwD * 2);  // + 32 discard rows
   L.gv = off;
-  off += al((size_t)(tc * kk + 8) * kBwD * 2);
+  off += al((size_t)(tc * kk + 32) * kBwD * 2);
   L.list = off;
   off += al((size_t)(tc * kk) * 4);
   L.cnt = off;
