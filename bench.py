@@ -99,6 +99,15 @@ def main():
         print("bench.py: only --gpus 1 is supported (single-GPU build).", file=sys.stderr)
         return 2
 
+    # The CPU baseline runs first, in a pool of forked single-threaded workers,
+    # before anything initialises the GPU (a process that has touched the GPU is
+    # not forked).
+    parts0 = set(args.only.split(",")) if args.only else {"prefill"}
+    cpu = None
+    if not args.no_cpu_baseline and "prefill" in parts0:
+        print("[bench] cpu baseline (float64 oracle, process pool)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+
     import torch
 
     import sparse_attention_long_hca_amd as sa
@@ -110,7 +119,8 @@ def main():
     sa.lib()
     dev = "cuda:0"
     timer = Timer(torch)
-    parts = set(args.only.split(",")) if args.only else {"prefill", "variants", "backward", "decode128k", "decode1m"}
+    parts = set(args.only.split(",")) if args.only else {"prefill", "variants", "backward", "decode128k", "decode1m",
+                                                          "tiny", "hbm"}
     result = {}
     kernels = {}
     if "copy" in parts:
@@ -124,6 +134,54 @@ def main():
 
     def progress(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # -------------------------------------------------------------------
+    # Measured HBM rate beside the 8 TB/s figure: a 2 GiB device copy
+    # -------------------------------------------------------------------
+    if "hbm" in parts:
+        progress("HBM copy")
+        n = 1 << 29  # 2 GiB of fp32
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b_ = torch.empty_like(a)
+        for _ in range(3):
+            b_.copy_(a)
+        torch.cuda.synchronize()
+        t_c = sorted(timer.time(lambda: b_.copy_(a), 10))[5]
+        result["hbm_measured"] = {"copy_GBs": 2 * 4 * n / (t_c * 1e-3) / 1e9, "peak_GBs": HBM_PEAK_GBS,
+                                  "note": "median of 10 device copies of 2 GiB (read + write bytes)"}
+        del a, b_
+        torch.cuda.empty_cache()
+
+    # -------------------------------------------------------------------
+    # Tiny HCA, fp32: T = 1024, 4 heads, d = 64, block 128, window 128
+    # (compression of K and V, then attention), with a 512 MB scrub write
+    # between runs so that no input is served from the caches
+    # -------------------------------------------------------------------
+    if "tiny" in parts:
+        progress("tiny fp32 HCA")
+        qt = synth.torch_normal((1, 4, 1024, 64), 1.0, torch.float32, 101, dev)
+        kt = synth.torch_normal((1, 4, 1024, 64), 1.0, torch.float32, 102, dev)
+        vt = synth.torch_normal((1, 4, 1024, 64), 1.0, torch.float32, 103, dev)
+        kct = torch.empty((1, 4, 8, 64), dtype=torch.float32, device=dev)
+        vct = torch.empty_like(kct)
+        scrub = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MB
+
+        def tiny():
+            sa.hca_compress(kt, BLK, out=kct)
+            sa.hca_compress(vt, BLK, out=vct)
+            return sa.hca_attention_fwd(sa.HCA_PREFILL, qt, kt, vt, kct, vct, BLK, WIN)
+
+        tiny()
+        times = []
+        for _ in range(max(20, args.steps)):
+            scrub.fill_(1.0)
+            times += timer.time(tiny, 1)
+        us = sorted(times)[len(times) // 2] * 1e3
+        result["tiny_hca_f32"] = {"us": us, "workload": "HCA f32 T=1024, 4 heads, d=64, block 128, window 128: "
+                                  "hca_compress(K), hca_compress(V), hca_attention_fwd(PREFILL); median of "
+                                  f"{len(times)} runs, 512 MB scrub write between runs"}
+        del qt, kt, vt, kct, vct, scrub
+        torch.cuda.empty_cache()
 
     # -------------------------------------------------------------------
     # Prefill: HCA layer + MLA-DSA layer over T = 32768 tokens
@@ -458,14 +516,6 @@ def main():
                         "unit": "GB/s", "frac": kd_["hbm_frac"]}
         roofline["traffic"] = traffic_for(dom)
 
-    # -------------------------------------------------------------------
-    # CPU baseline: the float64 oracle on a bounded sample
-    # -------------------------------------------------------------------
-    cpu = None
-    if not args.no_cpu_baseline and "prefill" in result:
-        progress("cpu baseline (float64 oracle)")
-        cpu = cpu_baseline()
-
     step_ms = result.get("prefill", {}).get("ms_per_step")
     line = {
         "metric": "HCA/DSA prefill tokens/s + decode us/step at 128K; % of MFMA/HBM peak",
@@ -488,6 +538,8 @@ def main():
             "parallelism": "single GPU",
         },
         "decode": {k_: v_ for k_, v_ in result.items() if k_.startswith("decode")},
+        "tiny_hca_f32": result.get("tiny_hca_f32"),
+        "hbm_measured": result.get("hbm_measured"),
         "variants": {k_: v_ for k_, v_ in result.items() if k_.startswith(("csa", "hca_prefill_qk576"))},
         "backward": {k_: v_ for k_, v_ in result.items() if k_.endswith("_bwd")},
         "kernels": kernels,
@@ -514,60 +566,93 @@ def traffic_for(kernel):
     return ent.get("bytes_per_launch")
 
 
+_CPU = {}
+
+
+def _cpu_hca_rows(rows):
+    import oracle
+
+    c = _CPU
+    t0 = time.perf_counter()
+    oracle.hca_attention_prefill(c["q"], c["k"], c["v"], c["kc"], c["vc"], BLK, WIN, rows=rows)
+    return time.perf_counter() - t0
+
+
+def _cpu_dsa_rows(rs):
+    import oracle
+
+    c = _CPU
+    t0 = time.perf_counter()
+    for r in rs:
+        p = c["pos"][r]
+        sc = oracle.dsa_indexer_scores(c["qi"][:, r:r + 1], c["ki"], c["w"][:, r:r + 1], q_pos=[p])
+        idx = oracle.dsa_topk(sc, TOPK, q_pos=[p])
+        oracle.dsa_sparse_attention(c["qd"][:, r:r + 1], c["kd"], c["vd"], idx)
+    return time.perf_counter() - t0
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+
+    threadpool_limits(1)  # one thread per worker: the pool size is the core count used
+
+
 def cpu_baseline():
-    """Time the float64 oracle on a bounded sample of the prefill workload (host cores)."""
+    """Time the float64 oracle on a bounded sample of the prefill workload on the host's cores: a pool of
+    forked single-threaded workers, one per core (at most 16, the machine's CPU share), splits the query rows.
+    Must run before anything initialises the GPU (the workers are forked)."""
+    import multiprocessing as mp
+
     import numpy as np
-    import torch
 
     import oracle
     import synth
 
-    cores = len(os.sched_getaffinity(0))
-    torch.set_num_threads(cores)
+    cores = min(16, len(os.sched_getaffinity(0)))
     g = np.random.default_rng(7)
     # HCA: 4 heads of the 32768 x 512 prefill.  Compression is a per-token cost
     # over all T tokens; attention is timed on query rows spread over T.
-    hs, rows = 4, list(np.linspace(0, T_PREFILL - 1, 8192).astype(int))
+    hs, rows = 4, list(np.linspace(0, T_PREFILL - 1, 1024 * cores).astype(int))
     sig = 1.0 / math.sqrt(D_HCA)
-    q = synth.np_normal((1, hs, T_PREFILL, D_HCA), sig, "bf16", 901, 0)
-    k = synth.np_normal((1, hs, T_PREFILL, D_HCA), sig, "bf16", 901, 1)
-    v = synth.np_normal((1, hs, T_PREFILL, D_HCA), sig, "bf16", 901, 2)
+    c = _CPU
+    c["q"] = synth.np_normal((1, hs, T_PREFILL, D_HCA), sig, "bf16", 901, 0)
+    c["k"] = synth.np_normal((1, hs, T_PREFILL, D_HCA), sig, "bf16", 901, 1)
+    c["v"] = synth.np_normal((1, hs, T_PREFILL, D_HCA), sig, "bf16", 901, 2)
     t0 = time.perf_counter()
-    kc, vc = oracle.hca_compress(k, BLK), oracle.hca_compress(v, BLK)
+    c["kc"], c["vc"] = oracle.hca_compress(c["k"], BLK), oracle.hca_compress(c["v"], BLK)
     t_comp = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.hca_attention_prefill(q, k, v, kc, vc, BLK, WIN, rows=rows)
-    t_att = time.perf_counter() - t0
-    hca_s_per_token = (t_comp / T_PREFILL + t_att / len(rows)) * (H / hs)
     # MLA-DSA: query rows at positions >= 2048 (indexer over the prefix, top-2048, 64-head attention).
-    S = T_PREFILL
-    nq = 384
-    qi = synth.np_normal((1, nq, HI, DI), DI ** -0.5, "bf16", 902, 0)
-    ki = synth.np_normal((1, S, DI), DI ** -0.5, "bf16", 902, 1)
-    w = synth.np_uniform((1, nq, HI), 902, 2)
-    qd = synth.np_normal((1, nq, HQ, D_DSA), 1.0 / 16, "bf16", 902, 3)
-    kd = synth.np_normal((1, S, D_DSA), 1.0 / 16, "bf16", 902, 4)
-    vd = synth.np_normal((1, S, D_DSA), 1.0 / 16, "bf16", 902, 5)
-    pos = [int(x) for x in g.integers(TOPK, S, size=nq)]
-    t0 = time.perf_counter()
-    for r, p in enumerate(pos):
-        sc = oracle.dsa_indexer_scores(qi[:, r:r + 1], ki, w[:, r:r + 1], q_pos=[p])
-        idx = oracle.dsa_topk(sc, TOPK, q_pos=[p])
-        oracle.dsa_sparse_attention(qd[:, r:r + 1], kd, vd, idx)
-    t_dsa = time.perf_counter() - t0
-    dsa_s_per_token = t_dsa / len(pos)
+    S, nq = T_PREFILL, 48 * cores
+    c["qi"] = synth.np_normal((1, nq, HI, DI), DI ** -0.5, "bf16", 902, 0)
+    c["ki"] = synth.np_normal((1, S, DI), DI ** -0.5, "bf16", 902, 1)
+    c["w"] = synth.np_uniform((1, nq, HI), 902, 2)
+    c["qd"] = synth.np_normal((1, nq, HQ, D_DSA), 1.0 / 16, "bf16", 902, 3)
+    c["kd"] = synth.np_normal((1, S, D_DSA), 1.0 / 16, "bf16", 902, 4)
+    c["vd"] = synth.np_normal((1, S, D_DSA), 1.0 / 16, "bf16", 902, 5)
+    c["pos"] = [int(x) for x in g.integers(TOPK, S, size=nq)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_cpu_worker_init) as pool:
+        t0 = time.perf_counter()
+        busy_h = sum(pool.map(_cpu_hca_rows, [rows[i::cores] for i in range(cores)]))
+        t_att = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        busy_d = sum(pool.map(_cpu_dsa_rows, [list(range(i, nq, cores)) for i in range(cores)]))
+        t_dsa = time.perf_counter() - t0
+    hca_s_per_token = (t_comp / T_PREFILL + t_att / len(rows)) * (H / hs)
+    dsa_s_per_token = t_dsa / nq
     per_token = hca_s_per_token + dsa_s_per_token
-    t_hca = t_comp + t_att
+    _CPU.clear()
     return {
         "value": 1.0 / per_token,
         "unit": "tokens/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"HCA: {hs} of 64 heads of the T=32768 d=512 prefill: block-mean compression of all 32768 "
-                  f"tokens ({t_comp:.1f} s) + attention for {len(rows)} query rows ({t_att:.1f} s), per-token cost "
-                  f"scaled x{H // hs} to 64 heads; MLA-DSA: {len(pos)} query rows at positions >= 2048 (indexer over "
-                  f"the causal prefix, top-2048, 64-head attention; {t_dsa:.1f} s)",
-        "seconds": t_hca + t_dsa,
+        "sample": f"{cores} single-threaded worker processes. HCA: {hs} of 64 heads of the T=32768 d=512 prefill: "
+                  f"block-mean compression of all 32768 tokens (one process, {t_comp:.1f} s) + attention for "
+                  f"{len(rows)} query rows ({t_att:.1f} s wall, {busy_h:.1f} s of worker time), per-token cost "
+                  f"scaled x{H // hs} to 64 heads; MLA-DSA: {nq} query rows at positions >= 2048 (indexer over the "
+                  f"causal prefix, top-2048, 64-head attention; {t_dsa:.1f} s wall, {busy_d:.1f} s of worker time)",
+        "seconds": t_comp + t_att + t_dsa,
     }
 
 
