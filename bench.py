@@ -12,7 +12,8 @@ A step is one prefill pass of the hybrid layer pair over T = 32768 tokens:
 dsa_topk; the line also times that pair and checks the two agree.)
 `value` is prefill tokens/s of that step (inputs resident in HBM).  The same
 JSON line carries decode microseconds per step for the 128K context
-(batch 64) and the 1M context (batch 4, HCA layer + MLA-DSA layer), per-kernel
+(batch 64) and the 1M context (batch 4, HCA layer + MLA-DSA layer, whose
+indices come from dsa_indexer_topk; the separate pair is timed beside it), per-kernel
 times, the roofline of the dominant kernel, and the float64 CPU oracle timed
 on a bounded sample of the same workload.
 """
@@ -467,7 +468,9 @@ def main():
         qpos5 = torch.full((B5,), L5 - 1, dtype=torch.int64, device=dev)
         sc5 = torch.empty((B5, 1, L5), dtype=torch.float32, device=dev)
         idx5 = torch.empty((B5, 1, TOPK), dtype=torch.int32, device=dev)
+        idx5s = torch.empty_like(idx5)
         wst5 = torch.empty(max(1, sa.dsa_topk_workspace_size(B5, 1, L5, TOPK)), dtype=torch.uint8, device=dev)
+        wsf5 = torch.empty(sa.dsa_indexer_topk_workspace_size(B5, 1, L5, TOPK), dtype=torch.uint8, device=dev)
         wss5 = torch.empty(max(1, sa.dsa_sparse_attention_fwd_workspace_size(B5, 1, HQ, D_DSA, TOPK)),
                            dtype=torch.uint8, device=dev)
 
@@ -475,28 +478,38 @@ def main():
             return sa.hca_attention_fwd(sa.HCA_DECODE, q5, rk5, rv5, kc5, vc5, BLK, WIN, pos=pos5, workspace=ws5)
 
         def dsa5():
-            sa.dsa_indexer_scores(qi5, ki5, wi5, q_pos=qpos5, out=sc5)
-            sa.dsa_topk(sc5, TOPK, q_pos=qpos5, out=idx5, workspace=wst5)
+            sa.dsa_indexer_topk(qi5, ki5, wi5, TOPK, q_pos=qpos5, out=idx5, workspace=wsf5)
             return sa.dsa_sparse_attention_fwd(qd5, kd5, vd5, idx5, workspace=wss5)
+
+        def dsa5_separate():
+            sa.dsa_indexer_scores(qi5, ki5, wi5, q_pos=qpos5, out=sc5)
+            sa.dsa_topk(sc5, TOPK, q_pos=qpos5, out=idx5s, workspace=wst5)
+            return sa.dsa_sparse_attention_fwd(qd5, kd5, vd5, idx5s, workspace=wss5)
 
         for _ in range(args.warmup):
             hca5()
             dsa5()
+            dsa5_separate()
         torch.cuda.synchronize()
         n_it = max(20, args.steps * 5)
         t_h = sorted(timer.time(hca5, n_it))[n_it // 2] * 1e3
         t_d = sorted(timer.time(dsa5, n_it))[n_it // 2] * 1e3
+        t_ds = sorted(timer.time(dsa5_separate, n_it))[n_it // 2] * 1e3
         keys5 = (NC5 - 1) + WIN
         b_h = B5 * H * keys5 * 2 * D_HCA * 2
-        b_d = B5 * L5 * DI * 2 + 2 * B5 * L5 * 4 + B5 * TOPK * 2 * D_DSA * 2
+        # indexer keys read once, the selected K and V rows gathered (the fused call
+        # writes no score row)
+        b_d = B5 * L5 * DI * 2 + B5 * TOPK * 2 * D_DSA * 2
         result["decode_1m_b4"] = {
             "us_per_step": t_h + t_d,
             "hca_us": t_h,
             "dsa_us": t_d,
             "hca_hbm_frac": b_h / (t_h * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "dsa_hbm_frac": b_d / (t_d * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "dsa_separate_us": t_ds,
+            "indices_equal_separate": bool(torch.equal(idx5, idx5s)),
         }
-        del q5, kc5, vc5, rk5, rv5, ws5, qi5, ki5, wi5, qd5, kd5, vd5, sc5, idx5, wst5, wss5
+        del q5, kc5, vc5, rk5, rv5, ws5, qi5, ki5, wi5, qd5, kd5, vd5, sc5, idx5, idx5s, wst5, wsf5, wss5
         torch.cuda.empty_cache()
 
     # -------------------------------------------------------------------

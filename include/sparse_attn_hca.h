@@ -372,9 +372,15 @@ int csa_topk(const float* scores, const int64_t* q_pos, int32_t* idx,
  * q_idx: [B,T,Hi,Di] bf16; k_idx: [B,S,Di] bf16; w: [B,T,Hi] fp32;
  * q_pos: device int64[B] or NULL (as for dsa_indexer_scores);
  * idx: [B,T,k] int32.
+ * Decode-shaped calls with long rows (T <= 4, S > 32768) take the register-
+ * operand decode indexer: it writes the candidates of each chunk of 128
+ * positions in position order, and one workgroup per row selects over them
+ * (at most 8192 candidates; otherwise the row is recomputed exactly from its
+ * full scores inside the call).
  * force_fallback: 0 normally; nonzero sends every row with more than k
  * candidates through the exact recomputation (a test of that path).
- * Supported: Hi = 4, Di = 128, S <= 32768, 1 <= k <= 2048.
+ * Supported: Hi = 4, Di = 128, 1 <= k <= 2048, and S <= 32768 or (T <= 4 and
+ * S <= 2^24).
  * Workspace: dsa_indexer_topk_workspace_size() bytes (it includes room for
  * the candidates and for the recomputed rows' scores).
  * ------------------------------------------------------------------------ */

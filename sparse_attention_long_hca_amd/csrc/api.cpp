@@ -431,9 +431,10 @@ int dsa_indexer_topk(const void* q_idx, const void* k_idx, const float* w, const
   if (!q_idx || !k_idx || !w || !idx) return fail(SA_ERR_NULL, "%s: q_idx, k_idx, w, idx must be non-NULL", fn);
   if (B <= 0 || T <= 0 || S <= 0 || Hi <= 0 || Di <= 0 || k <= 0) return fail(SA_ERR_SHAPE, "%s: sizes must be > 0", fn);
   if (Hi != 4 || Di != 128) return fail(SA_ERR_UNSUPPORTED, "%s: supported Hi = 4, Di = 128", fn);
-  if (S > 32768) return fail(SA_ERR_UNSUPPORTED, "%s: S must be <= 32768", fn);
+  if (S > 32768 && (T > 4 || S > ((int64_t)1 << 24)))
+    return fail(SA_ERR_UNSUPPORTED, "%s: S must be <= 32768, or <= 2^24 with T <= 4", fn);
   if (k > 2048) return fail(SA_ERR_UNSUPPORTED, "%s: k must be <= 2048", fn);
-  if (B * T > 0x7fffffffLL || B * ((T + 63) / 64) * ((S + 1023) / 1024) > 0x7fffffffLL)
+  if (B * T > 0x7fffffffLL || B * ((T + 63) / 64) * ((S + 127) / 128) > 0x7fffffffLL)
     return fail(SA_ERR_SHAPE, "%s: too many rows", fn);
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w) || !aligned16(idx))
     return fail(SA_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);

@@ -52,10 +52,12 @@ __host__ __device__ inline int fused_rank(int64_t k) {
   return m + (9 * sd + 1) / 2 + 8;
 }
 
+constexpr int kCapL = 8192;  // candidates the long-row select holds per row
 constexpr int kMaxSeg = 128;  // chunks of the candidate launch per row (S / 256 at most)
 
 struct FusedLayout {
   size_t ks, sscore, thresh, cnt, fail, anyf, cand, total;
+  size_t comp, ctot;  // long rows only
 };
 
 // Candidate rows are pitched at Sp = S rounded up to even: a row whose last
@@ -69,7 +71,7 @@ static FusedLayout fused_layout(int64_t B, int64_t T, int64_t S) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int64_t Ss = S / kSample, rows = B * T;
   const int64_t nseg = (S + dsa_indexer_chunk(T) - 1) / dsa_indexer_chunk(T);
-  FusedLayout L;
+  FusedLayout L{};
   size_t off = 0;
   L.ks = off;
   off += al((size_t)(B * Ss) * 256);
@@ -89,9 +91,43 @@ static FusedLayout fused_layout(int64_t B, int64_t T, int64_t S) {
   return L;
 }
 
+// Long decode rows (T <= 4, S > 32768): candidates per chunk of the decode
+// indexer (dsa_indexer_dec_chunk() positions), rows pitched at the chunks'
+// total; the exact fallback's scores ([rows, S] fp32) reuse the area.  The
+// compacted candidates take kCapL entries per row, and their count a word.
+static bool fused_long(int64_t T, int64_t S) { return T <= 4 && S > kMaxS; }
+
+__host__ __device__ inline int64_t pad8(int64_t x) { return (x + 7) & ~(int64_t)7; }
+static FusedLayout fused_layout_long(int64_t B, int64_t T, int64_t S) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const int64_t rows = B * T, ch = dsa_indexer_dec_chunk();
+  const int64_t nch = (S + ch - 1) / ch;
+  FusedLayout L{};
+  size_t off = 0;
+  L.ks = off;  // unused: the sampled keys are scored in place
+  L.sscore = off;  // rows pitched at a multiple of 8 keys
+  off += al((size_t)(rows * pad8(S / kSample)) * 2);
+  L.thresh = off;
+  off += al((size_t)rows * 4);
+  L.cnt = off;  // rows pitched at a multiple of 8 counts
+  off += al((size_t)(rows * pad8(nch)) * 4);
+  L.fail = off;
+  off += al((size_t)rows * 4);
+  L.anyf = off;
+  off += 256;
+  L.comp = off;
+  off += al((size_t)(rows * kCapL) * 8);
+  L.ctot = off;
+  off += al((size_t)rows * 4);
+  L.cand = off;
+  off += al((size_t)(rows * nch * ch) * 8);
+  L.total = off;
+  return L;
+}
+
 size_t dsa_indexer_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k) {
   (void)k;
-  return fused_layout(B, T, S).total;
+  return fused_long(T, S) ? fused_layout_long(B, T, S).total : fused_layout(B, T, S).total;
 }
 
 struct FusedPtrs {
@@ -103,6 +139,9 @@ struct FusedPtrs {
   uint32_t* anyf;
   const uint2* cand;  // [rows, Sp]: segment c at c * chunk
   int64_t Ss, chunk, nseg, pitch;
+  int64_t spitch, cpitch;  // long rows: row pitches of skey and cnt (multiples of 8)
+  uint2* comp;              // long rows: [rows, kCapL] candidates in position order
+  uint32_t* ctot;           // long rows: [rows] candidate count
 };
 
 // ks[b, j] = k[b, 16j + 15]: 16 threads per 256-byte row.
@@ -336,11 +375,390 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
   }
 }
 
+// ---------------------------------------------------------------------------
+// Long decode rows.  Sampled keys: the decode indexer scores every 16th key
+// in place (no copy of the sampled keys) and stores the top 16 bits of their
+// keys.  Threshold: one 1024-thread workgroup per row, the r-th largest
+// sampled key from LDS histograms.
+// Compaction: the rows' candidates, scattered over per-chunk segments, are
+// packed in position order by many workgroups.  Select: one workgroup per row
+// over the row's packed candidates, loaded into LDS with one round of
+// coalesced loads (kFromScores: over the row's full scores, for the
+// rows flagged for the exact fallback): the k-th largest key K by four rounds
+// of 8-bit histograms, then every key above K and the lowest-position `need`
+// copies of K, written in position order.
+// ---------------------------------------------------------------------------
+
+// The r-th largest of the row's sampled keys above zero (top 16 bits), in
+// two rounds: a 4096-bin histogram of their top 12 bits, then a 16-bin one of
+// the low 4 bits of the keys in the chosen bin.  (Bins of 12 bits split the
+// keys finely enough that a wave's lanes rarely add to one bin together,
+// where 8-bit bins put most of a row in a handful of bins.  A score is
+// exactly zero wherever every head's product is negative, about one position
+// in sixteen: zero and negative scores are left out, and a row with fewer
+// than r samples above zero gets threshold 0.)
+__global__ __launch_bounds__(1024) void fused_thresh_long_kernel(DsaIndexerTopkParams p, FusedPtrs f) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4096];
+  __shared__ uint32_t scr[32];
+  __shared__ uint32_t res[4];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t b = row / p.T, i = row % p.T;
+  const int64_t base = p.q_pos ? p.q_pos[b] : 0;
+  if (blockIdx.x == 0 && tid == 0) *f.anyf = 0u;
+  if (tid == 0) f.fail[row] = 0u;
+  int64_t n = base + i + 1;
+  n = n < p.S ? n : p.S;
+  if (p.force_fallback) {  // no finite score reaches it: every long row takes the exact fallback
+    if (tid == 0) f.thresh[row] = 0xffffffffu;
+    return;
+  }
+  int64_t ns = (base + i + 1) / kSample;  // the row's sampled positions
+  ns = ns < f.Ss ? ns : f.Ss;
+  const uint32_t r = (uint32_t)fused_rank(p.topk);
+  if (n <= p.topk || ns <= (int64_t)r) {  // every visible position is a candidate
+    if (tid == 0) f.thresh[row] = 0u;
+    return;
+  }
+  // The row's keys, 8 per 16-byte load (the row is pitched at a multiple of
+  // 8): each pass issues 8 loads per thread together, 65536 keys.
+  const uint4* ss = reinterpret_cast<const uint4*>(f.skey + row * f.spitch);
+  const int64_t nv = (ns + 7) / 8;
+  auto key_of = [&](const uint4& v, int e, int64_t j) -> uint32_t {  // key e of the group at vector j (0: none)
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    const uint32_t k16 = (e & 1) ? w >> 16 : w & 0xffffu;
+    return 8 * j + e < ns ? k16 : 0u;
+  };
+  uint32_t V = 0u;
+  // Round 1: top 12 bits.  (Rows of up to 65536 samples keep their keys in
+  // registers for round 2.)
+  for (int j = tid; j < 4096; j += 1024) hist[j] = 0u;
+  __syncthreads();
+  uint4 v[8];
+  for (int64_t j0 = 0; j0 < nv; j0 += 8 * 1024) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = j0 + u * 1024 + tid;
+      v[u] = j < nv ? ss[j] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t k16 = key_of(v[u], e, j0 + u * 1024 + tid);
+        if (k16 > 0x8000u) atomicAdd(&hist[k16 >> 4], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t tot;
+  {
+    // Thread t owns bins [4096 - 4(t+1), 4096 - 4t) (thread 0: the top bins).
+    const uint4 v = reinterpret_cast<const uint4*>(hist)[1023 - tid];
+    const uint32_t local = v.x + v.y + v.z + v.w;
+    const uint32_t incl = block_inclusive_scan(local, scr, tot);
+    uint32_t above = incl - local;
+    const uint32_t c[4] = {v.w, v.z, v.y, v.x};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (above < r && above + c[e] >= r) {
+        res[0] = (uint32_t)(4 * (1023 - tid) + 3 - e);
+        res[1] = above;
+      }
+      above += c[e];
+    }
+  }
+  if (tot >= r) {  // uniform: tot comes from the block scan
+    __syncthreads();
+    const uint32_t b12 = res[0], need = r - res[1];
+    // Round 2: low 4 bits of the keys in bin b12.
+    if (tid < 16) hist[tid] = 0u;
+    __syncthreads();
+    for (int64_t j0 = 0; j0 < nv; j0 += 8 * 1024) {
+      if (nv > 8 * 1024) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t j = j0 + u * 1024 + tid;
+          v[u] = j < nv ? ss[j] : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t k16 = key_of(v[u], e, j0 + u * 1024 + tid);
+          if (k16 > 0x8000u && (k16 >> 4) == b12) atomicAdd(&hist[k16 & 15u], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t above = 0u;
+      for (int e = 15; e >= 0; --e) {
+        if (above < need && above + hist[e] >= need) V = ((b12 << 4) | (uint32_t)e) << 16;
+        above += hist[e];
+      }
+    }
+  }
+  if (tid == 0) f.thresh[row] = V;
+}
+
+// Compaction: workgroup (row, c) takes segments [256c, 256c + 256) of the
+// row, one per thread; its offset is the count of the segments before them,
+// and its entries go to comp[row * kCapL + offset ..] in position order (the
+// entries past kCapL are dropped: the select step sends such rows to the
+// exact fallback).  The workgroup holding the row's last segment writes the
+// row's total.  Spread over many CUs, the scattered segment reads overlap.
+constexpr int kCompSeg = 256;
+__global__ __launch_bounds__(kCompSeg) void fused_compact_long_kernel(DsaIndexerTopkParams p, FusedPtrs f) {
+  __shared__ uint32_t scr[32];
+  const int tid = threadIdx.x;
+  const int64_t nblk = (f.nseg + kCompSeg - 1) / kCompSeg;
+  const int64_t row = blockIdx.x / nblk, bk = blockIdx.x % nblk;
+  const int64_t b = row / p.T, i = row % p.T;
+  const int64_t base = p.q_pos ? p.q_pos[b] : 0;
+  int64_t n = base + i + 1;
+  n = n < p.S ? n : p.S;
+  if (n <= p.topk) return;  // the select step writes such rows directly
+  const int64_t nseg = (n + f.chunk - 1) / f.chunk;
+  const int64_t sg0 = bk * kCompSeg;
+  if (sg0 >= nseg) return;
+  const uint32_t* cnt = f.cnt + row * f.cpitch;
+  const uint2* cr = f.cand + row * f.pitch;
+  const int64_t sg = sg0 + tid;
+  // This thread's segment: count and first two entries, loaded together.
+  const uint32_t c = sg < nseg ? cnt[sg] : 0u;
+  const uint4 x = sg < nseg ? *reinterpret_cast<const uint4*>(cr + sg * f.chunk) : make_uint4(0u, 0u, 0u, 0u);
+  // Counts of the earlier segments (sg0 is a multiple of 8: 16-byte loads).
+  uint32_t before = 0u;
+  for (int64_t j = 8 * tid; j < sg0; j += 8 * kCompSeg) {
+    const uint4 a = *reinterpret_cast<const uint4*>(cnt + j), d = *reinterpret_cast<const uint4*>(cnt + j + 4);
+    before += a.x + a.y + a.z + a.w + d.x + d.y + d.z + d.w;
+  }
+  uint32_t off0;
+  block_inclusive_scan(before, scr, off0);
+  uint32_t tb;
+  const uint32_t o = off0 + block_inclusive_scan(c, scr, tb) - c;
+  uint2* dst = f.comp + row * kCapL;
+  if (c > 0u && o < (uint32_t)kCapL) dst[o] = make_uint2(x.x, x.y);
+  if (c > 1u && o + 1u < (uint32_t)kCapL) dst[o + 1u] = make_uint2(x.z, x.w);
+  for (uint32_t e = 2; e < c && o + e < (uint32_t)kCapL; ++e) dst[o + e] = cr[sg * f.chunk + e];
+  if (sg0 + kCompSeg >= nseg && tid == 0) f.ctot[row] = off0 + tb;
+}
+
+template <bool kFromScores>
+__global__ __launch_bounds__(1024) void fused_select_long_kernel(DsaIndexerTopkParams p, FusedPtrs f, const float* scores) {
+  __shared__ uint32_t ckey[kFromScores ? 1 : kCapL];
+  __shared__ uint32_t cpos[kFromScores ? 1 : kCapL];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+  __shared__ uint32_t scr[32];
+  __shared__ uint32_t bc[2];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t b = row / p.T, i = row % p.T;
+  const int64_t base = p.q_pos ? p.q_pos[b] : 0;
+  int64_t n = base + i + 1;
+  n = n < p.S ? n : p.S;
+  const int k = (int)p.topk;
+  int32_t* out = p.idx + row * p.topk;
+  uint32_t m;  // elements: candidates, or the row's visible positions
+  if constexpr (kFromScores) {
+    if (*f.anyf == 0u || f.fail[row] == 0u) return;
+    m = (uint32_t)n;
+  } else {
+    if (n <= k) {  // every visible position
+      for (int j = tid; j < k; j += 1024) out[j] = j < n ? j : -1;
+      return;
+    }
+    // The row's candidates, compacted in position order.
+    const uint32_t tot = f.ctot[row];
+    if (tot < (uint32_t)k || tot > (uint32_t)kCapL) {  // the exact fallback writes this row
+      if (tid == 0) {
+        f.fail[row] = 1u;
+        atomicOr(f.anyf, 1u);
+      }
+      return;
+    }
+    const uint2* src = f.comp + row * kCapL;
+    uint2 x[kCapL / 1024];
+#pragma unroll
+    for (int u = 0; u < kCapL / 1024; ++u) {
+      const uint32_t j = (uint32_t)(u * 1024 + tid);
+      x[u] = j < tot ? src[j] : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kCapL / 1024; ++u) {
+      const uint32_t j = (uint32_t)(u * 1024 + tid);
+      if (j < tot) {
+        ckey[j] = x[u].x;
+        cpos[j] = x[u].y;
+      }
+    }
+    __syncthreads();
+    m = tot;
+  }
+  auto key_at = [&](uint32_t j) -> uint32_t {
+    if constexpr (kFromScores)
+      return score_key(scores[row * p.S + j]);
+    else
+      return ckey[j];
+  };
+  uint32_t prefix = 0u, mask = 0u, need = (uint32_t)k;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int sh = 24 - 8 * pass;
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+    for (uint32_t j0 = 0; j0 < m; j0 += 1024) {
+      const uint32_t j = j0 + tid;
+      const uint32_t key = j < m ? key_at(j) : 0u;
+      lds_hist_add(hist, (j < m && (key & mask) == prefix) ? (key >> sh) & 255u : 256u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t bin, above, cnt;
+      wave_top_bin256(hist, need, &bin, &above, &cnt);
+      if (tid == 0) {
+        bc[0] = bin;
+        bc[1] = above;
+      }
+    }
+    __syncthreads();
+    prefix |= bc[0] << sh;
+    mask |= 0xffu << sh;
+    need -= bc[1];
+    __syncthreads();
+  }
+  // prefix is the k-th largest key K; keep every key above it and the
+  // `need` lowest-position copies of it.  Each thread walks a contiguous
+  // range of elements (position order).
+  const uint32_t K = prefix;
+  const uint32_t per = (m + 1023u) / 1024u, j0 = tid * per, j1 = j0 + per < m ? j0 + per : m;
+  uint32_t ties = 0u;
+  for (uint32_t j = j0; j < j1; ++j) ties += key_at(j) == K ? 1u : 0u;
+  uint32_t tt;
+  const uint32_t tie0 = block_inclusive_scan(ties, scr, tt) - ties;
+  uint32_t kept = 0u, tr = tie0;
+  for (uint32_t j = j0; j < j1; ++j) {
+    const uint32_t key = key_at(j);
+    if (key > K) {
+      ++kept;
+    } else if (key == K) {
+      if (tr < need) ++kept;
+      ++tr;
+    }
+  }
+  uint32_t kt;
+  uint32_t ob = block_inclusive_scan(kept, scr, kt) - kept;
+  tr = tie0;
+  for (uint32_t j = j0; j < j1; ++j) {
+    const uint32_t key = key_at(j);
+    bool keep = key > K;
+    if (key == K) {
+      keep = tr < need;
+      ++tr;
+    }
+    if (keep) {
+      if constexpr (kFromScores)
+        out[ob] = (int32_t)j;
+      else
+        out[ob] = (int32_t)cpos[j];
+      ++ob;
+    }
+  }
+}
+
+static hipError_t launch_fused_long(const DsaIndexerTopkParams& p, hipStream_t stream) {
+  const FusedLayout L = fused_layout_long(p.B, p.T, p.S);
+  char* ws = reinterpret_cast<char*>(p.ws);
+  const int64_t Ss = p.S / kSample, rows = p.B * p.T, ch = dsa_indexer_dec_chunk();
+  FusedPtrs f{};
+  f.ks = nullptr;
+  f.skey = reinterpret_cast<const uint16_t*>(ws + L.sscore);
+  f.thresh = reinterpret_cast<uint32_t*>(ws + L.thresh);
+  f.cnt = reinterpret_cast<const uint32_t*>(ws + L.cnt);
+  f.fail = reinterpret_cast<uint32_t*>(ws + L.fail);
+  f.anyf = reinterpret_cast<uint32_t*>(ws + L.anyf);
+  f.cand = reinterpret_cast<const uint2*>(ws + L.cand);
+  f.Ss = Ss;
+  f.chunk = ch;
+  f.nseg = (p.S + ch - 1) / ch;
+  f.pitch = f.nseg * ch;
+  f.spitch = pad8(Ss);
+  f.cpitch = pad8(f.nseg);
+  f.comp = reinterpret_cast<uint2*>(ws + L.comp);
+  f.ctot = reinterpret_cast<uint32_t*>(ws + L.ctot);
+  float* fb = reinterpret_cast<float*>(ws + L.cand);
+  hipError_t e;
+  // 1. Sampled keys: every 16th key scored in place (ratio-16 visibility),
+  // top 16 bits of the score keys.
+  if (Ss > 0) {
+    DsaIndexerParams sp{};
+    sp.q = p.q;
+    sp.k = p.k;
+    sp.w = p.w;
+    sp.q_pos = p.q_pos;
+    sp.keys16 = const_cast<uint16_t*>(f.skey);
+    sp.B = p.B;
+    sp.T = p.T;
+    sp.S = Ss;
+    sp.ratio = kSample;
+    sp.dec_sample = 1;
+    sp.k_rows = p.S;
+    if ((e = launch_dsa_indexer(sp, stream)) != hipSuccess) return e;
+  }
+  // 2. Thresholds (also clears the fallback flags).
+  hipLaunchKernelGGL(fused_thresh_long_kernel, dim3((uint32_t)rows), dim3(1024), 0, stream, p, f);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 3. Candidates, per chunk in position order.
+  DsaIndexerParams ep{};
+  ep.q = p.q;
+  ep.k = p.k;
+  ep.w = p.w;
+  ep.q_pos = p.q_pos;
+  ep.B = p.B;
+  ep.T = p.T;
+  ep.S = p.S;
+  ep.ratio = 1;
+  ep.thresh = f.thresh;
+  ep.cnt = const_cast<uint32_t*>(f.cnt);
+  ep.cand = const_cast<uint2*>(f.cand);
+  ep.cand_pitch = f.pitch;
+  ep.topk = p.topk;
+  ep.dec_cand = 1;
+  if ((e = launch_dsa_indexer(ep, stream)) != hipSuccess) return e;
+  // 4. Compaction, then the exact selection over the candidates.
+  hipLaunchKernelGGL(fused_compact_long_kernel, dim3((uint32_t)(rows * ((f.nseg + kCompSeg - 1) / kCompSeg))),
+                     dim3(kCompSeg), 0, stream, p, f);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(fused_select_long_kernel<false>, dim3((uint32_t)rows), dim3(1024), 0, stream, p, f, fb);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 5. Exact fallback for flagged rows: their full scores, then the selection
+  // over them (both return at once when no row is flagged).
+  DsaIndexerParams fp{};
+  fp.q = p.q;
+  fp.k = p.k;
+  fp.w = p.w;
+  fp.q_pos = p.q_pos;
+  fp.scores = fb;
+  fp.B = p.B;
+  fp.T = p.T;
+  fp.S = p.S;
+  fp.ratio = 1;
+  fp.row_flag = f.fail;
+  fp.any_flag = f.anyf;
+  fp.dec_filter = 1;
+  if ((e = launch_dsa_indexer(fp, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL(fused_select_long_kernel<true>, dim3((uint32_t)rows), dim3(1024), 0, stream, p, f, fb);
+  return hipGetLastError();
+}
+
 hipError_t launch_dsa_indexer_topk(const DsaIndexerTopkParams& p, hipStream_t stream) {
+  if (fused_long(p.T, p.S)) return launch_fused_long(p, stream);
   const FusedLayout L = fused_layout(p.B, p.T, p.S);
   char* ws = reinterpret_cast<char*>(p.ws);
   const int64_t Ss = p.S / kSample, rows = p.B * p.T;
-  FusedPtrs f;
+  FusedPtrs f{};
   f.ks = reinterpret_cast<const bf16_t*>(ws + L.ks);
   f.skey = reinterpret_cast<const uint16_t*>(ws + L.sscore);
   f.thresh = reinterpret_cast<uint32_t*>(ws + L.thresh);

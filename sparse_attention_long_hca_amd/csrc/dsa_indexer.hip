@@ -371,9 +371,23 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
 // eight waves per CU keep a tile each in flight.
 constexpr int kIdxDecTiles = 2;  // 64-position tiles per workgroup (1, 2, 4, 8, 16 measured: 2 is fastest)
 
-__global__ __launch_bounds__(64) void dsa_indexer_dec_kernel(DsaIndexerParams p, int n_chunks) {
-  const int b = (int)(blockIdx.x / (uint32_t)n_chunks);
-  const int kc = (int)(blockIdx.x % (uint32_t)n_chunks);
+// Modes of the decode kernel.  kDecScores stores the scores.  kDecCand is the
+// candidate mode of the fused indexer -> top-k for long decode rows: instead
+// of scores, every score whose key reaches the row's threshold is written as
+// (key, position) to the row's segment for this workgroup's chunk
+// (cand[row * cand_pitch + kc * kChunk ..], room for the whole chunk), in
+// ascending position order, and the count to cnt[row * cnt_pitch + kc]
+// (cnt_pitch: n_chunks rounded up to a multiple of 8, so that a reader can
+// load a row's counts 16 bytes at a time).
+// kDecSample scores a strided subset of the keys: position s (of S = the
+// sample count) is key row s * ratio + ratio - 1 of a k_idx with k_rows rows
+// per batch, visible under the ratio rule, and keys16 (rows pitched at S
+// rounded up to a multiple of 8) receives the top 16 bits of the score's key.
+constexpr int kDecScores = 0, kDecCand = 1, kDecSample = 2;
+
+template <int kDec>
+__device__ __forceinline__ void dsa_indexer_dec_chunk(const DsaIndexerParams& p, int b, int kc, int n_chunks) {
+  constexpr bool kCand = kDec == kDecCand;
   const int T = (int)p.T, S = (int)p.S;
   const int base = p.q_pos ? (int)p.q_pos[b] : 0;
   const int64_t ratio = p.ratio;
@@ -391,9 +405,9 @@ __global__ __launch_bounds__(64) void dsa_indexer_dec_kernel(DsaIndexerParams p,
   const int lane = threadIdx.x & 63;
   const int L = lane & 15, g = lane >> 4;
   const bf16_t* qI = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)b * T * kIdxHi * kIdxDi;
-  const bf16_t* kI = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * S * kIdxDi;
+  const int64_t k_rows = kDec == kDecSample ? p.k_rows : (int64_t)S;
+  const bf16_t* kI = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * k_rows * kIdxDi;
   const float* wgt = p.w + (int64_t)b * T * kIdxHi;
-  float* out = p.scores + (int64_t)b * T * S;
 
   // A operand: row (query L/4, head L%4), dims g*8 + 32*ks (zero for rows past T).
   i16x8_t qa[4];
@@ -412,7 +426,11 @@ __global__ __launch_bounds__(64) void dsa_indexer_dec_kernel(DsaIndexerParams p,
 #pragma unroll
   for (int h = 0; h < 4; ++h) wq[h] = g < T ? wgt[(int64_t)g * kIdxHi + h] : 0.f;
   const int plim = g < T ? lim(g) : -1;
-  float* orow = out + (int64_t)g * S;
+  const int64_t crow = (int64_t)b * T + g;  // this lane's output row
+  // Candidate mode: threshold of this lane's query row (0xffffffff, which no
+  // key reaches, for rows that keep every visible position or lie past T).
+  const uint32_t thr = (kCand && g < T && plim + 1 > (int)p.topk) ? p.thresh[crow] : 0xffffffffu;
+  uint32_t c_run = 0u;
 
   // B operands of one tile: [nb][ks], 16 bytes each.  Positions past the
   // chunk's stop load the chunk's first row (finite, never stored).
@@ -421,7 +439,9 @@ __global__ __launch_bounds__(64) void dsa_indexer_dec_kernel(DsaIndexerParams p,
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int s = s0 + nb * 16 + L;
-      const bf16_t* row = kI + (int64_t)(s < s_stop ? s : s_begin) * kIdxDi + g * 8;
+      const int sv = s < s_stop ? s : s_begin;
+      const int64_t kr = kDec == kDecSample ? (int64_t)sv * ratio + (ratio - 1) : (int64_t)sv;
+      const bf16_t* row = kI + kr * kIdxDi + g * 8;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) bt[nb][ks] = *reinterpret_cast<const uint4*>(row + ks * 32);
     }
@@ -445,10 +465,38 @@ __global__ __launch_bounds__(64) void dsa_indexer_dec_kernel(DsaIndexerParams p,
   };
   auto store = [&](int tile) __attribute__((always_inline)) {
     const int s0 = s_begin + tile * kIdxKTile;
+    if constexpr (kCand) {
+      // Positions s0 + 16nb + L: for each nb in turn, the 16 lanes of query g
+      // take slots in L order (a scan over the 16 lanes), so a segment lists
+      // its candidates in ascending position order.
+      uint2* seg = p.cand + crow * p.cand_pitch + s_begin;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int s = s0 + nb * 16 + L;
-      if (s <= plim && s < s_stop) orow[s] = sc[nb];
+      for (int nb = 0; nb < 4; ++nb) {
+        const int s = s0 + nb * 16 + L;
+        const uint32_t key = score_key(sc[nb]);
+        const uint32_t fl = (s <= plim && s < s_stop && key >= thr) ? 1u : 0u;
+        uint32_t x = fl;
+        x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true);
+        x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);
+        x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);
+        x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);
+        if (fl) seg[c_run + x - 1u] = make_uint2(key, (uint32_t)s);
+        c_run += (uint32_t)__shfl(x, 15, 16);
+      }
+    } else if constexpr (kDec == kDecSample) {
+      uint16_t* o16 = p.keys16 + crow * (((int64_t)S + 7) & ~(int64_t)7);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int s = s0 + nb * 16 + L;
+        if (s <= plim && s < s_stop) o16[s] = (uint16_t)(score_key(sc[nb]) >> 16);
+      }
+    } else {
+      float* orow = p.scores + crow * S;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int s = s0 + nb * 16 + L;
+        if (s <= plim && s < s_stop) orow[s] = sc[nb];
+      }
     }
   };
 
@@ -463,7 +511,34 @@ __global__ __launch_bounds__(64) void dsa_indexer_dec_kernel(DsaIndexerParams p,
     compute(b1);
     store(tile + 1);
   }
+  if constexpr (kCand) {
+    if (L == 0 && g < T) p.cnt[crow * (((int64_t)n_chunks + 7) & ~(int64_t)7) + kc] = c_run;
+  }
 }
+
+// One chunk per workgroup.
+template <int kDec>
+__global__ __launch_bounds__(64) void dsa_indexer_dec_kernel(DsaIndexerParams p, int n_chunks) {
+  dsa_indexer_dec_chunk<kDec>(p, (int)(blockIdx.x / (uint32_t)n_chunks), (int)(blockIdx.x % (uint32_t)n_chunks),
+                              n_chunks);
+}
+
+// Row filter (scores): nothing runs unless *any_flag != 0; then a bounded grid
+// strides over the chunks of the batches holding a flagged row.  A call in
+// which no row is flagged costs one small launch, not one workgroup per chunk.
+constexpr uint32_t kIdxDecFilterGrid = 2048;
+__global__ __launch_bounds__(64) void dsa_indexer_dec_filtered_kernel(DsaIndexerParams p, int n_chunks) {
+  if (*p.any_flag == 0u) return;
+  const uint32_t nblk = (uint32_t)p.B * (uint32_t)n_chunks;
+  for (uint32_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int b = (int)(blk / (uint32_t)n_chunks);
+    bool run = false;
+    for (int qi = 0; qi < (int)p.T; ++qi) run |= p.row_flag[(int64_t)b * p.T + qi] != 0u;
+    if (run) dsa_indexer_dec_chunk<kDecScores>(p, b, (int)(blk % (uint32_t)n_chunks), n_chunks);
+  }
+}
+
+int64_t dsa_indexer_dec_chunk() { return (int64_t)kIdxDecTiles * kIdxKTile; }
 
 int64_t dsa_indexer_chunk(int64_t T) {
   return T <= kIdxQPerWave ? (int64_t)kIdxDecodeTiles * kIdxKTile : (int64_t)kIdxTilesPerChunk * kIdxKTile;
@@ -471,11 +546,21 @@ int64_t dsa_indexer_chunk(int64_t T) {
 
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
   if (p.T <= kIdxQPerWave) {
-    // Decode: one query tile, short chunks of positions.
-    // (Candidate mode and filtered launches take the staged kernel.)
-    if (p.T <= 4 && !p.cand && !p.row_flag && !p.keys16) {
-      const int64_t n_chunks = (p.S + kIdxDecTiles * kIdxKTile - 1) / (kIdxDecTiles * kIdxKTile);
-      hipLaunchKernelGGL(dsa_indexer_dec_kernel, dim3((uint32_t)(p.B * n_chunks)), dim3(64), 0, stream, p, (int)n_chunks);
+    // Decode: one query tile, short chunks of positions.  (The staged
+    // kernel's candidate, filtered and key modes serve the fused indexer ->
+    // top-k of rows up to 32768 positions.)
+    const int64_t dec_chunks = (p.S + kIdxDecTiles * kIdxKTile - 1) / (kIdxDecTiles * kIdxKTile);
+    const dim3 dgrid((uint32_t)(p.B * dec_chunks));
+    if (p.T <= 4 && p.dec_cand) {
+      hipLaunchKernelGGL(dsa_indexer_dec_kernel<kDecCand>, dgrid, dim3(64), 0, stream, p, (int)dec_chunks);
+    } else if (p.T <= 4 && p.dec_sample) {
+      hipLaunchKernelGGL(dsa_indexer_dec_kernel<kDecSample>, dgrid, dim3(64), 0, stream, p, (int)dec_chunks);
+    } else if (p.T <= 4 && p.dec_filter) {
+      const uint32_t n = (uint32_t)(p.B * dec_chunks);
+      hipLaunchKernelGGL(dsa_indexer_dec_filtered_kernel, dim3(n < kIdxDecFilterGrid ? n : kIdxDecFilterGrid), dim3(64),
+                         0, stream, p, (int)dec_chunks);
+    } else if (p.T <= 4 && !p.cand && !p.row_flag && !p.keys16) {
+      hipLaunchKernelGGL(dsa_indexer_dec_kernel<kDecScores>, dgrid, dim3(64), 0, stream, p, (int)dec_chunks);
     } else {
       const int chunk = kIdxDecodeTiles * kIdxKTile;
       const int64_t n_chunks = (p.S + chunk - 1) / chunk;

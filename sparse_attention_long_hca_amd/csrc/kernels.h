@@ -121,7 +121,23 @@ struct DsaIndexerParams {
   uint32_t* cnt;
   uint2* cand;
   int64_t cand_pitch;
+  // Decode candidate mode (dec_cand != 0, T <= 4): the register-operand decode
+  // kernel writes each row's candidates per chunk of dsa_indexer_dec_chunk()
+  // positions in ascending position order (cand, cand_pitch, thresh, topk as
+  // above, no pad entries); the count of chunk c goes to
+  // cnt[row * cnt_pitch + c], cnt_pitch = n_chunks rounded up to a multiple
+  // of 8 (n_chunks = ceil(S / dsa_indexer_dec_chunk())).
+  int dec_cand;
   int64_t topk;
+  // Decode sampled-key mode (dec_sample != 0, T <= 4, keys16 set): position
+  // s of S (the sample count) is key row s*ratio + ratio - 1 of a k with
+  // k_rows rows per batch, visible under the ratio rule; keys16 as below but
+  // with rows pitched at S rounded up to a multiple of 8.
+  int dec_sample;
+  int64_t k_rows;
+  // Decode row filter (dec_filter != 0, T <= 4, row_flag and any_flag set):
+  // the scores of the batches holding a flagged row, from a bounded grid.
+  int dec_filter;
   // Key mode (keys16 != NULL): instead of scores, keys16[b,i,s] (same layout)
   // receives the top 16 bits of the score's order-preserving key.
   uint16_t* keys16;
@@ -132,6 +148,7 @@ struct DsaIndexerParams {
 };
 hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream);
 int64_t dsa_indexer_chunk(int64_t T);  // positions per workgroup for T queries
+int64_t dsa_indexer_dec_chunk();       // positions per workgroup of the decode kernel
 
 // ---- dsa_topk ---------------------------------------------------------------
 struct DsaTopkParams {

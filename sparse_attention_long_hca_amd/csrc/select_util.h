@@ -48,6 +48,32 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// hist[bin] += 1 for every lane of the wave with bin < 256.  When the lowest
+// active lane's bin is shared by at least 16 lanes (scores near a row's top
+// fall in few high-byte bins, where lane-by-lane atomics to one address would
+// serialise) the lanes of each distinct bin are counted with one LDS atomic;
+// otherwise every lane adds its own.  Call from uniform control flow.
+__device__ __forceinline__ void lds_hist_add(uint32_t* hist, uint32_t bin) {
+  const int lane = threadIdx.x & 63;
+  uint64_t act = __ballot(bin < 256u);
+  if (act == 0ull) return;
+  {
+    const int ld = __builtin_ctzll(act);
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, ld);
+    if (__popcll(__ballot(bin == lb)) < 16) {
+      if (bin < 256u) atomicAdd(&hist[bin], 1u);
+      return;
+    }
+  }
+  while (act) {
+    const int ld = __builtin_ctzll(act);
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, ld);
+    const uint64_t m = __ballot(bin == lb);
+    if (lane == ld) atomicAdd(&hist[lb], (uint32_t)__popcll(m));
+    act &= ~m;
+  }
+}
+
 // One wave, 256 bins in LDS (16-byte aligned): the bin where the count from
 // the top reaches need (1 <= need <= total).  *bin, *above (count in higher
 // bins) and *count (the bin's count) are uniform over the wave.

@@ -224,7 +224,10 @@ def test_indexer_topk_validation(sa):
     # null, shape, unsupported, alignment, workspace
     assert L.dsa_indexer_topk(None, 4096, 4096, None, 4096, 1, 4, 4, 4, 128, 2, 0, ws, big, None) == SA_ERR_NULL
     assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 0, 4, 4, 128, 2, 0, ws, big, None) == SA_ERR_SHAPE
-    assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 4, 40000, 4, 128, 2, 0, ws, big, None) == SA_ERR_UNSUPPORTED
+    # rows longer than 32768 positions: decode shapes only (T <= 4), up to 2^24 positions
+    assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 5, 40000, 4, 128, 2, 0, ws, big, None) == SA_ERR_UNSUPPORTED
+    assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 1, (1 << 24) + 1, 4, 128, 2, 0, ws, big, None) == SA_ERR_UNSUPPORTED
+    assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 4, 40000, 4, 128, 2, 0, ws, 1, None) == SA_ERR_WORKSPACE
     assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 4, 4, 4, 128, 4096, 0, ws, big, None) == SA_ERR_UNSUPPORTED
     assert L.dsa_indexer_topk(4096, 4096, 4096, None, 4096, 1, 4, 4, 8, 128, 2, 0, ws, big, None) == SA_ERR_UNSUPPORTED
     assert L.dsa_indexer_topk(4100, 4096, 4096, None, 4096, 1, 4, 4, 4, 128, 2, 0, ws, big, None) == SA_ERR_ALIGN
@@ -235,6 +238,8 @@ def test_indexer_topk_validation(sa):
     # the workspace holds a candidate slot (8 bytes) per row and position; the
     # recomputed rows' scores reuse that area
     assert L.dsa_indexer_topk_workspace_size(1, 32768, 32768, 2048) >= 32768 * 32768 * 8
+    # decode-shaped long rows keep candidates per 128-position chunk and the full scores for recomputed rows
+    assert L.dsa_indexer_topk_workspace_size(4, 1, 1 << 20, 2048) >= 4 * (1 << 20) * 4
 
 
 def test_sparse_attention_bwd_validation(sa):

@@ -354,6 +354,37 @@ def test_indexer_topk_odd_width_all_candidate_rows(B, T, S, kk, q_pos, zero_w):
         assert np.array_equal(got.cpu().numpy(), exp)
 
 
+@pytest.mark.parametrize("B,T,S,kk,q_pos,zero_w", [(2, 1, 70000, 2048, [69999, 40000], False),
+                                                    (1, 3, 100000, 64, [99997], False),
+                                                    (2, 2, 40000, 2048, [39998, 100], False),
+                                                    (3, 1, 50001, 7, [50000, 33000, 1], False),
+                                                    (1, 4, 40000, 300, [39996], True),
+                                                    (4, 1, 1 << 20, 2048, [(1 << 20) - 1, 900000, 524287, 40000], False)])
+@pytest.mark.parametrize("force", [False, True])
+def test_indexer_topk_long_decode_rows(B, T, S, kk, q_pos, zero_w, force):
+    """Decode-shaped calls with rows longer than 32768 positions (up to the 1M context): the candidate path
+    of the decode indexer and the per-row select must return exactly the separate calls' indices; rows with
+    at most k visible positions keep all; w = 0 (every score 0.0, more candidates than the select holds) and
+    force=True take the exact recomputation from the full scores."""
+    sa = require_gpu()
+    print(f"[fused long] B={B} T={T} S={S} k={kk} q_pos={q_pos} zero_w={zero_w} force={force}", flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(90 + T + kk)
+    tqi = (torch.randn((B, T, 4, 128), generator=g, device=DEV) * 128 ** -0.5).to(torch.bfloat16)
+    tki = (torch.randn((B, S, 128), generator=g, device=DEV) * 128 ** -0.5).to(torch.bfloat16)
+    tw = torch.rand((B, T, 4), generator=g, device=DEV)
+    if zero_w:
+        tw.zero_()
+    qp = torch.tensor(q_pos, dtype=torch.int64, device=DEV)
+    want = sa.dsa_topk(sa.dsa_indexer_scores(tqi, tki, tw, q_pos=qp), kk, q_pos=qp)
+    got = sa.dsa_indexer_topk(tqi, tki, tw, kk, q_pos=qp, force_fallback=force)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    if zero_w:
+        n = min(S, q_pos[0] + 1)
+        assert torch.equal(got[0, 0, :min(n, kk)].cpu(), torch.arange(min(n, kk), dtype=torch.int32))
+
+
 def test_indexer_topk_32768_top2048():
     """Fused call at the prefill workload's size: identical to the separate calls on every row, and on
     sampled rows equal to the oracle's selection outside the 1e-6 tie band."""
