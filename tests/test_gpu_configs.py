@@ -28,7 +28,21 @@ pytestmark = pytest.mark.gpu
 BLK = WIN = 128
 
 
+def _spread_rows(T, n, seed, edges):
+    """At least n distinct rows: the given edges, an even spread over [0, T) and seeded random rows."""
+    rows = set(int(x) for x in edges)
+    rows |= set(int(x) for x in np.linspace(0, T - 1, n // 2).round())
+    g = np.random.default_rng(seed)
+    while len(rows) < n:
+        rows.add(int(g.integers(0, T)))
+    return sorted(rows)
+
+
 def _hca_prefill_case(sa, sigma, seed, dqk=512):
+    """Sampled outputs of the full prefill: 256+ spread rows (block and window edges, first and last
+    tokens) of three heads against the oracle's prefill (its own compression of those heads), and every
+    head of four rows against the oracle's decode over the GPU's compressed cache and the rows' windows
+    (decode at position t equals prefill row t)."""
     T, H, d = 32768, 64, 512
     q = synth.torch_normal((1, H, T, dqk), sigma, torch.bfloat16, seed, DEV)
     k = synth.torch_normal((1, H, T, dqk), sigma, torch.bfloat16, seed + 1, DEV)
@@ -37,9 +51,8 @@ def _hca_prefill_case(sa, sigma, seed, dqk=512):
     vc = sa.hca_compress(v, BLK)
     o, lse = sa.hca_attention_fwd(sa.HCA_PREFILL, q, k, v, kc, vc, BLK, WIN, return_lse=True)
     torch.cuda.synchronize()
-    rows = [0, 1, 126, 127, 128, 254, 255, 256, 383, 1000, 4097, 16384, 20000, 32639, 32640, 32767]
-    g = np.random.default_rng(seed)
-    rows += [int(x) for x in g.integers(0, T, size=8)]
+    edges = [0, 1, 126, 127, 128, 254, 255, 256, 383, 1000, 4097, 16384, 20000, 32639, 32640, 32767]
+    rows = _spread_rows(T, 256, seed, edges)
     worst = 0.0
     for h in (0, 37, 63):
         qh, kh, vh = f64(q[:, h:h + 1]), f64(k[:, h:h + 1]), f64(v[:, h:h + 1])
@@ -48,6 +61,19 @@ def _hca_prefill_case(sa, sigma, seed, dqk=512):
         got = f64(o[:, h:h + 1, rows])
         worst = max(worst, max_abs_err(got, ow))
         assert max_abs_err(f64(lse[:, h:h + 1, rows]), lw) <= 1e-2
+        print(f"[hca prefill full] head {h}: {len(rows)} rows, max err {worst:.3e}", flush=True)
+    kch, vch = f64(kc), f64(vc)
+    for t in (127, 128, 20000, T - 1):
+        lo = max(0, t - WIN + 1)
+        ring_k = np.zeros((1, H, WIN, dqk))
+        ring_v = np.zeros((1, H, WIN, d))
+        pos = np.arange(lo, t + 1)
+        ring_k[0][:, pos % WIN] = f64(k[0, :, lo:t + 1])
+        ring_v[0][:, pos % WIN] = f64(v[0, :, lo:t + 1])
+        ow, lw = oracle.hca_attention_decode(f64(q[:, :, t]), kch, vch, ring_k, ring_v, [t], BLK, WIN)
+        worst = max(worst, max_abs_err(f64(o[:, :, t]), ow))
+        assert max_abs_err(f64(lse[:, :, t]), lw) <= 1e-2, t
+    print(f"[hca prefill full] all 64 heads of 4 rows: max err {worst:.3e}", flush=True)
     del q, k, v, kc, vc, o, lse
     torch.cuda.empty_cache()
     return worst
@@ -156,10 +182,13 @@ def test_dsa_prefill_32768_top2048(sigma):
     idx = sa.dsa_topk(sc, kk)
     o, lse = sa.dsa_sparse_attention_fwd(q, k, v, idx, return_lse=True)
     torch.cuda.synchronize()
-    rows = [0, 1, 2046, 2047, 2048, 2049, 4095, 8191, 8192, 10000, 16383, 16384, 32767]
-    rows += [int(x) for x in np.random.default_rng(1501).integers(2048, T, size=6)]
+    # 256 spread rows at the workload's own distribution, 96 at unit variance (every row checks all 64 heads)
+    edges = [0, 1, 2046, 2047, 2048, 2049, 4095, 8191, 8192, 10000, 16383, 16384, 32767]
+    rows = _spread_rows(T, 256 if sigma < 1.0 else 96, 1501, edges)
     ki_h, q_h, k_h, v_h = f64(ki), None, f64(k), f64(v)
-    for i in rows:
+    for n_done, i in enumerate(rows):
+        if n_done % 64 == 0:
+            print(f"[dsa prefill full] sigma={sigma}: row {n_done} of {len(rows)}", flush=True)
         sc_row = sc[0, i, : i + 1].cpu().numpy().astype(np.float64)
         want_sc = oracle.dsa_indexer_scores(f64(qi[:, i:i + 1]), ki_h[:, : i + 1], f64(w[:, i:i + 1]), q_pos=[i])[0, 0]
         assert np.max(np.abs(sc_row - want_sc)) <= 2e-6, i
