@@ -304,29 +304,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       pv32_acc<2, 2, true>(av, bp, dos[hw], ad, nb0);
     }
     wait_lgkmcnt0();
-    // Lane l holds dim 64w + 32nb + l%32 of entries 32t + 8(j/4) + 4q + j%4.
-    // Values j and j+1 (entries E, E+1) are paired across lanes l, l^1: the
-    // even lane stores dims (l, l+1) of entry E, the odd lane dims (l-1, l)
-    // of entry E+1, so every store writes 64 contiguous bytes of 4 rows.
+    // Lane l holds dims 64w + l%32 (ak[0]) and 64w + 32 + l%32 (ak[1]) of
+    // entries 32t + 8(j/4) + 4q + j%4.  Lanes l, l^1 trade one value per j:
+    // the even lane then stores dims (l, l+1) and the odd lane dims
+    // (32 + l - 1, 32 + l) of the same entry, so each half-wave writes the 128
+    // contiguous bytes (one cache line) of its entry's 64 dims per store.
     const bool odd = lane & 1;
-    const int dcol = 64 * wave + (lane & 30);
+    const int dcol = 64 * wave + (lane & 30) + (odd ? 32 : 0);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        const int jj = 32 * t + 8 * (j >> 2) + 4 * qh + (j & 3) + (odd ? 1 : 0);
-        const int64_t e = tl * kk + jj;
-        const bool live = jj < kk;
-        const float k0 = ak[nb][j] * p.scale, k1 = ak[nb][j + 1] * p.scale;
-        const float kx = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? k0 : k1), 0xb1, 0xf, 0xf, false));
-        const float v0 = av[nb][j], v1 = av[nb][j + 1];
-        const float vx = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? v0 : v1), 0xb1, 0xf, 0xf, false));
-        const int d = dcol + 32 * nb;
-        uint16_t* rk = (live ? p.gk + e * kBwD : discard_k) + d;
-        uint16_t* rv = (live ? p.gv + e * kBwD : discard_v) + d;
-        *reinterpret_cast<uint32_t*>(rk) = odd ? pack_bf16x2(kx, k1) : pack_bf16x2(k0, kx);
-        *reinterpret_cast<uint32_t*>(rv) = odd ? pack_bf16x2(vx, v1) : pack_bf16x2(v0, vx);
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int jj = 32 * t + 8 * (j >> 2) + 4 * qh + (j & 3);
+      const int64_t e = tl * kk + jj;
+      const bool live = jj < kk;
+      const float k0 = ak[0][j] * p.scale, k1 = ak[1][j] * p.scale;
+      const float kx = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? k0 : k1), 0xb1, 0xf, 0xf, false));
+      const float v0 = av[0][j], v1 = av[1][j];
+      const float vx = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? v0 : v1), 0xb1, 0xf, 0xf, false));
+      uint16_t* rk = (live ? p.gk + e * kBwD : discard_k) + dcol;
+      uint16_t* rv = (live ? p.gv + e * kBwD : discard_v) + dcol;
+      *reinterpret_cast<uint32_t*>(rk) = odd ? pack_bf16x2(kx, k1) : pack_bf16x2(k0, kx);
+      *reinterpret_cast<uint32_t*>(rv) = odd ? pack_bf16x2(vx, v1) : pack_bf16x2(v0, vx);
+    }
     lds_barrier();  // the stage's buffer is free for the load two tiles on
   }
 }
@@ -348,19 +346,64 @@ __global__ __launch_bounds__(256) void dsa_sparse_bwd_count_kernel(DsaSparseBwdP
 }
 
 // Exclusive offsets of the counts (one workgroup): off[0..n], cursor = off.
+// Each thread takes a run of a multiple of 32 counts, loaded 32 at a time
+// (eight 16-byte loads in flight together; cnt, off and cursor are 16-byte
+// aligned) and written back the same way.
 __global__ __launch_bounds__(1024) void dsa_sparse_bwd_scan_kernel(const uint32_t* cnt, uint32_t* off, uint32_t* cursor,
                                                                    int64_t n) {
   __shared__ uint32_t scratch[32];
-  const int64_t per = (n + 1023) / 1024;
+  const int64_t per = ((n + 1023) / 1024 + 31) & ~(int64_t)31;
   const int64_t i0 = threadIdx.x * per, i1 = min(n, i0 + per);
+  auto load32 = [&](int64_t i, uint32_t (&c)[32]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = i + 4 * u;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (j + 4 <= i1) {
+        x = *reinterpret_cast<const uint4*>(cnt + j);
+      } else {
+        if (j < i1) x.x = cnt[j];
+        if (j + 1 < i1) x.y = cnt[j + 1];
+        if (j + 2 < i1) x.z = cnt[j + 2];
+      }
+      c[4 * u] = x.x;
+      c[4 * u + 1] = x.y;
+      c[4 * u + 2] = x.z;
+      c[4 * u + 3] = x.w;
+    }
+  };
   uint32_t local = 0;
-  for (int64_t i = i0; i < i1; ++i) local += cnt[i];
+  for (int64_t i = i0; i < i1; i += 32) {
+    uint32_t c[32];
+    load32(i, c);
+#pragma unroll
+    for (int u = 0; u < 32; ++u) local += c[u];
+  }
   uint32_t tot;
   uint32_t run = block_inclusive_scan(local, scratch, tot) - local;
-  for (int64_t i = i0; i < i1; ++i) {
-    off[i] = run;
-    cursor[i] = run;
-    run += cnt[i];
+  for (int64_t i = i0; i < i1; i += 32) {
+    uint32_t c[32];
+    load32(i, c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = i + 4 * u;
+      uint4 o;
+      o.x = run;
+      o.y = o.x + c[4 * u];
+      o.z = o.y + c[4 * u + 1];
+      o.w = o.z + c[4 * u + 2];
+      run = o.w + c[4 * u + 3];
+      if (j + 4 <= i1) {
+        *reinterpret_cast<uint4*>(off + j) = o;
+        *reinterpret_cast<uint4*>(cursor + j) = o;
+      } else {
+        const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+        for (int e = 0; e < 4 && j + e < i1; ++e) {
+          off[j + e] = ov[e];
+          cursor[j + e] = ov[e];
+        }
+      }
+    }
   }
   if (threadIdx.x == 0) off[n] = tot;
 }
