@@ -385,6 +385,25 @@ def test_indexer_topk_long_decode_rows(B, T, S, kk, q_pos, zero_w, force):
         assert torch.equal(got[0, 0, :min(n, kk)].cpu(), torch.arange(min(n, kk), dtype=torch.int32))
 
 
+def test_indexer_topk_query_blocks_equal_whole_call():
+    """A prefill run in query blocks (per-batch q_pos = the block's first position, a workspace sized for the
+    block) writes exactly the whole call's indices: rows are independent."""
+    sa = require_gpu()
+    B, T, S, kk, blk = 2, 4096, 4096, 2048, 1536
+    g = torch.Generator(device=DEV)
+    g.manual_seed(97)
+    qi = (torch.randn((B, T, 4, 128), generator=g, device=DEV) * 128 ** -0.5).to(torch.bfloat16)
+    ki = (torch.randn((B, S, 128), generator=g, device=DEV) * 128 ** -0.5).to(torch.bfloat16)
+    w = torch.rand((B, T, 4), generator=g, device=DEV)
+    whole = sa.dsa_indexer_topk(qi, ki, w, kk)
+    for o in range(0, T, blk):
+        e = min(T, o + blk)
+        qp = torch.full((B,), o, dtype=torch.int64, device=DEV)
+        part = sa.dsa_indexer_topk(qi[:, o:e].contiguous(), ki, w[:, o:e].contiguous(), kk, q_pos=qp)
+        torch.cuda.synchronize()
+        assert torch.equal(part, whole[:, o:e]), o
+
+
 def test_indexer_topk_32768_top2048():
     """Fused call at the prefill workload's size: identical to the separate calls on every row, and on
     sampled rows equal to the oracle's selection outside the 1e-6 tie band."""
