@@ -385,6 +385,27 @@ def test_indexer_topk_long_decode_rows(B, T, S, kk, q_pos, zero_w, force):
         assert torch.equal(got[0, 0, :min(n, kk)].cpu(), torch.arange(min(n, kk), dtype=torch.int32))
 
 
+def test_indexer_topk_long_decode_max_rows():
+    """The largest supported decode rows: S = 2^24 positions, two queries (q_pos near the end): the fused
+    call equals the separate indexer + top-k."""
+    sa = require_gpu()
+    B, T, S, kk = 1, 2, 1 << 24, 2048
+    print(f"[fused long max] B={B} T={T} S={S} k={kk}", flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(98)
+    tqi = (torch.randn((B, T, 4, 128), generator=g, device=DEV) * 128 ** -0.5).to(torch.bfloat16)
+    tki = torch.empty((B, S, 128), dtype=torch.bfloat16, device=DEV)
+    for c in range(0, S, 1 << 22):  # chunks keep the float32 draw small
+        tki[:, c:c + (1 << 22)] = (torch.randn((B, 1 << 22, 128), generator=g, device=DEV) * 128 ** -0.5).to(torch.bfloat16)
+    tw = torch.rand((B, T, 4), generator=g, device=DEV)
+    qp = torch.tensor([S - 2], dtype=torch.int64, device=DEV)
+    want = sa.dsa_topk(sa.dsa_indexer_scores(tqi, tki, tw, q_pos=qp), kk, q_pos=qp)
+    got = sa.dsa_indexer_topk(tqi, tki, tw, kk, q_pos=qp)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    assert bool((got[0, :, :-1] < got[0, :, 1:]).all())  # ascending, no padding
+
+
 def test_indexer_topk_query_blocks_equal_whole_call():
     """A prefill run in query blocks (per-batch q_pos = the block's first position, a workspace sized for the
     block) writes exactly the whole call's indices: rows are independent."""
