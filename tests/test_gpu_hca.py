@@ -150,6 +150,44 @@ def test_decode_equals_prefill_row():
         assert max_abs_err(f64(o_dec), f64(o_pre[:, :, t])) <= 1e-2, f"t={t}"
 
 
+def test_streaming_decode_loop_equals_prefill():
+    """A serving loop over positions 250..700 of two sequences: each step writes the new token's k, v into
+    the window ring (slot pos mod W), decodes, and when the step completes a block (pos + 1 = 128 (j + 1))
+    compresses the ring -- which then holds exactly that block -- into cache entry j in place.  Every step's
+    output equals prefill row pos (the cache before position 250 comes from hca_compress of the prefix)."""
+    sa = require_gpu()
+    B, H, T, blk, window, d = 2, 2, 701, 128, 128, 512
+    (q, k, v), (tq, tk, tv) = _inputs((B, H, T, d), "bf16", 1.0, 23)
+    kc_full, vc_full = sa.hca_compress(tk, blk), sa.hca_compress(tv, blk)
+    o_pre = sa.hca_attention_fwd(sa.HCA_PREFILL, tq, tk, tv, kc_full, vc_full, blk, window)
+    t0, ncap = 250, T // blk
+    kc = torch.zeros((B, H, ncap, d), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :t0 // blk] = sa.hca_compress(tk[:, :, :t0].contiguous(), blk)
+    vc[:, :, :t0 // blk] = sa.hca_compress(tv[:, :, :t0].contiguous(), blk)
+    ring_k = torch.zeros((B, H, window, d), dtype=torch.bfloat16, device=DEV)
+    ring_v = torch.zeros_like(ring_k)
+    for s in range(t0 - window, t0):
+        ring_k[:, :, s % window] = tk[:, :, s]
+        ring_v[:, :, s % window] = tv[:, :, s]
+    worst = 0.0
+    for t in range(t0, T):
+        ring_k[:, :, t % window] = tk[:, :, t]
+        ring_v[:, :, t % window] = tv[:, :, t]
+        pos = torch.full((B,), t, dtype=torch.int64, device=DEV)
+        o_dec = sa.hca_attention_fwd(sa.HCA_DECODE, tq[:, :, t].contiguous(), ring_k, ring_v, kc, vc, blk, window,
+                                     pos=pos)
+        worst = max(worst, float((o_dec.float() - o_pre[:, :, t].float()).abs().max()))
+        if (t + 1) % blk == 0:  # block j = (t + 1) / blk - 1 is complete: the ring holds exactly it
+            j = (t + 1) // blk - 1
+            sa.hca_compress(ring_k, blk, out=kc[:, :, j:j + 1])
+            sa.hca_compress(ring_v, blk, out=vc[:, :, j:j + 1])
+            assert torch.equal(kc[:, :, j], kc_full[:, :, j]) and torch.equal(vc[:, :, j], vc_full[:, :, j]), j
+    torch.cuda.synchronize()
+    print(f"[streaming decode] {T - t0} steps, max |decode - prefill row| {worst:.3e}", flush=True)
+    assert worst <= 1e-2
+
+
 # ---------------------------------------------------------------------------
 # Query/key head wider than the value head (qk 576 / v 512)
 # ---------------------------------------------------------------------------
