@@ -20,8 +20,10 @@
  *    keeps no pointer after a call returns.  Buffers must stay alive until
  *    the enqueued work has finished.
  *  - Every call only enqueues work on the given stream (NULL = the default
- *    stream) and never synchronises.  Results are deterministic: the same
- *    inputs give bit-identical outputs on every run.
+ *    stream) and never synchronises (dsa_sparse_attention_bwd also forks
+ *    part of its work to a stream of its own and joins it back with events,
+ *    so it orders on the given stream like any other work).  Results are
+ *    deterministic: the same inputs give bit-identical outputs on every run.
  *  - Inputs are read-only.  Outputs must not alias inputs.
  *  - Tensors are dense and row-major in the shapes given below, with the last
  *    (feature) dimension contiguous, unless strides are passed explicitly.
@@ -444,7 +446,15 @@ int dsa_sparse_attention_fwd(const void* q, const void* k, const void* v,
  * B*S < 2^32 - 1.
  * Workspace: dsa_sparse_attention_bwd_workspace_size(B, T, S, kk) bytes,
  * 16-byte aligned (for chunks of up to 2048 tokens: the P and dS blocks,
- * each entry's dk / dv rows and an inverse index: about 5.4 GB at kk = 2048).
+ * each entry's dk / dv rows and two inverse-index buffers: about 5.4 GB at
+ * kk = 2048).
+ * Streams: each chunk's inverse index (integer work that depends only on
+ * idx) is built on a second stream of the calling thread and device
+ * (created on first use, default priority, kept for the process), forked
+ * from `stream` after the work enqueued before the call and joined back
+ * before the reduction that reads it, so that it overlaps the previous
+ * chunks' attention passes.  If the current device is not `stream`'s, or
+ * the stream or its events cannot be created, everything runs on `stream`.
  * Errors: SA_ERR_NULL (any pointer NULL), SA_ERR_SHAPE, SA_ERR_UNSUPPORTED,
  * SA_ERR_ALIGN (every pointer 16-byte aligned), SA_ERR_WORKSPACE, SA_ERR_HIP.
  * ------------------------------------------------------------------------ */

@@ -27,7 +27,12 @@
 //     in ascending (token, entry) order into dk and dv.  Chunks run in order,
 //     so every output element is summed in a fixed order and the result is
 //     bit-identical from run to run.
+// The inverse index depends only on the selection, so it is built on a
+// second stream into one of two buffers, ahead of the chunks' MFMA passes;
+// events order each chunk's reduce after its index and each buffer's reuse
+// after the reduce that read it.
 #include <type_traits>
+#include <vector>
 
 #include "attn_core32.h"
 #include "kernels.h"
@@ -507,7 +512,7 @@ int64_t dsa_sparse_bwd_chunk(int64_t BT) { return BT < kChunkTokens ? BT : kChun
 
 namespace {
 struct BwdLayout {
-  size_t blocks, gk, gv, list, cnt, off, cursor, total;
+  size_t blocks, gk, gv, list[2], cnt[2], off[2], cursor[2], total;  // two inverse-index buffers
 };
 BwdLayout bwd_layout(int64_t B, int64_t T, int64_t S, int64_t kk) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -520,16 +525,57 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t S, int64_t kk) {
   off += al((size_t)(tc * kk + 32) * kBwD * 2);  // + 32 discard rows
   L.gv = off;
   off += al((size_t)(tc * kk + 32) * kBwD * 2);
-  L.list = off;
-  off += al((size_t)(tc * kk) * 4);
-  L.cnt = off;
-  off += al((size_t)(keys + 1) * 4);
-  L.off = off;
-  off += al((size_t)(keys + 1) * 4);
-  L.cursor = off;
-  off += al((size_t)(keys + 1) * 4);
+  for (int b = 0; b < 2; ++b) {
+    L.list[b] = off;
+    off += al((size_t)(tc * kk) * 4);
+    L.cnt[b] = off;
+    off += al((size_t)(keys + 1) * 4);
+    L.off[b] = off;
+    off += al((size_t)(keys + 1) * 4);
+    L.cursor[b] = off;
+    off += al((size_t)(keys + 1) * 4);
+  }
   L.total = off;
   return L;
+}
+
+// The inverse-index stream of this host thread for `dev` (default priority,
+// non-blocking), and a pool of this thread's events.  Both are created on
+// first use and kept for the life of the process: one stream per (thread,
+// device) is what a caller's threads need, and tearing streams down from a
+// thread-exit destructor could run after the runtime has shut down.
+constexpr int kMaxDevices = 64;
+hipError_t index_stream(int dev, hipStream_t* out) {
+  thread_local hipStream_t streams[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!streams[dev]) {
+    hipStream_t s = nullptr;
+    const hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    streams[dev] = s;
+  }
+  *out = streams[dev];
+  return hipSuccess;
+}
+struct EventPool {
+  int dev = -1;
+  std::vector<hipEvent_t> ev;
+};
+// n events of device dev (the current device), reused from call to call:
+// a wait enqueued before an event is recorded again still waits for the
+// record it was enqueued after.
+hipError_t thread_events(int dev, size_t n, hipEvent_t** out) {
+  thread_local EventPool pools[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  EventPool& pool = pools[dev];
+  while (pool.ev.size() < n) {
+    hipEvent_t e = nullptr;
+    const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (r != hipSuccess) return r;
+    pool.ev.push_back(e);
+  }
+  *out = pool.ev.data();
+  return hipSuccess;
 }
 }  // namespace
 
@@ -537,16 +583,12 @@ size_t dsa_sparse_bwd_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t kk) { re
 
 hipError_t launch_dsa_sparse_bwd(DsaSparseBwdParams p, hipStream_t stream) {
   const int64_t BT = p.B * p.T, keys = p.B * p.S, tc = dsa_sparse_bwd_chunk(BT);
+  const int64_t nch = (BT + tc - 1) / tc;
   const BwdLayout L = bwd_layout(p.B, p.T, p.S, p.kk);
   char* w = reinterpret_cast<char*>(p.ws);
   p.blocks = reinterpret_cast<uint16_t*>(w + L.blocks);
   p.gk = reinterpret_cast<uint16_t*>(w + L.gk);
   p.gv = reinterpret_cast<uint16_t*>(w + L.gv);
-  p.list = reinterpret_cast<uint32_t*>(w + L.list);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
-  uint32_t* off = reinterpret_cast<uint32_t*>(w + L.off);
-  uint32_t* cursor = reinterpret_cast<uint32_t*>(w + L.cursor);
-  p.off = off;
   const int64_t n4 = keys * kBwD / 4;
   const uint32_t zb = (uint32_t)std::min<int64_t>((n4 + 255) / 256, 4096);
   hipLaunchKernelGGL(dsa_sparse_bwd_zero_kernel, dim3(zb), dim3(256), 0, stream, reinterpret_cast<float4*>(p.dk), n4);
@@ -554,19 +596,51 @@ hipError_t launch_dsa_sparse_bwd(DsaSparseBwdParams p, hipStream_t stream) {
   const int64_t c4 = ((keys + 1 + 63) & ~(int64_t)63) / 4;  // the counts, zeroed per chunk as float4 words
   const uint32_t cb = (uint32_t)std::min<int64_t>((c4 + 255) / 256, 4096);
   const uint32_t rb = (uint32_t)std::min<int64_t>(keys, 65536);
-  for (int64_t tok0 = 0; tok0 < BT; tok0 += tc) {
-    p.tok0 = tok0;
-    p.ntok = std::min<int64_t>(tc, BT - tok0);
+
+  // The index stream and events (ev[0]: start; ev[1 + c]: chunk c's index
+  // built; ev[1 + nch + c]: chunk c's reduce done), on the caller stream's
+  // device.  Without them (another device current, or a creation failure)
+  // everything runs on the caller's stream in the same order.
+  hipStream_t aux = nullptr;
+  hipEvent_t* ev = nullptr;
+  {
+    int sdev = -1, cdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) == hipSuccess && hipGetDevice(&cdev) == hipSuccess && sdev == cdev &&
+        index_stream(cdev, &aux) == hipSuccess && thread_events(cdev, (size_t)(1 + 2 * nch), &ev) == hipSuccess) {
+    } else {
+      (void)hipGetLastError();  // a failed lookup leaves nothing to report: the single-stream order is used
+      aux = nullptr;
+    }
+  }
+  hipError_t e = hipSuccess;
+  if (aux) {
+    if ((e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(aux, ev[0], 0)) != hipSuccess) return e;
+  }
+  hipStream_t is = aux ? aux : stream;  // the index kernels' stream
+  for (int64_t c = 0; c < nch; ++c) {
+    const int b = (int)(c & 1);
+    p.tok0 = c * tc;
+    p.ntok = std::min<int64_t>(tc, BT - p.tok0);
+    p.list = reinterpret_cast<uint32_t*>(w + L.list[b]);
+    p.off = reinterpret_cast<const uint32_t*>(w + L.off[b]);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(w + L.cnt[b]);
+    uint32_t* off = reinterpret_cast<uint32_t*>(w + L.off[b]);
+    uint32_t* cursor = reinterpret_cast<uint32_t*>(w + L.cursor[b]);
     const uint32_t eb = (uint32_t)((p.ntok * p.kk + 255) / 256);
-    hipLaunchKernelGGL(dsa_sparse_bwd_zero_kernel, dim3(cb), dim3(256), 0, stream, reinterpret_cast<float4*>(cnt), c4);
-    hipLaunchKernelGGL(dsa_sparse_bwd_count_kernel, dim3(eb), dim3(256), 0, stream, p, cnt);
-    hipLaunchKernelGGL(dsa_sparse_bwd_scan_kernel, dim3(1), dim3(1024), 0, stream, cnt, off, cursor, keys);
-    hipLaunchKernelGGL(dsa_sparse_bwd_fill_kernel, dim3(eb), dim3(256), 0, stream, p, cursor);
+    // Buffer b was last read by chunk c - 2's reduce.
+    if (aux && c >= 2 && (e = hipStreamWaitEvent(aux, ev[1 + nch + c - 2], 0)) != hipSuccess) return e;
+    hipLaunchKernelGGL(dsa_sparse_bwd_zero_kernel, dim3(cb), dim3(256), 0, is, reinterpret_cast<float4*>(cnt), c4);
+    hipLaunchKernelGGL(dsa_sparse_bwd_count_kernel, dim3(eb), dim3(256), 0, is, p, cnt);
+    hipLaunchKernelGGL(dsa_sparse_bwd_scan_kernel, dim3(1), dim3(1024), 0, is, cnt, off, cursor, keys);
+    hipLaunchKernelGGL(dsa_sparse_bwd_fill_kernel, dim3(eb), dim3(256), 0, is, p, cursor);
+    if (aux && (e = hipEventRecord(ev[1 + c], aux)) != hipSuccess) return e;
     hipLaunchKernelGGL(dsa_bwd_ds_kernel, dim3((uint32_t)p.ntok), dim3(128), 0, stream, p);
     hipLaunchKernelGGL(dsa_bwd_contrib_kernel, dim3((uint32_t)p.ntok), dim3(256), 0, stream, p);
+    if (aux && (e = hipStreamWaitEvent(stream, ev[1 + c], 0)) != hipSuccess) return e;
     hipLaunchKernelGGL(dsa_sparse_bwd_reduce_kernel, dim3(rb), dim3(256), 0, stream, p, keys);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (aux && (e = hipEventRecord(ev[1 + nch + c], stream)) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }
