@@ -63,6 +63,17 @@ __device__ __forceinline__ f32x4_t mfma_f32_16x16x4(float a, float b, f32x4_t c)
 }
 
 // ---------------------------------------------------------------------------
+// Streaming global loads: 16 bytes with the non-temporal hint, for data read
+// once (decode caches, compression inputs).  A plain streaming read of 8 GiB
+// measures 7.05-7.15 TB/s with the hint against 6.0-6.3 TB/s without it.
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream_u4(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// ---------------------------------------------------------------------------
 // LDS access
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(kCompressThreads) void hca_compress_kernel(HcaCompr
   const int blk = (int)p.blk;
 #pragma unroll 8
   for (int r = r0; r < blk; r += rstep) {
-    const uint4 u = *reinterpret_cast<const uint4*>(src + (int64_t)r * p.x_st + c * kEPC);
+    // Read once: non-temporal loads (a wave reads whole 128-byte lines).
+    const uint4 u = load_stream_u4(src + (int64_t)r * p.x_st + c * kEPC);
     if constexpr (sizeof(T) == 2) {
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll

@@ -39,19 +39,21 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // kFp8: the K/V rows are E4M3 codes (one byte per dim) with one fp32 scale
-// per row; lane `part` of a key's 8 lanes then holds dims 64*part .. +63 (64
-// contiguous bytes), the codes are widened with the hardware conversion
-// (exact: every E4M3 value is an fp32 value), the dot product runs in fp32
-// and is multiplied by the K row's scale, and the V row's scale is folded
-// into the probability.  bf16 rows: lane `part` holds the 16-byte chunks
-// part, part+16, ... of the row.
+// per row; lane `part` of a key's 8 lanes then holds the 16-byte chunks
+// (16 dims each) part, part+8, part+16, part+24 of the row, the codes are
+// widened with the hardware conversion (exact: every E4M3 value is an fp32
+// value), the dot product runs in fp32 and is multiplied by the K row's
+// scale, and the V row's scale is folded into the probability.  bf16 rows:
+// lane `part` holds the 16-byte chunks part, part+16, ... of the row.  Either
+// way one load instruction reads whole 128-byte lines of a key's rows, which
+// the non-temporal loads need (they keep nothing in cache for a later
+// instruction to reuse).
 constexpr int kDecFp8Lanes = 8;  // lanes per key with the FP8 cache (more keys in flight per wave)
 
 template <int D, bool kFp8, int DR>
 __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams p) {
   constexpr int kLanes = kFp8 ? kDecFp8Lanes : 16;  // lanes per key
   static_assert(DR == 0 || (!kFp8 && DR == 4 * 16), "extra query/key dims: 4 per lane of a bf16 key");
-  constexpr int kLaneDims = D / kLanes;             // FP8: contiguous dims per lane
   constexpr int kSlots = kWave / kLanes;   // keys per wave step
   constexpr int kPer = D / 8 / kLanes;     // groups of 8 dims per lane
   constexpr int kRowBytes = kFp8 ? D : 2 * D;        // V row; the first D dims of a K row
@@ -66,10 +68,11 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
   const int64_t b = bh / p.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = lane / kLanes, part = lane % kLanes;
-  // First dim of this lane's group i of 8 dims.
-  auto dim0 = [&](int i) { return kFp8 ? kLaneDims * part + 8 * i : 8 * (part + kLanes * i); };
+  // First dim of this lane's group i of 8 dims (FP8: a 16-byte chunk holds
+  // groups 2j and 2j + 1).
+  auto dim0 = [&](int i) { return kFp8 ? 16 * (part + kLanes * (i >> 1)) + 8 * (i & 1) : 8 * (part + kLanes * i); };
   // Byte offset in a row of this lane's 16-byte load j.
-  auto load_off = [&](int j) { return kFp8 ? kLaneDims * part + 16 * j : 16 * (part + kLanes * j); };
+  auto load_off = [&](int j) { return 16 * (part + kLanes * j); };
 
   int64_t t = p.pos[b];
   if (t < 0) t = 0;
@@ -141,8 +144,8 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
       }
 #pragma unroll
       for (int j = 0; j < kLoads; ++j) {
-        r.k[j] = *reinterpret_cast<const uint4*>(krow + load_off(j));
-        r.v[j] = *reinterpret_cast<const uint4*>(vrow + load_off(j));
+        r.k[j] = load_stream_u4(krow + load_off(j));
+        r.v[j] = load_stream_u4(vrow + load_off(j));
       }
       r.kr = DR ? *reinterpret_cast<const uint2*>(krow + kRowBytes + 8 * part) : make_uint2(0u, 0u);
     } else {
@@ -159,7 +162,8 @@ __global__ __launch_bounds__(kDecThreads) void hca_decode_kernel(HcaDecodeParams
     const bool valid = g0 + slot < u_end;
     float dot = 0.f;
     if constexpr (kFp8) {
-      // Load j holds dims kLaneDims*part + 16*j .. +15, four codes per word.
+      // Load j holds this lane's dims 16*j .. +15 (local order: groups 2j and
+      // 2j + 1 of dim0), four codes per word.
 #pragma unroll
       for (int j = 0; j < kLoads; ++j) {
         const uint32_t w[4] = {r.k[j].x, r.k[j].y, r.k[j].z, r.k[j].w};
