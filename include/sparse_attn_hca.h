@@ -375,11 +375,12 @@ int csa_topk(const float* scores, const int64_t* q_pos, int32_t* idx,
  * q_pos: device int64[B] or NULL (as for dsa_indexer_scores);
  * idx: [B,T,k] int32.
  * Decode-shaped calls with long rows (T <= 4, S > 32768) take the register-
- * operand decode indexer: it scores every 16th key in place for the
- * threshold, then writes the candidates of each chunk of 128 positions in
- * position order; a compaction packs them and one workgroup per row selects
- * over them (at most 8192 candidates; otherwise the row is recomputed
- * exactly from its full scores inside the call).
+ * operand decode indexer: it scores every 64th key in place for the
+ * threshold (rank k/64 plus the same margin), then writes the candidates of
+ * each chunk of 128 positions in position order; a compaction packs them
+ * and one workgroup per row selects over them (at most 8192 candidates;
+ * otherwise the row is recomputed exactly from its full scores inside the
+ * call).
  * force_fallback: 0 normally; nonzero sends every row with more than k
  * candidates through the exact recomputation (a test of that path).
  * Supported: Hi = 4, Di = 128, 1 <= k <= 2048, and S <= 32768 or (T <= 4 and

@@ -40,17 +40,24 @@ constexpr int kSelPer = (int)(kCap / 64);           // candidates per lane (one 
 constexpr int kMaxS = 32768;                        // bitmap of the select step
 constexpr int kThrPer = 2048 / 64;                  // sampled keys per lane (S / 16 <= 2048)
 
-// Sample rank for k: k/16 rounded up, plus four and a half standard
-// deviations of a binomial count of that mean, plus a constant.  At k = 2048
-// (rank 190) a row has about 3040 candidates; with scores independent of
-// position, fewer than k or (pads included) more than kCap of them take
-// about 4.5 standard deviations of the sample either way.
-__host__ __device__ inline int fused_rank(int64_t k) {
-  const int m = (int)((k + kSample - 1) / kSample);
+// Sample rank for k at sample stride st: k/st rounded up, plus four and a
+// half standard deviations of a binomial count of that mean, plus a
+// constant.  At k = 2048 and stride 16 (rank 190) a row has about 3040
+// candidates; with scores independent of position, fewer than k or (pads
+// included) more than kCap of them take about 4.5 standard deviations of the
+// sample either way, whatever the stride.
+__host__ __device__ inline int fused_rank(int64_t k, int st = kSample) {
+  const int m = (int)((k + st - 1) / st);
   int sd = 1;
   while (sd * sd < m) ++sd;
   return m + (9 * sd + 1) / 2 + 8;
 }
+
+// Long decode rows sample every kSampleL-th key: a 1M-position row still has
+// 16384 samples, and the sampling pass and the threshold read a quarter of
+// what stride 16 reads.  At k = 2048 the rank is 66 and a row has about 4200
+// candidates (the sample's 4.5 standard deviations: about 2000 above k).
+constexpr int kSampleL = 64;
 
 constexpr int kCapL = 8192;  // candidates the long-row select holds per row
 constexpr int kMaxSeg = 128;  // chunks of the candidate launch per row (S / 256 at most)
@@ -106,7 +113,7 @@ static FusedLayout fused_layout_long(int64_t B, int64_t T, int64_t S) {
   size_t off = 0;
   L.ks = off;  // unused: the sampled keys are scored in place
   L.sscore = off;  // rows pitched at a multiple of 8 keys
-  off += al((size_t)(rows * pad8(S / kSample)) * 2);
+  off += al((size_t)(rows * pad8(S / kSampleL)) * 2);
   L.thresh = off;
   off += al((size_t)rows * 4);
   L.cnt = off;  // rows pitched at a multiple of 8 counts
@@ -376,9 +383,9 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
 }
 
 // ---------------------------------------------------------------------------
-// Long decode rows.  Sampled keys: the decode indexer scores every 16th key
-// in place (no copy of the sampled keys) and stores the top 16 bits of their
-// keys.  Threshold: one 1024-thread workgroup per row, the r-th largest
+// Long decode rows.  Sampled keys: the decode indexer scores every
+// kSampleL-th key in place (no copy of the sampled keys) and stores the top
+// 16 bits of their keys.  Threshold: one 1024-thread workgroup per row, the r-th largest
 // sampled key from LDS histograms.
 // Compaction: the rows' candidates, scattered over per-chunk segments, are
 // packed in position order by many workgroups.  Select: one workgroup per row
@@ -413,9 +420,9 @@ __global__ __launch_bounds__(1024) void fused_thresh_long_kernel(DsaIndexerTopkP
     if (tid == 0) f.thresh[row] = 0xffffffffu;
     return;
   }
-  int64_t ns = (base + i + 1) / kSample;  // the row's sampled positions
+  int64_t ns = (base + i + 1) / kSampleL;  // the row's sampled positions
   ns = ns < f.Ss ? ns : f.Ss;
-  const uint32_t r = (uint32_t)fused_rank(p.topk);
+  const uint32_t r = (uint32_t)fused_rank(p.topk, kSampleL);
   if (n <= p.topk || ns <= (int64_t)r) {  // every visible position is a candidate
     if (tid == 0) f.thresh[row] = 0u;
     return;
@@ -671,7 +678,7 @@ __global__ __launch_bounds__(1024) void fused_select_long_kernel(DsaIndexerTopkP
 static hipError_t launch_fused_long(const DsaIndexerTopkParams& p, hipStream_t stream) {
   const FusedLayout L = fused_layout_long(p.B, p.T, p.S);
   char* ws = reinterpret_cast<char*>(p.ws);
-  const int64_t Ss = p.S / kSample, rows = p.B * p.T, ch = dsa_indexer_dec_chunk();
+  const int64_t Ss = p.S / kSampleL, rows = p.B * p.T, ch = dsa_indexer_dec_chunk();
   FusedPtrs f{};
   f.ks = nullptr;
   f.skey = reinterpret_cast<const uint16_t*>(ws + L.sscore);
@@ -690,8 +697,8 @@ static hipError_t launch_fused_long(const DsaIndexerTopkParams& p, hipStream_t s
   f.ctot = reinterpret_cast<uint32_t*>(ws + L.ctot);
   float* fb = reinterpret_cast<float*>(ws + L.cand);
   hipError_t e;
-  // 1. Sampled keys: every 16th key scored in place (ratio-16 visibility),
-  // top 16 bits of the score keys.
+  // 1. Sampled keys: every kSampleL-th key scored in place (ratio-kSampleL
+  // visibility), top 16 bits of the score keys.
   if (Ss > 0) {
     DsaIndexerParams sp{};
     sp.q = p.q;
@@ -702,7 +709,7 @@ static hipError_t launch_fused_long(const DsaIndexerTopkParams& p, hipStream_t s
     sp.B = p.B;
     sp.T = p.T;
     sp.S = Ss;
-    sp.ratio = kSample;
+    sp.ratio = kSampleL;
     sp.dec_sample = 1;
     sp.k_rows = p.S;
     if ((e = launch_dsa_indexer(sp, stream)) != hipSuccess) return e;

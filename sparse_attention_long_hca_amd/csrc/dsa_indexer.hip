@@ -360,15 +360,16 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
 }
 
 // Decode calls of up to 4 queries: one 16-row M-block (4 queries x 4 heads)
-// per wave and no LDS.  Each lane loads its MFMA B operands straight from
-// k_idx into registers: for 16-position block nb and 32-dim step ks, lane
-// (L = lane % 16, g = lane / 16) takes dims 32*ks + 8*g .. +7 of position
-// 16*nb + L, i.e. 16 bytes of a row, and a tile of 64 positions is 16 such
-// loads per lane.  Tiles are double-buffered in registers; a tile's scores
-// are stored after the next tile's loads are sent, so the wait before a tile
-// (which also covers the wave's earlier stores) finds those stores long done.
-// Without the LDS limit of the staged kernel (5 one-wave workgroups per CU)
-// eight waves per CU keep a tile each in flight.
+// per wave.  Each lane loads 16 bytes of the tile per load, 16 loads per
+// 64-position tile, as whole 128-byte lines with the non-temporal hint
+// (a streaming read of this GPU's HBM reaches about 7 TB/s that way, about
+// 6 TB/s when each load instruction reads half of every line it touches, as
+// loads straight into the MFMA operand layout do); the tile then passes
+// through a 16 KB LDS region of the wave into that layout (no barriers: one
+// wave per workgroup).  Tiles are double-buffered in registers; a tile's
+// scores are stored after the next tile's loads are sent, so the wait before
+// a tile (which also covers the wave's earlier stores) finds those stores
+// long done.
 constexpr int kIdxDecTiles = 2;  // 64-position tiles per workgroup (1, 2, 4, 8, 16 measured: 2 is fastest)
 
 // Modes of the decode kernel.  kDecScores stores the scores.  kDecCand is the
@@ -432,22 +433,42 @@ __device__ __forceinline__ void dsa_indexer_dec_chunk(const DsaIndexerParams& p,
   const uint32_t thr = (kCand && g < T && plim + 1 > (int)p.topk) ? p.thresh[crow] : 0xffffffffu;
   uint32_t c_run = 0u;
 
-  // B operands of one tile: [nb][ks], 16 bytes each.  Positions past the
-  // chunk's stop load the chunk's first row (finite, never stored).
-  auto load_tile = [&](int tile, uint4 (&bt)[4][4]) __attribute__((always_inline)) {
+  // One tile (64 positions x 256-byte rows) in whole 128-byte lines: load i
+  // of a lane is 16-byte chunk lane % 16 of tile row 4i + lane / 16, with the
+  // non-temporal hint (each row is read once).  Positions past the chunk's
+  // stop load the chunk's first row (finite, never stored).
+  const int rr = lane >> 4, cc = lane & 15;
+  auto load_tile = [&](int tile, uint4 (&raw)[16]) __attribute__((always_inline)) {
     const int s0 = s_begin + tile * kIdxKTile;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int s = s0 + nb * 16 + L;
+    for (int i = 0; i < 16; ++i) {
+      const int s = s0 + 4 * i + rr;
       const int sv = s < s_stop ? s : s_begin;
       const int64_t kr = kDec == kDecSample ? (int64_t)sv * ratio + (ratio - 1) : (int64_t)sv;
-      const bf16_t* row = kI + kr * kIdxDi + g * 8;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bt[nb][ks] = *reinterpret_cast<const uint4*>(row + ks * 32);
+      raw[i] = load_stream_u4(kI + kr * kIdxDi + cc * 8);
     }
   };
+  // The loaded tile goes through this wave's LDS region (row r, chunk c at
+  // r*256 + 16*(c ^ (r % 16)): conflict-free for both the row-wise writes
+  // and the operand reads) into the MFMA B operand layout: for 16-position
+  // block nb and 32-dim step ks, lane (L, g) takes chunk 4ks + g of row
+  // 16nb + L.
+  __shared__ __attribute__((aligned(16))) char stage[kIdxKTile * kIdxDi * 2];
   float sc[4];
-  auto compute = [&](const uint4 (&bt)[4][4]) __attribute__((always_inline)) {
+  auto compute = [&](const uint4 (&raw)[16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 4 * i + rr;
+      lds_write_b128(stage, (uint32_t)(r * 256 + 16 * (cc ^ (r & 15))), raw[i]);
+    }
+    // The raw tile's registers are free before the operands are read.
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 bt[4][4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        bt[nb][ks] = lds_read_b128(stage, (uint32_t)((16 * nb + L) * 256 + 16 * ((4 * ks + g) ^ L)));
     f32x4_t acc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
@@ -500,7 +521,7 @@ __device__ __forceinline__ void dsa_indexer_dec_chunk(const DsaIndexerParams& p,
     }
   };
 
-  uint4 b0[4][4], b1[4][4];
+  uint4 b0[16], b1[16];
   load_tile(0, b0);
   for (int tile = 0; tile < n_tiles; tile += 2) {
     if (tile + 1 < n_tiles) load_tile(tile + 1, b1);
