@@ -327,8 +327,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float vx = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? v0 : v1), 0xb1, 0xf, 0xf, false));
       uint16_t* rk = (live ? p.gk + e * kBwD : discard_k) + dcol;
       uint16_t* rv = (live ? p.gv + e * kBwD : discard_v) + dcol;
-      *reinterpret_cast<uint32_t*>(rk) = odd ? pack_bf16x2(kx, k1) : pack_bf16x2(k0, kx);
-      *reinterpret_cast<uint32_t*>(rv) = odd ? pack_bf16x2(vx, v1) : pack_bf16x2(v0, vx);
+      // Streamed out (read once, by the reduction): non-temporal stores.
+      __builtin_nontemporal_store(odd ? pack_bf16x2(kx, k1) : pack_bf16x2(k0, kx), reinterpret_cast<uint32_t*>(rk));
+      __builtin_nontemporal_store(odd ? pack_bf16x2(vx, v1) : pack_bf16x2(v0, vx), reinterpret_cast<uint32_t*>(rv));
     }
     lds_barrier();  // the stage's buffer is free for the load two tiles on
   }
@@ -433,6 +434,9 @@ __global__ __launch_bounds__(256) void dsa_sparse_bwd_reduce_kernel(DsaSparseBwd
   __shared__ uint32_t wtot[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d = tid;
+  // The rows are read once: non-temporal loads (each wave reads a whole
+  // 128-byte line per load).
+  auto ld = [](const uint16_t* q) -> float { return bf16_to_f32(__builtin_nontemporal_load(q)); };
   auto row_sum = [&](int m, float& ak, float& av) __attribute__((always_inline)) {
     int r = 0;
     for (; r + 8 <= m; r += 8) {
@@ -440,8 +444,8 @@ __global__ __launch_bounds__(256) void dsa_sparse_bwd_reduce_kernel(DsaSparseBwd
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int64_t row = (int64_t)ids[r + u] * kBwD + d;
-        xk[u] = bf16_to_f32(p.gk[row]);
-        xv[u] = bf16_to_f32(p.gv[row]);
+        xk[u] = ld(p.gk + row);
+        xv[u] = ld(p.gv + row);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -451,8 +455,8 @@ __global__ __launch_bounds__(256) void dsa_sparse_bwd_reduce_kernel(DsaSparseBwd
     }
     for (; r < m; ++r) {
       const int64_t row = (int64_t)ids[r] * kBwD + d;
-      ak += bf16_to_f32(p.gk[row]);
-      av += bf16_to_f32(p.gv[row]);
+      ak += ld(p.gk + row);
+      av += ld(p.gv + row);
     }
   };
   for (int64_t key = blockIdx.x; key < nkeys; key += gridDim.x) {
