@@ -359,13 +359,16 @@ def test_indexer_topk_odd_width_all_candidate_rows(B, T, S, kk, q_pos, zero_w):
                                                     (2, 2, 40000, 2048, [39998, 100], False),
                                                     (3, 1, 50001, 7, [50000, 33000, 1], False),
                                                     (1, 4, 40000, 300, [39996], True),
-                                                    (4, 1, 1 << 20, 2048, [(1 << 20) - 1, 900000, 524287, 40000], False)])
+                                                    (4, 1, 1 << 20, 2048, [(1 << 20) - 1, 900000, 524287, 40000], False),
+                                                    (1, 2, 50000, 2048, [3000], False)])
 @pytest.mark.parametrize("force", [False, True])
 def test_indexer_topk_long_decode_rows(B, T, S, kk, q_pos, zero_w, force):
     """Decode-shaped calls with rows longer than 32768 positions (up to the 1M context): the candidate path
     of the decode indexer and the per-row select must return exactly the separate calls' indices; rows with
-    at most k visible positions keep all; w = 0 (every score 0.0, more candidates than the select holds) and
-    force=True take the exact recomputation from the full scores."""
+    at most k visible positions keep all; rows with more than k positions but too few samples for a
+    threshold (3001 and 3002 positions: 46 samples at stride 64, rank 66) make every position a candidate;
+    w = 0 (every score 0.0, more candidates than the select holds) and force=True take the exact
+    recomputation from the full scores."""
     sa = require_gpu()
     print(f"[fused long] B={B} T={T} S={S} k={kk} q_pos={q_pos} zero_w={zero_w} force={force}", flush=True)
     g = torch.Generator(device=DEV)
