@@ -168,6 +168,52 @@ def test_sparse_bwd_bit_reproducible():
         assert torch.equal(x, y)
 
 
+def test_sparse_bwd_user_stream_and_graph():
+    """The call forks its inverse index to a second stream and joins it back with events.  On a
+    non-default stream, with the index list written by the work just before the call on that stream,
+    and captured in a graph (replayed three times with eager work between), it gives the bits of the
+    plain call."""
+    sa = require_gpu()
+    B, T, S, kk = 1, 3000, 3100, 128
+    q, k, v, do = _inputs(B, T, S, 71)
+    idx = _causal_idx(B, T, S, kk, np.random.default_rng(72))
+    t = lambda a: synth.to_torch(a, "bf16", DEV)
+    ti = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    tq, tk, tv, tdo = t(q), t(k), t(v), t(do)
+    o, lse = sa.dsa_sparse_attention_fwd(tq, tk, tv, ti, return_lse=True)
+    ref = sa.dsa_sparse_attention_bwd(tq, tk, tv, ti, o, lse, tdo)
+    torch.cuda.synchronize()
+    ws = torch.empty(sa.dsa_sparse_attention_bwd_workspace_size(B, T, S, kk), dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ti2 = torch.full_like(ti, -1)
+        ti2.copy_(ti)  # written on s just before the call: the index must see it
+        got = sa.dsa_sparse_attention_bwd(tq, tk, tv, ti2, o, lse, tdo, workspace=ws)
+    torch.cuda.synchronize()
+    for x, y in zip(got, ref):
+        assert torch.equal(x, y)
+    # Graph capture (the forked stream joins the capture through the events).
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        sa.dsa_sparse_attention_bwd(tq, tk, tv, ti, o, lse, tdo, workspace=ws)  # warm-up outside the graph
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        cap = sa.dsa_sparse_attention_bwd(tq, tk, tv, ti, o, lse, tdo, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in cap:
+            x.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(cap, ref):
+            assert torch.equal(x, y), rep
+        eager = sa.dsa_sparse_attention_bwd(tq, tk, tv, ti, o, lse, tdo)  # eager work between replays
+        torch.cuda.synchronize()
+        for x, y in zip(eager, ref):
+            assert torch.equal(x, y), rep
+
+
 def _sampled_check(q, k, v, o, do, idx, dq, dk, dv, rows, positions, scale):
     """dq of sampled rows, and dk, dv at sampled positions from every token that lists them."""
     B = q.shape[0]
