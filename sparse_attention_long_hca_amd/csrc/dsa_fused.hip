@@ -385,7 +385,7 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
 // ---------------------------------------------------------------------------
 // Long decode rows.  Sampled keys: the decode indexer scores every
 // kSampleL-th key in place (no copy of the sampled keys) and stores the top
-// 16 bits of their keys.  Threshold: one 1024-thread workgroup per row, the r-th largest
+// 16 bits of their keys.  Threshold: one 256-thread workgroup per row, the r-th largest
 // sampled key from LDS histograms.
 // Compaction: the rows' candidates, scattered over per-chunk segments, are
 // packed in position order by many workgroups.  Select: one workgroup per row
@@ -404,7 +404,10 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
 // exactly zero wherever every head's product is negative, about one position
 // in sixteen: zero and negative scores are left out, and a row with fewer
 // than r samples above zero gets threshold 0.)
-__global__ __launch_bounds__(1024) void fused_thresh_long_kernel(DsaIndexerTopkParams p, FusedPtrs f) {
+// Threads of the long-row threshold workgroup: a 1M-position row has 16384
+// samples, 64 per thread in one round of loads.
+constexpr int kThrL = 256;
+__global__ __launch_bounds__(kThrL) void fused_thresh_long_kernel(DsaIndexerTopkParams p, FusedPtrs f) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[4096];
   __shared__ uint32_t scr[32];
   __shared__ uint32_t res[4];
@@ -428,7 +431,7 @@ __global__ __launch_bounds__(1024) void fused_thresh_long_kernel(DsaIndexerTopkP
     return;
   }
   // The row's keys, 8 per 16-byte load (the row is pitched at a multiple of
-  // 8): each pass issues 8 loads per thread together, 65536 keys.
+  // 8): each pass issues 8 loads per thread together, 64 * kThrL keys.
   const uint4* ss = reinterpret_cast<const uint4*>(f.skey + row * f.spitch);
   const int64_t nv = (ns + 7) / 8;
   auto key_of = [&](const uint4& v, int e, int64_t j) -> uint32_t {  // key e of the group at vector j (0: none)
@@ -437,22 +440,22 @@ __global__ __launch_bounds__(1024) void fused_thresh_long_kernel(DsaIndexerTopkP
     return 8 * j + e < ns ? k16 : 0u;
   };
   uint32_t V = 0u;
-  // Round 1: top 12 bits.  (Rows of up to 65536 samples keep their keys in
-  // registers for round 2.)
-  for (int j = tid; j < 4096; j += 1024) hist[j] = 0u;
+  // Round 1: top 12 bits.  (Rows of up to 64 * kThrL samples keep their keys
+  // in registers for round 2.)
+  for (int j = tid; j < 4096; j += kThrL) hist[j] = 0u;
   __syncthreads();
   uint4 v[8];
-  for (int64_t j0 = 0; j0 < nv; j0 += 8 * 1024) {
+  for (int64_t j0 = 0; j0 < nv; j0 += 8 * kThrL) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t j = j0 + u * 1024 + tid;
+      const int64_t j = j0 + u * kThrL + tid;
       v[u] = j < nv ? ss[j] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t k16 = key_of(v[u], e, j0 + u * 1024 + tid);
+        const uint32_t k16 = key_of(v[u], e, j0 + u * kThrL + tid);
         if (k16 > 0x8000u) atomicAdd(&hist[k16 >> 4], 1u);
       }
     }
@@ -460,16 +463,27 @@ __global__ __launch_bounds__(1024) void fused_thresh_long_kernel(DsaIndexerTopkP
   __syncthreads();
   uint32_t tot;
   {
-    // Thread t owns bins [4096 - 4(t+1), 4096 - 4t) (thread 0: the top bins).
-    const uint4 v = reinterpret_cast<const uint4*>(hist)[1023 - tid];
-    const uint32_t local = v.x + v.y + v.z + v.w;
+    // Thread t owns bins [4096 - kPer(t+1), 4096 - kPer t) (thread 0: the top
+    // bins), read as kPer/4 16-byte words.
+    constexpr int kPer = 4096 / kThrL;
+    uint32_t c[kPer];  // c[e]: bin 4096 - kPer t - 1 - e
+#pragma unroll
+    for (int w = 0; w < kPer / 4; ++w) {
+      const uint4 h = reinterpret_cast<const uint4*>(hist)[(4096 - kPer * (tid + 1)) / 4 + (kPer / 4 - 1 - w)];
+      c[4 * w] = h.w;
+      c[4 * w + 1] = h.z;
+      c[4 * w + 2] = h.y;
+      c[4 * w + 3] = h.x;
+    }
+    uint32_t local = 0u;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) local += c[e];
     const uint32_t incl = block_inclusive_scan(local, scr, tot);
     uint32_t above = incl - local;
-    const uint32_t c[4] = {v.w, v.z, v.y, v.x};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < kPer; ++e) {
       if (above < r && above + c[e] >= r) {
-        res[0] = (uint32_t)(4 * (1023 - tid) + 3 - e);
+        res[0] = (uint32_t)(4096 - kPer * tid - 1 - e);
         res[1] = above;
       }
       above += c[e];
@@ -481,11 +495,11 @@ __global__ __launch_bounds__(1024) void fused_thresh_long_kernel(DsaIndexerTopkP
     // Round 2: low 4 bits of the keys in bin b12.
     if (tid < 16) hist[tid] = 0u;
     __syncthreads();
-    for (int64_t j0 = 0; j0 < nv; j0 += 8 * 1024) {
-      if (nv > 8 * 1024) {
+    for (int64_t j0 = 0; j0 < nv; j0 += 8 * kThrL) {
+      if (nv > 8 * kThrL) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int64_t j = j0 + u * 1024 + tid;
+          const int64_t j = j0 + u * kThrL + tid;
           v[u] = j < nv ? ss[j] : make_uint4(0u, 0u, 0u, 0u);
         }
       }
@@ -493,7 +507,7 @@ __global__ __launch_bounds__(1024) void fused_thresh_long_kernel(DsaIndexerTopkP
       for (int u = 0; u < 8; ++u) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t k16 = key_of(v[u], e, j0 + u * 1024 + tid);
+          const uint32_t k16 = key_of(v[u], e, j0 + u * kThrL + tid);
           if (k16 > 0x8000u && (k16 >> 4) == b12) atomicAdd(&hist[k16 & 15u], 1u);
         }
       }
@@ -715,7 +729,7 @@ static hipError_t launch_fused_long(const DsaIndexerTopkParams& p, hipStream_t s
     if ((e = launch_dsa_indexer(sp, stream)) != hipSuccess) return e;
   }
   // 2. Thresholds (also clears the fallback flags).
-  hipLaunchKernelGGL(fused_thresh_long_kernel, dim3((uint32_t)rows), dim3(1024), 0, stream, p, f);
+  hipLaunchKernelGGL(fused_thresh_long_kernel, dim3((uint32_t)rows), dim3(kThrL), 0, stream, p, f);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 3. Candidates, per chunk in position order.
   DsaIndexerParams ep{};
