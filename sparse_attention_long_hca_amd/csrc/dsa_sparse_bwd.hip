@@ -562,7 +562,6 @@ hipError_t index_stream(int dev, hipStream_t* out) {
   return hipSuccess;
 }
 struct EventPool {
-  int dev = -1;
   std::vector<hipEvent_t> ev;
 };
 // n events of device dev (the current device), reused from call to call:
