@@ -38,6 +38,7 @@ constexpr int kSample = 16;     // sample stride (positions)
 constexpr int64_t kCap = 4096;  // most candidates the select step holds per row
 constexpr int kSelPer = (int)(kCap / 64);           // candidates per lane (one wave per row)
 constexpr int kMaxS = 32768;                        // bitmap of the select step
+constexpr int kSelStage = 1024;  // kept positions the select stages in LDS per output step
 constexpr int kThrPer = 2048 / 64;                  // sampled keys per lane (S / 16 <= 2048)
 
 // Sample rank for k at sample stride st: k/st rounded up, plus four and a
@@ -228,6 +229,7 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
   __shared__ __attribute__((aligned(16))) uint32_t hist[256];
   __shared__ __attribute__((aligned(16))) uint32_t bm[kMaxS / 32];
   __shared__ uint32_t pre[kMaxSeg + 1];
+  __shared__ uint32_t ostage[kSelStage];
   const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int64_t b = row / p.T, i = row % p.T;
@@ -366,19 +368,35 @@ __global__ __launch_bounds__(64) void fused_select_kernel(DsaIndexerTopkParams p
     }
   }
   wave_lds_sync();
-  // Output: 64 words (2048 positions) per step, one word per lane.
+  // Output: 64 words (2048 positions) per step, one word per lane.  A step's
+  // kept positions go to an LDS stage in order and then out with full-wave
+  // stores (a lane's own positions, stored one by one, would take a store
+  // instruction per position with few lanes active); a step keeping more
+  // than the stage holds (short, dense rows) stores directly.
   const int nw = (int)((n + 31) / 32);
   uint32_t o_base = 0u;
   for (int cw = 0; cw < nw; cw += 64) {
     uint32_t w = cw + lane < nw ? bm[cw + lane] : 0u;
     const uint32_t pc = (uint32_t)__popc(w);
     const uint32_t incl = wave_incl_scan(pc);
-    uint32_t o = o_base + incl - pc;
-    while (w != 0u) {
-      out[o++] = (cw + lane) * 32 + (__ffs((int)w) - 1);
-      w &= w - 1u;
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (total <= (uint32_t)kSelStage) {
+      uint32_t o = incl - pc;
+      while (w != 0u) {
+        ostage[o++] = (cw + lane) * 32 + (__ffs((int)w) - 1);
+        w &= w - 1u;
+      }
+      wave_lds_sync();
+      for (uint32_t j = lane; j < total; j += 64) out[o_base + j] = (int32_t)ostage[j];
+      wave_lds_sync();  // the stage's reads are done before the next step writes it
+    } else {
+      uint32_t o = o_base + incl - pc;
+      while (w != 0u) {
+        out[o++] = (cw + lane) * 32 + (__ffs((int)w) - 1);
+        w &= w - 1u;
+      }
     }
-    o_base += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    o_base += total;
   }
 }
 
