@@ -64,9 +64,11 @@ __device__ __forceinline__ void idx_stage(char* buf, buffer_rsrc_t rsrc, int s0,
 // hold a flagged row only (the row filter); kIdxKeys16 stores the top 16 bits
 // of each score's order-preserving key instead of the score.
 constexpr int kIdxScores = 0, kIdxCand = 1, kIdxFiltered = 2, kIdxKeys16 = 3;
+// One workgroup's query tile x key chunk; lid is its logical id (after the
+// XCD renumbering).
 template <int kWaves, int kMode>
-__global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerParams p, int n_qtiles, int n_chunks,
-                                                                   int chunk) {
+__device__ __forceinline__ void dsa_indexer_block(DsaIndexerParams p, int n_qtiles, int n_chunks, int chunk,
+                                                  const uint32_t lid) {
   constexpr bool kEmit = kMode == kIdxCand;
   __shared__ __attribute__((aligned(16))) char lds0[kIdxTileBytes];
   __shared__ __attribute__((aligned(16))) char lds1[kIdxTileBytes];
@@ -77,7 +79,6 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   // causal limit chunk c has work for the queries past 1024*c only, so a
   // heavy chunk is followed by a light one and every XCD's contiguous range
   // of workgroups gets about the same amount of work.
-  const uint32_t lid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_b = n_qtiles * n_chunks;
   const int b = (int)(lid / (uint32_t)per_b);
   const int rem = (int)(lid % (uint32_t)per_b);
@@ -359,6 +360,27 @@ __global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerPara
   }
 }
 
+// The filtered mode (exact fallback of the fused call) runs on a bounded grid
+// that walks the logical workgroups: with no row flagged (the usual case) the
+// launch costs a few hundred workgroups rather than one per query tile and
+// chunk.
+constexpr uint32_t kIdxFilterGrid = 1024;
+
+template <int kWaves, int kMode>
+__global__ __launch_bounds__(kWaves * 64) void dsa_indexer_kernel(DsaIndexerParams p, int n_qtiles, int n_chunks,
+                                                                   int chunk) {
+  if constexpr (kMode == kIdxFiltered) {
+    if (*p.any_flag == 0u) return;
+    const uint32_t n = (uint32_t)(p.B * n_qtiles * n_chunks);
+    for (uint32_t v = blockIdx.x; v < n; v += gridDim.x) {
+      dsa_indexer_block<kWaves, kMode>(p, n_qtiles, n_chunks, chunk, xcd_remap(v, n));
+      __syncthreads();  // LDS is reused by the next workgroup's tiles
+    }
+  } else {
+    dsa_indexer_block<kWaves, kMode>(p, n_qtiles, n_chunks, chunk, xcd_remap(blockIdx.x, gridDim.x));
+  }
+}
+
 // Decode calls of up to 4 queries: one 16-row M-block (4 queries x 4 heads)
 // per wave.  Each lane loads 16 bytes of the tile per load, 16 loads per
 // 64-position tile, as whole 128-byte lines with the non-temporal hint
@@ -589,7 +611,8 @@ hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
       if (p.cand)
         hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxCand>), grid, dim3(64), 0, stream, p, 1, (int)n_chunks, chunk);
       else if (p.row_flag)
-        hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxFiltered>), grid, dim3(64), 0, stream, p, 1, (int)n_chunks, chunk);
+        hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxFiltered>), dim3(std::min(grid.x, kIdxFilterGrid)), dim3(64), 0,
+                           stream, p, 1, (int)n_chunks, chunk);
       else if (p.keys16)
         hipLaunchKernelGGL((dsa_indexer_kernel<1, kIdxKeys16>), grid, dim3(64), 0, stream, p, 1, (int)n_chunks, chunk);
       else
@@ -605,8 +628,8 @@ hipError_t launch_dsa_indexer(const DsaIndexerParams& p, hipStream_t stream) {
       hipLaunchKernelGGL((dsa_indexer_kernel<4, kIdxCand>), grid, dim3(256), 0, stream, p, (int)n_qtiles, (int)n_chunks,
                          chunk);
     else if (p.row_flag)
-      hipLaunchKernelGGL((dsa_indexer_kernel<4, kIdxFiltered>), grid, dim3(256), 0, stream, p, (int)n_qtiles,
-                         (int)n_chunks, chunk);
+      hipLaunchKernelGGL((dsa_indexer_kernel<4, kIdxFiltered>), dim3(std::min(grid.x, kIdxFilterGrid)), dim3(256), 0,
+                         stream, p, (int)n_qtiles, (int)n_chunks, chunk);
     else if (p.keys16)
       hipLaunchKernelGGL((dsa_indexer_kernel<4, kIdxKeys16>), grid, dim3(256), 0, stream, p, (int)n_qtiles,
                          (int)n_chunks, chunk);

@@ -74,6 +74,7 @@ __device__ __forceinline__ int64_t row_len(const DsaTopkParams& p, int64_t b, in
 // ---------------------------------------------------------------------------
 constexpr int kRegVec = 16;                  // 4-element groups per thread
 constexpr int kRegRow = 512 * kRegVec * 4;   // 32768: longest row of the largest workgroup
+constexpr int64_t kFilterGrid = 512;  // workgroups of the flagged-rows launch (two 512-thread ones per CU)
 constexpr int kCandPer = 4;                  // LDS candidates per thread
 constexpr int kCandCap = kWave;              // ranked pairwise by one wave
 
@@ -81,7 +82,7 @@ constexpr int kCandCap = kWave;              // ranked pairwise by one wave
 // Rows i0 .. i0 + ni - 1 of every batch entry, one workgroup each.
 // kFilter: only rows with row_flag[row] != 0 run (and none unless *any_flag).
 template <int kThreads, bool kFilter>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void dsa_topk_reg_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFilter ? 2 : 4))) void dsa_topk_reg_kernel(
     DsaTopkParams p, int64_t i0, int64_t ni) {
   constexpr int kRegThreads = kThreads;
   constexpr int kRegWaves = kRegThreads / kWave;
@@ -98,12 +99,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // Rows are dealt round-robin over the XCDs (the hardware's own order):
   // causal rows grow with i, and a contiguous range per XCD would give the
   // last XCD the longest loads.
-  const int64_t lid = blockIdx.x;
+  // One row (lid: its index among the launch's rows).
+  auto run_row = [&](const int64_t lid) __attribute__((always_inline)) {
   const int64_t b = lid / ni, i = i0 + lid % ni;
   const int64_t row = b * p.T + i;
-  if constexpr (kFilter) {
-    if (*p.any_flag == 0u || p.row_flag[row] == 0u) return;
-  }
   const int n = (int)row_len(p, b, i);
   const int k = (int)p.k;
   int32_t* out = p.idx + row * p.k;
@@ -486,6 +485,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // keys) are padded with -1.
   const uint32_t taken = nsel > (uint32_t)k ? (uint32_t)k : nsel;
   for (uint32_t j = tid; j < (uint32_t)k; j += kRegThreads) out[j] = j < taken ? sel[j] : -1;
+  };
+  if constexpr (kFilter) {
+    // A bounded grid walks the rows and runs the flagged ones, so a launch
+    // with no row flagged (the usual case) costs a few hundred workgroups
+    // rather than one per row.
+    if (*p.any_flag == 0u) return;
+    const int64_t total = p.B * ni;
+    for (int64_t lid = blockIdx.x; lid < total; lid += gridDim.x) {
+      if (p.row_flag[(lid / ni) * p.T + i0 + lid % ni] != 0u) {
+        run_row(lid);
+        __syncthreads();  // LDS is reused by the next row
+      }
+    }
+  } else {
+    run_row((int64_t)blockIdx.x);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -751,11 +766,13 @@ size_t dsa_topk_ws_bytes(int64_t B, int64_t T, int64_t S, int64_t k) {
 hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream) {
   const int64_t rows = p.B * p.T;
   if (p.S <= kRegRow) {
+    if (p.row_flag) {  // the flagged rows only, any length: one bounded launch
+      const uint32_t grid = (uint32_t)std::min<int64_t>(rows, kFilterGrid);
+      hipLaunchKernelGGL((dsa_topk_reg_kernel<512, true>), dim3(grid), dim3(512), 0, stream, p, (int64_t)0, p.T);
+      return hipGetLastError();
+    }
     if (p.q_pos) {  // row lengths are on the device: one size fits all
-      if (p.row_flag)
-        hipLaunchKernelGGL((dsa_topk_reg_kernel<512, true>), dim3((uint32_t)rows), dim3(512), 0, stream, p, (int64_t)0, p.T);
-      else
-        hipLaunchKernelGGL((dsa_topk_reg_kernel<512, false>), dim3((uint32_t)rows), dim3(512), 0, stream, p, (int64_t)0, p.T);
+      hipLaunchKernelGGL((dsa_topk_reg_kernel<512, false>), dim3((uint32_t)rows), dim3(512), 0, stream, p, (int64_t)0, p.T);
       return hipGetLastError();
     }
     // Causal rows from position 0: row i holds min((i + 1) / ratio, S)
@@ -768,10 +785,7 @@ hipError_t launch_dsa_topk(const DsaTopkParams& p, hipStream_t stream) {
       const int64_t i1 = kThreads == 512 ? p.T : std::min<int64_t>(p.T, (cap + 1) * p.ratio - 1);
       if (i1 > i0) {
         const dim3 grid((uint32_t)(p.B * (i1 - i0)));
-        if (p.row_flag)
-          hipLaunchKernelGGL((dsa_topk_reg_kernel<kThreads, true>), grid, dim3(kThreads), 0, stream, p, i0, i1 - i0);
-        else
-          hipLaunchKernelGGL((dsa_topk_reg_kernel<kThreads, false>), grid, dim3(kThreads), 0, stream, p, i0, i1 - i0);
+        hipLaunchKernelGGL((dsa_topk_reg_kernel<kThreads, false>), grid, dim3(kThreads), 0, stream, p, i0, i1 - i0);
         i0 = i1;
       }
     };
