@@ -217,8 +217,8 @@ __global__ __launch_bounds__(256) void fused_thresh_kernel(DsaIndexerTopkParams 
   if (lane == 0) f.thresh[row] = V;
 }
 
-// One wave per row.  The row's candidates stay in registers (keys, and
-// positions packed two per register).  Rounds of 256-bin histograms over the
+// One wave per row.  The row's candidates stay in registers (keys and
+// positions, one register each).  Rounds of 256-bin histograms over the
 // key interval [lo, hi] (first [threshold, max]) narrow it to the bin where
 // the count from the top reaches k, until the interval holds exactly the
 // keys still needed or a single key.  Keys above the interval are kept; of

@@ -74,13 +74,14 @@ __device__ __forceinline__ int64_t row_len(const DsaTopkParams& p, int64_t b, in
 // ---------------------------------------------------------------------------
 constexpr int kRegVec = 16;                  // 4-element groups per thread
 constexpr int kRegRow = 512 * kRegVec * 4;   // 32768: longest row of the largest workgroup
-constexpr int64_t kFilterGrid = 512;  // workgroups of the flagged-rows launch (two 512-thread ones per CU)
+constexpr int64_t kFilterGrid = 512;  // workgroups of the flagged-rows launch (one per CU at a time: two rounds)
 constexpr int kCandPer = 4;                  // LDS candidates per thread
 constexpr int kCandCap = kWave;              // ranked pairwise by one wave
 
 
 // Rows i0 .. i0 + ni - 1 of every batch entry, one workgroup each.
-// kFilter: only rows with row_flag[row] != 0 run (and none unless *any_flag).
+// kFilter: only rows with row_flag[row] != 0 run (and none unless *any_flag),
+// on a bounded grid whose workgroups walk the rows.
 template <int kThreads, bool kFilter>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFilter ? 2 : 4))) void dsa_topk_reg_kernel(
     DsaTopkParams p, int64_t i0, int64_t ni) {
