@@ -30,9 +30,10 @@ constexpr int kIdxHi = 4;
 constexpr int kIdxQPerWave = 16;                // queries per wave (4 M-blocks)
 constexpr int kIdxKTile = 64;                   // positions per LDS tile
 constexpr int kIdxTilesPerChunk = 16;  // prefill: positions per workgroup = 16 tiles
-// Decode: 4 tiles (256 positions) per 1-wave workgroup.  At 1M positions and
-// B = 4 that is 16384 workgroups; measured against 1, 2, 8, 16 and 52 tiles
-// (one resident round), 4 is fastest.
+// 1-wave workgroups (T <= 16, except the calls the register-operand decode
+// kernel takes): 4 tiles (256 positions) each.  Measured when the
+// 1M-position, B = 4 decode still ran this kernel (16384 workgroups): 1, 2,
+// 8, 16 and 52 tiles (one resident round) were slower.
 constexpr int kIdxDecodeTiles = 4;
 constexpr int kIdxRowBytes = kIdxDi * 2;                  // 256
 constexpr int kIdxRowChunks = kIdxRowBytes / 16;          // 16
