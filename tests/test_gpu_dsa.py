@@ -312,12 +312,17 @@ def test_dsa_end_to_end_k_ge_context_is_dense():
                                                   (1, 4096, 4096, 2048, None, False), (2, 17, 3000, 100, [2900, 1500], False),
                                                   (1, 3, 1000, 16, [999], False), (2, 9, 2100, 7, [2000, 30], False),
                                                   (1, 700, 700, 64, None, True), (1, 1500, 1500, 1, None, False),
-                                                  (1, 33, 10, 4, None, False)])
+                                                  (1, 33, 10, 4, None, False), (1, 8320, 8320, 2048, None, False),
+                                                  (9, 2, 32768, 2048, [32766 - 3001 * b for b in range(9)], False)])
 @pytest.mark.parametrize("force", [False, True])
 def test_indexer_topk_equals_separate_calls(B, T, S, kk, q_pos, grid, force):
     """dsa_indexer_topk returns exactly dsa_topk(dsa_indexer_scores(...)): several chunks, ragged sizes,
     per-batch q_pos, decode-sized calls, integer-grid inputs (heavy ties), k = 1, S < 16 (no samples);
-    force=True sends every long row through the exact recomputation instead of the candidates."""
+    force=True sends every long row through the exact recomputation instead of the candidates.  The
+    exact recomputation runs on bounded grids that walk the work: T = S = 8320 gives the 4-wave
+    filtered indexer 130 x 9 = 1170 query tile x chunk blocks (more than its 1024 workgroups) and
+    the filtered top-k 6272 flagged rows (more than its 512); B = 9, T = 2, S = 32768 gives the
+    1-wave filtered indexer 9 x 128 = 1152 blocks."""
     sa = require_gpu()
     qi, ki, w = _indexer_inputs(B, T, S, 50 + T, grid=grid)
     tqi, tki, tw = synth.to_torch(qi, "bf16", DEV), synth.to_torch(ki, "bf16", DEV), synth.to_torch(w, "f32", DEV)
