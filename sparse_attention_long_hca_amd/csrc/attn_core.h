@@ -141,6 +141,33 @@ __device__ __forceinline__ void stage_rows_async(char* buf, const T* base_ptr, R
   }
 }
 
+// The same loads with the rows looked up beforehand: row[j] is the row of
+// this lane's load j, i.e. of tile row stage_row_of(j).  A caller whose rows
+// come from LDS can read them well ahead of the loads, so that sending the
+// loads does not wait on that read.
+template <typename T, int D, int kWaves, int kSwz>
+__device__ __forceinline__ int stage_row_of(int j) {
+  using G = AttnGeom<T, D, kSwz>;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  return (int)(((unsigned)(j * kWaves + wave) * kWave + lane) / G::kChunks);
+}
+
+template <typename T, int D, int kWaves, int kSwz>
+__device__ __forceinline__ void stage_rows_pre(char* buf, const T* base_ptr, const int* row) {
+  using G = AttnGeom<T, D, kSwz>;
+  using SG = StageGeom<T, D, kWaves>;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const buffer_rsrc_t rsrc = make_buffer_rsrc(base_ptr);
+#pragma unroll
+  for (int j = 0; j < SG::kPerWave; ++j) {
+    const unsigned P = (unsigned)(j * kWaves + wave) * kWave + lane;
+    const int r = (int)(P / G::kChunks), cp = (int)(P % G::kChunks);
+    const int c = cp ^ G::swz(r);
+    const uint32_t off = (uint32_t)(row[j] < 0 ? 0 : row[j]) * (uint32_t)G::kRowBytes + (uint32_t)c * 16u;
+    buffer_load_lds_16(rsrc, off, buf + (j * kWaves + wave) * kWave * 16);
+  }
+}
+
 template <typename T, int D, typename RowFn>
 __device__ __forceinline__ void stage_async(char* kbuf, char* vbuf, const T* kbase, const T* vbase,
                                             RowFn&& rowfn) {
